@@ -1,0 +1,244 @@
+"""NVFP4 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and the two share no code.
+
+Thin numpy/ctypes wrapper around ``nvfp4_oracle.c``: argument marshalling
+only; every step of the arithmetic lives in the C file, which cites the pages
+("nvfp4-megamoe-kernel": NVFP4-1.1_APPROACH_PART_2.md, NVFP4-1.1_APPROACH.md,
+DEBUG_LOG.md "NVFP4 MoE Pipeline") it follows.
+
+``Oracle(path)`` wraps one build of the library (tests also load deliberately
+mutated builds to show that the pins catch plausible mistakes); the module
+level functions use the default build next to this file.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+DEFAULT_LIB = os.path.join(_HERE, "liborc.so")
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+class MoeProblem(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+        ("E", ctypes.c_int64), ("topk", ctypes.c_int64),
+        ("x", _u16p), ("x_gs_in", _f32p),
+        ("topk_ids", _i32p), ("topk_w", _f32p),
+        ("w1_q", _u8p), ("w1_sf", _u8p), ("w1_gs", _f32p),
+        ("w2_q", _u8p), ("w2_sf", _u8p), ("w2_gs", _f32p),
+        ("a2_gs", ctypes.c_float),
+    ]
+
+
+_SIGNATURES = {
+    "orc_bf16_to_float": (ctypes.c_float, [ctypes.c_uint16]),
+    "orc_double_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
+    "orc_e4m3_value": (ctypes.c_double, [ctypes.c_uint32]),
+    "orc_e4m3_encode": (ctypes.c_uint32, [ctypes.c_float]),
+    "orc_e4m3_encode_array": (None, [_f32p, ctypes.c_int64, _u8p]),
+    "orc_step_to_idx": (ctypes.c_int, [ctypes.c_int]),
+    "orc_e2m1_value": (ctypes.c_double, [ctypes.c_uint32]),
+    "orc_e2m1_nibble": (ctypes.c_uint32, [ctypes.c_float, ctypes.c_int]),
+    "orc_global_scale": (ctypes.c_float, [_u16p, ctypes.c_int64]),
+    "orc_quantize_block": (ctypes.c_uint32, [_f32p, ctypes.c_float, _u8p]),
+    "orc_quantize": (None, [_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float, _u8p, _u8p,
+                            ctypes.c_int]),
+    "orc_dequantize": (None, [_u8p, _u8p, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+                              _f32p]),
+    "orc_dequantize_bf16": (None, [_u8p, _u8p, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+                                   _u16p]),
+    "orc_l1_swiglu_rows": (None, [_u8p, _u8p, ctypes.c_float, ctypes.c_int64, _u8p, _u8p,
+                                  ctypes.c_float, ctypes.c_int64, _i64p, ctypes.c_int64, _f64p,
+                                  _u16p, ctypes.c_int]),
+    "orc_moe_tokens": (ctypes.c_float, [ctypes.POINTER(MoeProblem), _i64p, ctypes.c_int64,
+                                        _f32p, _u16p, _u8p, _u8p, ctypes.c_int]),
+}
+
+
+def _ptr(a, typ):
+    if a is None:
+        return ctypes.cast(None, typ)
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(typ)
+
+
+def default_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class Oracle:
+    """One loaded build of the oracle library."""
+
+    def __init__(self, path=DEFAULT_LIB):
+        if path == DEFAULT_LIB and not os.path.exists(path):
+            from . import build as _b
+            _b.build()
+        self.path = path
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        self.L = L
+
+    # ------------------------------------------------------------ scalars
+    def e4m3_value(self, code):
+        return self.L.orc_e4m3_value(int(code))
+
+    def e4m3_encode(self, v):
+        return int(self.L.orc_e4m3_encode(float(v)))
+
+    def e4m3_encode_array(self, v):
+        v = np.ascontiguousarray(v, np.float32)
+        out = np.zeros(v.shape, np.uint8)
+        self.L.orc_e4m3_encode_array(_ptr(v, _f32p), v.size, _ptr(out, _u8p))
+        return out
+
+    def step_to_idx(self, hs):
+        return int(self.L.orc_step_to_idx(int(hs)))
+
+    def e2m1_value(self, nibble):
+        return self.L.orc_e2m1_value(int(nibble))
+
+    def e2m1_nibble(self, s, negative):
+        return int(self.L.orc_e2m1_nibble(float(s), 1 if negative else 0))
+
+    def double_to_bf16(self, v):
+        return int(self.L.orc_double_to_bf16(float(v)))
+
+    # ------------------------------------------------------------ tensors
+    def global_scale(self, x_bf16):
+        """x_bf16: uint16 array of bf16 bit patterns."""
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        return np.float32(self.L.orc_global_scale(_ptr(x, _u16p), x.size))
+
+    def quantize_block(self, xb, g):
+        xb = np.ascontiguousarray(xb, dtype=np.float32)
+        assert xb.size == 16
+        q = np.zeros(8, np.uint8)
+        sf = self.L.orc_quantize_block(_ptr(xb, _f32p), float(np.float32(g)), _ptr(q, _u8p))
+        return q, int(sf)
+
+    def quantize(self, x_bf16, g, threads=None):
+        """x_bf16: uint16 [M][K] bf16 bit patterns, K % 16 == 0.
+        Returns (q uint8 [M][K/2], sf uint8 [M][K/16])."""
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M, K = x.shape
+        assert K % 16 == 0
+        q = np.zeros((M, K // 2), np.uint8)
+        sf = np.zeros((M, K // 16), np.uint8)
+        if M:
+            self.L.orc_quantize(_ptr(x, _u16p), M, K, float(np.float32(g)), _ptr(q, _u8p),
+                                _ptr(sf, _u8p), threads or default_threads())
+        return q, sf
+
+    def dequantize(self, q, sf, g, out_dtype="f32"):
+        """Returns fp32 values, or bf16 bit patterns (uint16) for "bf16"."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        sf = np.ascontiguousarray(sf, dtype=np.uint8)
+        M, K2 = q.shape
+        K = 2 * K2
+        assert sf.shape == (M, K // 16)
+        if out_dtype == "f32":
+            out = np.zeros((M, K), np.float32)
+            self.L.orc_dequantize(_ptr(q, _u8p), _ptr(sf, _u8p), float(np.float32(g)), M, K,
+                                  _ptr(out, _f32p))
+        else:
+            out = np.zeros((M, K), np.uint16)
+            self.L.orc_dequantize_bf16(_ptr(q, _u8p), _ptr(sf, _u8p), float(np.float32(g)), M,
+                                       K, _ptr(out, _u16p))
+        return out
+
+    def l1_swiglu_rows(self, aq, asf, a_gs, wq, wsf, w_gs, rows, want_h=False, threads=None):
+        """Single-expert L1 GEMM + SwiGLU for a list of activation rows.
+        aq [M][K/2], asf [M][K/16]; wq [N2][K/2], wsf [N2][K/16] (rows
+        interleaved by 8: gate, up).  Returns (c bf16 bits [n][N2/2],
+        h fp64 [n][N2] or None)."""
+        aq = np.ascontiguousarray(aq, np.uint8)
+        asf = np.ascontiguousarray(asf, np.uint8)
+        wq = np.ascontiguousarray(wq, np.uint8)
+        wsf = np.ascontiguousarray(wsf, np.uint8)
+        rows = np.ascontiguousarray(rows, np.int64)
+        K = aq.shape[1] * 2
+        N2 = wq.shape[0]
+        n = rows.size
+        c = np.zeros((n, N2 // 2), np.uint16)
+        h = np.zeros((n, N2), np.float64) if want_h else None
+        if n:
+            self.L.orc_l1_swiglu_rows(_ptr(aq, _u8p), _ptr(asf, _u8p), float(np.float32(a_gs)),
+                                      K, _ptr(wq, _u8p), _ptr(wsf, _u8p),
+                                      float(np.float32(w_gs)), N2, _ptr(rows, _i64p), n,
+                                      _ptr(h, _f64p), _ptr(c, _u16p),
+                                      threads or default_threads())
+        return c, h
+
+    def moe_tokens(self, x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
+                   tokens=None, x_gs=None, want_pairs=False, threads=None):
+        """MoE expert FFN for the listed tokens (all tokens by default).
+        Returns dict: y fp32 [n][H], x_gs; with want_pairs also c [n][k][I]
+        bf16 bits, a2_q [n][k][I/2], a2_sf [n][k][I/16]."""
+        x = np.ascontiguousarray(x, np.uint16)
+        T, H = x.shape
+        topk_ids = np.ascontiguousarray(topk_ids, np.int32)
+        topk_w = np.ascontiguousarray(topk_w, np.float32)
+        k = topk_ids.shape[1]
+        w1_q = np.ascontiguousarray(w1_q, np.uint8)
+        w1_sf = np.ascontiguousarray(w1_sf, np.uint8)
+        w2_q = np.ascontiguousarray(w2_q, np.uint8)
+        w2_sf = np.ascontiguousarray(w2_sf, np.uint8)
+        w1_gs = np.ascontiguousarray(w1_gs, np.float32)
+        w2_gs = np.ascontiguousarray(w2_gs, np.float32)
+        E, N2 = w1_q.shape[0], w1_q.shape[1]
+        I = N2 // 2
+        assert w1_q.shape == (E, 2 * I, H // 2) and w1_sf.shape == (E, 2 * I, H // 16)
+        assert w2_q.shape == (E, H, I // 2) and w2_sf.shape == (E, H, I // 16)
+        if tokens is None:
+            tokens = np.arange(T, dtype=np.int64)
+        tokens = np.ascontiguousarray(tokens, np.int64)
+        n = tokens.size
+        xg = None if x_gs is None else np.array([x_gs], np.float32)
+        pb = MoeProblem(T, H, I, E, k, _ptr(x, _u16p), _ptr(xg, _f32p), _ptr(topk_ids, _i32p),
+                        _ptr(topk_w, _f32p), _ptr(w1_q, _u8p), _ptr(w1_sf, _u8p),
+                        _ptr(w1_gs, _f32p), _ptr(w2_q, _u8p), _ptr(w2_sf, _u8p),
+                        _ptr(w2_gs, _f32p), float(np.float32(a2_gs)))
+        y = np.zeros((n, H), np.float32)
+        c = a2q = a2sf = None
+        if want_pairs:
+            c = np.zeros((n, k, I), np.uint16)
+            a2q = np.zeros((n, k, I // 2), np.uint8)
+            a2sf = np.zeros((n, k, I // 16), np.uint8)
+        used = self.L.orc_moe_tokens(ctypes.byref(pb), _ptr(tokens, _i64p), n, _ptr(y, _f32p),
+                                     _ptr(c, _u16p), _ptr(a2q, _u8p), _ptr(a2sf, _u8p),
+                                     threads or default_threads())
+        out = {"y": y, "x_gs": np.float32(used)}
+        if want_pairs:
+            out.update(c=c, a2_q=a2q, a2_sf=a2sf)
+        return out
+
+
+_default = None
+
+
+def default():
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def __getattr__(name):
+    # module-level access to the default build's methods: oracle.quantize(...)
+    if name.startswith("_"):
+        raise AttributeError(name)
+    return getattr(default(), name)
