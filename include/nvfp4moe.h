@@ -1,0 +1,164 @@
+/*
+ * nvfp4moe.h -- C ABI of libnvfp4moe.so, the MI355X (gfx950) NVFP4 MoE
+ * expert-FFN hot path.
+ *
+ * Source of the operations: the "nvfp4-megamoe-kernel" pages.
+ *   NVFP4-1.1_APPROACH_PART_2.md -- the NVFP4 activation quantizer: 16-element
+ *     blocks, FP8 E4M3 block scale (bias 7, exponent 15 valid, 0x7e = 448 the
+ *     maximum, exp15/mant7 NaN never emitted, subnormal m * 2^-9), E2M1 nibbles
+ *     by two-stage round-to-nearest-even (half steps, then a table), packed two
+ *     per byte; 9 bytes per block; fusing that quantizer into the SwiGLU
+ *     epilogue of the L1 grouped GEMM (fp4 output, scale output, and the L2
+ *     global scale as kernel inputs).
+ *   NVFP4-1.1_APPROACH.md, "Revised approach: Compact SwiGLU output" -- write
+ *     only the SwiGLU columns of the gate/up GEMM.
+ *   DEBUG_LOG.md, "NVFP4 MoE Pipeline" -- quantize activations (fp4, scales,
+ *     global scale) -> L1 GEMM with alpha = activation global scale * weight
+ *     global scale -> SiLU(gate) * up -> quantize -> L2 GEMM with alpha ->
+ *     scatter with routing weights.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
+ *     owned by the caller.  The library never allocates, frees, synchronizes
+ *     with the host or copies to the host.  Scratch memory comes from the
+ *     caller's workspace (`ws`, `ws_bytes`), sized by the matching
+ *     *_workspace_size query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously on it; calls are re-entrant.
+ *   - Global scales are fp32 DECODE multipliers held in device memory
+ *     (a real value = e2m1 * block scale * global scale).
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - NVFP4 tensor layout for a logical [R][K] matrix (K % 16 == 0):
+ *       q  uint8 [R][K/2]   element 2i in the low nibble of byte i, 2i+1 high;
+ *                           nibble = sign(bit 3) | E2M1 index (bits 2..0)
+ *       sf uint8 [R][K/16]  one E4M3 block scale per 16 consecutive elements
+ *   - Alignment: bf16/fp32 tensors 16-byte aligned, q 4-byte aligned,
+ *     workspace 256-byte aligned.
+ *   - Return value: NVFP4_OK (0) or a negative nvfp4_status.  All argument
+ *     checks happen before anything is enqueued, so an error return means
+ *     nothing was launched.  nvfp4_last_error() gives a message (per thread).
+ *   - Data-dependent conditions are not checked: non-finite inputs give
+ *     unspecified bytes; out-of-range expert ids are skipped.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = -1, /* null pointer, bad size or alignment */
+  NVFP4_ERR_UNSUPPORTED = -2, /* shape outside what the kernels handle */
+  NVFP4_ERR_WORKSPACE = -3,   /* workspace smaller than required */
+  NVFP4_ERR_HIP = -4          /* a launch failed (hipGetLastError) */
+} nvfp4_status;
+
+/*
+ * nvfp4_quantize -- bf16 [M][K] -> NVFP4 (NVFP4-1.1_APPROACH_PART_2.md, the
+ * quantizer whose bytes are matched 0/500 against the reference there; the
+ * pages' quantize_nvfp4_gpu(x, global_scale) / stage_activation(x)).
+ *   x      bf16 [M][K], M >= 0, K > 0, K % 16 == 0
+ *   gs_in  nullable.  If NULL the global scale is computed from the tensor:
+ *          g = max|x| / (6 * 448), or 1 for an all-zero (or empty) tensor.
+ *          If non-NULL, *gs_in (device, 1 float, finite, > 0) is used.
+ *   q      uint8 [M][K/2] out;  sf uint8 [M][K/16] out
+ *   gs_out device float out, the g used.  Required when gs_in is NULL;
+ *          nullable otherwise (then nothing is written).
+ *   ws     workspace of nvfp4_quantize_workspace_size(M, K) bytes (0 is
+ *          returned when none is needed; ws may then be NULL).
+ * Per block of 16: bsf = (bmax / 6) * (1/g) rounded to E4M3 (saturating at
+ * 448); r = (1/g) / sfd; each element's nibble comes from x * r by the
+ * two-stage E2M1 rounding.
+ */
+size_t nvfp4_quantize_workspace_size(int64_t M, int64_t K);
+int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, const float *gs_in, uint8_t *q,
+                   uint8_t *sf, float *gs_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * nvfp4_dequantize -- NVFP4 -> real values: x = f32(f32(e2m1 * sfd) * g),
+ * rounded to nearest-even bf16 for bf16 output (FP8 E4M3 decode rules and
+ * E2M1 grid of NVFP4-1.1_APPROACH_PART_2.md).
+ *   q [M][K/2], sf [M][K/16], gs (device, 1 float); M >= 0, K % 16 == 0
+ *   out_dtype: 0 = bf16 (uint16 [M][K]), 1 = fp32 ([M][K])
+ */
+int nvfp4_dequantize(const uint8_t *q, const uint8_t *sf, const float *gs, int64_t M, int64_t K,
+                     int out_dtype, void *out, void *stream);
+
+/*
+ * nvfp4_gemm_swiglu_quant -- one expert's L1 stage (the fused_swiglu kernel
+ * of NVFP4-1.1_APPROACH_PART_2.md in fp4 mode, with the compact output of
+ * NVFP4-1.1_APPROACH.md):
+ *   h[m][n] = (sum_k a[m][k] * w[n][k]) * f32(a_gs * w_gs)     n < N2 = 2I
+ *   c[m][j] = bf16(silu(h[m][gate(j)]) * h[m][up(j)])          j < I
+ *   (c_q, c_sf) = NVFP4 of c's rows with the supplied global scale out_gs.
+ * The weight rows are interleaved by 8: rows 16t..16t+7 are gate rows
+ * 8t..8t+7, rows 16t+8..16t+15 the matching up rows (interleave_l1_weights).
+ *   a_q [M][K/2], a_sf [M][K/16], a_gs (device float)
+ *   w_q [N2][K/2], w_sf [N2][K/16], w_gs (device float)
+ *   out_gs (device float, > 0)
+ *   c_bf16 bf16 [M][I] out, nullable (skips the bf16 store)
+ *   c_q [M][I/2], c_sf [M][I/16] out
+ *   M >= 0; K % 64 == 0; N2 % 32 == 0 (I % 16 == 0)
+ */
+size_t nvfp4_gemm_swiglu_quant_workspace_size(int64_t M, int64_t K, int64_t N2);
+int nvfp4_gemm_swiglu_quant(const uint8_t *a_q, const uint8_t *a_sf, const float *a_gs, int64_t M,
+                            int64_t K, const uint8_t *w_q, const uint8_t *w_sf, const float *w_gs,
+                            int64_t N2, const float *out_gs, uint16_t *c_bf16, uint8_t *c_q,
+                            uint8_t *c_sf, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * MoE expert FFN (DEBUG_LOG.md, "NVFP4 MoE Pipeline"), T tokens, hidden H,
+ * intermediate I, E experts, top-k routing; P = T * k (token, expert) pairs,
+ * pair p = t * k + j.
+ */
+typedef struct {
+  int64_t T, H, I, E, topk;
+  const uint16_t *x;        /* bf16 [T][H] */
+  const float *x_gs_in;     /* nullable: supplied activation global scale */
+  const int32_t *topk_ids;  /* [T][k]; ids outside [0, E) are skipped */
+  const float *topk_w;      /* [T][k] routing weights */
+  const uint8_t *w1_q;      /* [E][2I][H/2]  gate/up rows interleaved by 8 */
+  const uint8_t *w1_sf;     /* [E][2I][H/16] */
+  const float *w1_gs;       /* [E] */
+  const uint8_t *w2_q;      /* [E][H][I/2] */
+  const uint8_t *w2_sf;     /* [E][H][I/16] */
+  const float *w2_gs;       /* [E] */
+  const float *a2_gs;       /* device float: supplied global scale of the L1 output */
+  void *out;                /* [T][H] */
+  int out_dtype;            /* 0 = bf16, 1 = fp32 */
+  /* nullable outputs (pair order p = t*k + j) */
+  uint8_t *xq;              /* [T][H/2] */
+  uint8_t *xsf;             /* [T][H/16] */
+  float *x_gs_out;          /* 1 float: the activation global scale used */
+  uint16_t *l1_c_bf16;      /* [P][I] compact SwiGLU output */
+  uint8_t *l1_q;            /* [P][I/2] */
+  uint8_t *l1_sf;           /* [P][I/16] */
+  int32_t *err_count;       /* 1 int: number of skipped pairs (written, not added) */
+} nvfp4_moe_args;
+
+/*
+ * moe_expert_ffn_nvfp4 -- y[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x[t]) with
+ *   FFN_e(x) = L2_e(NVFP4(bf16(silu(gate) * up)))  and  (gate, up) = L1_e(NVFP4(x))
+ * where L1_e carries alpha1 = x_gs * w1_gs[e], L2_e carries alpha2 =
+ * a2_gs * w2_gs[e], the L1 output is quantized with the supplied a2_gs, and
+ * the k terms of a token are summed in fixed order j = 0..k-1 in fp32.
+ * Requirements: T >= 0, H % 64 == 0, I % 64 == 0, E >= 1, 1 <= k <= 32.
+ */
+size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);
+int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, void *stream);
+
+/* Helpers. */
+const char *nvfp4_status_string(int status);
+const char *nvfp4_last_error(void);
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,241 @@
+"""Python binding of libnvfp4moe.so, the MI355X (gfx950) NVFP4 MoE hot path.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/nvfp4moe.h``.  torch supplies
+device memory (``data_ptr()``) and the current stream; nothing here computes
+on the host.  If the shared library has not been built this module raises on
+import -- there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python quantization_nvfp4_quantize_amd/build.py` (needs hipcc for gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+
+class MoeArgs(ctypes.Structure):
+    """Mirror of nvfp4_moe_args (include/nvfp4moe.h)."""
+    _fields_ = [
+        ("T", _i64), ("H", _i64), ("I", _i64), ("E", _i64), ("topk", _i64),
+        ("x", _vp), ("x_gs_in", _vp), ("topk_ids", _vp), ("topk_w", _vp),
+        ("w1_q", _vp), ("w1_sf", _vp), ("w1_gs", _vp),
+        ("w2_q", _vp), ("w2_sf", _vp), ("w2_gs", _vp),
+        ("a2_gs", _vp), ("out", _vp), ("out_dtype", ctypes.c_int),
+        ("xq", _vp), ("xsf", _vp), ("x_gs_out", _vp),
+        ("l1_c_bf16", _vp), ("l1_q", _vp), ("l1_sf", _vp), ("err_count", _vp),
+    ]
+
+
+_SIG = {
+    "nvfp4_version": (ctypes.c_int, []),
+    "nvfp4_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "nvfp4_last_error": (ctypes.c_char_p, []),
+    "nvfp4_quantize_workspace_size": (_sz, [_i64, _i64]),
+    "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
+    "nvfp4_gemm_swiglu_quant_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_gemm_swiglu_quant": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64,
+                                               _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_nvfp4_workspace_size": (_sz, [ctypes.POINTER(MoeArgs)]),
+    "moe_expert_ffn_nvfp4": (ctypes.c_int, [ctypes.POINTER(MoeArgs), _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTS = tuple(_SIG)
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, where):
+        msg = _lib.nvfp4_last_error().decode() or _lib.nvfp4_status_string(status).decode()
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(status, where):
+    if status != 0:
+        raise Nvfp4Error(status, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_WS = {}
+
+
+def _workspace(nbytes, device):
+    """A cached device workspace of at least nbytes (per device)."""
+    key = torch.device(device).index
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+# ------------------------------------------------------------------ API
+def quantize(x, gs=None, out=None):
+    """bf16 [M][K] -> (q uint8 [M][K/2], sf uint8 [M][K/16], gs float32 [1]).
+
+    gs: optional float32 [1] device tensor (supplied global scale); by default
+    the global scale is max|x| / 2688 computed on the device."""
+    _require(x, torch.bfloat16, "x")
+    _require(gs, torch.float32, "gs")
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        sf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+        gs_out = torch.empty(1, dtype=torch.float32, device=dev) if gs is None else None
+    else:
+        q, sf, gs_out = out
+        if gs is not None:
+            gs_out = None  # the supplied scale is returned as is; nothing to copy
+    wsz = _lib.nvfp4_quantize_workspace_size(M, K)
+    ws = _workspace(wsz, dev)
+    _check(_lib.nvfp4_quantize(_p(x), M, K, _p(gs), _p(q), _p(sf), _p(gs_out), _p(ws), ws.numel(),
+                               _stream(dev)), "nvfp4_quantize")
+    return q, sf, (gs if gs is not None else gs_out)
+
+
+def dequantize(q, sf, gs, out_dtype=torch.bfloat16, out=None):
+    """NVFP4 -> bf16 or float32 [M][K]."""
+    _require(q, torch.uint8, "q")
+    _require(sf, torch.uint8, "sf")
+    _require(gs, torch.float32, "gs")
+    M, K2 = q.shape
+    K = 2 * K2
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=q.device)
+    code = {torch.bfloat16: 0, torch.float32: 1}[out.dtype]
+    _check(_lib.nvfp4_dequantize(_p(q), _p(sf), _p(gs), M, K, code, _p(out), _stream(q.device)),
+           "nvfp4_dequantize")
+    return out
+
+
+def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, out=None):
+    """One expert's L1 stage: returns (c bf16 [M][I] or None, c_q [M][I/2],
+    c_sf [M][I/16]).  Weight rows are gate/up interleaved by 8."""
+    for t, n, d in ((a_q, "a_q", torch.uint8), (a_sf, "a_sf", torch.uint8), (a_gs, "a_gs", torch.float32),
+                    (w_q, "w_q", torch.uint8), (w_sf, "w_sf", torch.uint8), (w_gs, "w_gs", torch.float32),
+                    (out_gs, "out_gs", torch.float32)):
+        _require(t, d, n)
+    M, K = a_q.shape[0], a_q.shape[1] * 2
+    N2 = w_q.shape[0]
+    I = N2 // 2
+    dev = a_q.device
+    if out is None:
+        c = torch.empty((M, I), dtype=torch.bfloat16, device=dev) if want_bf16 else None
+        cq = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
+        csf = torch.empty((M, I // 16), dtype=torch.uint8, device=dev)
+    else:
+        c, cq, csf = out
+    wsz = _lib.nvfp4_gemm_swiglu_quant_workspace_size(M, K, N2)
+    ws = _workspace(wsz, dev)
+    _check(_lib.nvfp4_gemm_swiglu_quant(_p(a_q), _p(a_sf), _p(a_gs), M, K, _p(w_q), _p(w_sf), _p(w_gs),
+                                        N2, _p(out_gs), _p(c), _p(cq), _p(csf), _p(ws), ws.numel(),
+                                        _stream(dev)), "nvfp4_gemm_swiglu_quant")
+    return c, cq, csf
+
+
+def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
+             x_gs=None, xq=None, xsf=None, x_gs_out=None, l1_c=None, l1_q=None, l1_sf=None,
+             err_count=None):
+    """Build the nvfp4_moe_args struct from tensors (keeps no references)."""
+    _require(x, torch.bfloat16, "x")
+    _require(topk_ids, torch.int32, "topk_ids")
+    _require(topk_w, torch.float32, "topk_w")
+    T, H = x.shape
+    E, N2 = w1_q.shape[0], w1_q.shape[1]
+    k = topk_ids.shape[1]
+    code = {torch.bfloat16: 0, torch.float32: 1}[out.dtype]
+    return MoeArgs(T, H, N2 // 2, E, k, _p(x), _p(x_gs), _p(topk_ids), _p(topk_w),
+                   _p(w1_q), _p(w1_sf), _p(w1_gs), _p(w2_q), _p(w2_sf), _p(w2_gs), _p(a2_gs),
+                   _p(out), code, _p(xq), _p(xsf), _p(x_gs_out), _p(l1_c), _p(l1_q), _p(l1_sf),
+                   _p(err_count))
+
+
+def moe_workspace_size(args):
+    return int(_lib.moe_expert_ffn_nvfp4_workspace_size(ctypes.byref(args)))
+
+
+def moe_expert_ffn_raw(args, device, ws=None):
+    """Launch with a prepared MoeArgs (the bench's hot loop uses this)."""
+    need = moe_workspace_size(args)
+    if ws is None:
+        ws = _workspace(need, device)
+    _check(_lib.moe_expert_ffn_nvfp4(ctypes.byref(args), _p(ws), ws.numel(), _stream(device)),
+           "moe_expert_ffn_nvfp4")
+
+
+def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
+                   out_dtype=torch.bfloat16, x_gs=None, debug=False):
+    """NVFP4 MoE expert FFN.  Returns y [T][H] (out_dtype), plus with
+    debug=True a dict of the intermediate outputs (xq, xsf, x_gs, l1_c,
+    l1_q, l1_sf, err_count)."""
+    T, H = x.shape
+    I = w1_q.shape[1] // 2
+    k = topk_ids.shape[1]
+    P = T * k
+    dev = x.device
+    out = torch.empty((T, H), dtype=out_dtype, device=dev)
+    dbg = {}
+    if debug:
+        dbg = dict(xq=torch.empty((T, H // 2), dtype=torch.uint8, device=dev),
+                   xsf=torch.empty((T, H // 16), dtype=torch.uint8, device=dev),
+                   x_gs_out=torch.empty(1, dtype=torch.float32, device=dev),
+                   l1_c=torch.zeros((P, I), dtype=torch.bfloat16, device=dev),
+                   l1_q=torch.zeros((P, I // 2), dtype=torch.uint8, device=dev),
+                   l1_sf=torch.zeros((P, I // 16), dtype=torch.uint8, device=dev),
+                   err_count=torch.zeros(1, dtype=torch.int32, device=dev))
+    args = moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
+                    x_gs=x_gs, **dbg)
+    moe_expert_ffn_raw(args, dev)
+    if debug:
+        return out, dbg
+    return out
+
+
+def quantize_experts(w, gs_out=None):
+    """Quantize a stack of expert weight matrices [E][R][K] (bf16), each with
+    its own dynamic global scale.  Returns (q [E][R][K/2], sf [E][R][K/16],
+    gs float32 [E]).  Model preparation, not part of the hot path."""
+    E, R, K = w.shape
+    dev = w.device
+    q = torch.empty((E, R, K // 2), dtype=torch.uint8, device=dev)
+    sf = torch.empty((E, R, K // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty(E, dtype=torch.float32, device=dev) if gs_out is None else gs_out
+    for e in range(E):
+        quantize(w[e], out=(q[e], sf[e], gs[e:e + 1]))
+    return q, sf, gs

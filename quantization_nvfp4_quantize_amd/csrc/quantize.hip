@@ -1,0 +1,191 @@
+// NVFP4 quantize / dequantize / global-scale kernels for gfx950.
+//
+// The tensor is handled as a flat sequence of 16-element blocks (rows are
+// contiguous and K % 16 == 0, so no block straddles a row and the scale index
+// of block b is simply b).  Each lane loads 16 bytes (8 bf16 = half a block)
+// with one dwordx4 load, so a wavefront reads 1 KiB of consecutive memory per
+// load instruction; the two lanes of a block exchange their partial maxima
+// with one DPP swap.  Each lane stores one dword of nibbles (a wavefront
+// stores 256 consecutive bytes), the even lane of a pair stores the scale.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+
+constexpr int kQThreads = 256;  // threads per workgroup
+constexpr int kQUnroll = 4;     // 8-element chunks per thread (loads in flight)
+constexpr int kQChunksPerWG = kQThreads * kQUnroll;
+constexpr int kAmaxMaxWG = 2048;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load (non-temporal: the data is read once).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------------------ amax
+// Pass 1: per-workgroup max |x| over a grid-stride range of 8-element chunks.
+__global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint4* __restrict__ x,
+                                                                 int64_t n8,
+                                                                 float* __restrict__ partial) {
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kQThreads)
+    m = fmaxf(m, abs_max8(load_nt(x + i)));
+  // wavefront reduction then across the 4 wavefronts
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kQThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kQThreads / 64; ++w) r = fmaxf(r, red[w]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+// Pass 2: one workgroup reduces the partials; g = amax / (6 * 448), or 1 when
+// the tensor is all zero (or empty).
+__global__ __launch_bounds__(1024) void amax_finalize_kernel(const float* __restrict__ partial,
+                                                             int npartial, float* __restrict__ gs) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npartial; i += 1024) m = fmaxf(m, partial[i]);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[16];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < 16; ++w) r = fmaxf(r, red[w]);
+    gs[0] = (r > 0.0f) ? r / 2688.0f : 1.0f;
+  }
+}
+
+__global__ void copy_scalar_kernel(const float* __restrict__ src, float* __restrict__ dst) {
+  if (threadIdx.x == 0) dst[0] = src[0];
+}
+
+// ------------------------------------------------------------------ quantize
+__global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t n8,
+                                                             const float* __restrict__ gs,
+                                                             uint32_t* __restrict__ q,
+                                                             uint8_t* __restrict__ sf) {
+  __shared__ float rtab[128];
+  const float E = 1.0f / gs[0];
+  fill_rtab(rtab, E, threadIdx.x);
+  const int64_t base = (int64_t)blockIdx.x * kQChunksPerWG + threadIdx.x;
+  uint4 w[kQUnroll];
+#pragma unroll
+  for (int u = 0; u < kQUnroll; ++u) {
+    int64_t i = base + u * kQThreads;
+    w[u] = (i < n8) ? load_nt(x + i) : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kQUnroll; ++u) {
+    int64_t i = base + u * kQThreads;  // i and i^1 hold the two halves of block i/2
+    uint32_t code;
+    uint32_t p = quantize_half_block(w[u], E, rtab, &code);
+    if (i < n8) {
+      q[i] = p;
+      if ((i & 1) == 0) sf[i >> 1] = (uint8_t)code;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dequantize
+// Each lane handles 8 elements: one dword of nibbles and its block scale.
+// x = f32(f32(e2m1 * sfd) * g); the gfx950 FP4 -> f32 conversion gives the
+// exact E2M1 values, the product with the E4M3 scale is exact in fp32.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(kQThreads) void dequantize_kernel(const uint32_t* __restrict__ q,
+                                                               const uint8_t* __restrict__ sf,
+                                                               const float* __restrict__ gs,
+                                                               int64_t n8, void* __restrict__ out) {
+  const float g = gs[0];
+  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kQThreads) {
+    uint32_t p = q[i];
+    float sfd = e4m3_decode_signed(sf[i >> 1]);
+    float v[8];
+    auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+    auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
+    auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
+    auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
+    v[0] = (f0[0] * sfd) * g;
+    v[1] = (f0[1] * sfd) * g;
+    v[2] = (f1[0] * sfd) * g;
+    v[3] = (f1[1] * sfd) * g;
+    v[4] = (f2[0] * sfd) * g;
+    v[5] = (f2[1] * sfd) * g;
+    v[6] = (f3[0] * sfd) * g;
+    v[7] = (f3[1] * sfd) * g;
+    if (BF16_OUT) {
+      uint4 o;
+      __bf16 h[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) h[k] = (__bf16)v[k];
+      __builtin_memcpy(&o, h, 16);
+      reinterpret_cast<uint4*>(out)[i] = o;
+    } else {
+      float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+int amax_workgroups(int64_t n8) {
+  int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
+  if (wg < 1) wg = 1;
+  if (wg > kAmaxMaxWG) wg = kAmaxMaxWG;
+  return (int)wg;
+}
+
+size_t global_scale_workspace_bytes() { return kAmaxMaxWG * sizeof(float); }
+
+hipError_t launch_global_scale(const uint16_t* x, int64_t n, float* partial, float* gs,
+                               hipStream_t s) {
+  int64_t n8 = n / 8;
+  int wg = amax_workgroups(n8);
+  amax_partial_kernel<<<wg, kQThreads, 0, s>>>(reinterpret_cast<const uint4*>(x), n8, partial);
+  amax_finalize_kernel<<<1, 1024, 0, s>>>(partial, wg, gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s) {
+  copy_scalar_kernel<<<1, 64, 0, s>>>(src, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_t* q, uint8_t* sf,
+                           hipStream_t s) {
+  int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
+  quantize_kernel<<<(unsigned)wg, kQThreads, 0, s>>>(reinterpret_cast<const uint4*>(x), n8, gs,
+                                                     reinterpret_cast<uint32_t*>(q), sf);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* gs, int64_t n,
+                             bool bf16_out, void* out, hipStream_t s) {
+  int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t wg = (n8 + kQThreads - 1) / kQThreads;
+  if (wg > 65536) wg = 65536;
+  if (bf16_out)
+    dequantize_kernel<true><<<(unsigned)wg, kQThreads, 0, s>>>(
+        reinterpret_cast<const uint32_t*>(q), sf, gs, n8, out);
+  else
+    dequantize_kernel<false><<<(unsigned)wg, kQThreads, 0, s>>>(
+        reinterpret_cast<const uint32_t*>(q), sf, gs, n8, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4
