@@ -115,21 +115,151 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
                             int64_t K, const uint8_t* w_q, const uint8_t* w_sf, const float* w_gs,
                             int64_t N2, const float* out_gs, uint16_t* c_bf16, uint8_t* c_q,
                             uint8_t* c_sf, void* ws, size_t ws_bytes, void* stream) {
-  (void)a_q; (void)a_sf; (void)a_gs; (void)M; (void)K; (void)w_q; (void)w_sf; (void)w_gs;
-  (void)N2; (void)out_gs; (void)c_bf16; (void)c_q; (void)c_sf; (void)ws; (void)ws_bytes;
-  (void)stream;
-  return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: not available in this build");
+  (void)ws;
+  (void)ws_bytes;
+  g_last_error[0] = 0;
+  if (M < 0 || K <= 0 || N2 <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: need M >= 0, K > 0, N2 > 0");
+  if (K % 64 != 0 || N2 % 256 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "nvfp4_gemm_swiglu_quant: need K %% 64 == 0 and N2 %% 256 == 0 (K=%lld N2=%lld)",
+                (long long)K, (long long)N2);
+  if (M > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: M too large");
+  if (M == 0) return NVFP4_OK;
+  if (!a_q || !a_sf || !a_gs || !w_q || !w_sf || !w_gs || !out_gs || !c_q || !c_sf)
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: null pointer");
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(a_sf, 4) || !aligned(w_sf, 4) ||
+      !aligned(c_q, 4) || !aligned(c_bf16, 16))
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: misaligned pointer");
+  const int tiles = (int)((M + nvfp4::gemm_tile_rows() - 1) / nvfp4::gemm_tile_rows());
+  return hip_status(nvfp4::launch_l1(a_q, a_sf, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q,
+                                     c_sf, nullptr, nullptr, tiles, M, nullptr, 1,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "nvfp4_gemm_swiglu_quant");
 }
 
 // ------------------------------------------------------------------ MoE
-size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args* args) {
-  (void)args;
-  return 0;
+namespace {
+
+struct MoeLayout {
+  size_t partial, x_gs, xq, xsf, offsets, perm, tiles, ntiles, err, a2q, a2sf, o, total;
+  int max_tiles;
+};
+
+MoeLayout moe_layout(const nvfp4_moe_args* a) {
+  MoeLayout L;
+  const int64_t T = a->T, H = a->H, I = a->I, E = a->E, P = a->T * a->topk;
+  const int64_t bm = nvfp4::gemm_tile_rows();
+  L.max_tiles = (int)((P + bm - 1) / bm + E);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = off;
+    off = round_up(off + bytes, 256);
+    return r;
+  };
+  L.partial = take(nvfp4::global_scale_workspace_bytes());
+  L.x_gs = take(sizeof(float));
+  L.xq = take((size_t)(T * H / 2));
+  L.xsf = take((size_t)(T * H / 16));
+  L.offsets = take(sizeof(int) * (size_t)(E + 1));
+  L.perm = take(sizeof(int) * (size_t)(P > 0 ? P : 1));
+  L.tiles = take(sizeof(nvfp4::GemmTile) * (size_t)L.max_tiles);
+  L.ntiles = take(sizeof(int));
+  L.err = take(sizeof(int));
+  L.a2q = take((size_t)(P * I / 2));
+  L.a2sf = take((size_t)(P * I / 16));
+  L.o = take(sizeof(float) * (size_t)(P * H));
+  L.total = off;
+  return L;
 }
 
-int moe_expert_ffn_nvfp4(const nvfp4_moe_args* args, void* ws, size_t ws_bytes, void* stream) {
-  (void)args; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: not available in this build");
+int moe_validate(const nvfp4_moe_args* a) {
+  if (!a) return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: args is null");
+  if (a->T < 0 || a->H <= 0 || a->I <= 0 || a->E < 1 || a->topk < 1)
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: need T >= 0, H, I > 0, E >= 1, topk >= 1");
+  if (a->H % 256 != 0 || a->I % 128 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: need H %% 256 == 0 and I %% 128 == 0 (H=%lld I=%lld)",
+                (long long)a->H, (long long)a->I);
+  if (a->E > 512 || a->topk > 32)
+    return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: need E <= 512 and topk <= 32");
+  if (a->T * a->topk > ((int64_t)1 << 30))
+    return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: too many (token, expert) pairs");
+  if (a->out_dtype != 0 && a->out_dtype != 1)
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (a->T > 0 && (!a->x || !a->topk_ids || !a->topk_w || !a->w1_q || !a->w1_sf || !a->w1_gs ||
+                   !a->w2_q || !a->w2_sf || !a->w2_gs || !a->a2_gs || !a->out))
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: null required pointer");
+  if (!aligned(a->x, 16) || !aligned(a->w1_q, 16) || !aligned(a->w2_q, 16) || !aligned(a->out, 16) ||
+      !aligned(a->xq, 16) || !aligned(a->l1_q, 16) || !aligned(a->l1_c_bf16, 16) ||
+      !aligned(a->w1_sf, 4) || !aligned(a->w2_sf, 4) || !aligned(a->xsf, 4) || !aligned(a->l1_sf, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: misaligned pointer");
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args* args) {
+  if (!args || args->T < 0 || args->topk < 1 || args->E < 1) return 0;
+  return moe_layout(args).total;
+}
+
+int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int st = moe_validate(a);
+  if (st) return st;
+  const MoeLayout L = moe_layout(a);
+  if (!ws || ws_bytes < L.total)
+    return fail(NVFP4_ERR_WORKSPACE, "moe_expert_ffn_nvfp4: workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (!aligned(ws, 256)) return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: ws must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const int64_t T = a->T, H = a->H, I = a->I, E = a->E, k = a->topk, P = T * k;
+
+  // a1: activation global scale
+  const float* x_gs;
+  if (a->x_gs_in) {
+    x_gs = a->x_gs_in;
+    if (a->x_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a->x_gs_in, a->x_gs_out, s), "copy x_gs")))
+      return st;
+  } else {
+    float* g = a->x_gs_out ? a->x_gs_out : reinterpret_cast<float*>(w + L.x_gs);
+    if ((st = hip_status(nvfp4::launch_global_scale(a->x, T * H, reinterpret_cast<float*>(w + L.partial), g, s),
+                         "global scale")))
+      return st;
+    x_gs = g;
+  }
+  if (T == 0) return NVFP4_OK;
+  // a2: quantize the activations
+  uint8_t* xq = a->xq ? a->xq : reinterpret_cast<uint8_t*>(w + L.xq);
+  uint8_t* xsf = a->xsf ? a->xsf : reinterpret_cast<uint8_t*>(w + L.xsf);
+  if ((st = hip_status(nvfp4::launch_quantize(a->x, T * H, x_gs, xq, xsf, s), "quantize x"))) return st;
+  // a3: group pairs by expert
+  int* offsets = reinterpret_cast<int*>(w + L.offsets);
+  int* perm = reinterpret_cast<int*>(w + L.perm);
+  nvfp4::GemmTile* tiles = reinterpret_cast<nvfp4::GemmTile*>(w + L.tiles);
+  int* ntiles = reinterpret_cast<int*>(w + L.ntiles);
+  int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
+  if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, nvfp4::gemm_tile_rows(), offsets, perm,
+                                           tiles, ntiles, err, s),
+                       "route")))
+    return st;
+  // a4-a6: L1 GEMM + SwiGLU + compact bf16 + NVFP4
+  uint8_t* a2q = a->l1_q ? a->l1_q : reinterpret_cast<uint8_t*>(w + L.a2q);
+  uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
+  if ((st = hip_status(nvfp4::launch_l1(xq, xsf, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs,
+                                        a->l1_c_bf16, a2q, a2sf, tiles, ntiles, L.max_tiles, 0, perm,
+                                        (int)k, s),
+                       "L1 GEMM")))
+    return st;
+  // a7: L2 GEMM, weighted by the routing weights
+  float* o = reinterpret_cast<float*>(w + L.o);
+  if ((st = hip_status(nvfp4::launch_l2(a2q, a2sf, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o,
+                                        tiles, ntiles, L.max_tiles, perm, s),
+                       "L2 GEMM")))
+    return st;
+  // a8: combine the k rows of every token
+  return hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s),
+                    "combine");
 }
 
 }  // extern "C"

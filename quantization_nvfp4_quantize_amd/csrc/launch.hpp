@@ -7,6 +7,15 @@
 
 namespace nvfp4 {
 
+// One block of up to gemm_tile_rows() rows of one expert in the
+// expert-grouped (sorted) row order.
+struct GemmTile {
+  int expert;
+  int row0;   // first sorted position
+  int nrows;
+  int pad;
+};
+
 // ---- quantize.hip
 size_t global_scale_workspace_bytes();
 // g = max|x| / 2688 (1 if all zero) over n bf16 values (n % 8 == 0) -> gs[0]
@@ -18,5 +27,29 @@ hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_
                            hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* gs, int64_t n,
                              bool bf16_out, void* out, hipStream_t s);
+
+// ---- gemm.hip
+int gemm_tile_rows();
+// L1: c = SwiGLU(alpha * A @ W^T) -> bf16 (optional) and NVFP4 (c_q, c_sf).
+// tiles == nullptr: identity tiling of M rows with expert 0.  perm != nullptr:
+// tile rows are sorted positions, perm gives the pair id, the activation row
+// is pair / topk and the output row is the pair id.
+hipError_t launch_l1(const uint8_t* a_q, const uint8_t* a_sf, const float* a_gs, int64_t K,
+                     const uint8_t* w_q, const uint8_t* w_sf, const float* w_gs, int64_t N2,
+                     const float* out_gs, uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf,
+                     const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
+                     const int* perm, int topk, hipStream_t s);
+// L2: o[pair] = alpha * row_w[pair] * (A[pair] @ W_e^T) in fp32.
+hipError_t launch_l2(const uint8_t* a_q, const uint8_t* a_sf, const float* a_gs, int64_t K,
+                     const uint8_t* w_q, const uint8_t* w_sf, const float* w_gs, int64_t N,
+                     const float* row_w, float* o, const GemmTile* tiles, const int* ntiles,
+                     int max_tiles, const int* perm, hipStream_t s);
+
+// ---- moe.hip
+size_t route_lds_bytes(int E);
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
+                        GemmTile* tiles, int* ntiles, int* err_count, hipStream_t s);
+hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,
+                          bool bf16_out, void* out, hipStream_t s);
 
 }  // namespace nvfp4

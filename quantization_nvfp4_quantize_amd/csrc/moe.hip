@@ -1,0 +1,199 @@
+// Expert grouping and the weighted combine of the MoE expert FFN on gfx950
+// (the gather into expert-grouped rows and the "scatter with routing weights"
+// steps of DEBUG_LOG.md "NVFP4 MoE Pipeline", "nvfp4-megamoe-kernel").
+//
+// route_kernel: one workgroup of 1024 threads (16 waves) turns topk_ids into
+//   offsets[E+1]  exclusive prefix sum of the per-expert pair counts,
+//   perm[P']      sorted position -> pair id, pairs grouped by expert and in
+//                 increasing pair id inside each expert (stable, so the result
+//                 is deterministic),
+//   tiles[]       (expert, first sorted position, rows) for every block of up
+//                 to `tile_rows` rows of one expert, and their count.
+// Each wave owns a contiguous range of pairs.  Pass 1 counts its pairs per
+// expert in LDS; a prefix over (expert, wave) gives every wave its own
+// starting position per expert; pass 2 re-reads the range 64 pairs at a time
+// and ranks equal experts inside the wavefront with ballots on the expert id
+// bits, so positions follow pair order without atomics on the output.
+// Expert ids outside [0, E) are skipped and counted.
+//
+// combine_kernel: y[t] = sum over j of o[t*k + j] in fixed order j = 0..k-1
+// (each o row already carries alpha2 * routing weight).
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
+                                                              int64_t P, int E, int tile_rows,
+                                                              int* __restrict__ offsets,
+                                                              int* __restrict__ perm,
+                                                              GemmTile* __restrict__ tiles,
+                                                              int* __restrict__ ntiles,
+                                                              int* __restrict__ err_count) {
+  extern __shared__ int sm[];
+  int* cnt = sm;                            // [waves][E]: pass-1 counts, then running positions
+  int* total = cnt + kRouteWaves * E;       // [E]
+  int* scan = total + E;                    // [1024] block scan scratch
+  __shared__ int s_err;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+
+  const int64_t p0 = P * wave / kRouteWaves, p1 = P * (wave + 1) / kRouteWaves;
+  int* mycnt = cnt + wave * E;
+  for (int64_t p = p0 + lane; p < p1; p += 64) {
+    int e = ids[p];
+    if (e >= 0 && e < E)
+      atomicAdd(&mycnt[e], 1);
+    else
+      atomicAdd(&s_err, 1);
+  }
+  __syncthreads();
+
+  // per expert: total, and each wave's start relative to the expert start
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = 0;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+    total[e] = run;
+  }
+  __syncthreads();
+
+  // exclusive scans over experts of (pairs, tiles), 1024 experts per chunk
+  int base_pairs = 0, base_tiles = 0;
+  for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
+    const int e = e0 + tid;
+    const int np = (e < E) ? total[e] : 0;
+    const int nt = (np + tile_rows - 1) / tile_rows;
+    // inclusive scan of np and nt packed in one int64-free pass: two scans
+    scan[tid] = np;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+      int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl_p = scan[tid];
+    const int chunk_p = scan[kRouteThreads - 1];
+    __syncthreads();
+    scan[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+      int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl_t = scan[tid];
+    const int chunk_t = scan[kRouteThreads - 1];
+    __syncthreads();
+    if (e < E) {
+      const int start = base_pairs + incl_p - np;
+      offsets[e] = start;
+      for (int w = 0; w < kRouteWaves; ++w) cnt[w * E + e] += start;
+      int tb = base_tiles + incl_t - nt;
+      for (int k = 0; k < nt; ++k) {
+        GemmTile t;
+        t.expert = e;
+        t.row0 = start + k * tile_rows;
+        t.nrows = min(tile_rows, np - k * tile_rows);
+        t.pad = 0;
+        tiles[tb + k] = t;
+      }
+    }
+    base_pairs += chunk_p;
+    base_tiles += chunk_t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    offsets[E] = base_pairs;
+    *ntiles = base_tiles;
+    if (err_count) *err_count = s_err;
+  }
+
+  // pass 2: stable placement, 64 pairs per step, ranks by ballot matching
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t b = p0; b < p1; b += 64) {
+    const int64_t p = b + lane;
+    int e = (p < p1) ? ids[p] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+      match &= ((e >> bit) & 1) ? ones : ~ones;
+    }
+    if (valid) {
+      const int rank = __popcll(match & lt_mask);
+      const int pos = mycnt[e] + rank;
+      perm[pos] = (int)p;
+      if ((match & lt_mask) == 0) mycnt[e] = pos - rank + __popcll(match);
+    }
+  }
+}
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
+                                                      const int32_t* __restrict__ ids, int E,
+                                                      int64_t T, int k, int64_t H,
+                                                      void* __restrict__ out) {
+  const int64_t n4 = H / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * n4;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / n4, c = (i % n4) * 4;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j];
+      if (e < 0 || e >= E) continue;
+      const float4 v = *reinterpret_cast<const float4*>(o + (t * k + j) * H + c);
+      y.x += v.x;
+      y.y += v.y;
+      y.z += v.z;
+      y.w += v.w;
+    }
+    if (BF16_OUT) {
+      __bf16 h[4] = {(__bf16)y.x, (__bf16)y.y, (__bf16)y.z, (__bf16)y.w};
+      uint2 u;
+      __builtin_memcpy(&u, h, 8);
+      reinterpret_cast<uint2*>(out)[(t * H + c) / 4] = u;
+    } else {
+      reinterpret_cast<float4*>(out)[(t * H + c) / 4] = y;
+    }
+  }
+}
+
+size_t route_lds_bytes(int E) { return sizeof(int) * ((size_t)kRouteWaves * E + E + kRouteThreads); }
+
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
+                        GemmTile* tiles, int* ntiles, int* err_count, hipStream_t s) {
+  size_t lds = route_lds_bytes(E);
+  route_kernel<<<1, kRouteThreads, lds, s>>>(ids, P, E, tile_rows, offsets, perm, tiles, ntiles,
+                                             err_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,
+                          bool bf16_out, void* out, hipStream_t s) {
+  int64_t n = T * (H / 4);
+  if (n == 0) return hipSuccess;
+  int64_t wg = (n + 255) / 256;
+  if (wg > 65536) wg = 65536;
+  if (bf16_out)
+    combine_kernel<true><<<(unsigned)wg, 256, 0, s>>>(o, ids, E, T, k, H, out);
+  else
+    combine_kernel<false><<<(unsigned)wg, 256, 0, s>>>(o, ids, E, T, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

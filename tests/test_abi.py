@@ -69,3 +69,50 @@ def test_dequantize_rejects(lib):
     assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 16, 2, FAKE, None) == -1
     assert lib.nvfp4_dequantize(FAKE, FAKE, FAKE, 4, 17, 0, FAKE, None) == -1
     assert lib.nvfp4_dequantize(None, FAKE, FAKE, 4, 16, 0, FAKE, None) == -1
+
+
+def test_gemm_stage_rejects(lib):
+    # K not a multiple of 64, N2 not a multiple of 256, negative M
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, 4, 48, FAKE, FAKE, FAKE, 256, FAKE, None,
+                                       FAKE, FAKE, None, 0, None) == -2
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, 4, 64, FAKE, FAKE, FAKE, 128, FAKE, None,
+                                       FAKE, FAKE, None, 0, None) == -2
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, -1, 64, FAKE, FAKE, FAKE, 256, FAKE, None,
+                                       FAKE, FAKE, None, 0, None) == -1
+    assert lib.nvfp4_gemm_swiglu_quant(None, FAKE, FAKE, 4, 64, FAKE, FAKE, FAKE, 256, FAKE, None,
+                                       FAKE, FAKE, None, 0, None) == -1
+    # M == 0 is a valid no-op
+    assert lib.nvfp4_gemm_swiglu_quant(None, None, None, 0, 64, None, None, None, 256, None, None,
+                                       None, None, None, 0, None) == 0
+
+
+def _moe_args(**kw):
+    import quantization_nvfp4_quantize_amd as q
+    f = dict(T=4, H=256, I=128, E=8, topk=2, x=0x10000, x_gs_in=None, topk_ids=0x10000,
+             topk_w=0x10000, w1_q=0x10000, w1_sf=0x10000, w1_gs=0x10000, w2_q=0x10000,
+             w2_sf=0x10000, w2_gs=0x10000, a2_gs=0x10000, out=0x10000, out_dtype=1)
+    f.update(kw)
+    a = q.MoeArgs()
+    for k, v in f.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_moe_rejects(lib):
+    import quantization_nvfp4_quantize_amd as q
+    by = ctypes.byref
+    assert lib.moe_expert_ffn_nvfp4(None, FAKE, 1 << 30, None) == -1
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(H=200)), FAKE, 1 << 30, None) == -2
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(I=96)), FAKE, 1 << 30, None) == -2
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(E=0)), FAKE, 1 << 30, None) == -1
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(E=513)), FAKE, 1 << 30, None) == -2
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(topk=33)), FAKE, 1 << 30, None) == -2
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(out_dtype=3)), FAKE, 1 << 30, None) == -1
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w2_gs=None)), FAKE, 1 << 30, None) == -1
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(x=0x10008)), FAKE, 1 << 30, None) == -1
+    a = _moe_args()
+    need = lib.moe_expert_ffn_nvfp4_workspace_size(by(a))
+    assert need > 0
+    assert lib.moe_expert_ffn_nvfp4(by(a), FAKE, need - 1, None) == -3
+    assert b"workspace" in lib.nvfp4_last_error()
+    del q

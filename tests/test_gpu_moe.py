@@ -1,0 +1,183 @@
+"""GPU parity of the full NVFP4 MoE expert FFN (moe_expert_ffn_nvfp4) against
+the CPU oracle.
+
+Gates (fp32-output mode): relative Frobenius error <= 1e-3 and cosine >=
+0.9999 against the oracle's fp32 y.  The activation quantization (bytes and
+global scale) is bit-exact; the L1 SwiGLU output meets the same tolerance;
+the fused NVFP4 bytes of the L1 output equal the GPU's standalone quantizer
+on the GPU's own bf16 output.  bf16-output mode is compared with the oracle's
+y rounded to bf16 (reported, bounded loosely: bf16 rounding alone costs
+~1.7e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import cosine, dev_bf16, dev_f32, host, host_bits, rel_fro
+from moe_util import gpu_weights, oracle_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import quantization_nvfp4_quantize_amd as nv
+    return nv
+
+
+def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32):
+    x = dev_bf16(x_bits)
+    ti = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
+    tw = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).cuda()
+    y, dbg = nv.moe_expert_ffn(x, ti, tw, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"],
+                               w["w2gs"], dev_f32(cfg.a2_gs), out_dtype=out_dtype, debug=True)
+    torch.cuda.synchronize()
+    return y, dbg
+
+
+def _check_tokens(nv, orc, cfg, w, x_bits, ids, wts, tokens, y, dbg, device="cuda:0"):
+    ref = oracle_tokens(orc, cfg, x_bits, ids, wts, tokens, device=device)
+    yg = host(y)[tokens]
+    err, cos = rel_fro(yg, ref["y"]), cosine(yg, ref["y"])
+    # activation quantization: bit-exact
+    gx = orc.global_scale(x_bits)
+    assert host(dbg["x_gs_out"])[0] == gx
+    xq, xsf = orc.quantize(x_bits[tokens], gx)
+    assert np.array_equal(host(dbg["xq"])[tokens], xq) and np.array_equal(host(dbg["xsf"])[tokens], xsf)
+    # L1 compact output (pairs of the sampled tokens)
+    k = cfg.topk
+    pairs = (tokens[:, None] * k + np.arange(k)[None, :]).reshape(-1)
+    valid = (ids[tokens] >= 0).reshape(-1) & (ids[tokens] < cfg.E).reshape(-1)
+    cg = synth.bf16_values(host_bits(dbg["l1_c"])[pairs][valid])
+    co = synth.bf16_values(ref["c"].reshape(-1, cfg.I)[valid])
+    c_err, c_cos = rel_fro(cg, co), cosine(cg, co)
+    # fused NVFP4 == standalone quantizer on the same bf16 values
+    cq2, csf2, _ = nv.quantize(dbg["l1_c"], dev_f32(cfg.a2_gs))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dbg["l1_q"])[pairs][valid], host(cq2)[pairs][valid])
+    assert np.array_equal(host(dbg["l1_sf"])[pairs][valid], host(csf2)[pairs][valid])
+    flips = float((host(dbg["l1_sf"])[pairs][valid] != ref["a2_sf"].reshape(-1, cfg.I // 16)[valid]).mean())
+    return err, cos, c_err, c_cos, flips
+
+
+def _gate(err, cos, c_err, c_cos):
+    assert err <= 1e-3 and cos >= 0.9999, (err, cos)
+    assert c_err <= 1e-3 and c_cos >= 0.9999, (c_err, c_cos)
+
+
+def test_moe_tiny_full(nv, orc):
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    print("tiny: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
+    assert host(dbg["err_count"])[0] == 0
+
+
+def test_moe_tiny_bf16_output(nv, orc):
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, _ = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16)
+    ref = oracle_tokens(orc, cfg, x, ids, wts, np.arange(cfg.T), device="cuda:0")
+    yb = synth.bf16_values(host_bits(y))
+    yo = synth.bf16_values(synth.bf16_bits(ref["y"]))
+    err, cos = rel_fro(yb, yo), cosine(yb, yo)
+    print(f"tiny bf16 output vs bf16(oracle): rel_fro {err:.3e} cos {cos:.7f}")
+    assert err <= 5e-3 and cos >= 0.9999
+
+
+def test_moe_invalid_ids_and_duplicates(nv, orc):
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ids = ids.copy()
+    ids[3, 0] = -1
+    ids[7, 1] = cfg.E
+    ids[11, 1] = 99
+    ids[20, 1] = ids[20, 0]  # the same expert twice for one token
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    assert host(dbg["err_count"])[0] == 3
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    _gate(*res[:4])
+
+
+def test_moe_single_expert_topk1(nv, orc):
+    """E = 1, k = 1, w = 1: the MoE reduces to one dense expert FFN."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, E=1, topk=1, name="dense")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids = np.zeros((cfg.T, 1), np.int32)
+    wts = np.ones((cfg.T, 1), np.float32)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    _gate(*res[:4])
+
+
+def test_moe_ragged_token_counts(nv, orc):
+    """Token counts that leave ragged row tiles (and an empty expert)."""
+    import dataclasses
+    for T in (1, 3, 130, 257):
+        cfg = dataclasses.replace(synth.TINY, T=T, name=f"tiny{T}")
+        w = gpu_weights(nv, cfg)
+        x = synth.activations(cfg)
+        ids, wts = synth.routing(cfg)
+        y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+        res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(T), y, dbg)
+        _gate(*res[:4])
+
+
+def test_moe_deterministic(nv):
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    a, _ = _gpu_moe(nv, cfg, w, x, ids, wts)
+    b, _ = _gpu_moe(nv, cfg, w, x, ids, wts)
+    assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
+
+
+def test_moe_decode_config_sampled(nv, orc):
+    """Decode-shaped layer (T128 H7168 I2048 E256 top-8, Zipf routing), full
+    GPU run, oracle on 6 sampled tokens."""
+    cfg = synth.DEC
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    tokens = np.array([0, 1, 37, 64, 126, 127])
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, y, dbg, device="cuda:0")
+    print("decode: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
+
+
+def test_moe_prefill_config_sampled(nv, orc):
+    """Prefill-shaped layer (T16384, uniform top-8), full GPU run, oracle on
+    3 sampled tokens."""
+    cfg = synth.PRE
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    tokens = np.array([0, 8191, 16383])
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, y, dbg, device="cuda:0")
+    print("prefill: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
+
+
+def test_moe_empty(nv):
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg, experts=[])
+    x = torch.zeros((0, cfg.H), dtype=torch.bfloat16, device="cuda:0")
+    ti = torch.zeros((0, cfg.topk), dtype=torch.int32, device="cuda:0")
+    tw = torch.zeros((0, cfg.topk), dtype=torch.float32, device="cuda:0")
+    y = nv.moe_expert_ffn(x, ti, tw, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"], w["w2gs"],
+                          dev_f32(cfg.a2_gs))
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.H)
