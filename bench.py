@@ -1,19 +1,24 @@
 """Benchmark of the NVFP4 MoE expert-FFN hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dec,pre] [--no-cpu]
 
-Prints one JSON line.  Legs:
-  quantize   8192 x 7168 bf16 -> NVFP4 with a supplied global scale (HBM-bound,
-             2.5625 algorithmic bytes per element), inputs rotated over enough
-             copies that the 256 MiB Infinity Cache cannot serve repeats;
-             also the dynamic-scale variant and dequantize.
-  moe        the prefill-shaped MoE layer (T16384 H7168 I2048 E256 top-8) when
-             the grouped GEMMs are available.
-Timing: HIP events on the stream the library launches on (torch's current
-stream), W untimed warmups then K timed steps between synchronizations.
-cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line.  `value` is the prefill-shaped MoE layer (T16384 H7168
+I2048 E256 top-8: activation global scale + quantize, grouping, L1 GEMM with
+fused SwiGLU -> bf16 -> NVFP4, L2 GEMM, weighted combine) in algorithmic
+TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
+  quantize  8192 x 7168 bf16 -> NVFP4, supplied global scale (HBM-bound,
+            2.5625 algorithmic bytes per element), inputs rotated over five
+            copies (> 256 MiB Infinity Cache); also dynamic scale, dequantize
+  expert    single-expert L1 stage M4096 K7168 N 2x2048
+  dec       decode-shaped layer T128 (Zipf routing; weight-streaming bound)
+Timing: W untimed warmups, then K timed steps.  quantize and expert replay a
+HIP graph of K launches between two events (no host gaps); the MoE legs run
+eagerly and the library records HIP events between its stages on the same
+stream, which gives every stage's duration (the L1 GEMM's feeds `roofline`).
+cpu_baseline: the CPU oracle timed on a bounded sample of the prefill layer.
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -26,13 +31,37 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
+STAGES = ["global_scale", "quantize_x", "route", "l1_gemm_swiglu_quant", "l2_gemm", "combine"]
 
 
-def _events(n):
-    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+def _ev():
+    e = torch.cuda.Event(enable_timing=True)
+    e.record()  # materialize the underlying hipEvent_t
+    return e
 
 
+def graph_time(fn, steps, warmup):
+    """Mean ms per call of fn(i) from one replay of a graph of `steps` calls."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = _ev(), _ev()
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+# ------------------------------------------------------------------ quantize
 def bench_quantize(nv, steps, warmup):
     import synth
     M, K = synth.QUANT_SHAPE
@@ -40,42 +69,147 @@ def bench_quantize(nv, steps, warmup):
     dev = torch.device("cuda:0")
     bits = synth.quant_tensor()
     x0 = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    ncopy = 5  # 5 x 117 MB inputs (> 256 MiB Infinity Cache)
+    ncopy = 5
     xs = [x0] + [x0.clone() for _ in range(ncopy - 1)]
     outs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
              torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
              torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(ncopy)]
     _, _, g = nv.quantize(x0)
-    torch.cuda.synchronize()
-
-    def run(fn, nsteps, nwarm):
-        for i in range(nwarm):
-            fn(i % ncopy)
-        torch.cuda.synchronize()
-        ev = _events(nsteps + 1)
-        ev[0].record()
-        for i in range(nsteps):
-            fn(i % ncopy)
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(nsteps)]
-        return float(np.mean(per)), float(np.median(per))
-
-    q_ms, q_med = run(lambda i: nv.quantize(xs[i], g, out=outs[i]), steps, warmup)
-    d_ms, _ = run(lambda i: nv.quantize(xs[i], None, out=outs[i]), steps, warmup)
+    g = g.clone()
     deq = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(ncopy)]
-    dq_ms, _ = run(lambda i: nv.dequantize(outs[i][0], outs[i][1], g, out=deq[i]), steps, warmup)
+    q_ms = graph_time(lambda i: nv.quantize(xs[i % ncopy], g, out=outs[i % ncopy]), steps, warmup)
+    d_ms = graph_time(lambda i: nv.quantize(xs[i % ncopy], None, out=outs[i % ncopy]), steps, warmup)
+    dq_ms = graph_time(lambda i: nv.dequantize(outs[i % ncopy][0], outs[i % ncopy][1], g,
+                                               out=deq[i % ncopy]), steps, warmup)
     qbytes = 2 * n + n // 2 + n // 16
+    return dict(shape=[M, K], algorithmic_bytes=qbytes, quantize_ms=q_ms,
+                quantize_GBps=qbytes / q_ms / 1e6, quantize_frac=qbytes / q_ms / 1e6 / HBM_PEAK_GBS,
+                quantize_dynamic_ms=d_ms,
+                quantize_dynamic_GBps=(qbytes + 2 * n) / d_ms / 1e6,
+                dequantize_ms=dq_ms, dequantize_GBps=(n // 2 + n // 16 + 2 * n) / dq_ms / 1e6)
+
+
+# ------------------------------------------------------------------ MoE
+def moe_weights(nv, cfg):
+    """All experts' NVFP4 weights on the GPU (model preparation, untimed)."""
+    import synth
+    E, I, H = cfg.E, cfg.I, cfg.H
+    dev = torch.device("cuda:0")
+    w1q = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+    w1sf = torch.empty((E, 2 * I, H // 16), dtype=torch.uint8, device=dev)
+    w1gs = torch.empty(E, dtype=torch.float32, device=dev)
+    w2q = torch.empty((E, H, I // 2), dtype=torch.uint8, device=dev)
+    w2sf = torch.empty((E, H, I // 16), dtype=torch.uint8, device=dev)
+    w2gs = torch.empty(E, dtype=torch.float32, device=dev)
+    for e in range(E):
+        a, b = synth.expert_weights(cfg, e, device=dev)
+        nv.quantize(a, out=(w1q[e], w1sf[e], w1gs[e:e + 1]))
+        nv.quantize(b, out=(w2q[e], w2sf[e], w2gs[e:e + 1]))
+    torch.cuda.synchronize()
+    return w1q, w1sf, w1gs, w2q, w2sf, w2gs
+
+
+def bench_moe(nv, cfg, steps, warmup):
+    import synth
+    dev = torch.device("cuda:0")
+    w = moe_weights(nv, cfg)
+    xb = synth.activations(cfg)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids, wts = synth.routing(cfg)
+    ti = torch.from_numpy(ids).to(dev)
+    tw = torch.from_numpy(wts).to(dev)
+    a2 = torch.tensor([cfg.a2_gs], dtype=torch.float32, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    args = nv.moe_args(x, ti, tw, *w, a2, out)
+    ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        nv.moe_expert_ffn_raw(args, dev, ws)
+    torch.cuda.synchronize()
+    evs = [[_ev() for _ in range(7)] for _ in range(steps)]
+    handles = [(ctypes.c_void_p * 7)(*[e.cuda_event for e in row]) for row in evs]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        args.stage_events = ctypes.cast(handles[i], ctypes.POINTER(ctypes.c_void_p))
+        nv.moe_expert_ffn_raw(args, dev, ws)
+    torch.cuda.synchronize()
+    args.stage_events = None
+    total = evs[0][0].elapsed_time(evs[-1][6])
+    ms = total / steps
+    stage_ms = {name: float(np.mean([evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)]))
+                for s, name in enumerate(STAGES)}
+    flops = cfg.flops()
+    used = np.unique(ids[(ids >= 0) & (ids < cfg.E)])
+    wbytes_per_expert = (2 * cfg.I * cfg.H + cfg.H * cfg.I) * (0.5 + 1 / 16)
+    l1_flops = 2.0 * cfg.P * cfg.H * 2 * cfg.I
+    l2_flops = 2.0 * cfg.P * cfg.I * cfg.H
     return dict(
-        shape=[M, K], algorithmic_bytes=qbytes,
-        quantize_ms=q_ms, quantize_ms_median=q_med, quantize_GBps=qbytes / q_ms / 1e6,
-        quantize_dynamic_ms=d_ms, quantize_dynamic_GBps=(qbytes + 2 * n) / d_ms / 1e6,
-        dequantize_ms=dq_ms, dequantize_GBps=(n // 2 + n // 16 + 2 * n) / dq_ms / 1e6,
-    )
+        workload=f"T{cfg.T} H{cfg.H} I{cfg.I} E{cfg.E} top{cfg.topk} ({cfg.routing} routing)",
+        ms_per_step=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
+        experts_touched=int(used.size),
+        weight_GBps=used.size * wbytes_per_expert / ms / 1e6,
+        stage_ms=stage_ms,
+        l1_TFLOPs=l1_flops / stage_ms["l1_gemm_swiglu_quant"] / 1e9,
+        l2_TFLOPs=l2_flops / stage_ms["l2_gemm"] / 1e9,
+        l1_flops=l1_flops, l2_flops=l2_flops,
+    ), (w, x, ids, wts)
 
 
-def cpu_baseline_quantize(target_s=10.0):
-    """Oracle quantize on a bounded sample of the 8192 x 7168 tensor's rows."""
+def bench_expert(nv, steps, warmup):
+    import synth
+    dev = torch.device("cuda:0")
+    M, K, I = synth.EXPERT_SHAPE["M"], synth.EXPERT_SHAPE["K"], synth.EXPERT_SHAPE["I"]
+    xb, w1 = synth.expert_problem()
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    xq, xsf, xg = nv.quantize(x)
+    wq, wsf, wg = nv.quantize(w1.to(dev))
+    og = torch.tensor([synth.EXPERT_A2_GS], dtype=torch.float32, device=dev)
+    outs = (torch.empty((M, I), dtype=torch.bfloat16, device=dev),
+            torch.empty((M, I // 2), dtype=torch.uint8, device=dev),
+            torch.empty((M, I // 16), dtype=torch.uint8, device=dev))
+    ms = graph_time(lambda i: nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, out=outs), steps, warmup)
+    flops = 2.0 * M * K * 2 * I
+    return dict(workload=f"M{M} K{K} N2x{I}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
+                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline_moe(cfg, x_bits, ids, wts, ntok=8):
+    """The oracle on a bounded sample of the prefill layer: ntok tokens (all
+    their top-k pairs), weights of the experts they use quantized by the
+    oracle beforehand (untimed, like the GPU's weight preparation)."""
+    import oracle
+    import synth
+    orc = oracle.default()
+    tokens = np.linspace(0, cfg.T - 1, ntok).astype(np.int64)
+    used = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
+    remap = {e: i for i, e in enumerate(used)}
+    ids_r = np.full_like(ids, -1)
+    for t in tokens:
+        ids_r[t] = [remap[int(e)] for e in ids[t]]
+    n = len(used)
+    W = dict(w1q=np.zeros((n, 2 * cfg.I, cfg.H // 2), np.uint8), w1sf=np.zeros((n, 2 * cfg.I, cfg.H // 16), np.uint8),
+             w1gs=np.zeros(n, np.float32), w2q=np.zeros((n, cfg.H, cfg.I // 2), np.uint8),
+             w2sf=np.zeros((n, cfg.H, cfg.I // 16), np.uint8), w2gs=np.zeros(n, np.float32))
+    for i, e in enumerate(used):
+        a, b = synth.expert_weights(cfg, e, device="cuda:0")
+        a, b = synth.torch_bits(a), synth.torch_bits(b)
+        W["w1gs"][i] = orc.global_scale(a)
+        W["w1q"][i], W["w1sf"][i] = orc.quantize(a, W["w1gs"][i])
+        W["w2gs"][i] = orc.global_scale(b)
+        W["w2q"][i], W["w2sf"][i] = orc.quantize(b, W["w2gs"][i])
+    threads = min(oracle.default_threads(), ntok)
+    t0 = time.time()
+    orc.moe_tokens(x_bits, ids_r, wts, W["w1q"], W["w1sf"], W["w1gs"], W["w2q"], W["w2sf"], W["w2gs"],
+                   cfg.a2_gs, tokens=tokens, threads=threads)
+    dt = time.time() - t0
+    flops = 6.0 * ntok * cfg.topk * cfg.H * cfg.I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{ntok} of the {cfg.T} prefill tokens ({ntok * cfg.topk} pairs, all stages "
+                      f"from activation quantization to the combine) in {dt:.1f} s; "
+                      f"oracle weight quantization of {n} experts excluded"}
+
+
+def cpu_baseline_quantize(target_s=5.0):
     import oracle
     import synth
     orc = oracle.default()
@@ -90,43 +224,65 @@ def cpu_baseline_quantize(target_s=10.0):
         reps += 1
     dt = time.time() - t0
     n = rows * synth.QUANT_SHAPE[1] * reps
-    gbs = (2 * n + n // 2 + n // 16) / dt / 1e9
-    return {"value": gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"quantize of {rows} x {synth.QUANT_SHAPE[1]} rows of the workload, "
-                      f"{reps} repetitions in {dt:.1f} s"}
+    return {"value": (2 * n + n // 2 + n // 16) / dt / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": f"{rows} x {synth.QUANT_SHAPE[1]} rows, {reps} repetitions"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="quant,expert,dec,pre")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
     import quantization_nvfp4_quantize_amd as nv
-
-    qres = bench_quantize(nv, args.steps, args.warmup)
-    cpu = None if args.no_cpu else cpu_baseline_quantize()
-    achieved = qres["quantize_GBps"]
+    import synth
+    legs = set(args.legs.split(","))
+    res = {}
+    if "quant" in legs:
+        res["quantize"] = bench_quantize(nv, args.steps, args.warmup)
+        print("# quantize done", flush=True, file=sys.stderr)
+    if "expert" in legs:
+        res["expert_l1"] = bench_expert(nv, args.steps, args.warmup)
+        print("# expert done", flush=True, file=sys.stderr)
+    if "dec" in legs:
+        res["decode"], _ = bench_moe(nv, synth.DEC, args.steps, args.warmup)
+        print("# decode done", flush=True, file=sys.stderr)
+        torch.cuda.empty_cache()
+    pre = None
+    if "pre" in legs:
+        res["prefill"], pre = bench_moe(nv, synth.PRE, args.steps, args.warmup)
+        print("# prefill done", flush=True, file=sys.stderr)
+    cpu = None
+    if not args.no_cpu and pre is not None:
+        _, xdev, ids, wts = pre
+        xb = synth.activations(synth.PRE)
+        cpu = cpu_baseline_moe(synth.PRE, xb, ids, wts)
+        if "quantize" in res:
+            res["quantize"]["cpu_baseline"] = cpu_baseline_quantize()
+    p = res.get("prefill")
     line = {
         "metric": "MoE expert-FFN TFLOP/s + quantize GB/s, % of MI355X roofline (1 GPU)",
-        "value": achieved,
-        "unit": "GB/s",
+        "value": p["TFLOPs"] if p else None,
+        "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": qres["quantize_ms"],
+        "ms_per_step": p["ms_per_step"] if p else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "standalone NVFP4 quantize 8192x7168 bf16 (supplied global scale)",
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "prefill-shaped NVFP4 MoE layer T16384 H7168 I2048 E256 top-8 "
+                               "(uniform routing), bf16 in/out; plus standalone quantize 8192x7168",
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "roofline": ({"bound": "mfma", "kernel": "l1_gemm_swiglu_quant",
+                      "achieved": p["l1_TFLOPs"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": p["l1_TFLOPs"] / F16_PEAK_TFLOPS, "traffic": None} if p else None),
         "cpu_baseline": cpu,
-        "quantize": qres,
     }
+    line.update(res)
     print(json.dumps(line), flush=True)
 
 

@@ -65,7 +65,9 @@ typedef enum {
  *   x      bf16 [M][K], M >= 0, K > 0, K % 16 == 0
  *   gs_in  nullable.  If NULL the global scale is computed from the tensor:
  *          g = max|x| / (6 * 448), or 1 for an all-zero (or empty) tensor.
- *          If non-NULL, *gs_in (device, 1 float, finite, > 0) is used.
+ *          If non-NULL, *gs_in (device, 1 float) is used.  Supported range
+ *          of g: finite and above 2^-117 (a dynamic g is below that only when
+ *          0 < max|x| < ~1.6e-32); outside it the bytes are unspecified.
  *   q      uint8 [M][K/2] out;  sf uint8 [M][K/16] out
  *   gs_out device float out, the g used.  Required when gs_in is NULL;
  *          nullable otherwise (then nothing is written).
@@ -103,7 +105,7 @@ int nvfp4_dequantize(const uint8_t *q, const uint8_t *sf, const float *gs, int64
  *   out_gs (device float, > 0)
  *   c_bf16 bf16 [M][I] out, nullable (skips the bf16 store)
  *   c_q [M][I/2], c_sf [M][I/16] out
- *   M >= 0; K % 64 == 0; N2 % 32 == 0 (I % 16 == 0)
+ *   M >= 0; K % 64 == 0; N2 % 256 == 0 (else NVFP4_ERR_UNSUPPORTED)
  */
 size_t nvfp4_gemm_swiglu_quant_workspace_size(int64_t M, int64_t K, int64_t N2);
 int nvfp4_gemm_swiglu_quant(const uint8_t *a_q, const uint8_t *a_sf, const float *a_gs, int64_t M,
@@ -139,6 +141,10 @@ typedef struct {
   uint8_t *l1_q;            /* [P][I/2] */
   uint8_t *l1_sf;           /* [P][I/16] */
   int32_t *err_count;       /* 1 int: number of skipped pairs (written, not added) */
+  /* nullable, for profiling: 7 hipEvent_t created by the caller, recorded on
+     `stream` before the global scale, then after the global scale, the
+     activation quantization, the grouping, L1, L2 and the combine. */
+  void *const *stage_events;
 } nvfp4_moe_args;
 
 /*
@@ -147,7 +153,9 @@ typedef struct {
  * where L1_e carries alpha1 = x_gs * w1_gs[e], L2_e carries alpha2 =
  * a2_gs * w2_gs[e], the L1 output is quantized with the supplied a2_gs, and
  * the k terms of a token are summed in fixed order j = 0..k-1 in fp32.
- * Requirements: T >= 0, H % 64 == 0, I % 64 == 0, E >= 1, 1 <= k <= 32.
+ * Requirements: T >= 0; H % 256 == 0, I % 128 == 0, E <= 512, k <= 32 (else
+ * NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.  Workspace: the query's bytes,
+ * which include the fp32 per-pair rows [P][H] of the L2 output.
  */
 size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);
 int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, void *stream);

@@ -36,6 +36,7 @@ class MoeArgs(ctypes.Structure):
         ("a2_gs", _vp), ("out", _vp), ("out_dtype", ctypes.c_int),
         ("xq", _vp), ("xsf", _vp), ("x_gs_out", _vp),
         ("l1_c_bf16", _vp), ("l1_q", _vp), ("l1_sf", _vp), ("err_count", _vp),
+        ("stage_events", ctypes.POINTER(_vp)),
     ]
 
 

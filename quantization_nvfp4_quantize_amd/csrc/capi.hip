@@ -214,6 +214,10 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, k = a->topk, P = T * k;
+  auto mark = [&](int i) {
+    if (a->stage_events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(a->stage_events[i]), s);
+  };
+  mark(0);
 
   // a1: activation global scale
   const float* x_gs;
@@ -228,11 +232,16 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
       return st;
     x_gs = g;
   }
-  if (T == 0) return NVFP4_OK;
+  mark(1);
+  if (T == 0) {
+    for (int i = 2; i < 7; ++i) mark(i);
+    return NVFP4_OK;
+  }
   // a2: quantize the activations
   uint8_t* xq = a->xq ? a->xq : reinterpret_cast<uint8_t*>(w + L.xq);
   uint8_t* xsf = a->xsf ? a->xsf : reinterpret_cast<uint8_t*>(w + L.xsf);
   if ((st = hip_status(nvfp4::launch_quantize(a->x, T * H, x_gs, xq, xsf, s), "quantize x"))) return st;
+  mark(2);
   // a3: group pairs by expert
   int* offsets = reinterpret_cast<int*>(w + L.offsets);
   int* perm = reinterpret_cast<int*>(w + L.perm);
@@ -243,6 +252,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
                                            tiles, ntiles, err, s),
                        "route")))
     return st;
+  mark(3);
   // a4-a6: L1 GEMM + SwiGLU + compact bf16 + NVFP4
   uint8_t* a2q = a->l1_q ? a->l1_q : reinterpret_cast<uint8_t*>(w + L.a2q);
   uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
@@ -251,15 +261,20 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
                                         (int)k, s),
                        "L1 GEMM")))
     return st;
+  mark(4);
   // a7: L2 GEMM, weighted by the routing weights
   float* o = reinterpret_cast<float*>(w + L.o);
   if ((st = hip_status(nvfp4::launch_l2(a2q, a2sf, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o,
                                         tiles, ntiles, L.max_tiles, perm, s),
                        "L2 GEMM")))
     return st;
+  mark(5);
   // a8: combine the k rows of every token
-  return hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s),
-                    "combine");
+  if ((st = hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s),
+                       "combine")))
+    return st;
+  mark(6);
+  return NVFP4_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,69 @@
+"""The C-ABI entry points under HIP graph capture: every replay must equal the
+eager result (no hidden allocation, memset or host synchronization in the
+launch sequence).  Replays are separated by eager work and synchronizations."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import dev_bf16, dev_f32, host
+from moe_util import gpu_weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import quantization_nvfp4_quantize_amd as nv
+    return nv
+
+
+def test_quantize_graph_replays(nv):
+    x = dev_bf16(synth.quant_tensor(512, 7168, seed=8))
+    ref = [host(t) for t in nv.quantize(x)]
+    q = torch.empty_like(torch.from_numpy(ref[0])).cuda()
+    sf = torch.empty_like(torch.from_numpy(ref[1])).cuda()
+    g = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    nv.quantize(x, out=(q, sf, g))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.quantize(x, out=(q, sf, g))
+    for _ in range(4):
+        q.zero_()
+        sf.zero_()
+        g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), ref[0]) and np.array_equal(host(sf), ref[1])
+        assert host(g)[0] == ref[2][0]
+        _ = nv.quantize(x)  # eager work between replays
+
+
+def test_moe_graph_replays(nv):
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = dev_bf16(synth.activations(cfg))
+    ids, wts = synth.routing(cfg)
+    ti = torch.from_numpy(ids).cuda()
+    tw = torch.from_numpy(wts).cuda()
+    a2 = dev_f32(cfg.a2_gs)
+    wl = (w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"], w["w2gs"])
+    ref = host(nv.moe_expert_ffn(x, ti, tw, *wl, a2, out_dtype=torch.float32))
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda:0")
+    args = nv.moe_args(x, ti, tw, *wl, a2, out)
+    ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device="cuda:0")
+    nv.moe_expert_ffn_raw(args, x.device, ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.moe_expert_ffn_raw(args, x.device, ws)
+    for _ in range(4):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+        _ = nv.moe_expert_ffn(x, ti, tw, *wl, a2)
