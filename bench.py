@@ -89,6 +89,17 @@ def bench_quantize(nv, steps, warmup):
                 dequantize_ms=dq_ms, dequantize_GBps=(n // 2 + n // 16 + 2 * n) / dq_ms / 1e6)
 
 
+def bench_copy(steps):
+    """A plain 512 MiB device copy (torch copy_): the reference whose FETCH_SIZE
+    and WRITE_SIZE counters calibrate the HBM traffic of the other kernels."""
+    dev = torch.device("cuda:0")
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    ms = graph_time(lambda i: b.copy_(a), steps, 2)
+    return dict(bytes_each_way=n, ms=ms, GBps=2 * n / ms / 1e6)
+
+
 # ------------------------------------------------------------------ MoE
 def moe_weights(nv, cfg):
     """All experts' NVFP4 weights on the GPU (model preparation, untimed)."""
@@ -244,6 +255,8 @@ def main():
     import synth
     legs = set(args.legs.split(","))
     res = {}
+    if "copy" in legs:
+        res["copy"] = bench_copy(args.steps)
     if "quant" in legs:
         res["quantize"] = bench_quantize(nv, args.steps, args.warmup)
         print("# quantize done", flush=True, file=sys.stderr)

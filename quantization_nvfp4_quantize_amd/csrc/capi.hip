@@ -83,7 +83,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* gs_in, 
     int st = hip_status(nvfp4::launch_copy_scalar(gs_in, gs_out, s), "nvfp4_quantize (copy scale)");
     if (st) return st;
   }
-  return hip_status(nvfp4::launch_quantize(x, n, gs, q, sf, s), "nvfp4_quantize");
+  return hip_status(nvfp4::launch_quantize(x, n, gs, q, sf, nullptr, s), "nvfp4_quantize");
 }
 
 // ------------------------------------------------------------------ dequantize
@@ -105,18 +105,15 @@ int nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* gs, int64
 
 // ------------------------------------------------------------------ GEMM stage
 size_t nvfp4_gemm_swiglu_quant_workspace_size(int64_t M, int64_t K, int64_t N2) {
-  (void)M;
-  (void)K;
   (void)N2;
-  return 0;
+  if (M <= 0 || K <= 0) return 0;
+  return round_up((size_t)(M * K) * sizeof(uint16_t), 256);  // exact f16 copy of the activations
 }
 
 int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float* a_gs, int64_t M,
                             int64_t K, const uint8_t* w_q, const uint8_t* w_sf, const float* w_gs,
                             int64_t N2, const float* out_gs, uint16_t* c_bf16, uint8_t* c_q,
                             uint8_t* c_sf, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   g_last_error[0] = 0;
   if (M < 0 || K <= 0 || N2 <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: need M >= 0, K > 0, N2 > 0");
@@ -131,10 +128,18 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(a_sf, 4) || !aligned(w_sf, 4) ||
       !aligned(c_q, 4) || !aligned(c_bf16, 16))
     return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: misaligned pointer");
+  const size_t need = nvfp4_gemm_swiglu_quant_workspace_size(M, K, N2);
+  if (!ws || ws_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "nvfp4_gemm_swiglu_quant: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(ws, 256)) return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: ws must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint16_t* a_f16 = static_cast<uint16_t*>(ws);
+  int st = hip_status(nvfp4::launch_dequantize_f16(a_q, a_sf, M * K, a_f16, s),
+                      "nvfp4_gemm_swiglu_quant (operand)");
+  if (st) return st;
   const int tiles = (int)((M + nvfp4::gemm_tile_rows() - 1) / nvfp4::gemm_tile_rows());
-  return hip_status(nvfp4::launch_l1(a_q, a_sf, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q,
-                                     c_sf, nullptr, nullptr, tiles, M, nullptr, 1,
-                                     reinterpret_cast<hipStream_t>(stream)),
+  return hip_status(nvfp4::launch_l1(a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf,
+                                     nullptr, nullptr, nullptr, tiles, M, nullptr, 1, s),
                     "nvfp4_gemm_swiglu_quant");
 }
 
@@ -142,7 +147,8 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
 namespace {
 
 struct MoeLayout {
-  size_t partial, x_gs, xq, xsf, offsets, perm, tiles, ntiles, err, a2q, a2sf, o, total;
+  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, a2q, a2sf, a2_f16, o,
+      total;
   int max_tiles;
 };
 
@@ -161,6 +167,7 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.x_gs = take(sizeof(float));
   L.xq = take((size_t)(T * H / 2));
   L.xsf = take((size_t)(T * H / 16));
+  L.x_f16 = take(sizeof(uint16_t) * (size_t)(T * H));
   L.offsets = take(sizeof(int) * (size_t)(E + 1));
   L.perm = take(sizeof(int) * (size_t)(P > 0 ? P : 1));
   L.tiles = take(sizeof(nvfp4::GemmTile) * (size_t)L.max_tiles);
@@ -168,6 +175,7 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.err = take(sizeof(int));
   L.a2q = take((size_t)(P * I / 2));
   L.a2sf = take((size_t)(P * I / 16));
+  L.a2_f16 = take(sizeof(uint16_t) * (size_t)(P * I));
   L.o = take(sizeof(float) * (size_t)(P * H));
   L.total = off;
   return L;
@@ -240,7 +248,9 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   // a2: quantize the activations
   uint8_t* xq = a->xq ? a->xq : reinterpret_cast<uint8_t*>(w + L.xq);
   uint8_t* xsf = a->xsf ? a->xsf : reinterpret_cast<uint8_t*>(w + L.xsf);
-  if ((st = hip_status(nvfp4::launch_quantize(a->x, T * H, x_gs, xq, xsf, s), "quantize x"))) return st;
+  uint16_t* x_f16 = reinterpret_cast<uint16_t*>(w + L.x_f16);
+  if ((st = hip_status(nvfp4::launch_quantize(a->x, T * H, x_gs, xq, xsf, x_f16, s), "quantize x")))
+    return st;
   mark(2);
   // a3: group pairs by expert
   int* offsets = reinterpret_cast<int*>(w + L.offsets);
@@ -256,15 +266,16 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   // a4-a6: L1 GEMM + SwiGLU + compact bf16 + NVFP4
   uint8_t* a2q = a->l1_q ? a->l1_q : reinterpret_cast<uint8_t*>(w + L.a2q);
   uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
-  if ((st = hip_status(nvfp4::launch_l1(xq, xsf, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs,
-                                        a->l1_c_bf16, a2q, a2sf, tiles, ntiles, L.max_tiles, 0, perm,
-                                        (int)k, s),
+  uint16_t* a2_f16 = reinterpret_cast<uint16_t*>(w + L.a2_f16);
+  if ((st = hip_status(nvfp4::launch_l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs,
+                                        a->l1_c_bf16, a2q, a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0,
+                                        perm, (int)k, s),
                        "L1 GEMM")))
     return st;
   mark(4);
   // a7: L2 GEMM, weighted by the routing weights
   float* o = reinterpret_cast<float*>(w + L.o);
-  if ((st = hip_status(nvfp4::launch_l2(a2q, a2sf, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o,
+  if ((st = hip_status(nvfp4::launch_l2(a2_f16, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o,
                                         tiles, ntiles, L.max_tiles, perm, s),
                        "L2 GEMM")))
     return st;

@@ -22,9 +22,13 @@ size_t global_scale_workspace_bytes();
 hipError_t launch_global_scale(const uint16_t* x, int64_t n, float* partial, float* gs,
                                hipStream_t s);
 hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s);
-// n bf16 values (n % 16 == 0) -> q [n/2], sf [n/16] with global scale gs[0]
+// n bf16 values (n % 16 == 0) -> q [n/2], sf [n/16] with global scale gs[0];
+// f16out (nullable) [n]: exact f16 of e2m1 * block scale (the GEMM operand)
 hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_t* q, uint8_t* sf,
-                           hipStream_t s);
+                           uint16_t* f16out, hipStream_t s);
+// NVFP4 (n values) -> exact f16 of e2m1 * block scale
+hipError_t launch_dequantize_f16(const uint8_t* q, const uint8_t* sf, int64_t n, uint16_t* out,
+                                 hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* gs, int64_t n,
                              bool bf16_out, void* out, hipStream_t s);
 
@@ -34,16 +38,18 @@ int gemm_tile_rows();
 // tiles == nullptr: identity tiling of M rows with expert 0.  perm != nullptr:
 // tile rows are sorted positions, perm gives the pair id, the activation row
 // is pair / topk and the output row is the pair id.
-hipError_t launch_l1(const uint8_t* a_q, const uint8_t* a_sf, const float* a_gs, int64_t K,
-                     const uint8_t* w_q, const uint8_t* w_sf, const float* w_gs, int64_t N2,
-                     const float* out_gs, uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf,
+// a_f16: exact f16 activations [rows][K]; c_f16 (nullable): exact f16 of the
+// quantized SwiGLU output (the L2 operand).
+hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
+                     const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
+                     uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
                      const int* perm, int topk, hipStream_t s);
 // L2: o[pair] = alpha * row_w[pair] * (A[pair] @ W_e^T) in fp32.
-hipError_t launch_l2(const uint8_t* a_q, const uint8_t* a_sf, const float* a_gs, int64_t K,
-                     const uint8_t* w_q, const uint8_t* w_sf, const float* w_gs, int64_t N,
-                     const float* row_w, float* o, const GemmTile* tiles, const int* ntiles,
-                     int max_tiles, const int* perm, hipStream_t s);
+hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
+                     const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
+                     const GemmTile* tiles, const int* ntiles, int max_tiles, const int* perm,
+                     hipStream_t s);
 
 // ---- moe.hip
 size_t route_lds_bytes(int E);

@@ -13,6 +13,9 @@
 
 namespace nvfp4 {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -98,6 +101,25 @@ __device__ __forceinline__ uint32_t quantize_half_block(uint4 w, float E, const 
   p = e2m1_pack2<2>(p, bf16_lo(w.z) * r, bf16_hi(w.z) * r);
   p = e2m1_pack2<3>(p, bf16_lo(w.w) * r, bf16_hi(w.w) * r);
   return p;
+}
+
+// 8 E2M1 nibbles (one dword) times one block scale (as an f16 pair) -> the 8
+// exact products as f16 (at most 6 significant bits, within f16's normal
+// range for every E4M3 scale): gfx950 FP4 -> f16 conversion, then one packed
+// f16 multiply per pair.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 sc) {
+  f16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sc;
+  f16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sc;
+  f16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sc;
+  f16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sc;
+  f16x8 v = {e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+  return v;
+}
+
+// An E4M3 scale byte as an f16 pair {s, s} (exact).
+__device__ __forceinline__ f16x2 scale_pair(uint32_t code) {
+  f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(code, 1.0f, false);
+  return f16x2{s[0], s[0]};
 }
 
 // Fill the per-tensor multiplier table rtab[c] = f32(E / decode(c)) (c < 127),

@@ -70,10 +70,14 @@ __global__ void copy_scalar_kernel(const float* __restrict__ src, float* __restr
 }
 
 // ------------------------------------------------------------------ quantize
+// F16OUT: also write the exact f16 of each quantized value (e2m1 * block
+// scale, without the global scale) -- the GEMM operand form of the tensor.
+template <bool F16OUT>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t n8,
                                                              const float* __restrict__ gs,
                                                              uint32_t* __restrict__ q,
-                                                             uint8_t* __restrict__ sf) {
+                                                             uint8_t* __restrict__ sf,
+                                                             f16x8* __restrict__ f16out) {
   __shared__ float rtab[128];
   const float E = 1.0f / gs[0];
   fill_rtab(rtab, E, threadIdx.x);
@@ -93,6 +97,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     if (i < n8) {
       q[i] = p;
       if ((i & 1) == 0) sf[i >> 1] = (uint8_t)code;
+      if (F16OUT) f16out[i] = dequant8(p, scale_pair(code));
     }
   }
 }
@@ -139,6 +144,17 @@ __global__ __launch_bounds__(kQThreads) void dequantize_kernel(const uint32_t* _
   }
 }
 
+// NVFP4 -> exact f16 of e2m1 * block scale (no global scale): the GEMM
+// operand form of an already-quantized tensor.
+__global__ __launch_bounds__(kQThreads) void dequantize_f16_kernel(const uint32_t* __restrict__ q,
+                                                                   const uint8_t* __restrict__ sf,
+                                                                   int64_t n8,
+                                                                   f16x8* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kQThreads)
+    out[i] = dequant8(q[i], scale_pair(sf[i >> 1]));
+}
+
 // ------------------------------------------------------------------ launchers
 int amax_workgroups(int64_t n8) {
   int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
@@ -164,12 +180,28 @@ hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s) {
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_t* q, uint8_t* sf,
-                           hipStream_t s) {
+                           uint16_t* f16out, hipStream_t s) {
   int64_t n8 = n / 8;
   if (n8 == 0) return hipSuccess;
   int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
-  quantize_kernel<<<(unsigned)wg, kQThreads, 0, s>>>(reinterpret_cast<const uint4*>(x), n8, gs,
-                                                     reinterpret_cast<uint32_t*>(q), sf);
+  if (f16out)
+    quantize_kernel<true><<<(unsigned)wg, kQThreads, 0, s>>>(
+        reinterpret_cast<const uint4*>(x), n8, gs, reinterpret_cast<uint32_t*>(q), sf,
+        reinterpret_cast<f16x8*>(f16out));
+  else
+    quantize_kernel<false><<<(unsigned)wg, kQThreads, 0, s>>>(
+        reinterpret_cast<const uint4*>(x), n8, gs, reinterpret_cast<uint32_t*>(q), sf, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_f16(const uint8_t* q, const uint8_t* sf, int64_t n, uint16_t* out,
+                                 hipStream_t s) {
+  int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  int64_t wg = (n8 + kQThreads - 1) / kQThreads;
+  if (wg > 65536) wg = 65536;
+  dequantize_f16_kernel<<<(unsigned)wg, kQThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(q), sf,
+                                                            n8, reinterpret_cast<f16x8*>(out));
   return hipGetLastError();
 }
 
