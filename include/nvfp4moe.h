@@ -105,7 +105,8 @@ int nvfp4_dequantize(const uint8_t *q, const uint8_t *sf, const float *gs, int64
  *   out_gs (device float, > 0)
  *   c_bf16 bf16 [M][I] out, nullable (skips the bf16 store)
  *   c_q [M][I/2], c_sf [M][I/16] out
- *   M >= 0; K % 64 == 0; N2 % 256 == 0 (else NVFP4_ERR_UNSUPPORTED)
+ *   M >= 0; K % 64 == 0; N2 % 256 == 0; M * K * 2 and N2 * K / 2 at most 4 GiB
+ *   (else NVFP4_ERR_UNSUPPORTED)
  */
 size_t nvfp4_gemm_swiglu_quant_workspace_size(int64_t M, int64_t K, int64_t N2);
 int nvfp4_gemm_swiglu_quant(const uint8_t *a_q, const uint8_t *a_sf, const float *a_gs, int64_t M,
@@ -153,8 +154,9 @@ typedef struct {
  * where L1_e carries alpha1 = x_gs * w1_gs[e], L2_e carries alpha2 =
  * a2_gs * w2_gs[e], the L1 output is quantized with the supplied a2_gs, and
  * the k terms of a token are summed in fixed order j = 0..k-1 in fp32.
- * Requirements: T >= 0; H % 256 == 0, I % 128 == 0, E <= 512, k <= 32 (else
- * NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.  Workspace: the query's bytes,
+ * Requirements: T >= 0; H % 256 == 0, I % 128 == 0, E <= 512, k <= 32, and the
+ * f16 GEMM operands T * H * 2, T * k * I * 2 and one expert's I * H nibble
+ * bytes at most 4 GiB each (else NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.  Workspace: the query's bytes,
  * which include the fp32 per-pair rows [P][H] of the L2 output.
  */
 size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);

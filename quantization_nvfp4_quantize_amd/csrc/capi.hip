@@ -12,6 +12,8 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+constexpr int64_t kMaxOperandBytes = (int64_t)1 << 32;
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -122,6 +124,9 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
                 "nvfp4_gemm_swiglu_quant: need K %% 64 == 0 and N2 %% 256 == 0 (K=%lld N2=%lld)",
                 (long long)K, (long long)N2);
   if (M > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: M too large");
+  // the GEMM addresses its operands with 32-bit byte offsets
+  if ((__int128)M * K * 2 > kMaxOperandBytes || (__int128)N2 * (K / 2) > kMaxOperandBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: an operand exceeds 4 GiB");
   if (M == 0) return NVFP4_OK;
   if (!a_q || !a_sf || !a_gs || !w_q || !w_sf || !w_gs || !out_gs || !c_q || !c_sf)
     return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: null pointer");
@@ -192,6 +197,12 @@ int moe_validate(const nvfp4_moe_args* a) {
     return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: need E <= 512 and topk <= 32");
   if (a->T * a->topk > ((int64_t)1 << 30))
     return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: too many (token, expert) pairs");
+  // the GEMMs address the f16 activations and one expert's weights with
+  // 32-bit byte offsets
+  if ((__int128)a->T * a->H * 2 > kMaxOperandBytes ||
+      (__int128)a->T * a->topk * a->I * 2 > kMaxOperandBytes ||
+      (__int128)a->I * a->H > kMaxOperandBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: a GEMM operand exceeds 4 GiB");
   if (a->out_dtype != 0 && a->out_dtype != 1)
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: out_dtype must be 0 (bf16) or 1 (fp32)");
   if (a->T > 0 && (!a->x || !a->topk_ids || !a->topk_w || !a->w1_q || !a->w1_sf || !a->w1_gs ||

@@ -14,24 +14,23 @@
 //     operand (B) is dequantized inside the GEMM; the activation operand (A)
 //     arrives already dequantized to exact f16 -- written once per row by its
 //     producer (the activation quantizer, or the L1 epilogue for the L2 input)
-//     instead of once per (row, N tile) here.  gfx950 executes a wave's VALU
-//     work between that wave's MFMAs, not under them; another wave's VALU does
-//     run under them, but only about 2 VALU instructions per MFMA fit.
-//     Dequantizing B alone costs ~1 per MFMA; dequantizing both would cost ~2.
+//     instead of once per (row, N tile) here.
 //   * A workgroup of 512 threads (8 wave64s, two per SIMD) owns a 256 x 256
 //     output tile; wave w owns rows 128 (w & 1) .. +128 and columns
 //     64 (w >> 1) .. +64 as 4 x 2 MFMA 32x32x16 f16 tiles (128 fp32
 //     accumulators per lane).
-//   * Per K step of 64, thread t moves half a row of each operand: 64 B of A
-//     (f16) and 16 B of B nibbles plus 2 block scales, loaded two steps ahead
-//     into one of two register sets.  The B half is dequantized with the
-//     gfx950 FP4 -> f16 and FP8 -> f16 conversions and one packed f16
-//     multiply per pair.  Both halves are written to the other stage of a
-//     double-buffered LDS tile in 8 pieces placed between the wave's 32 MFMAs
-//     of the step (scheduling fences keep the order); MFMA operand fragments
-//     are read one sub-step ahead.
+//   * K steps of 64.  A goes from global memory straight into LDS
+//     (global_load_lds_dwordx4: 8 lanes fetch one 128 B row, so every request
+//     uses whole cache lines and no VGPRs or LDS write instructions are
+//     spent on it) through three stages, issued two steps ahead.  B moves
+//     through registers: thread t loads half a row of nibbles and its two
+//     block scales two steps ahead, dequantizes them with the gfx950 FP4 -> f16
+//     and FP8 -> f16 conversions and one packed f16 multiply per pair, and
+//     writes the next step's B stage (two stages).  The conversions and the A
+//     loads are spread over the 8 MFMA groups of a step (scheduling fences
+//     keep the order); MFMA operand fragments are read one sub-step ahead.
 //   * LDS rows are 64 f16 = 8 chunks of 16 B, chunk c stored at
-//     c ^ ((row ^ row >> 3) & 7), which keeps the row-wise writes and the MFMA
+//     c ^ ((row ^ row >> 3) & 7), which keeps the B writes and the MFMA
 //     operand reads free of bank conflicts (16-lane groups on 64 banks).
 //   * The K order inside a 64-chunk is permuted identically for A and B (lane
 //     half g reads physical chunk 4g + s at MFMA step s).
@@ -49,56 +48,69 @@
 namespace nvfp4 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 constexpr int kStepK = 64;
 constexpr int kGemmThreads = 512;
-constexpr int kLdsOperand = kTileM * (kStepK / 8);  // f16x8 chunks per operand per stage
+constexpr int kLdsOperand = kTileM * (kStepK / 8);  // 16 B chunks of one operand stage (32 KiB)
+constexpr int kAStages = 3;
+constexpr int kBStages = 2;
+constexpr int kLdsB = kAStages * kLdsOperand;                    // first chunk of B stage 0
+constexpr int kLdsChunks = (kAStages + kBStages) * kLdsOperand;  // 160 KiB
 
-// ------------------------------------------------------------------ operands
-// This thread's share of one K step: half an A row (32 f16) and half a B row
-// (32 nibbles and their 2 block scales).
-struct StepChunk {
-  uint4 a[4];
-  uint4 bq;
-  uint32_t bs;
-};
-
-__device__ __forceinline__ StepChunk load_step(const uint16_t* a_row, const uint8_t* bq_row,
-                                               const uint8_t* bsf_row, int kb, int half) {
-  StepChunk c;
-  const uint4* pa = reinterpret_cast<const uint4*>(a_row + (size_t)kb * 64 + half * 32);
-  c.a[0] = pa[0];
-  c.a[1] = pa[1];
-  c.a[2] = pa[2];
-  c.a[3] = pa[3];
-  c.bq = *reinterpret_cast<const uint4*>(bq_row + (size_t)kb * 32 + half * 16);
-  c.bs = *reinterpret_cast<const uint16_t*>(bsf_row + (size_t)kb * 4 + half * 2);
-  return c;
+// ------------------------------------------------------------------ sync
+// Workgroup barrier over LDS only: waits for this wave's LDS traffic, not for
+// its outstanding global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited on
+  asm volatile("s_barrier" ::: "memory");
 }
 
-// 16-byte chunk c of LDS row `row` lives at c ^ ((row ^ row >> 3) & 7): any
-// 16 consecutive rows reading or writing the same logical chunk hit 16
-// distinct 16-byte bank groups (64 banks), and any 8 consecutive rows hit 8.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 8 + (chunk ^ ((row ^ (row >> 3)) & 7));
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (the counter retires loads in issue order).  The direct-to-LDS loads are
+// not tracked by the compiler for later LDS reads, so their completion is
+// waited for explicitly with this before the barrier that publishes them.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// ------------------------------------------------------------------ operands
+// LDS during the main loop: A0 | A1 | A2 | B0 | B1, 32 KiB each, every stage
+// 256 rows of 64 f16 = 8 chunks of 16 B.
+
+// 16-byte chunk c of LDS row `row` lives at c ^ key(row), key(row) =
+// (row ^ row >> 3) & 7: any 16 consecutive rows reading or writing the same
+// logical chunk hit 16 distinct 16-byte bank groups (64 banks), and any 8
+// consecutive rows hit 8.  key(32 m + r) for r < 32 depends only on r and on
+// the parity of m, so the fragments of a wave's four A tiles (two B tiles)
+// are two base pointers plus compile-time offsets.
+__device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 3)) & 7; }
+
+// This thread's B share of one K step: half a B row (32 nibbles) and its 2
+// block scales.
+struct BChunk {
+  uint4 q;
+  uint32_t s;
+};
+
+// bq / bsf: the workgroup's B nibbles and scales advanced to step kb (wave-
+// uniform); bq_off / bsf_off: this thread's byte offsets (row and half).
+__device__ __forceinline__ BChunk load_b(const uint8_t* bq, const uint8_t* bsf, uint32_t bq_off,
+                                         uint32_t bsf_off) {
+  BChunk c;
+  c.q = *reinterpret_cast<const uint4*>(bq + bq_off);
+  c.s = *reinterpret_cast<const uint16_t*>(bsf + bsf_off);
+  return c;
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
-}
-
-// Write piece k (0..7) of this thread's step share into LDS stage `stage`:
-// pieces 0..3 are A chunks 4 half + k, pieces 4..7 the dequantized B chunks.
-__device__ __forceinline__ void store_piece(f16x8* stage, int row, int half, const StepChunk& c,
-                                            f16x2 s0, f16x2 s1, int k) {
-  if (k < 4) {
-    stage[swz(row, 4 * half + k)] = __builtin_bit_cast(f16x8, c.a[k]);
-  } else {
-    const int j = k - 4;
-    stage[kLdsOperand + swz(row, 4 * half + j)] = dequant8(word_of(c.bq, j), (j < 2) ? s0 : s1);
-  }
 }
 
 __device__ __forceinline__ void scale_pairs(uint32_t bs, f16x2* s0, f16x2* s1) {
@@ -107,35 +119,78 @@ __device__ __forceinline__ void scale_pairs(uint32_t bs, f16x2* s0, f16x2* s1) {
   *s1 = f16x2{s[1], s[1]};
 }
 
-__device__ __forceinline__ void store_step(f16x8* stage, int row, int half, const StepChunk& c) {
-  f16x2 s0, s1;
-  scale_pairs(c.bs, &s0, &s1);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) store_piece(stage, row, half, c, s0, s1, k);
+// Direct-to-LDS load of one 1 KiB piece of an A stage: LDS chunks
+// 64 q .. 64 q + 63 (rows 8 q .. 8 q + 7), lane i writing chunk 64 q + i.
+// a: the A matrix advanced to the step (wave-uniform); off: this lane's byte
+// offset (row 8 q + i / 8, logical chunk (i & 7) ^ key(row)).
+__device__ __forceinline__ void dma_a(f16x8* a_stage, const uint8_t* a, uint32_t off, int q) {
+  __builtin_amdgcn_global_load_lds((const void*)(a + off), (lds_void*)(a_stage + q * 64), 16, 0, 0);
 }
+
+// Per-workgroup operand sources of the main loop.  Byte offsets are 32-bit:
+// the A matrix and one expert's weights stay below 4 GiB.
+struct Operands {
+  const uint8_t* a;    // A matrix (f16 rows of K), wave-uniform
+  uint32_t a_off[4];   // this lane's direct-load sources: tile rows 32 wave + 8 u + lane / 8
+  const uint8_t* bq;   // B nibbles of the tile's expert, wave-uniform
+  const uint8_t* bsf;  // B scales of the tile's expert, wave-uniform
+  uint32_t bq_off;     // this thread's B row and half: row * K / 2 + 16 half
+  uint32_t bsf_off;    // row * K / 16 + 2 half
+};
 
 struct Frags {
   f16x8 a[4], b[2];
 };
 
-#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+// A wave's fragment pointers: the A fragment of MFMA sub-step s for rows
+// wm * 128 + 32 mt + (lane & 31) of A stage st is a[s][mt & 1] + 512 (mt >> 1)
+// + st * kLdsOperand; the B fragment for rows wn * 64 + 32 nt + (lane & 31) of
+// B stage st is b[s][nt] + st * kLdsOperand.  Lane half g = lane >> 5 reads
+// logical chunk 4 g + s (the same K permutation for A and B).
+struct ReadPtrs {
+  const f16x8* a[4][2];
+  const f16x8* b[4][2];
+};
 
-// One K step on LDS stage `cur` (A at cur, B at cur + kLdsOperand): the wave's
-// 32 MFMAs, with this thread's next-step share `n` written into stage `nxt`
-// one piece per 4 MFMAs.  Fragments of MFMA sub-step s + 1 are read while
-// sub-step s runs.
-__device__ __forceinline__ void mma_step_overlapped(const f16x8* cur, f16x8* nxt, int row,
-                                                    int half, const StepChunk& n,
-                                                    f32x16 (&acc)[4][2], int wm, int wn,
-                                                    int lane) {
+__device__ __forceinline__ ReadPtrs read_ptrs(const f16x8* lds, int wm, int wn, int lane) {
+  ReadPtrs rp;
   const int g = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int ra = wm * 128 + 32 * p + r, rb = wn * 64 + 32 * p + r;
+      rp.a[s][p] = lds + ra * 8 + ((4 * g + s) ^ swz_key(ra));
+      rp.b[s][p] = lds + kLdsB + rb * 8 + ((4 * g + s) ^ swz_key(rb));
+    }
+  return rp;
+}
+
+// One K step kb on A stage KA = kb % 3 and B stage KB = kb % 2: the wave's 32
+// MFMAs in 8 groups of 4.  Between the groups the thread writes its B share of
+// step kb + 1 (held in `cn`, four dequantized chunks), refills `cn` with the B
+// share of step kb + 3, and issues its four direct loads of A step kb + 2
+// into A stage (KA + 2) % 3.  Every step issues 6 vector-memory loads, so at
+// its end at most 6 are outstanding once A of step kb + 1 (issued one step
+// earlier) has landed.  Loads past the end re-read the last step; what they
+// write lands in stages that are not read again.
+template <int KA, int KB>
+__device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const int (&pos)[4],
+                                          BChunk& cn, int kb, int last, const Operands& op,
+                                          int wave, f32x16 (&acc)[4][2]) {
+  f16x8* const bw = lds + kLdsB + ((KB + 1) & 1) * kLdsOperand;
+  f16x8* const aw = lds + ((KA + 2) % 3) * kLdsOperand;
+  const uint8_t* const a_next = op.a + (size_t)min(kb + 2, last) * (kStepK * 2);
+  const int kb3 = min(kb + 3, last);
+  constexpr int aoff = KA * kLdsOperand, boff = KB * kLdsOperand;
+  f16x2 s0, s1;
+  scale_pairs(cn.s, &s0, &s1);
+  const uint4 q = cn.q;
   Frags f[2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) f[0].a[mt] = cur[swz(wm * 128 + mt * 32 + r, 4 * g)];
+  for (int mt = 0; mt < 4; ++mt) f[0].a[mt] = rp.a[0][mt & 1][aoff + 512 * (mt >> 1)];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) f[0].b[nt] = cur[kLdsOperand + swz(wn * 64 + nt * 32 + r, 4 * g)];
-  f16x2 s0, s1;
-  scale_pairs(n.bs, &s0, &s1);
+  for (int nt = 0; nt < 2; ++nt) f[0].b[nt] = rp.b[0][nt][boff];
   SCHED_FENCE();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -144,15 +199,14 @@ __device__ __forceinline__ void mma_step_overlapped(const f16x8* cur, f16x8* nxt
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (s < 3) {
-        const int k = 4 * g + s + 1;
         if (h == 0) {
-          G.a[0] = cur[swz(wm * 128 + 0 * 32 + r, k)];
-          G.a[1] = cur[swz(wm * 128 + 1 * 32 + r, k)];
-          G.a[2] = cur[swz(wm * 128 + 2 * 32 + r, k)];
+          G.a[0] = rp.a[s + 1][0][aoff];
+          G.a[1] = rp.a[s + 1][1][aoff];
+          G.a[2] = rp.a[s + 1][0][aoff + 512];
         } else {
-          G.a[3] = cur[swz(wm * 128 + 3 * 32 + r, k)];
-          G.b[0] = cur[kLdsOperand + swz(wn * 64 + 0 * 32 + r, k)];
-          G.b[1] = cur[kLdsOperand + swz(wn * 64 + 1 * 32 + r, k)];
+          G.a[3] = rp.a[s + 1][1][aoff + 512];
+          G.b[0] = rp.b[s + 1][0][boff];
+          G.b[1] = rp.b[s + 1][1][boff];
         }
       }
 #pragma unroll
@@ -162,49 +216,71 @@ __device__ __forceinline__ void mma_step_overlapped(const f16x8* cur, f16x8* nxt
           const int mt = 2 * h + mi;
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[mt], F.b[nt], acc[mt][nt], 0, 0, 0);
         }
-      store_piece(nxt, row, half, n, s0, s1, 2 * s + h);
+      const int slot = 2 * s + h;
+      if (slot < 4) bw[pos[slot]] = dequant8(word_of(q, slot), (slot < 2) ? s0 : s1);
+      if (slot == 3) cn = load_b(op.bq + (size_t)kb3 * 32, op.bsf + (size_t)kb3 * 4, op.bq_off, op.bsf_off);
+      if (slot >= 4) dma_a(aw, a_next, op.a_off[slot - 4], 4 * wave + slot - 4);
       SCHED_FENCE();
     }
   }
+  wait_vmcnt<6>();
+  lds_barrier();
 }
 
-// The whole K loop over nk steps of 64.  a_row: this thread's A row (f16),
-// bq_row / bsf_row: its B row (NVFP4); the thread moves half `half` of each.
-// Global loads run two steps ahead of the MFMAs in two register sets; the
-// loop body is branch-free (loads past the end re-read the last step and the
-// extra pieces land in a stage nobody reads).
-__device__ __forceinline__ void gemm_mainloop(f16x8* lds, const uint16_t* a_row,
-                                              const uint8_t* bq_row, const uint8_t* bsf_row,
-                                              int nk, f32x16 (&acc)[4][2]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The whole K loop over nk steps of 64 (operand sources in `op`; the thread
+// moves half `half` of B row tid / 2).  B register set c[j & 1] holds step j's
+// share from two steps before it is written.  Ends with every load landed and
+// all waves past the last LDS read, so the caller may reuse the LDS.
+__device__ __forceinline__ void gemm_mainloop(f16x8* lds, const Operands& op, int nk,
+                                              f32x16 (&acc)[4][2]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int row = tid >> 1, half = tid & 1;
+  const int last = nk - 1;
+  int pos[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pos[k] = row * 8 + ((4 * half + k) ^ swz_key(row));
+  const int k1 = min(1, last), k2 = min(2, last);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dma_a(lds, op.a, op.a_off[u], 4 * wave + u);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) dma_a(lds + kLdsOperand, op.a + (size_t)k1 * (kStepK * 2), op.a_off[u], 4 * wave + u);
+  BChunk c0 = load_b(op.bq, op.bsf, op.bq_off, op.bsf_off);
+  BChunk c1 = load_b(op.bq + (size_t)k1 * 32, op.bsf + (size_t)k1 * 4, op.bq_off, op.bsf_off);
+  {
+    f16x2 s0, s1;
+    scale_pairs(c0.s, &s0, &s1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds[kLdsB + pos[j]] = dequant8(word_of(c0.q, j), (j < 2) ? s0 : s1);
+  }
+  c0 = load_b(op.bq + (size_t)k2 * 32, op.bsf + (size_t)k2 * 4, op.bq_off, op.bsf_off);
+  const ReadPtrs rp = read_ptrs(lds, wm, wn, lane);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
-  f16x8* S0 = lds;
-  f16x8* S1 = lds + 2 * kLdsOperand;
-  const int last = nk - 1;
-  StepChunk c0 = load_step(a_row, bq_row, bsf_row, 0, half);
-  StepChunk c1 = load_step(a_row, bq_row, bsf_row, min(1, last), half);
-  store_step(S0, row, half, c0);
-  __syncthreads();
+  wait_vmcnt<4>();  // A of steps 0 and 1 landed (only the two B refills may be outstanding)
+  lds_barrier();
+  // whole groups of 6 steps (A stage period 3, B stage period 2), then the
+  // remaining 0..5 steps
   int kb = 0;
-  for (; kb + 1 < nk; kb += 2) {
-    // even step kb: stage S0; the next step's share is in c1; refill c0
-    c0 = load_step(a_row, bq_row, bsf_row, min(kb + 2, last), half);
-    mma_step_overlapped(S0, S1, row, half, c1, acc, wm, wn, lane);
-    __syncthreads();
-    // odd step kb + 1: stage S1; the next step's share is in c0; refill c1
-    c1 = load_step(a_row, bq_row, bsf_row, min(kb + 3, last), half);
-    mma_step_overlapped(S1, S0, row, half, c0, acc, wm, wn, lane);
-    __syncthreads();
+  for (; kb + 6 <= nk; kb += 6) {
+    gemm_step<0, 0>(lds, rp, pos, c1, kb, last, op, wave, acc);
+    gemm_step<1, 1>(lds, rp, pos, c0, kb + 1, last, op, wave, acc);
+    gemm_step<2, 0>(lds, rp, pos, c1, kb + 2, last, op, wave, acc);
+    gemm_step<0, 1>(lds, rp, pos, c0, kb + 3, last, op, wave, acc);
+    gemm_step<1, 0>(lds, rp, pos, c1, kb + 4, last, op, wave, acc);
+    gemm_step<2, 1>(lds, rp, pos, c0, kb + 5, last, op, wave, acc);
   }
-  if (kb < nk) {
-    mma_step_overlapped(S0, S1, row, half, c1, acc, wm, wn, lane);
-    __syncthreads();
-  }
+  const int rem = nk - kb;
+  if (rem > 0) gemm_step<0, 0>(lds, rp, pos, c1, kb, last, op, wave, acc);
+  if (rem > 1) gemm_step<1, 1>(lds, rp, pos, c0, kb + 1, last, op, wave, acc);
+  if (rem > 2) gemm_step<2, 0>(lds, rp, pos, c1, kb + 2, last, op, wave, acc);
+  if (rem > 3) gemm_step<0, 1>(lds, rp, pos, c0, kb + 3, last, op, wave, acc);
+  if (rem > 4) gemm_step<1, 0>(lds, rp, pos, c1, kb + 4, last, op, wave, acc);
+  wait_vmcnt<0>();
+  lds_barrier();
 }
 
 // Accumulator element i of MFMA tile (mt, nt) for this lane sits at row
@@ -262,41 +338,50 @@ __device__ __forceinline__ int l1_weight_row(int nt, int rb) {
 }
 
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
-  __shared__ f16x8 lds[2 * 2 * kLdsOperand];  // 128 KiB: 2 stages x (A, B)
-  __shared__ float rtab[128];
-  __shared__ int out_row[kTileM];
+  __shared__ f16x8 lds[kLdsChunks];
 
   const int ti = blockIdx.x / p.n_ntiles;
   const int nt = blockIdx.x % p.n_ntiles;
   GemmTile t;
   if (!tile_of(p.tiles, p.ntiles, p.M, ti, &t)) return;
 
-  const int tid = threadIdx.x;
-  const int row = tid >> 1;
-  // A row of this thread (padding rows repeat the tile's first row; their
-  // outputs are never stored)
-  const int r = row < t.nrows ? row : 0;
-  int arow, orow;
-  if (p.perm) {
-    const int pair = p.perm[t.row0 + r];
-    arow = pair / p.topk;
-    orow = pair;
-  } else {
-    arow = t.row0 + r;
-    orow = arow;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Output row (pair id, or activation row without routing) and activation
+  // row of tile row r; padding rows repeat the tile's first row and their
+  // outputs are never stored.
+  auto out_row_of = [&](int r) -> int {
+    const int rr = r < t.nrows ? r : 0;
+    return p.perm ? p.perm[t.row0 + rr] : t.row0 + rr;
+  };
+  Operands op;
+  op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int R = 32 * wave + 8 * u + (lane >> 3);
+    const int o = out_row_of(R);
+    const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
+    op.a_off[u] = arow * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
   }
-  if ((tid & 1) == 0) out_row[row] = orow;
-  const int64_t wrow = (int64_t)t.expert * p.N2 + l1_weight_row(nt, row);
+  const int row = tid >> 1;
+  op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);
+  op.bq_off = (uint32_t)l1_weight_row(nt, row) * (uint32_t)(p.K / 2) + 16u * (tid & 1);
+  op.bsf_off = (uint32_t)l1_weight_row(nt, row) * (uint32_t)(p.K / 16) + 2u * (tid & 1);
 
   f32x16 acc[4][2];
-  gemm_mainloop(lds, p.a_f16 + (int64_t)arow * p.K, p.w_q + wrow * (p.K / 2),
-                p.w_sf + wrow * (p.K / 16), (int)(p.K / kStepK), acc);
+  gemm_mainloop(lds, op, (int)(p.K / kStepK), acc);
 
+  // The LDS now holds the epilogue's arrays: the bf16 SwiGLU tile, the
+  // reciprocal table and the output row of every tile row.
+  constexpr int kCStride = 136;  // bf16 per LDS row (128 + 8 padding)
+  constexpr int kCTileChunks = kTileM * kCStride * 2 / 16;
+  uint16_t* ctile = reinterpret_cast<uint16_t*>(lds);
+  float* rtab = reinterpret_cast<float*>(lds + kCTileChunks);
+  int* out_row = reinterpret_cast<int*>(lds + kCTileChunks + 32);
+  if (tid < kTileM) out_row[tid] = out_row_of(tid);
   // ---- epilogue: alpha, SwiGLU, bf16 tile in LDS
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  const int lane = tid & 63, wave = tid >> 6, wm = wave & 1, wn = wave >> 1;
-  constexpr int kCStride = 136;  // bf16 per LDS row (128 + 8 padding)
-  uint16_t* ctile = reinterpret_cast<uint16_t*>(lds);
+  const int wm = wave & 1, wn = wave >> 1;
   const int col = 32 * wn + (lane & 31);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -351,23 +436,34 @@ struct L2Params {
 };
 
 __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
-  __shared__ f16x8 lds[2 * 2 * kLdsOperand];
-  __shared__ int out_row[kTileM];
+  __shared__ f16x8 lds[kLdsChunks];
   const int ti = blockIdx.x / p.n_ntiles;
   const int nt = blockIdx.x % p.n_ntiles;
   if (ti >= *p.ntiles) return;
   const GemmTile t = p.tiles[ti];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // pair id of tile row r (padding rows repeat the first row, never stored)
+  auto pair_of = [&](int r) -> int { return p.perm[t.row0 + (r < t.nrows ? r : 0)]; };
+  Operands op;
+  op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int R = 32 * wave + 8 * u + (lane >> 3);
+    op.a_off[u] = (uint32_t)pair_of(R) * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
+  }
   const int row = tid >> 1;
-  const int r = row < t.nrows ? row : 0;
-  const int pair = p.perm[t.row0 + r];
-  if ((tid & 1) == 0) out_row[row] = pair;
-  const int64_t wrow = (int64_t)t.expert * p.N + (int64_t)nt * kTileN + row;
+  const uint32_t brow = (uint32_t)(nt * kTileN + row);
+  op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
+  op.bq_off = brow * (uint32_t)(p.K / 2) + 16u * (tid & 1);
+  op.bsf_off = brow * (uint32_t)(p.K / 16) + 2u * (tid & 1);
   f32x16 acc[4][2];
-  gemm_mainloop(lds, p.a_f16 + (int64_t)pair * p.K, p.w_q + wrow * (p.K / 2),
-                p.w_sf + wrow * (p.K / 16), (int)(p.K / kStepK), acc);
+  gemm_mainloop(lds, op, (int)(p.K / kStepK), acc);
+  int* out_row = reinterpret_cast<int*>(lds);
+  if (tid < kTileM) out_row[tid] = pair_of(tid);
+  __syncthreads();
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  const int lane = tid & 63, wave = tid >> 6, wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll

@@ -81,6 +81,10 @@ def test_gemm_stage_rejects(lib):
                                        FAKE, FAKE, None, 0, None) == -1
     assert lib.nvfp4_gemm_swiglu_quant(None, FAKE, FAKE, 4, 64, FAKE, FAKE, FAKE, 256, FAKE, None,
                                        FAKE, FAKE, None, 0, None) == -1
+    # the f16 operand (M * K * 2 bytes) above 4 GiB
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, (1 << 25) + 1, 64, FAKE, FAKE, FAKE, 256,
+                                       FAKE, None, FAKE, FAKE, None, 0, None) == -2
+    assert b"4 GiB" in lib.nvfp4_last_error()
     # M == 0 is a valid no-op
     assert lib.nvfp4_gemm_swiglu_quant(None, None, None, 0, 64, None, None, None, 256, None, None,
                                        None, None, None, 0, None) == 0
@@ -110,6 +114,11 @@ def test_moe_rejects(lib):
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(out_dtype=3)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w2_gs=None)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(x=0x10008)), FAKE, 1 << 30, None) == -1
+    # f16 operands above 4 GiB: x (T * H * 2) and the L2 input (T * k * I * 2)
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(T=1 << 19, H=1 << 13)), FAKE, 1 << 30, None) == -2
+    assert b"4 GiB" in lib.nvfp4_last_error()
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(T=1 << 17, topk=8, I=1 << 12)), FAKE, 1 << 30,
+                                    None) == -2
     a = _moe_args()
     need = lib.moe_expert_ffn_nvfp4_workspace_size(by(a))
     assert need > 0
