@@ -16,9 +16,16 @@
 //     producer (the activation quantizer, or the L1 epilogue for the L2 input)
 //     instead of once per (row, N tile) here.
 //   * A workgroup of 512 threads (8 wave64s, two per SIMD) owns a 256 x 256
-//     output tile; wave w owns rows 128 (w & 1) .. +128 and columns
-//     64 (w >> 1) .. +64 as 4 x 2 MFMA 32x32x16 f16 tiles (128 fp32
-//     accumulators per lane).
+//     output tile; wave w owns rows 128 (w >> 2) .. +128 and columns
+//     64 (w & 3) .. +64 as 4 x 2 MFMA 32x32x16 f16 tiles (128 fp32
+//     accumulators per lane).  The two waves of a SIMD (w, w + 4) hold
+//     different row halves, and MFMAs of 32-row groups that lie wholly past
+//     the tile's valid rows are skipped, so a partly filled tile (an expert's
+//     last rows, a decode batch) costs MFMA time in proportion to its rows on
+//     every SIMD.
+//   * Workgroups are dealt to the 8 XCDs in turn; work items are assigned so
+//     that each XCD takes one contiguous range of (M tile, N tile) items,
+//     M-tile-major, and the N tiles of an M tile share one XCD's L2.
 //   * K steps of 64.  A goes from global memory straight into LDS
 //     (global_load_lds_dwordx4: 8 lanes fetch one 128 B row, so every request
 //     uses whole cache lines and no VGPRs or LDS write instructions are
@@ -79,6 +86,29 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Tile rows and columns of wave w: rows 128 wave_m .. +128, columns
+// 64 wave_n .. +64 (waves w and w + 4 share a SIMD).
+__device__ __forceinline__ int wave_m(int wave) { return wave >> 2; }
+__device__ __forceinline__ int wave_n(int wave) { return wave & 3; }
+
+// Active 32-row MFMA groups of a wave whose rows start at 128 wm in a tile
+// of nrows valid rows (0..4).
+__device__ __forceinline__ int active_groups(int nrows, int wm) {
+  return min(4, max(0, (nrows - 128 * wm + 31) >> 5));
+}
+
+// Work item of this workgroup among W items.  Workgroup b runs on XCD b % 8;
+// XCD x takes the contiguous items x q + min(x, r) .. (q = W / 8, r = W % 8,
+// q + 1 items on the first r XCDs), so the workgroups running together on
+// one XCD work on neighbouring items.  False for workgroups beyond W.
+__device__ __forceinline__ bool work_item(int W, int* item) {
+  const int b = blockIdx.x, x = b & 7, j = b >> 3;
+  const int q = W >> 3, r = W & 7;
+  if (j >= q + (x < r ? 1 : 0)) return false;
+  *item = x * q + min(x, r) + j;
+  return true;
+}
 
 // ------------------------------------------------------------------ operands
 // LDS during the main loop: A0 | A1 | A2 | B0 | B1, 32 KiB each, every stage
@@ -167,17 +197,17 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const f16x8* lds, int wm, int wn, 
 }
 
 // One K step kb on A stage KA = kb % 3 and B stage KB = kb % 2: the wave's 32
-// MFMAs in 8 groups of 4.  Between the groups the thread writes its B share of
+// MFMAs in 8 groups of 4 (those of row groups mt >= nmt skipped).  Between the groups the thread writes its B share of
 // step kb + 1 (held in `cn`, four dequantized chunks), refills `cn` with the B
 // share of step kb + 3, and issues its four direct loads of A step kb + 2
 // into A stage (KA + 2) % 3.  Every step issues 6 vector-memory loads, so at
 // its end at most 6 are outstanding once A of step kb + 1 (issued one step
 // earlier) has landed.  Loads past the end re-read the last step; what they
 // write lands in stages that are not read again.
-template <int KA, int KB>
+template <int KA, int KB, bool FULL>
 __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const int (&pos)[4],
                                           BChunk& cn, int kb, int last, const Operands& op,
-                                          int wave, f32x16 (&acc)[4][2]) {
+                                          int wave, int nmt, f32x16 (&acc)[4][2]) {
   f16x8* const bw = lds + kLdsB + ((KB + 1) & 1) * kLdsOperand;
   f16x8* const aw = lds + ((KA + 2) % 3) * kLdsOperand;
   const uint8_t* const a_next = op.a + (size_t)min(kb + 2, last) * (kStepK * 2);
@@ -186,11 +216,17 @@ __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const 
   f16x2 s0, s1;
   scale_pairs(cn.s, &s0, &s1);
   const uint4 q = cn.q;
+  // A partial wave (FULL false) reads and multiplies only its row groups
+  // mt < nmt; the reads of a full wave stay unconditional, which keeps the
+  // compiler's LDS wait counts exact.
+  auto on = [&](int mt) { return FULL || mt < nmt; };
   Frags f[2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) f[0].a[mt] = rp.a[0][mt & 1][aoff + 512 * (mt >> 1)];
+  for (int mt = 0; mt < 4; ++mt)
+    if (on(mt)) f[0].a[mt] = rp.a[0][mt & 1][aoff + 512 * (mt >> 1)];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) f[0].b[nt] = rp.b[0][nt][boff];
+  for (int nt = 0; nt < 2; ++nt)
+    if (on(0)) f[0].b[nt] = rp.b[0][nt][boff];
   SCHED_FENCE();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -200,22 +236,24 @@ __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const 
     for (int h = 0; h < 2; ++h) {
       if (s < 3) {
         if (h == 0) {
-          G.a[0] = rp.a[s + 1][0][aoff];
-          G.a[1] = rp.a[s + 1][1][aoff];
-          G.a[2] = rp.a[s + 1][0][aoff + 512];
+          if (on(0)) G.a[0] = rp.a[s + 1][0][aoff];
+          if (on(1)) G.a[1] = rp.a[s + 1][1][aoff];
+          if (on(2)) G.a[2] = rp.a[s + 1][0][aoff + 512];
         } else {
-          G.a[3] = rp.a[s + 1][1][aoff + 512];
-          G.b[0] = rp.b[s + 1][0][boff];
-          G.b[1] = rp.b[s + 1][1][boff];
+          if (on(3)) G.a[3] = rp.a[s + 1][1][aoff + 512];
+          if (on(0)) G.b[0] = rp.b[s + 1][0][boff];
+          if (on(0)) G.b[1] = rp.b[s + 1][1][boff];
         }
       }
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 2; ++mi) {
+        const int mt = 2 * h + mi;
+        if (on(mt)) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int mt = 2 * h + mi;
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[mt], F.b[nt], acc[mt][nt], 0, 0, 0);
+          for (int nt = 0; nt < 2; ++nt)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[mt], F.b[nt], acc[mt][nt], 0, 0, 0);
         }
+      }
       const int slot = 2 * s + h;
       if (slot < 4) bw[pos[slot]] = dequant8(word_of(q, slot), (slot < 2) ? s0 : s1);
       if (slot == 3) cn = load_b(op.bq + (size_t)kb3 * 32, op.bsf + (size_t)kb3 * 4, op.bq_off, op.bsf_off);
@@ -227,15 +265,40 @@ __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const 
   lds_barrier();
 }
 
+// All nk steps, A stage period 3 and B stage period 2: whole groups of 6,
+// then the remaining 0..5 steps.  Both instantiations pass the same barriers.
+template <bool FULL>
+__device__ __forceinline__ void gemm_steps(f16x8* lds, const ReadPtrs& rp, const int (&pos)[4],
+                                           BChunk& c0, BChunk& c1, int nk, const Operands& op,
+                                           int wave, int nmt, f32x16 (&acc)[4][2]) {
+  const int last = nk - 1;
+  int kb = 0;
+  for (; kb + 6 <= nk; kb += 6) {
+    gemm_step<0, 0, FULL>(lds, rp, pos, c1, kb, last, op, wave, nmt, acc);
+    gemm_step<1, 1, FULL>(lds, rp, pos, c0, kb + 1, last, op, wave, nmt, acc);
+    gemm_step<2, 0, FULL>(lds, rp, pos, c1, kb + 2, last, op, wave, nmt, acc);
+    gemm_step<0, 1, FULL>(lds, rp, pos, c0, kb + 3, last, op, wave, nmt, acc);
+    gemm_step<1, 0, FULL>(lds, rp, pos, c1, kb + 4, last, op, wave, nmt, acc);
+    gemm_step<2, 1, FULL>(lds, rp, pos, c0, kb + 5, last, op, wave, nmt, acc);
+  }
+  const int rem = nk - kb;
+  if (rem > 0) gemm_step<0, 0, FULL>(lds, rp, pos, c1, kb, last, op, wave, nmt, acc);
+  if (rem > 1) gemm_step<1, 1, FULL>(lds, rp, pos, c0, kb + 1, last, op, wave, nmt, acc);
+  if (rem > 2) gemm_step<2, 0, FULL>(lds, rp, pos, c1, kb + 2, last, op, wave, nmt, acc);
+  if (rem > 3) gemm_step<0, 1, FULL>(lds, rp, pos, c0, kb + 3, last, op, wave, nmt, acc);
+  if (rem > 4) gemm_step<1, 0, FULL>(lds, rp, pos, c1, kb + 4, last, op, wave, nmt, acc);
+}
+
 // The whole K loop over nk steps of 64 (operand sources in `op`; the thread
-// moves half `half` of B row tid / 2).  B register set c[j & 1] holds step j's
+// moves half `half` of B row tid / 2; the tile has nrows valid rows).  B register set c[j & 1] holds step j's
 // share from two steps before it is written.  Ends with every load landed and
 // all waves past the last LDS read, so the caller may reuse the LDS.
-__device__ __forceinline__ void gemm_mainloop(f16x8* lds, const Operands& op, int nk,
+__device__ __forceinline__ void gemm_mainloop(f16x8* lds, const Operands& op, int nk, int nrows,
                                               f32x16 (&acc)[4][2]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
+  const int nmt = __builtin_amdgcn_readfirstlane(active_groups(nrows, wm));  // tile-uniform
   const int row = tid >> 1, half = tid & 1;
   const int last = nk - 1;
   int pos[4];
@@ -262,23 +325,10 @@ __device__ __forceinline__ void gemm_mainloop(f16x8* lds, const Operands& op, in
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
   wait_vmcnt<4>();  // A of steps 0 and 1 landed (only the two B refills may be outstanding)
   lds_barrier();
-  // whole groups of 6 steps (A stage period 3, B stage period 2), then the
-  // remaining 0..5 steps
-  int kb = 0;
-  for (; kb + 6 <= nk; kb += 6) {
-    gemm_step<0, 0>(lds, rp, pos, c1, kb, last, op, wave, acc);
-    gemm_step<1, 1>(lds, rp, pos, c0, kb + 1, last, op, wave, acc);
-    gemm_step<2, 0>(lds, rp, pos, c1, kb + 2, last, op, wave, acc);
-    gemm_step<0, 1>(lds, rp, pos, c0, kb + 3, last, op, wave, acc);
-    gemm_step<1, 0>(lds, rp, pos, c1, kb + 4, last, op, wave, acc);
-    gemm_step<2, 1>(lds, rp, pos, c0, kb + 5, last, op, wave, acc);
-  }
-  const int rem = nk - kb;
-  if (rem > 0) gemm_step<0, 0>(lds, rp, pos, c1, kb, last, op, wave, acc);
-  if (rem > 1) gemm_step<1, 1>(lds, rp, pos, c0, kb + 1, last, op, wave, acc);
-  if (rem > 2) gemm_step<2, 0>(lds, rp, pos, c1, kb + 2, last, op, wave, acc);
-  if (rem > 3) gemm_step<0, 1>(lds, rp, pos, c0, kb + 3, last, op, wave, acc);
-  if (rem > 4) gemm_step<1, 0>(lds, rp, pos, c1, kb + 4, last, op, wave, acc);
+  if (nmt == 4)
+    gemm_steps<true>(lds, rp, pos, c0, c1, nk, op, wave, nmt, acc);
+  else
+    gemm_steps<false>(lds, rp, pos, c0, c1, nk, op, wave, nmt, acc);
   wait_vmcnt<0>();
   lds_barrier();
 }
@@ -287,15 +337,21 @@ __device__ __forceinline__ void gemm_mainloop(f16x8* lds, const Operands& op, in
 // 8*(i/4) + 4*(lane/32) + i%4 and column lane%32 of that 32 x 32 tile.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
-__device__ __forceinline__ bool tile_of(const GemmTile* tiles, const int* ntiles, int64_t M, int ti,
-                                        GemmTile* t) {
+// Tile and N tile of this workgroup: tiles come from the routing (tiles,
+// *ntiles), or without routing are the ceil(M / 256) row blocks of M rows
+// (expert 0).  False for workgroups without work.
+__device__ __forceinline__ bool tile_of(const GemmTile* tiles, const int* ntiles, int64_t M,
+                                        int n_ntiles, GemmTile* t, int* nt) {
+  const int mtiles = tiles ? *ntiles : (int)((M + kTileM - 1) / kTileM);
+  int item;
+  if (!work_item(mtiles * n_ntiles, &item)) return false;
+  const int ti = item / n_ntiles;
+  *nt = item % n_ntiles;
   if (tiles) {
-    if (ti >= *ntiles) return false;
     *t = tiles[ti];
     return true;
   }
-  int64_t r0 = (int64_t)ti * kTileM;
-  if (r0 >= M) return false;
+  const int64_t r0 = (int64_t)ti * kTileM;
   t->expert = 0;
   t->row0 = (int)r0;
   t->nrows = (int)((M - r0) < kTileM ? (M - r0) : kTileM);
@@ -340,10 +396,9 @@ __device__ __forceinline__ int l1_weight_row(int nt, int rb) {
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
   __shared__ f16x8 lds[kLdsChunks];
 
-  const int ti = blockIdx.x / p.n_ntiles;
-  const int nt = blockIdx.x % p.n_ntiles;
   GemmTile t;
-  if (!tile_of(p.tiles, p.ntiles, p.M, ti, &t)) return;
+  int nt;
+  if (!tile_of(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Output row (pair id, or activation row without routing) and activation
@@ -369,7 +424,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   op.bsf_off = (uint32_t)l1_weight_row(nt, row) * (uint32_t)(p.K / 16) + 2u * (tid & 1);
 
   f32x16 acc[4][2];
-  gemm_mainloop(lds, op, (int)(p.K / kStepK), acc);
+  gemm_mainloop(lds, op, (int)(p.K / kStepK), t.nrows, acc);
 
   // The LDS now holds the epilogue's arrays: the bf16 SwiGLU tile, the
   // reciprocal table and the output row of every tile row.
@@ -381,7 +436,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   if (tid < kTileM) out_row[tid] = out_row_of(tid);
   // ---- epilogue: alpha, SwiGLU, bf16 tile in LDS
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
   const int col = 32 * wn + (lane & 31);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -437,10 +492,9 @@ struct L2Params {
 
 __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   __shared__ f16x8 lds[kLdsChunks];
-  const int ti = blockIdx.x / p.n_ntiles;
-  const int nt = blockIdx.x % p.n_ntiles;
-  if (ti >= *p.ntiles) return;
-  const GemmTile t = p.tiles[ti];
+  GemmTile t;
+  int nt;
+  if (!tile_of(p.tiles, p.ntiles, 0, p.n_ntiles, &t, &nt)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // pair id of tile row r (padding rows repeat the first row, never stored)
   auto pair_of = [&](int r) -> int { return p.perm[t.row0 + (r < t.nrows ? r : 0)]; };
@@ -458,12 +512,12 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   op.bq_off = brow * (uint32_t)(p.K / 2) + 16u * (tid & 1);
   op.bsf_off = brow * (uint32_t)(p.K / 16) + 2u * (tid & 1);
   f32x16 acc[4][2];
-  gemm_mainloop(lds, op, (int)(p.K / kStepK), acc);
+  gemm_mainloop(lds, op, (int)(p.K / kStepK), t.nrows, acc);
   int* out_row = reinterpret_cast<int*>(lds);
   if (tid < kTileM) out_row[tid] = pair_of(tid);
   __syncthreads();
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave_m(wave), wn = wave_n(wave);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
