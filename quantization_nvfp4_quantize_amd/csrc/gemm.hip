@@ -55,17 +55,25 @@
 namespace nvfp4 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 constexpr int kStepK = 64;
 constexpr int kGemmThreads = 512;
 constexpr int kLdsOperand = kTileM * (kStepK / 8);  // 16 B chunks of one operand stage (32 KiB)
-constexpr int kAStages = 3;
-constexpr int kBStages = 2;
-constexpr int kLdsB = kAStages * kLdsOperand;                    // first chunk of B stage 0
-constexpr int kLdsChunks = (kAStages + kBStages) * kLdsOperand;  // 160 KiB
+constexpr int kAStages = 4;
+constexpr int kBStages = 3;
+constexpr int kBRaw = kTileN * (kStepK / 2) / 16;              // 16 B chunks of raw B per stage (8 KiB)
+constexpr int kBScale = kTileN * (kStepK / 16) / 16;           // 16 B chunks of B scales per stage (1 KiB)
+
+// The main loop's LDS: three arrays (A stages, raw B stages, scale stages),
+// so that the compiler can tell the A fragment reads and the raw B reads
+// apart from the direct loads still in flight into the other arrays.
+struct Lds {
+  f16x8* a;     // kAStages x kLdsOperand chunks (also the epilogue's arrays)
+  f16x8* b;     // kBStages x kBRaw chunks
+  uint32_t* s;  // kBStages x kBScale x 4 words
+};
 
 // ------------------------------------------------------------------ sync
 // Workgroup barrier over LDS only: waits for this wave's LDS traffic, not for
@@ -111,111 +119,167 @@ __device__ __forceinline__ bool work_item(int W, int* item) {
 }
 
 // ------------------------------------------------------------------ operands
-// LDS during the main loop: A0 | A1 | A2 | B0 | B1, 32 KiB each, every stage
-// 256 rows of 64 f16 = 8 chunks of 16 B.
+// LDS during the main loop: A0 .. A3 (32 KiB each: 256 rows of 64 f16 =
+// 8 chunks of 16 B) | B0 .. B2 (8 KiB each: 256 rows of 64 raw nibbles =
+// 2 chunks; half h of row r at chunk 2 r + (h ^ ((r >> 3) & 1)), which keeps
+// the 16-lane groups of the fragment reads on distinct banks) | S0 .. S2
+// (1 KiB each: the 4 block-scale bytes of 256 rows).  155 KiB in all.
 
-// 16-byte chunk c of LDS row `row` lives at c ^ key(row), key(row) =
-// (row ^ row >> 3) & 7: any 16 consecutive rows reading or writing the same
-// logical chunk hit 16 distinct 16-byte bank groups (64 banks), and any 8
-// consecutive rows hit 8.  key(32 m + r) for r < 32 depends only on r and on
-// the parity of m, so the fragments of a wave's four A tiles (two B tiles)
-// are two base pointers plus compile-time offsets.
+// 16-byte chunk c of A row `row` lives at c ^ key(row), key(row) =
+// (row ^ row >> 3) & 7: any 16 consecutive rows reading the same logical
+// chunk hit 16 distinct 16-byte bank groups (64 banks).  key(32 m + r) for
+// r < 32 depends only on r and on the parity of m, so the fragments of a
+// wave's four A tiles are two base pointers plus compile-time offsets.
 __device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 3)) & 7; }
-
-// This thread's B share of one K step: half a B row (32 nibbles) and its 2
-// block scales.
-struct BChunk {
-  uint4 q;
-  uint32_t s;
-};
-
-// bq / bsf: the workgroup's B nibbles and scales advanced to step kb (wave-
-// uniform); bq_off / bsf_off: this thread's byte offsets (row and half).
-__device__ __forceinline__ BChunk load_b(const uint8_t* bq, const uint8_t* bsf, uint32_t bq_off,
-                                         uint32_t bsf_off) {
-  BChunk c;
-  c.q = *reinterpret_cast<const uint4*>(bq + bq_off);
-  c.s = *reinterpret_cast<const uint16_t*>(bsf + bsf_off);
-  return c;
-}
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-__device__ __forceinline__ void scale_pairs(uint32_t bs, f16x2* s0, f16x2* s1) {
-  f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs, 1.0f, false);
-  *s0 = f16x2{s[0], s[0]};
-  *s1 = f16x2{s[1], s[1]};
+// Direct-to-LDS loads.  They are issued from inline assembly so that the
+// compiler neither orders later LDS reads of other stages behind them nor
+// counts them: their completion is waited for explicitly (wait_vmcnt before
+// the barrier that publishes a stage).  Waits the compiler inserts for its own
+// loads can only become stricter for the loads it does not count.  M0 (the
+// LDS destination) is saved and restored around each load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-// Direct-to-LDS load of one 1 KiB piece of an A stage: LDS chunks
-// 64 q .. 64 q + 63 (rows 8 q .. 8 q + 7), lane i writing chunk 64 q + i.
-// a: the A matrix advanced to the step (wave-uniform); off: this lane's byte
-// offset (row 8 q + i / 8, logical chunk (i & 7) ^ key(row)).
-__device__ __forceinline__ void dma_a(f16x8* a_stage, const uint8_t* a, uint32_t off, int q) {
-  __builtin_amdgcn_global_load_lds((const void*)(a + off), (lds_void*)(a_stage + q * 64), 16, 0, 0);
+// 1 KiB: lane i writes chunk i of `dst` (wave-uniform) with the 16 B at src.
+__device__ __forceinline__ void dma16(f16x8* dst, const uint8_t* src) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(dst)), "v"(src)
+      : "memory");
+}
+
+// 256 B: lane i writes dword i of `dst` (wave-uniform) with the 4 B at src.
+__device__ __forceinline__ void dma4(uint32_t* dst, const uint8_t* src) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(dst)), "v"(src)
+      : "memory");
 }
 
 // Per-workgroup operand sources of the main loop.  Byte offsets are 32-bit:
 // the A matrix and one expert's weights stay below 4 GiB.
 struct Operands {
-  const uint8_t* a;    // A matrix (f16 rows of K), wave-uniform
-  uint32_t a_off[4];   // this lane's direct-load sources: tile rows 32 wave + 8 u + lane / 8
-  const uint8_t* bq;   // B nibbles of the tile's expert, wave-uniform
-  const uint8_t* bsf;  // B scales of the tile's expert, wave-uniform
-  uint32_t bq_off;     // this thread's B row and half: row * K / 2 + 16 half
-  uint32_t bsf_off;    // row * K / 16 + 2 half
+  const uint8_t* a;     // A matrix (f16 rows of K), wave-uniform
+  uint32_t a_off[4];    // this lane's A sources: tile rows 32 wave + 8 u + lane / 8
+  const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
+  uint32_t bq_off;      // this lane's B source: tile row 32 wave + lane / 2, half (lane ^ lane >> 4) & 1
+  const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
+  uint32_t bsf_off;     // this lane's scale source: tile row 64 (wave % 4) + lane
 };
+
+// B state of one K step in a lane: for each of its two 32-column tiles nt,
+// the 16 B of nibbles of column 64 wn + 32 nt + lane % 32 at K chunks
+// 4 g .. 4 g + 3 (g = lane / 32: exactly what its MFMA B fragments of the
+// step need), and the column's four block-scale bytes.
+struct BRaw {
+  uint4 q[2];
+};
+struct BScale {
+  uint32_t w[2];
+};
+
+// f16 pairs of the block scales 2 g and 2 g + 1 of a scale word: the
+// fragments of sub-steps 0, 1 use lo, those of 2, 3 use hi.
+struct ScalePairs {
+  f16x2 lo[2], hi[2];
+};
+
+__device__ __forceinline__ ScalePairs scale_pairs(const BScale& sc, int g) {
+  ScalePairs p;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc.w[nt] >> (16 * g), 1.0f, false);
+    p.lo[nt] = f16x2{s[0], s[0]};
+    p.hi[nt] = f16x2{s[1], s[1]};
+  }
+  return p;
+}
+
+// Exact f16 B fragment of sub-step s for column tile nt.
+__device__ __forceinline__ f16x8 b_frag(const BRaw& r, const ScalePairs& p, int nt, int s) {
+  return dequant8(word_of(r.q[nt], s), (s < 2) ? p.lo[nt] : p.hi[nt]);
+}
 
 struct Frags {
   f16x8 a[4], b[2];
 };
 
-// A wave's fragment pointers: the A fragment of MFMA sub-step s for rows
+// A wave's A fragment pointers: the fragment of MFMA sub-step s for rows
 // wm * 128 + 32 mt + (lane & 31) of A stage st is a[s][mt & 1] + 512 (mt >> 1)
-// + st * kLdsOperand; the B fragment for rows wn * 64 + 32 nt + (lane & 31) of
-// B stage st is b[s][nt] + st * kLdsOperand.  Lane half g = lane >> 5 reads
-// logical chunk 4 g + s (the same K permutation for A and B).
+// + st * kLdsOperand.  Lane half g = lane >> 5 reads logical chunk 4 g + s
+// (B uses the same K permutation).
 struct ReadPtrs {
   const f16x8* a[4][2];
-  const f16x8* b[4][2];
+  const f16x8* b;     // this lane's raw B chunk of column tile 0 in B stage 0 (tile 1: + 64,
+                      // rows 32 apart keep the same swizzle bit)
+  const uint32_t* s;  // its scale word of column tile 0 in scale stage 0 (tile 1: + 32)
 };
 
-__device__ __forceinline__ ReadPtrs read_ptrs(const f16x8* lds, int wm, int wn, int lane) {
+__device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int lane) {
   ReadPtrs rp;
   const int g = lane >> 5, r = lane & 31;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int ra = wm * 128 + 32 * p + r, rb = wn * 64 + 32 * p + r;
-      rp.a[s][p] = lds + ra * 8 + ((4 * g + s) ^ swz_key(ra));
-      rp.b[s][p] = lds + kLdsB + rb * 8 + ((4 * g + s) ^ swz_key(rb));
+      const int ra = wm * 128 + 32 * p + r;
+      rp.a[s][p] = L.a + ra * 8 + ((4 * g + s) ^ swz_key(ra));
     }
+  rp.b = L.b + 2 * (wn * 64 + r) + (g ^ ((r >> 3) & 1));
+  rp.s = L.s + wn * 64 + r;
   return rp;
 }
 
-// One K step kb on A stage KA = kb % 3 and B stage KB = kb % 2: the wave's 32
-// MFMAs in 8 groups of 4 (those of row groups mt >= nmt skipped).  Between the groups the thread writes its B share of
-// step kb + 1 (held in `cn`, four dequantized chunks), refills `cn` with the B
-// share of step kb + 3, and issues its four direct loads of A step kb + 2
-// into A stage (KA + 2) % 3.  Every step issues 6 vector-memory loads, so at
-// its end at most 6 are outstanding once A of step kb + 1 (issued one step
-// earlier) has landed.  Loads past the end re-read the last step; what they
-// write lands in stages that are not read again.
+// One K step kb on A stage KA = kb % 4; bs = kb % 3 is the B / scale stage
+// holding step kb, and the register sets R, S alternate with KB = kb % 2.
+// The wave's 32 MFMAs run in 8 groups of 4 (those of row groups mt >= nmt
+// skipped); ahead of each group it reads the next A fragments from LDS and
+// dequantizes the next B fragments in registers, the last group preparing the
+// B fragments of sub-step 0 of step kb + 1 (bf).  Between the groups it reads
+// the raw B and the scales of step kb + 1 into R[KB ^ 1], S[KB ^ 1], then
+// issues, in this order, the direct loads of B step kb + 3 into B stage bs,
+// of its scales (waves 4 KB .. 4 KB + 3, a quarter of the rows each) into
+// scale stage bs, and of A step kb + 3 into A stage (KA + 3) % 4.  Over any
+// two consecutive steps a wave issues 11 loads (5 + 6), so waiting at the end
+// of step kb until at most 10 are outstanding means: everything up to and
+// including the first load of step kb - 1 has landed -- B and scales of
+// step kb + 2 (read at the start of step kb + 1) and A of step kb + 1, each
+// about two steps after it was issued.  Loads past the end re-read the last
+// step; what they write lands where it is not read again.
 template <int KA, int KB, bool FULL>
-__device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const int (&pos)[4],
-                                          BChunk& cn, int kb, int last, const Operands& op,
-                                          int wave, int nmt, f32x16 (&acc)[4][2]) {
-  f16x8* const bw = lds + kLdsB + ((KB + 1) & 1) * kLdsOperand;
-  f16x8* const aw = lds + ((KA + 2) % 3) * kLdsOperand;
-  const uint8_t* const a_next = op.a + (size_t)min(kb + 2, last) * (kStepK * 2);
-  const int kb3 = min(kb + 3, last);
-  constexpr int aoff = KA * kLdsOperand, boff = KB * kLdsOperand;
-  f16x2 s0, s1;
-  scale_pairs(cn.s, &s0, &s1);
-  const uint4 q = cn.q;
+__device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
+                                          BScale (&S)[2], f16x8 (&bf)[2], int kb, int bs, int last,
+                                          const Operands& op, int wave, int lane, int nmt,
+                                          f32x16 (&acc)[4][2]) {
+  const int g = lane >> 5;
+  const bool scales = (wave >> 2) == KB;  // this wave loads a quarter of the scales
+  f16x8* const a_dst = L.a + ((KA + 3) % 4) * kLdsOperand + (4 * wave) * 64;
+  f16x8* const b_dst = L.b + bs * kBRaw + wave * 64;
+  uint32_t* const s_dst = L.s + bs * kBScale * 4 + (wave & 3) * 64;
+  const int bn = (bs == 2) ? 0 : bs + 1;  // B / scale stage of step kb + 1
+  const f16x8* const b_next = rp.b + bn * kBRaw;
+  const uint32_t* const s_next = rp.s + bn * kBScale * 4;
+  const uint8_t* const a_src = op.a + (size_t)min(kb + 3, last) * (kStepK * 2);
+  const uint8_t* const b_src = op.bq + (size_t)min(kb + 3, last) * (kStepK / 2);
+  const uint8_t* const s_src = op.bsf + (size_t)min(kb + 3, last) * (kStepK / 16);
+  constexpr int aoff = KA * kLdsOperand;
+  const ScalePairs pc = scale_pairs(S[KB], g);
   // A partial wave (FULL false) reads and multiplies only its row groups
   // mt < nmt; the reads of a full wave stay unconditional, which keeps the
   // compiler's LDS wait counts exact.
@@ -224,9 +288,8 @@ __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const 
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
     if (on(mt)) f[0].a[mt] = rp.a[0][mt & 1][aoff + 512 * (mt >> 1)];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-    if (on(0)) f[0].b[nt] = rp.b[0][nt][boff];
+  f[0].b[0] = bf[0];
+  f[0].b[1] = bf[1];
   SCHED_FENCE();
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -241,9 +304,11 @@ __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const 
           if (on(2)) G.a[2] = rp.a[s + 1][0][aoff + 512];
         } else {
           if (on(3)) G.a[3] = rp.a[s + 1][1][aoff + 512];
-          if (on(0)) G.b[0] = rp.b[s + 1][0][boff];
-          if (on(0)) G.b[1] = rp.b[s + 1][1][boff];
         }
+        G.b[h] = b_frag(R[KB], pc, h, s + 1);
+      } else {
+        const ScalePairs pn = scale_pairs(S[KB ^ 1], g);
+        bf[h] = b_frag(R[KB ^ 1], pn, h, 0);
       }
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
@@ -255,80 +320,100 @@ __device__ __forceinline__ void gemm_step(f16x8* lds, const ReadPtrs& rp, const 
         }
       }
       const int slot = 2 * s + h;
-      if (slot < 4) bw[pos[slot]] = dequant8(word_of(q, slot), (slot < 2) ? s0 : s1);
-      if (slot == 3) cn = load_b(op.bq + (size_t)kb3 * 32, op.bsf + (size_t)kb3 * 4, op.bq_off, op.bsf_off);
-      if (slot >= 4) dma_a(aw, a_next, op.a_off[slot - 4], 4 * wave + slot - 4);
+      if (slot == 0) {
+        R[KB ^ 1].q[0] = __builtin_bit_cast(uint4, b_next[0]);
+        R[KB ^ 1].q[1] = __builtin_bit_cast(uint4, b_next[64]);
+        S[KB ^ 1].w[0] = s_next[0];
+        S[KB ^ 1].w[1] = s_next[32];
+        dma16(b_dst, b_src + op.bq_off);
+        if (scales) dma4(s_dst, s_src + op.bsf_off);
+      }
+      if (slot >= 1 && slot < 5) dma16(a_dst + (slot - 1) * 64, a_src + op.a_off[slot - 1]);
       SCHED_FENCE();
     }
   }
-  wait_vmcnt<6>();
+  wait_vmcnt<10>();
   lds_barrier();
 }
 
-// All nk steps, A stage period 3 and B stage period 2: whole groups of 6,
-// then the remaining 0..5 steps.  Both instantiations pass the same barriers.
+// All nk steps, A stage period 4 and register-set period 2: whole groups of
+// 4, then the remaining 0..3 steps; bs runs through the B stages 0, 1, 2.
+// Both instantiations pass the same barriers.
 template <bool FULL>
-__device__ __forceinline__ void gemm_steps(f16x8* lds, const ReadPtrs& rp, const int (&pos)[4],
-                                           BChunk& c0, BChunk& c1, int nk, const Operands& op,
-                                           int wave, int nmt, f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
+                                           BScale (&S)[2], f16x8 (&bf)[2], int nk,
+                                           const Operands& op, int wave, int lane, int nmt,
+                                           f32x16 (&acc)[4][2]) {
   const int last = nk - 1;
-  int kb = 0;
-  for (; kb + 6 <= nk; kb += 6) {
-    gemm_step<0, 0, FULL>(lds, rp, pos, c1, kb, last, op, wave, nmt, acc);
-    gemm_step<1, 1, FULL>(lds, rp, pos, c0, kb + 1, last, op, wave, nmt, acc);
-    gemm_step<2, 0, FULL>(lds, rp, pos, c1, kb + 2, last, op, wave, nmt, acc);
-    gemm_step<0, 1, FULL>(lds, rp, pos, c0, kb + 3, last, op, wave, nmt, acc);
-    gemm_step<1, 0, FULL>(lds, rp, pos, c1, kb + 4, last, op, wave, nmt, acc);
-    gemm_step<2, 1, FULL>(lds, rp, pos, c0, kb + 5, last, op, wave, nmt, acc);
+  int kb = 0, bs = 0;
+  auto next = [](int b) { return b == 2 ? 0 : b + 1; };
+  for (; kb + 4 <= nk; kb += 4) {
+    gemm_step<0, 0, FULL>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+    bs = next(bs);
+    gemm_step<1, 1, FULL>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
+    bs = next(bs);
+    gemm_step<2, 0, FULL>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
+    bs = next(bs);
+    gemm_step<3, 1, FULL>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
+    bs = next(bs);
   }
   const int rem = nk - kb;
-  if (rem > 0) gemm_step<0, 0, FULL>(lds, rp, pos, c1, kb, last, op, wave, nmt, acc);
-  if (rem > 1) gemm_step<1, 1, FULL>(lds, rp, pos, c0, kb + 1, last, op, wave, nmt, acc);
-  if (rem > 2) gemm_step<2, 0, FULL>(lds, rp, pos, c1, kb + 2, last, op, wave, nmt, acc);
-  if (rem > 3) gemm_step<0, 1, FULL>(lds, rp, pos, c0, kb + 3, last, op, wave, nmt, acc);
-  if (rem > 4) gemm_step<1, 0, FULL>(lds, rp, pos, c1, kb + 4, last, op, wave, nmt, acc);
+  if (rem > 0) gemm_step<0, 0, FULL>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+  if (rem > 1) gemm_step<1, 1, FULL>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
+  if (rem > 2) gemm_step<2, 0, FULL>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
 }
 
-// The whole K loop over nk steps of 64 (operand sources in `op`; the thread
-// moves half `half` of B row tid / 2; the tile has nrows valid rows).  B register set c[j & 1] holds step j's
-// share from two steps before it is written.  Ends with every load landed and
-// all waves past the last LDS read, so the caller may reuse the LDS.
-__device__ __forceinline__ void gemm_mainloop(f16x8* lds, const Operands& op, int nk, int nrows,
+// The whole K loop over nk steps of 64 (operand sources in `op`; the tile has
+// nrows valid rows).  The prologue brings A steps 0..2 and B steps 0..2 with
+// their scales into LDS, then reads the raw B and scales of step 0 and
+// dequantizes its sub-step 0 fragments.  Ends with every load
+// landed and all waves past the last LDS read, so the caller may reuse the
+// LDS.
+__device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, int nk, int nrows,
                                               f32x16 (&acc)[4][2]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave_m(wave), wn = wave_n(wave);
+  const int wm = wave_m(wave), wn = wave_n(wave), g = lane >> 5;
   const int nmt = __builtin_amdgcn_readfirstlane(active_groups(nrows, wm));  // tile-uniform
-  const int row = tid >> 1, half = tid & 1;
   const int last = nk - 1;
-  int pos[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) pos[k] = row * 8 + ((4 * half + k) ^ swz_key(row));
-  const int k1 = min(1, last), k2 = min(2, last);
+  for (int j = 0; j < 3; ++j) {
+    const uint8_t* a_src = op.a + (size_t)min(j, last) * (kStepK * 2);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) dma_a(lds, op.a, op.a_off[u], 4 * wave + u);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) dma_a(lds + kLdsOperand, op.a + (size_t)k1 * (kStepK * 2), op.a_off[u], 4 * wave + u);
-  BChunk c0 = load_b(op.bq, op.bsf, op.bq_off, op.bsf_off);
-  BChunk c1 = load_b(op.bq + (size_t)k1 * 32, op.bsf + (size_t)k1 * 4, op.bq_off, op.bsf_off);
-  {
-    f16x2 s0, s1;
-    scale_pairs(c0.s, &s0, &s1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lds[kLdsB + pos[j]] = dequant8(word_of(c0.q, j), (j < 2) ? s0 : s1);
+    for (int u = 0; u < 4; ++u)
+      dma16(L.a + j * kLdsOperand + (4 * wave + u) * 64, a_src + op.a_off[u]);
   }
-  c0 = load_b(op.bq + (size_t)k2 * 32, op.bsf + (size_t)k2 * 4, op.bq_off, op.bsf_off);
-  const ReadPtrs rp = read_ptrs(lds, wm, wn, lane);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    dma16(L.b + j * kBRaw + wave * 64, op.bq + (size_t)min(j, last) * (kStepK / 2) + op.bq_off);
+    if ((wave >> 2) == (j & 1))
+      dma4(L.s + j * kBScale * 4 + (wave & 3) * 64,
+           op.bsf + (size_t)min(j, last) * (kStepK / 16) + op.bsf_off);
+  }
+  const ReadPtrs rp = read_ptrs(L, wm, wn, lane);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
-  wait_vmcnt<4>();  // A of steps 0 and 1 landed (only the two B refills may be outstanding)
+  wait_vmcnt<0>();
   lds_barrier();
+  BRaw R[2];
+  BScale S[2];
+  R[0].q[0] = __builtin_bit_cast(uint4, rp.b[0]);
+  R[0].q[1] = __builtin_bit_cast(uint4, rp.b[64]);
+  S[0].w[0] = rp.s[0];
+  S[0].w[1] = rp.s[32];
+  f16x8 bf[2];
+  {
+    const ScalePairs p0 = scale_pairs(S[0], g);
+    bf[0] = b_frag(R[0], p0, 0, 0);
+    bf[1] = b_frag(R[0], p0, 1, 0);
+  }
+  lds_barrier();  // B and scale stage 0 are refilled during step 0
   if (nmt == 4)
-    gemm_steps<true>(lds, rp, pos, c0, c1, nk, op, wave, nmt, acc);
+    gemm_steps<true>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   else
-    gemm_steps<false>(lds, rp, pos, c0, c1, nk, op, wave, nmt, acc);
+    gemm_steps<false>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   wait_vmcnt<0>();
   lds_barrier();
 }
@@ -394,7 +479,10 @@ __device__ __forceinline__ int l1_weight_row(int nt, int rb) {
 }
 
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
-  __shared__ f16x8 lds[kLdsChunks];
+  __shared__ f16x8 lds_a[kAStages * kLdsOperand];
+  __shared__ f16x8 lds_b[kBStages * kBRaw];
+  __shared__ uint32_t lds_s[kBStages * kBScale * 4];
+  const Lds L{lds_a, lds_b, lds_s};
 
   GemmTile t;
   int nt;
@@ -417,22 +505,23 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
     const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
     op.a_off[u] = arow * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
   }
-  const int row = tid >> 1;
   op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);
-  op.bq_off = (uint32_t)l1_weight_row(nt, row) * (uint32_t)(p.K / 2) + 16u * (tid & 1);
-  op.bsf_off = (uint32_t)l1_weight_row(nt, row) * (uint32_t)(p.K / 16) + 2u * (tid & 1);
+  op.bq_off = (uint32_t)l1_weight_row(nt, 32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) +
+              16u * ((lane ^ (lane >> 4)) & 1);
+  op.bsf_off = (uint32_t)l1_weight_row(nt, 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
 
   f32x16 acc[4][2];
-  gemm_mainloop(lds, op, (int)(p.K / kStepK), t.nrows, acc);
+  gemm_mainloop(L, op, (int)(p.K / kStepK), t.nrows, acc);
 
   // The LDS now holds the epilogue's arrays: the bf16 SwiGLU tile, the
   // reciprocal table and the output row of every tile row.
   constexpr int kCStride = 136;  // bf16 per LDS row (128 + 8 padding)
   constexpr int kCTileChunks = kTileM * kCStride * 2 / 16;
-  uint16_t* ctile = reinterpret_cast<uint16_t*>(lds);
-  float* rtab = reinterpret_cast<float*>(lds + kCTileChunks);
-  int* out_row = reinterpret_cast<int*>(lds + kCTileChunks + 32);
+  static_assert(kCTileChunks + 32 + kTileM / 4 <= kAStages * kLdsOperand, "epilogue LDS");
+  uint16_t* ctile = reinterpret_cast<uint16_t*>(lds_a);
+  float* rtab = reinterpret_cast<float*>(lds_a + kCTileChunks);
+  int* out_row = reinterpret_cast<int*>(lds_a + kCTileChunks + 32);
   if (tid < kTileM) out_row[tid] = out_row_of(tid);
   // ---- epilogue: alpha, SwiGLU, bf16 tile in LDS
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
@@ -491,7 +580,10 @@ struct L2Params {
 };
 
 __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
-  __shared__ f16x8 lds[kLdsChunks];
+  __shared__ f16x8 lds_a[kAStages * kLdsOperand];
+  __shared__ f16x8 lds_b[kBStages * kBRaw];
+  __shared__ uint32_t lds_s[kBStages * kBScale * 4];
+  const Lds L{lds_a, lds_b, lds_s};
   GemmTile t;
   int nt;
   if (!tile_of(p.tiles, p.ntiles, 0, p.n_ntiles, &t, &nt)) return;
@@ -505,15 +597,14 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     const int R = 32 * wave + 8 * u + (lane >> 3);
     op.a_off[u] = (uint32_t)pair_of(R) * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
   }
-  const int row = tid >> 1;
-  const uint32_t brow = (uint32_t)(nt * kTileN + row);
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
-  op.bq_off = brow * (uint32_t)(p.K / 2) + 16u * (tid & 1);
-  op.bsf_off = brow * (uint32_t)(p.K / 16) + 2u * (tid & 1);
+  op.bq_off = (uint32_t)(nt * kTileN + 32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) +
+              16u * ((lane ^ (lane >> 4)) & 1);
+  op.bsf_off = (uint32_t)(nt * kTileN + 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
   f32x16 acc[4][2];
-  gemm_mainloop(lds, op, (int)(p.K / kStepK), t.nrows, acc);
-  int* out_row = reinterpret_cast<int*>(lds);
+  gemm_mainloop(L, op, (int)(p.K / kStepK), t.nrows, acc);
+  int* out_row = reinterpret_cast<int*>(lds_a);
   if (tid < kTileM) out_row[tid] = pair_of(tid);
   __syncthreads();
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
