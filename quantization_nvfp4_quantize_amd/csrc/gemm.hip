@@ -279,11 +279,12 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
   const uint8_t* const b_src = op.bq + (size_t)min(kb + 3, last) * (kStepK / 2);
   const uint8_t* const s_src = op.bsf + (size_t)min(kb + 3, last) * (kStepK / 16);
   constexpr int aoff = KA * kLdsOperand;
-  const ScalePairs pc = scale_pairs(S[KB], g);
   // A partial wave (FULL false) reads and multiplies only its row groups
   // mt < nmt; the reads of a full wave stay unconditional, which keeps the
   // compiler's LDS wait counts exact.
   auto on = [&](int mt) { return FULL || mt < nmt; };
+  ScalePairs pc;
+  if (on(0)) pc = scale_pairs(S[KB], g);
   Frags f[2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -305,8 +306,8 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
         } else {
           if (on(3)) G.a[3] = rp.a[s + 1][1][aoff + 512];
         }
-        G.b[h] = b_frag(R[KB], pc, h, s + 1);
-      } else {
+        if (on(0)) G.b[h] = b_frag(R[KB], pc, h, s + 1);
+      } else if (on(0)) {
         const ScalePairs pn = scale_pairs(S[KB ^ 1], g);
         bf[h] = b_frag(R[KB ^ 1], pn, h, 0);
       }
@@ -321,10 +322,12 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
       }
       const int slot = 2 * s + h;
       if (slot == 0) {
-        R[KB ^ 1].q[0] = __builtin_bit_cast(uint4, b_next[0]);
-        R[KB ^ 1].q[1] = __builtin_bit_cast(uint4, b_next[64]);
-        S[KB ^ 1].w[0] = s_next[0];
-        S[KB ^ 1].w[1] = s_next[32];
+        if (on(0)) {  // a wave without valid rows needs no B
+          R[KB ^ 1].q[0] = __builtin_bit_cast(uint4, b_next[0]);
+          R[KB ^ 1].q[1] = __builtin_bit_cast(uint4, b_next[64]);
+          S[KB ^ 1].w[0] = s_next[0];
+          S[KB ^ 1].w[1] = s_next[32];
+        }
         dma16(b_dst, b_src + op.bq_off);
         if (scales) dma4(s_dst, s_src + op.bsf_off);
       }
@@ -527,26 +530,31 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
   const int wm = wave_m(wave), wn = wave_n(wave);
   const int col = 32 * wn + (lane & 31);
+  // only the row groups holding valid rows (rows past nrows are never stored)
+  const int nmt = __builtin_amdgcn_readfirstlane(active_groups(t.nrows, wm));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
+    if (mt < nmt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float gate = acc[mt][0][i] * alpha;
-      float up = acc[mt][1][i] * alpha;
-      float c = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
-      __bf16 b = (__bf16)c;
-      ctile[(wm * 128 + mt * 32 + acc_row(i, lane)) * kCStride + col] = __builtin_bit_cast(uint16_t, b);
+      for (int i = 0; i < 16; ++i) {
+        float gate = acc[mt][0][i] * alpha;
+        float up = acc[mt][1][i] * alpha;
+        float c = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
+        __bf16 b = (__bf16)c;
+        ctile[(wm * 128 + mt * 32 + acc_row(i, lane)) * kCStride + col] = __builtin_bit_cast(uint16_t, b);
+      }
     }
   }
   const float E2 = 1.0f / p.out_gs[0];
   fill_rtab(rtab, E2, tid);
   __syncthreads();
 
-  // ---- quantize the bf16 tile: 16 lanes per row (8 blocks, two halves each)
+  // ---- quantize the bf16 tile: 16 lanes per row (8 blocks, two halves
+  // each), 32 rows per pass, passes up to the last valid row
   const int64_t I = p.N2 / 2;
   const int hb = tid & 15;
-#pragma unroll 2
-  for (int pass = 0; pass < kTileM / (kGemmThreads / 16); ++pass) {
+  const int npass = (t.nrows + kGemmThreads / 16 - 1) / (kGemmThreads / 16);
+  for (int pass = 0; pass < npass; ++pass) {
     const int qrow = pass * (kGemmThreads / 16) + (tid >> 4);
     uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
     uint32_t code;
