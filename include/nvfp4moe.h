@@ -146,6 +146,12 @@ typedef struct {
      `stream` before the global scale, then after the global scale, the
      activation quantization, the grouping, L1, L2 and the combine. */
   void *const *stage_events;
+  /* GEMM tile height: 0 chooses from the routing shape (32-row tiles that
+     stream the weights when there are at most 16 pairs per expert on
+     average, else 256-row tiles); 32 or 256 forces one (other values:
+     NVFP4_ERR_INVALID_ARG).  The results are the same either way up to the
+     fp32 summation order inside the GEMMs. */
+  int32_t tile_rows;
 } nvfp4_moe_args;
 
 /*

@@ -37,6 +37,7 @@ class MoeArgs(ctypes.Structure):
         ("xq", _vp), ("xsf", _vp), ("x_gs_out", _vp),
         ("l1_c_bf16", _vp), ("l1_q", _vp), ("l1_sf", _vp), ("err_count", _vp),
         ("stage_events", ctypes.POINTER(_vp)),
+        ("tile_rows", ctypes.c_int32),
     ]
 
 
@@ -172,8 +173,9 @@ def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, 
 
 def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
              x_gs=None, xq=None, xsf=None, x_gs_out=None, l1_c=None, l1_q=None, l1_sf=None,
-             err_count=None):
-    """Build the nvfp4_moe_args struct from tensors (keeps no references)."""
+             err_count=None, tile_rows=0):
+    """Build the nvfp4_moe_args struct from tensors (keeps no references).
+    tile_rows: 0 lets the library choose the GEMM tiles, 32 or 256 forces."""
     _require(x, torch.bfloat16, "x")
     _require(topk_ids, torch.int32, "topk_ids")
     _require(topk_w, torch.float32, "topk_w")
@@ -181,10 +183,12 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
     E, N2 = w1_q.shape[0], w1_q.shape[1]
     k = topk_ids.shape[1]
     code = {torch.bfloat16: 0, torch.float32: 1}[out.dtype]
-    return MoeArgs(T, H, N2 // 2, E, k, _p(x), _p(x_gs), _p(topk_ids), _p(topk_w),
-                   _p(w1_q), _p(w1_sf), _p(w1_gs), _p(w2_q), _p(w2_sf), _p(w2_gs), _p(a2_gs),
-                   _p(out), code, _p(xq), _p(xsf), _p(x_gs_out), _p(l1_c), _p(l1_q), _p(l1_sf),
-                   _p(err_count))
+    a = MoeArgs(T, H, N2 // 2, E, k, _p(x), _p(x_gs), _p(topk_ids), _p(topk_w),
+                _p(w1_q), _p(w1_sf), _p(w1_gs), _p(w2_q), _p(w2_sf), _p(w2_gs), _p(a2_gs),
+                _p(out), code, _p(xq), _p(xsf), _p(x_gs_out), _p(l1_c), _p(l1_q), _p(l1_sf),
+                _p(err_count))
+    a.tile_rows = int(tile_rows)
+    return a
 
 
 def moe_workspace_size(args):
@@ -201,10 +205,10 @@ def moe_expert_ffn_raw(args, device, ws=None):
 
 
 def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
-                   out_dtype=torch.bfloat16, x_gs=None, debug=False):
+                   out_dtype=torch.bfloat16, x_gs=None, debug=False, tile_rows=0):
     """NVFP4 MoE expert FFN.  Returns y [T][H] (out_dtype), plus with
     debug=True a dict of the intermediate outputs (xq, xsf, x_gs, l1_c,
-    l1_q, l1_sf, err_count)."""
+    l1_q, l1_sf, err_count).  tile_rows: see moe_args."""
     T, H = x.shape
     I = w1_q.shape[1] // 2
     k = topk_ids.shape[1]
@@ -221,7 +225,7 @@ def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, 
                    l1_sf=torch.zeros((P, I // 16), dtype=torch.uint8, device=dev),
                    err_count=torch.zeros(1, dtype=torch.int32, device=dev))
     args = moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
-                    x_gs=x_gs, **dbg)
+                    x_gs=x_gs, tile_rows=tile_rows, **dbg)
     moe_expert_ffn_raw(args, dev)
     if debug:
         return out, dbg

@@ -157,10 +157,18 @@ struct MoeLayout {
   int max_tiles;
 };
 
+// Rows per GEMM tile: 32-row tiles (weights streamed through registers) when
+// the experts get few rows each, else 256-row tiles (MFMA-bound).
+int64_t moe_tile_rows(const nvfp4_moe_args* a) {
+  if (a->tile_rows) return a->tile_rows;
+  const int64_t P = a->T * a->topk;
+  return P <= 16 * a->E ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
+}
+
 MoeLayout moe_layout(const nvfp4_moe_args* a) {
   MoeLayout L;
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, P = a->T * a->topk;
-  const int64_t bm = nvfp4::gemm_tile_rows();
+  const int64_t bm = moe_tile_rows(a);
   L.max_tiles = (int)((P + bm - 1) / bm + E);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -205,6 +213,10 @@ int moe_validate(const nvfp4_moe_args* a) {
     return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4: a GEMM operand exceeds 4 GiB");
   if (a->out_dtype != 0 && a->out_dtype != 1)
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (a->tile_rows != 0 && a->tile_rows != nvfp4::skinny_tile_rows() &&
+      a->tile_rows != nvfp4::gemm_tile_rows())
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: tile_rows must be 0, %d or %d",
+                nvfp4::skinny_tile_rows(), nvfp4::gemm_tile_rows());
   if (a->T > 0 && (!a->x || !a->topk_ids || !a->topk_w || !a->w1_q || !a->w1_sf || !a->w1_gs ||
                    !a->w2_q || !a->w2_sf || !a->w2_gs || !a->a2_gs || !a->out))
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: null required pointer");
@@ -218,7 +230,7 @@ int moe_validate(const nvfp4_moe_args* a) {
 }  // namespace
 
 size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args* args) {
-  if (!args || args->T < 0 || args->topk < 1 || args->E < 1) return 0;
+  if (!args || args->T < 0 || args->topk < 1 || args->E < 1 || args->tile_rows < 0) return 0;
   return moe_layout(args).total;
 }
 
@@ -269,7 +281,8 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   nvfp4::GemmTile* tiles = reinterpret_cast<nvfp4::GemmTile*>(w + L.tiles);
   int* ntiles = reinterpret_cast<int*>(w + L.ntiles);
   int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
-  if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, nvfp4::gemm_tile_rows(), offsets, perm,
+  const bool skinny = moe_tile_rows(a) == nvfp4::skinny_tile_rows();
+  if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, (int)moe_tile_rows(a), offsets, perm,
                                            tiles, ntiles, err, s),
                        "route")))
     return st;
@@ -278,16 +291,17 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   uint8_t* a2q = a->l1_q ? a->l1_q : reinterpret_cast<uint8_t*>(w + L.a2q);
   uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
   uint16_t* a2_f16 = reinterpret_cast<uint16_t*>(w + L.a2_f16);
-  if ((st = hip_status(nvfp4::launch_l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs,
-                                        a->l1_c_bf16, a2q, a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0,
-                                        perm, (int)k, s),
+  auto l1 = skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1;
+  if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs, a->l1_c_bf16, a2q,
+                          a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s),
                        "L1 GEMM")))
     return st;
   mark(4);
   // a7: L2 GEMM, weighted by the routing weights
   float* o = reinterpret_cast<float*>(w + L.o);
-  if ((st = hip_status(nvfp4::launch_l2(a2_f16, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o,
-                                        tiles, ntiles, L.max_tiles, perm, s),
+  auto l2 = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
+  if ((st = hip_status(l2(a2_f16, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
+                          L.max_tiles, perm, s),
                        "L2 GEMM")))
     return st;
   mark(5);

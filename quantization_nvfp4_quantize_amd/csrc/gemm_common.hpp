@@ -1,0 +1,210 @@
+// Device pieces shared by the token-grouped NVFP4 GEMM kernels (the 256-row
+// tile kernels for many rows per expert, the 32-row kernels for few): LDS-only
+// barriers and explicit load-counter waits, direct-to-LDS loads, the XCD-aware
+// work order, the operand swizzle, in-register weight dequantization, and the
+// L1 (gate/up + SwiGLU + NVFP4) and L2 (down, routing-weighted) parameters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kStepK = 64;    // K per main-loop step (4 MFMA sub-steps of 16)
+constexpr int kTileN = 256;   // B rows (output columns of the GEMM) per workgroup
+
+// ------------------------------------------------------------------ sync
+// Workgroup barrier over LDS only: waits for this wave's LDS traffic, not for
+// its outstanding global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited on
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (the counter retires loads in issue order).  The direct-to-LDS loads are
+// not tracked by the compiler for later LDS reads, so their completion is
+// waited for explicitly with this before the barrier that publishes them.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Work item of this workgroup among W items.  Workgroup b runs on XCD b % 8;
+// XCD x takes the contiguous items x q + min(x, r) .. (q = W / 8, r = W % 8,
+// q + 1 items on the first r XCDs), so the workgroups running together on
+// one XCD work on neighbouring items.  False for workgroups beyond W.
+__device__ __forceinline__ bool work_item(int W, int* item) {
+  const int b = blockIdx.x, x = b & 7, j = b >> 3;
+  const int q = W >> 3, r = W & 7;
+  if (j >= q + (x < r ? 1 : 0)) return false;
+  *item = x * q + min(x, r) + j;
+  return true;
+}
+
+// 16-byte chunk c of A row `row` lives at c ^ key(row), key(row) =
+// (row ^ row >> 3) & 7: any 16 consecutive rows reading the same logical
+// chunk hit 16 distinct 16-byte bank groups (64 banks).  key(32 m + r) for
+// r < 32 depends only on r and on the parity of m, so the fragments of a
+// wave's four A tiles are two base pointers plus compile-time offsets.
+__device__ __forceinline__ int swz_key(int row) { return (row ^ (row >> 3)) & 7; }
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Direct-to-LDS loads.  They are issued from inline assembly so that the
+// compiler neither orders later LDS reads of other stages behind them nor
+// counts them: their completion is waited for explicitly (wait_vmcnt before
+// the barrier that publishes a stage).  Waits the compiler inserts for its own
+// loads can only become stricter for the loads it does not count.  M0 (the
+// LDS destination) is saved and restored around each load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// 1 KiB: lane i writes chunk i of `dst` (wave-uniform) with the 16 B at src.
+__device__ __forceinline__ void dma16(f16x8* dst, const uint8_t* src) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(dst)), "v"(src)
+      : "memory");
+}
+
+// 256 B: lane i writes dword i of `dst` (wave-uniform) with the 4 B at src.
+__device__ __forceinline__ void dma4(uint32_t* dst, const uint8_t* src) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(dst)), "v"(src)
+      : "memory");
+}
+
+// B state of one K step in a lane: for each of its two 32-column tiles nt,
+// the 16 B of nibbles of column 64 wn + 32 nt + lane % 32 at K chunks
+// 4 g .. 4 g + 3 (g = lane / 32: exactly what its MFMA B fragments of the
+// step need), and the column's four block-scale bytes.
+struct BRaw {
+  uint4 q[2];
+};
+struct BScale {
+  uint32_t w[2];
+};
+
+// f16 pairs of the block scales 2 g and 2 g + 1 of a scale word: the
+// fragments of sub-steps 0, 1 use lo, those of 2, 3 use hi.
+struct ScalePairs {
+  f16x2 lo[2], hi[2];
+};
+
+__device__ __forceinline__ ScalePairs scale_pairs(const BScale& sc, int g) {
+  ScalePairs p;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc.w[nt] >> (16 * g), 1.0f, false);
+    p.lo[nt] = f16x2{s[0], s[0]};
+    p.hi[nt] = f16x2{s[1], s[1]};
+  }
+  return p;
+}
+
+// Exact f16 B fragment of sub-step s for column tile nt.
+__device__ __forceinline__ f16x8 b_frag(const BRaw& r, const ScalePairs& p, int nt, int s) {
+  return dequant8(word_of(r.q[nt], s), (s < 2) ? p.lo[nt] : p.hi[nt]);
+}
+
+// Accumulator element i of MFMA tile (mt, nt) for this lane sits at row
+// 8*(i/4) + 4*(lane/32) + i%4 and column lane%32 of that 32 x 32 tile.
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+
+// Tile and N tile of this workgroup: tiles come from the routing (tiles,
+// *ntiles), or without routing are the ceil(M / TM) row blocks of M rows
+// (expert 0).  False for workgroups without work.
+template <int TM>
+__device__ __forceinline__ bool tile_of(const GemmTile* tiles, const int* ntiles, int64_t M,
+                                        int n_ntiles, GemmTile* t, int* nt) {
+  const int mtiles = tiles ? *ntiles : (int)((M + TM - 1) / TM);
+  int item;
+  if (!work_item(mtiles * n_ntiles, &item)) return false;
+  const int ti = item / n_ntiles;
+  *nt = item % n_ntiles;
+  if (tiles) {
+    *t = tiles[ti];
+    return true;
+  }
+  const int64_t r0 = (int64_t)ti * TM;
+  t->expert = 0;
+  t->row0 = (int)r0;
+  t->nrows = (int)((M - r0) < TM ? (M - r0) : TM);
+  t->pad = 0;
+  return true;
+}
+
+// ------------------------------------------------------------------ L1 / L2 parameters
+struct L1Params {
+  const uint16_t* a_f16;  // exact f16 activations [rows][K] (e2m1 * block scale)
+  const float* a_gs;
+  int64_t K;
+  const uint8_t* w_q;   // [E][N2][K/2], rows interleaved by 8 (gate, up)
+  const uint8_t* w_sf;  // [E][N2][K/16]
+  const float* w_gs;    // [E]
+  int64_t N2;
+  const float* out_gs;  // global scale of the SwiGLU output
+  uint16_t* c_bf16;     // nullable [out rows][N2/2]
+  uint8_t* c_q;         // [out rows][N2/4]
+  uint8_t* c_sf;        // [out rows][N2/32]
+  uint16_t* c_f16;      // nullable [out rows][N2/2]: exact f16 of the quantized values
+  const GemmTile* tiles;  // nullable: identity tiling of M rows, expert 0
+  const int* ntiles;
+  int64_t M;            // rows when tiles == nullptr
+  const int* perm;      // nullable: sorted position -> pair id
+  int topk;             // pair id / topk = activation row
+  int n_ntiles;
+};
+
+// Global weight row of the L1 B tile row rb (0..255) for n tile nt: the tile
+// covers compact SwiGLU columns [128 nt, 128 nt + 128); the 64 B rows of wave
+// column wn = rb / 64 are the gate rows (rb & 32 == 0) and then the up rows of
+// compact columns 128 nt + 32 wn + (rb & 31), so that MFMA n tile 0 (gate)
+// and 1 (up) of a wave hold matching columns in the same lanes.
+__device__ __forceinline__ int l1_weight_row(int nt, int rb) {
+  int wn = rb >> 6, up = (rb >> 5) & 1, c = rb & 31;
+  int j = 128 * nt + 32 * wn + c;
+  int gate = 16 * (j >> 3) + (j & 7);
+  return up ? gate + 8 : gate;
+}
+
+struct L2Params {
+  const uint16_t* a_f16;  // exact f16 of the quantized L1 output [P][K], pair order
+  const float* a_gs;
+  int64_t K;            // I
+  const uint8_t* w_q;   // [E][N][K/2]
+  const uint8_t* w_sf;
+  const float* w_gs;
+  int64_t N;            // H
+  const float* row_w;   // [P] routing weight of each pair
+  float* o;             // [P][N] fp32
+  const GemmTile* tiles;
+  const int* ntiles;
+  const int* perm;
+  int n_ntiles;
+};
+
+}  // namespace nvfp4

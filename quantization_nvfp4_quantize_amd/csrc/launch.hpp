@@ -34,6 +34,8 @@ hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* g
 
 // ---- gemm.hip
 int gemm_tile_rows();
+// Rows per tile of the few-rows-per-expert kernels (decode shape).
+int skinny_tile_rows();
 // L1: c = SwiGLU(alpha * A @ W^T) -> bf16 (optional) and NVFP4 (c_q, c_sf).
 // tiles == nullptr: identity tiling of M rows with expert 0.  perm != nullptr:
 // tile rows are sorted positions, perm gives the pair id, the activation row
@@ -53,6 +55,17 @@ hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
 
 // ---- moe.hip
 size_t route_lds_bytes(int E);
+// Same operations as launch_l1 / launch_l2 on tiles of at most
+// skinny_tile_rows() rows (weights streamed through registers).
+hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
+                            const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
+                            uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
+                            const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
+                            const int* perm, int topk, hipStream_t s);
+hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
+                            const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
+                            float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
+                            const int* perm, hipStream_t s);
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
                         GemmTile* tiles, int* ntiles, int* err_count, hipStream_t s);
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,

@@ -114,6 +114,13 @@ def test_moe_rejects(lib):
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(out_dtype=3)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w2_gs=None)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(x=0x10008)), FAKE, 1 << 30, None) == -1
+    # GEMM tile height: 0 (automatic), 32 or 256 only
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(tile_rows=64)), FAKE, 1 << 30, None) == -1
+    assert b"tile_rows" in lib.nvfp4_last_error()
+    # the workspace follows the tile height (the tile list is sized per tile)
+    small = lib.moe_expert_ffn_nvfp4_workspace_size(by(_moe_args(T=4096, tile_rows=32)))
+    large = lib.moe_expert_ffn_nvfp4_workspace_size(by(_moe_args(T=4096, tile_rows=256)))
+    assert small > large > 0
     # f16 operands above 4 GiB: x (T * H * 2) and the L2 input (T * k * I * 2)
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(T=1 << 19, H=1 << 13)), FAKE, 1 << 30, None) == -2
     assert b"4 GiB" in lib.nvfp4_last_error()

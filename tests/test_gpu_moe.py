@@ -25,12 +25,16 @@ def nv():
     return nv
 
 
-def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32):
+TILES = [32, 256]  # both GEMM tile modes (32: weights streamed, 256: MFMA-bound)
+
+
+def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32, tile_rows=0):
     x = dev_bf16(x_bits)
     ti = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     tw = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).cuda()
     y, dbg = nv.moe_expert_ffn(x, ti, tw, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"],
-                               w["w2gs"], dev_f32(cfg.a2_gs), out_dtype=out_dtype, debug=True)
+                               w["w2gs"], dev_f32(cfg.a2_gs), out_dtype=out_dtype, debug=True,
+                               tile_rows=tile_rows)
     torch.cuda.synchronize()
     return y, dbg
 
@@ -65,12 +69,13 @@ def _gate(err, cos, c_err, c_cos):
     assert c_err <= 1e-3 and c_cos >= 0.9999, (c_err, c_cos)
 
 
-def test_moe_tiny_full(nv, orc):
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_tiny_full(nv, orc, tile_rows):
     cfg = synth.TINY
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
-    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
     print("tiny: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
     _gate(*res[:4])
@@ -91,7 +96,8 @@ def test_moe_tiny_bf16_output(nv, orc):
     assert err <= 5e-3 and cos >= 0.9999
 
 
-def test_moe_invalid_ids_and_duplicates(nv, orc):
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_invalid_ids_and_duplicates(nv, orc, tile_rows):
     cfg = synth.TINY
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
@@ -101,13 +107,14 @@ def test_moe_invalid_ids_and_duplicates(nv, orc):
     ids[7, 1] = cfg.E
     ids[11, 1] = 99
     ids[20, 1] = ids[20, 0]  # the same expert twice for one token
-    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
     assert host(dbg["err_count"])[0] == 3
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
     _gate(*res[:4])
 
 
-def test_moe_single_expert_topk1(nv, orc):
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_single_expert_topk1(nv, orc, tile_rows):
     """E = 1, k = 1, w = 1: the MoE reduces to one dense expert FFN."""
     import dataclasses
     cfg = dataclasses.replace(synth.TINY, E=1, topk=1, name="dense")
@@ -115,12 +122,13 @@ def test_moe_single_expert_topk1(nv, orc):
     x = synth.activations(cfg)
     ids = np.zeros((cfg.T, 1), np.int32)
     wts = np.ones((cfg.T, 1), np.float32)
-    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
     _gate(*res[:4])
 
 
-def test_moe_ragged_token_counts(nv, orc):
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_ragged_token_counts(nv, orc, tile_rows):
     """Token counts that leave ragged row tiles (and an empty expert)."""
     import dataclasses
     for T in (1, 3, 130, 257):
@@ -128,29 +136,47 @@ def test_moe_ragged_token_counts(nv, orc):
         w = gpu_weights(nv, cfg)
         x = synth.activations(cfg)
         ids, wts = synth.routing(cfg)
-        y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+        y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
         res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(T), y, dbg)
         _gate(*res[:4])
 
 
-def test_moe_deterministic(nv):
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_deterministic(nv, tile_rows):
     cfg = synth.TINY
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
-    a, _ = _gpu_moe(nv, cfg, w, x, ids, wts)
-    b, _ = _gpu_moe(nv, cfg, w, x, ids, wts)
+    a, _ = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
+    b, _ = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
     assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
 
 
-def test_moe_decode_config_sampled(nv, orc):
+def test_moe_tile_modes_agree(nv):
+    """The 32-row and the 256-row GEMM tiles sum every output element over K
+    in the same order with the same MFMA, so their results are bit-identical
+    (decode shape: every intermediate and the output)."""
+    cfg = synth.DEC
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ya, da = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=32)
+    yb, db = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=256)
+    assert np.array_equal(host_bits(da["l1_c"]), host_bits(db["l1_c"]))
+    for key in ("l1_q", "l1_sf"):
+        assert np.array_equal(host(da[key]), host(db[key])), key
+    assert np.array_equal(host(ya).view(np.uint32), host(yb).view(np.uint32))
+
+
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_decode_config_sampled(nv, orc, tile_rows):
     """Decode-shaped layer (T128 H7168 I2048 E256 top-8, Zipf routing), full
     GPU run, oracle on 6 sampled tokens."""
     cfg = synth.DEC
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
-    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
     tokens = np.array([0, 1, 37, 64, 126, 127])
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, y, dbg, device="cuda:0")
     print("decode: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
