@@ -90,14 +90,153 @@ def bench_quantize(nv, steps, warmup):
 
 
 def bench_copy(steps):
-    """A plain 512 MiB device copy (torch copy_): the reference whose FETCH_SIZE
-    and WRITE_SIZE counters calibrate the HBM traffic of the other kernels."""
+    """A plain 512 MiB device-to-device copy (torch copy_, the runtime's copy
+    kernel), launched eagerly `steps` times: the reference whose FETCH_SIZE
+    and WRITE_SIZE counters calibrate the HBM traffic of the other kernels.
+    Profile it in a run of its own (--legs copy), since the other legs also
+    copy tensors with the same kernel."""
     dev = torch.device("cuda:0")
     n = 512 << 20
     a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
-    ms = graph_time(lambda i: b.copy_(a), steps, 2)
+    torch.cuda.synchronize()
+    t0, t1 = _ev(), _ev()
+    t0.record()
+    for _ in range(steps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
     return dict(bytes_each_way=n, ms=ms, GBps=2 * n / ms / 1e6)
+
+
+# ------------------------------------------------------------------ HBM traffic
+# Kernel -> the sources it is compiled from.  Traffic taken by rocprofv3 is
+# reported only while these files are byte-identical to the profiled ones.
+KERNEL_SOURCES = {
+    "l1_gemm_swiglu_quant_kernel": ["gemm.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
+    "l2_gemm_kernel": ["gemm.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
+    "quantize_kernel": ["quantize.hip", "nvfp4_device.hpp", "launch.hpp"],
+    "dequantize_kernel": ["quantize.hip", "nvfp4_device.hpp", "launch.hpp"],
+    "combine_kernel": ["moe.hip", "launch.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "quantization_nvfp4_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, grid):
+    """HBM bytes per launch of `kernel` at grid size `grid` from the
+    committed counter summary, or None when absent or when the kernel's
+    sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic-json: "):
+            d = json.loads(line[len("traffic-json: "):])
+            if d["kernel"] == kernel and d["grid"] == grid and d["src"] == source_hash(kernel):
+                return d["bytes_per_launch"]
+    return None
+
+
+def _demangle_last(name):
+    """Innermost identifier of an Itanium-mangled function name (_Z...)."""
+    i = 3 if name.startswith("_ZN") else 2
+    last = name
+    while i < len(name) and name[i].isdigit():
+        j = i
+        while name[j].isdigit():
+            j += 1
+        n = int(name[i:j])
+        last = name[j:j + n]
+        i = j + n
+    return last
+
+
+def _short_name(name):
+    if name.startswith("_Z"):
+        return _demangle_last(name)
+    base = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    base = base.split("(")[0].split("<")[0]
+    return base.split("::")[-1].strip()
+
+
+def _read_counters(path, counter):
+    import csv
+    rows = []
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] == counter:
+                rows.append((_short_name(r["Kernel_Name"]), int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(copy_fetch, copy_write, fetch, write, cmds):
+    """Markdown summary of two counter runs (FETCH_SIZE, WRITE_SIZE in KiB
+    per dispatch), each scaled by what the same counter reads for the 512 MiB
+    copy of known size; one traffic-json line per (kernel, grid)."""
+    import collections
+    n_copy = 512 << 20
+    cf = [v for k, g, v in _read_counters(copy_fetch, "FETCH_SIZE") if k == "__amd_rocclr_copyBuffer"]
+    cw = [v for k, g, v in _read_counters(copy_write, "WRITE_SIZE") if k == "__amd_rocclr_copyBuffer"]
+    f_fac = n_copy / (np.median(cf) * 1024.0)
+    w_fac = n_copy / (np.median(cw) * 1024.0)
+    agg = collections.defaultdict(lambda: [[], []])
+    for i, (path, ctr) in enumerate(((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE"))):
+        for k, g, v in _read_counters(path, ctr):
+            if k in KERNEL_SOURCES:
+                agg[(k, g)][i].append(v)
+    out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
+           "Commands (from the repository root, on one MI355X; R = repository root):", ""]
+    out += ["    " + c for c in cmds]
+    out += ["",
+            f"Calibration: a 512 MiB device copy reads FETCH_SIZE {np.median(cf):.0f} KiB and "
+            f"WRITE_SIZE {np.median(cw):.0f} KiB per dispatch (median of {len(cf)}, {len(cw)}), "
+            f"so the scale factors are {f_fac:.4f} (fetch) and {w_fac:.4f} (write).", "",
+            "| kernel | grid | dispatches | FETCH KiB | WRITE KiB | HBM bytes per launch (scaled) |",
+            "|---|---|---|---|---|---|"]
+    js = []
+    for (k, g), (fv, wv) in sorted(agg.items()):
+        if not fv or not wv:
+            continue
+        fk, wk = float(np.mean(fv)), float(np.mean(wv))
+        b = fk * 1024 * f_fac + wk * 1024 * w_fac
+        out.append(f"| {k} | {g} | {len(fv)} | {fk:.0f} | {wk:.0f} | {b / 1e6:.2f} MB |")
+        js.append("traffic-json: " + json.dumps({"kernel": k, "grid": g, "src": source_hash(k),
+                                                 "bytes_per_launch": b, "fetch_bytes": fk * 1024 * f_fac,
+                                                 "write_bytes": wk * 1024 * w_fac}))
+    out += ["", "Machine-readable lines (bench.py reads these; src = hash of the kernel's sources):", ""]
+    out += js
+    return "\n".join(out) + "\n"
+
+
+def trace_summary(trace_csv, cmd):
+    """Markdown table of a rocprofv3 kernel trace: dispatches and average
+    duration per (kernel, grid)."""
+    import collections
+    import csv
+    agg = collections.defaultdict(list)
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            agg[(_short_name(r["Kernel_Name"]), grid)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    out = ["# Kernel trace (rocprofv3 --kernel-trace --stats)", "", "Command (from the repository root, on one "
+           "MI355X; R = repository root):", "", "    " + cmd, "",
+           "| kernel | grid (work-items) | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (k, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {g} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
+    return "\n".join(out) + "\n"
 
 
 # ------------------------------------------------------------------ MoE
@@ -246,7 +385,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="quant,expert,dec,pre")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                    help="print the markdown HBM-traffic summary of four rocprofv3 counter CSVs")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print the markdown summary of a rocprofv3 kernel trace")
+    ap.add_argument("--cmd", action="append", default=[], help="command lines quoted in a summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        sys.stdout.write(traffic_summary(*args.traffic_summary, args.cmd))
+        return
+    if args.trace_summary:
+        sys.stdout.write(trace_summary(args.trace_summary, " ".join(args.cmd)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -275,10 +425,17 @@ def main():
     if not args.no_cpu and pre is not None:
         _, xdev, ids, wts = pre
         xb = synth.activations(synth.PRE)
-        cpu = cpu_baseline_moe(synth.PRE, xb, ids, wts)
+        cpu = cpu_baseline_moe(synth.PRE, xb, ids, wts, ntok=48)
         if "quantize" in res:
             res["quantize"]["cpu_baseline"] = cpu_baseline_quantize()
     p = res.get("prefill")
+    traffic = None
+    if p:
+        cfg = synth.PRE
+        # the library's L1 launch: (ceil(P / 256) + E) row tiles x 2I / 256
+        # column tiles, 512 threads each
+        grid = ((cfg.P + 255) // 256 + cfg.E) * (2 * cfg.I // 256) * 512
+        traffic = load_traffic("l1_gemm_swiglu_quant_kernel", grid)
     line = {
         "metric": "MoE expert-FFN TFLOP/s + quantize GB/s, % of MI355X roofline (1 GPU)",
         "value": p["TFLOPs"] if p else None,
@@ -292,7 +449,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": ({"bound": "mfma", "kernel": "l1_gemm_swiglu_quant",
                       "achieved": p["l1_TFLOPs"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                      "frac": p["l1_TFLOPs"] / F16_PEAK_TFLOPS, "traffic": None} if p else None),
+                      "frac": p["l1_TFLOPs"] / F16_PEAK_TFLOPS, "traffic": traffic,
+                      "traffic_unit": "bytes per launch (HBM, rocprofv3)"} if p else None),
         "cpu_baseline": cpu,
     }
     line.update(res)
