@@ -6,21 +6,27 @@
 // same operations as in the 256-row tile kernels).
 //
 // MI355X design.  A 256-row tile leaves one workgroup per CU, and the weight
-// bytes one CU keeps in flight (two steps of 9 KiB) are far below what HBM
-// latency needs; with few rows the MFMAs are idle anyway.  Here:
+// bytes one CU keeps in flight are far below what HBM latency needs; with few
+// rows the MFMAs are idle anyway.  Here:
 //   * A workgroup of 4 waves owns 32 rows x 256 B rows (output columns); wave
 //     w owns B rows 64 w .. +64 as two 32-column MFMA tiles (for L1: the gate
 //     and the up rows of the same 32 SwiGLU columns, so SwiGLU stays within a
 //     lane), 32 fp32 accumulators per lane.
-//   * Weights never touch LDS: each lane loads, per K step of 64, the 16 B of
-//     nibbles its MFMA B fragments need from each of its two column tiles
-//     plus their scale words straight into registers, four steps ahead, and
-//     dequantizes them to exact f16 in registers (each weight once).
-//   * The 32 activation rows (exact f16) go through a 4-stage LDS ring with
-//     direct-to-LDS loads, one 1 KiB load per wave and step, issued three
-//     steps ahead; one LDS-only barrier per step.
-//   * At most 128 VGPRs and 16 KiB of LDS, so four workgroups (16 waves) share
-//     a CU and about 128 KiB of weights are in flight per CU.
+//   * K advances in super-steps of 256 (four MFMA steps of 64).  The K order
+//     inside a super-step is permuted identically for A and B so that lane
+//     half g of a column holds the contiguous K range [128 g, 128 g + 128):
+//     the two lanes of a column read one whole 128 B line of nibbles with
+//     four back-to-back 16 B loads (plus 8 scale bytes), so every line of the
+//     weight stream is used by loads issued together instead of by loads one
+//     K step apart, which the L2 would have to keep the line for.
+//   * Weights never touch LDS: each lane loads its super-step of nibbles and
+//     scales straight into registers one super-step ahead (two register sets)
+//     and dequantizes them to exact f16 in registers (each weight once).
+//   * The 32 activation rows (exact f16) of a super-step go to one of two LDS
+//     buffers with direct-to-LDS loads issued one super-step ahead; one
+//     LDS-only barrier per super-step.
+//   * 32 KiB of LDS and at most 168 VGPRs, so three workgroups (12 waves)
+//     share a CU.
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.hpp"
@@ -29,112 +35,154 @@ namespace nvfp4 {
 
 constexpr int kSkTileM = 32;
 constexpr int kSkThreads = 256;
-constexpr int kSkAStage = kSkTileM * (kStepK / 8);  // 16 B chunks of one A stage (4 KiB)
-constexpr int kSkAStages = 4;
-constexpr int kSkDepth = 4;  // weight register sets: step kb's are loaded during step kb - 4
+constexpr int kSkSteps = 4;                          // K steps of 64 per super-step
+constexpr int kSkAStage = kSkTileM * (kStepK / 8);  // 16 B chunks of one A step (4 KiB)
+constexpr int kSkABuf = kSkSteps * kSkAStage;       // one super-step of A (16 KiB)
 
 // Per-workgroup operand sources (32-bit byte offsets, as in the 256-row
-// kernels).
+// kernels).  A super-step of m K steps (m = 4, or m = 2 for a K tail of 128)
+// starting at K step kb0 holds K chunks of 8 (physical index q within the
+// super-step) as follows: MFMA step j, sub-step s, lane half g uses
+// q = 4 m g + 4 j + s, for A and for B alike.
 struct SkOperands {
-  const uint8_t* a;      // A matrix (f16 rows of K), wave-uniform
-  uint32_t a_off;        // this lane's A source: tile row 8 wave + lane / 8, chunk (lane & 7) ^ key
-  const uint8_t* bq;     // B nibbles of the tile's expert, wave-uniform
-  const uint8_t* bsf;    // B scales of the tile's expert, wave-uniform
-  uint32_t bq_off[2];    // this lane's nibbles: tile rows 64 wave + 32 nt + lane % 32, K half lane / 32
-  uint32_t bsf_off[2];   // and their scale words
+  const uint8_t* a;     // A matrix (f16 rows of K), wave-uniform
+  uint32_t a_base;      // this lane's A row (tile row 8 wave + lane / 8) + 16 (c & 3)
+  uint32_t a_hi;        // 64 (c >> 2); c = (lane & 7) ^ key(row) is the logical chunk it fetches
+  const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
+  const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
+  uint32_t bq_row[2];   // byte offsets of this lane's column rows (tile rows 64 wave + 32 nt + lane % 32)
+  uint32_t bsf_row[2];  // and of their scale rows
+  int g;                // lane half
 };
 
-// Weights of one K step in a lane (both column tiles): nibbles and scales.
+// One super-step of weights in a lane: for each column tile nt, the 16 B of
+// nibbles of each MFMA step j and the scale bytes (two per step: step j's
+// pair is bits 16 (j & 1) of s[nt][j >> 1]).
 struct SkB {
-  BRaw r;
-  BScale s;
+  uint4 q[2][kSkSteps];
+  uint32_t s[2][2];
 };
 
-__device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int kb) {
+// Steps of super-step ss (nfull whole super-steps, then a tail of 2 steps if
+// the K steps are not a multiple of 4).
+__device__ __forceinline__ int sk_steps(int ss, int nfull) { return ss < nfull ? kSkSteps : 2; }
+
+// Direct loads of A for super-step ss into buf: step j's 32 rows x 128 B;
+// wave w fetches rows 8 w .. 8 w + 7 (1 KiB per step).  A tail super-step
+// loads its two steps twice (the second copy is not read).
+__device__ __forceinline__ void sk_load_a(f16x8* buf, const SkOperands& op, int ss, int m, int wave) {
+  const uint8_t* src = op.a + (size_t)ss * (kSkSteps * kStepK * 2) + op.a_hi * (uint32_t)m + op.a_base;
+#pragma unroll
+  for (int j = 0; j < kSkSteps; ++j) dma16(buf + j * kSkAStage + wave * 64, src + 64 * (j & (m - 1)));
+}
+
+// Weights of super-step ss: four 16 B loads of consecutive addresses per
+// column tile (one 128 B line for the two lanes of a column) and its scale
+// bytes; a tail super-step repeats its two steps.
+__device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int ss, int m) {
   SkB b;
-  const uint8_t* q = op.bq + (size_t)kb * (kStepK / 2);
-  const uint8_t* sf = op.bsf + (size_t)kb * (kStepK / 16);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    b.r.q[nt] = *reinterpret_cast<const uint4*>(q + op.bq_off[nt]);
-    b.s.w[nt] = *reinterpret_cast<const uint32_t*>(sf + op.bsf_off[nt]);
+    const uint8_t* q = op.bq + (size_t)ss * (kSkSteps * kStepK / 2) + op.bq_row[nt] + 16 * m * op.g;
+    const uint8_t* sf = op.bsf + (size_t)ss * (kSkSteps * kStepK / 16) + op.bsf_row[nt] + 2 * m * op.g;
+#pragma unroll
+    for (int j = 0; j < kSkSteps; ++j) b.q[nt][j] = *reinterpret_cast<const uint4*>(q + 16 * (j & (m - 1)));
+    b.s[nt][0] = *reinterpret_cast<const uint32_t*>(sf);
+    b.s[nt][1] = *reinterpret_cast<const uint32_t*>(sf + (m == kSkSteps ? 4 : 0));
   }
   return b;
 }
 
-// One K step kb on A stage KA = kb % 4 with weight set W[KA]: 8 MFMAs (4
-// sub-steps x 2 column tiles), each sub-step's B fragments dequantized just
-// before its MFMAs.  Then W[KA] is refilled with step kb + 4 (4 loads) and the
-// wave's direct load of A step kb + 3 goes to A stage (KA + 3) % 4 (last read
-// in step kb - 1), in that order: 5 loads per step, so waiting at the end of
-// step kb until at most 10 are outstanding means A of step kb + 1 (the last
-// load of step kb - 2) has landed.  Loads past the end re-read the last step.
-template <int KA>
-__device__ __forceinline__ void sk_step(f16x8* lds_a, const f16x8* const (&ra)[4], SkB (&W)[kSkDepth],
-                                        int kb, int last, const SkOperands& op, int wave, int lane,
+// The MFMAs of step j from A buffer buf and weights W.
+__device__ __forceinline__ void sk_step(const f16x8* buf, const int (&ra)[4], const SkB& W, int j,
                                         f32x16 (&acc)[2]) {
-  const int g = lane >> 5;
-  const ScalePairs pc = scale_pairs(W[KA].s, g);
-  constexpr int aoff = KA * kSkAStage;
-  f16x8 fa[2];
-  fa[0] = ra[0][aoff];
+  f16x2 lo[2], hi[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(W.s[nt][j >> 1] >> (16 * (j & 1)), 1.0f, false);
+    lo[nt] = f16x2{sc[0], sc[0]};
+    hi[nt] = f16x2{sc[1], sc[1]};
+  }
+  const int off = j * kSkAStage;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    if (s < 3) fa[(s + 1) & 1] = ra[s + 1][aoff];
-    const f16x8 b0 = b_frag(W[KA].r, pc, 0, s);
-    const f16x8 b1 = b_frag(W[KA].r, pc, 1, s);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1], b0, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1], b1, acc[1], 0, 0, 0);
+    const f16x8 fa = buf[ra[s] + off];
+    const f16x8 b0 = dequant8(word_of(W.q[0][j], s), s < 2 ? lo[0] : hi[0]);
+    const f16x8 b1 = dequant8(word_of(W.q[1][j], s), s < 2 ? lo[1] : hi[1]);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, b0, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, b1, acc[1], 0, 0, 0);
   }
-  SCHED_FENCE();
-  W[KA] = sk_load_b(op, min(kb + kSkDepth, last));
-  dma16(lds_a + ((KA + 3) % 4) * kSkAStage + wave * 64,
-        op.a + (size_t)min(kb + 3, last) * (kStepK * 2) + op.a_off);
-  SCHED_FENCE();
-  wait_vmcnt<10>();
-  lds_barrier();
+  SCHED_FENCE();  // keeps each step's fragments from being hoisted into the previous one
 }
 
-// The K loop over nk steps; ends with all loads landed and every wave past
-// its last LDS read.
+// Super-step ss on A buffer BUF and register set W[BUF]: wait for its loads
+// (issued one super-step earlier) and publish A with a barrier (which also
+// tells every wave that buffer BUF ^ 1 is no longer read), issue the loads of
+// super-step ss + 1 (A first, then B; past the end they repeat the last
+// super-step and are not used), then run its MFMAs.
+template <int BUF>
+__device__ __forceinline__ void sk_super(f16x8* lds_a, const int (&ra)[4], SkB (&W)[2], const SkOperands& op,
+                                         int ss, int nss, int nfull, int wave, f32x16 (&acc)[2]) {
+  wait_vmcnt<0>();
+  lds_barrier();
+  const int nx = min(ss + 1, nss - 1);
+  const int mx = sk_steps(nx, nfull);
+  sk_load_a(lds_a + (BUF ^ 1) * kSkABuf, op, nx, mx, wave);
+  W[BUF ^ 1] = sk_load_b(op, nx, mx);
+  SCHED_FENCE();
+  const f16x8* buf = lds_a + BUF * kSkABuf;
+  sk_step(buf, ra, W[BUF], 0, acc);
+  sk_step(buf, ra, W[BUF], 1, acc);
+  if (ss < nfull) {
+    sk_step(buf, ra, W[BUF], 2, acc);
+    sk_step(buf, ra, W[BUF], 3, acc);
+  }
+}
+
+// The K loop over nk steps of 64 (nk even); ends with all loads landed and
+// every wave past its last LDS read.
 __device__ __forceinline__ void sk_mainloop(f16x8* lds_a, const SkOperands& op, int nk,
                                             f32x16 (&acc)[2]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r = lane & 31;
-  const int last = nk - 1;
+  const int nfull = nk / kSkSteps;
+  const int nss = nfull + (nk % kSkSteps ? 1 : 0);
+  SkB W[2];
+  sk_load_a(lds_a, op, 0, sk_steps(0, nfull), wave);
+  W[0] = sk_load_b(op, 0, sk_steps(0, nfull));
+  // A fragment chunk of sub-step s: row r, logical chunk 4 g + s
+  int ra[4];
 #pragma unroll
-  for (int j = 0; j < 3; ++j)
-    dma16(lds_a + j * kSkAStage + wave * 64, op.a + (size_t)min(j, last) * (kStepK * 2) + op.a_off);
-  SkB W[kSkDepth];
-#pragma unroll
-  for (int j = 0; j < kSkDepth; ++j) W[j] = sk_load_b(op, min(j, last));
-  // A fragment pointers of sub-step s: row r, logical chunk 4 g + s
-  const f16x8* ra[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) ra[s] = lds_a + r * 8 + ((4 * g + s) ^ swz_key(r));
+  for (int s = 0; s < 4; ++s) ra[s] = r * 8 + ((4 * g + s) ^ swz_key(r));
   acc[0] = f32x16{};
   acc[1] = f32x16{};
-  wait_vmcnt<0>();
-  lds_barrier();
-  int kb = 0;
-  for (; kb + 4 <= nk; kb += 4) {
-    sk_step<0>(lds_a, ra, W, kb, last, op, wave, lane, acc);
-    sk_step<1>(lds_a, ra, W, kb + 1, last, op, wave, lane, acc);
-    sk_step<2>(lds_a, ra, W, kb + 2, last, op, wave, lane, acc);
-    sk_step<3>(lds_a, ra, W, kb + 3, last, op, wave, lane, acc);
+  for (int ss = 0; ss < nss; ss += 2) {
+    sk_super<0>(lds_a, ra, W, op, ss, nss, nfull, wave, acc);
+    if (ss + 1 < nss) sk_super<1>(lds_a, ra, W, op, ss + 1, nss, nfull, wave, acc);
   }
-  const int rem = nk - kb;
-  if (rem > 0) sk_step<0>(lds_a, ra, W, kb, last, op, wave, lane, acc);
-  if (rem > 1) sk_step<1>(lds_a, ra, W, kb + 1, last, op, wave, lane, acc);
-  if (rem > 2) sk_step<2>(lds_a, ra, W, kb + 2, last, op, wave, lane, acc);
   wait_vmcnt<0>();
   lds_barrier();
 }
 
+// Operand sources of this lane for a tile: A row `arow` (lane's tile row is
+// 8 wave + lane / 8), and the B rows (global weight rows) brow[0], brow[1].
+__device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64_t K, const uint32_t (&brow)[2],
+                                            int lane, int R) {
+  const int c = (lane & 7) ^ swz_key(R);
+  op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)(c & 3);
+  op.a_hi = 64u * (uint32_t)(c >> 2);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    op.bq_row[j] = brow[j] * (uint32_t)(K / 2);
+    op.bsf_row[j] = brow[j] * (uint32_t)(K / 16);
+  }
+  op.g = lane >> 5;
+}
+
 // ------------------------------------------------------------------ L1
-__global__ __launch_bounds__(kSkThreads, 4) void l1_skinny_kernel(L1Params p) {
-  __shared__ f16x8 lds_a[kSkAStages * kSkAStage];
+__global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
+  __shared__ f16x8 lds_a[2 * kSkABuf];
   GemmTile t;
   int nt;
   if (!tile_of<kSkTileM>(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
@@ -146,19 +194,16 @@ __global__ __launch_bounds__(kSkThreads, 4) void l1_skinny_kernel(L1Params p) {
   };
   SkOperands op;
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
+  op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);
   {
     const int R = 8 * wave + (lane >> 3);
     const int o = out_row_of(R);
     const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
-    op.a_off = arow * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
-  }
-  op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
-  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);
+    uint32_t brow[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t row = (uint32_t)l1_weight_row(nt, 64 * wave + 32 * j + (lane & 31));
-    op.bq_off[j] = row * (uint32_t)(p.K / 2) + 16u * (lane >> 5);
-    op.bsf_off[j] = row * (uint32_t)(p.K / 16);
+    for (int j = 0; j < 2; ++j) brow[j] = (uint32_t)l1_weight_row(nt, 64 * wave + 32 * j + (lane & 31));
+    sk_operands(op, arow, p.K, brow, lane, R);
   }
   f32x16 acc[2];
   sk_mainloop(lds_a, op, (int)(p.K / kStepK), acc);
@@ -166,7 +211,7 @@ __global__ __launch_bounds__(kSkThreads, 4) void l1_skinny_kernel(L1Params p) {
   // epilogue: SwiGLU -> bf16 tile (32 x 128) in LDS, then NVFP4 of its rows
   constexpr int kCStride = 136;
   constexpr int kCTileChunks = kSkTileM * kCStride * 2 / 16;
-  static_assert(kCTileChunks + 32 + kSkTileM / 4 <= kSkAStages * kSkAStage, "epilogue LDS");
+  static_assert(kCTileChunks + 32 + kSkTileM / 4 <= 2 * kSkABuf, "epilogue LDS");
   uint16_t* ctile = reinterpret_cast<uint16_t*>(lds_a);
   float* rtab = reinterpret_cast<float*>(lds_a + kCTileChunks);
   int* out_row = reinterpret_cast<int*>(lds_a + kCTileChunks + 32);
@@ -203,8 +248,8 @@ __global__ __launch_bounds__(kSkThreads, 4) void l1_skinny_kernel(L1Params p) {
 }
 
 // ------------------------------------------------------------------ L2
-__global__ __launch_bounds__(kSkThreads, 4) void l2_skinny_kernel(L2Params p) {
-  __shared__ f16x8 lds_a[kSkAStages * kSkAStage];
+__global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
+  __shared__ f16x8 lds_a[2 * kSkABuf];
   GemmTile t;
   int nt;
   if (!tile_of<kSkTileM>(p.tiles, p.ntiles, 0, p.n_ntiles, &t, &nt)) return;
@@ -213,17 +258,14 @@ __global__ __launch_bounds__(kSkThreads, 4) void l2_skinny_kernel(L2Params p) {
   auto pair_of = [&](int r) -> int { return p.perm[t.row0 + (r < t.nrows ? r : 0)]; };
   SkOperands op;
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
-  {
-    const int R = 8 * wave + (lane >> 3);
-    op.a_off = (uint32_t)pair_of(R) * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
-  }
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
+  {
+    const int R = 8 * wave + (lane >> 3);
+    uint32_t brow[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t row = (uint32_t)(nt * kTileN + 64 * wave + 32 * j + (lane & 31));
-    op.bq_off[j] = row * (uint32_t)(p.K / 2) + 16u * (lane >> 5);
-    op.bsf_off[j] = row * (uint32_t)(p.K / 16);
+    for (int j = 0; j < 2; ++j) brow[j] = (uint32_t)(nt * kTileN + 64 * wave + 32 * j + (lane & 31));
+    sk_operands(op, (uint32_t)pair_of(R), p.K, brow, lane, R);
   }
   f32x16 acc[2];
   sk_mainloop(lds_a, op, (int)(p.K / kStepK), acc);
@@ -256,6 +298,7 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
+  if (K % (2 * kStepK) != 0) return hipErrorInvalidValue;  // whole super-steps or a tail of 2 steps
   l1_skinny_kernel<<<(unsigned)grid, kSkThreads, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -267,6 +310,7 @@ hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, tiles, ntiles, perm, (int)(N / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
+  if (K % (2 * kStepK) != 0) return hipErrorInvalidValue;  // whole super-steps or a tail of 2 steps
   l2_skinny_kernel<<<(unsigned)grid, kSkThreads, 0, s>>>(p);
   return hipGetLastError();
 }
