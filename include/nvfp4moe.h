@@ -148,9 +148,10 @@ typedef struct {
   void *const *stage_events;
   /* GEMM tile height: 0 chooses from the routing shape (32-row tiles that
      stream the weights when there are at most 16 pairs per expert on
-     average, else 256-row tiles); 32 or 256 forces one (other values:
-     NVFP4_ERR_INVALID_ARG).  The results are the same either way up to the
-     fp32 summation order inside the GEMMs. */
+     average and H and I are multiples of 256 or equal 128, else 256-row
+     tiles); 32 or 256 forces one (other values: NVFP4_ERR_INVALID_ARG; 32
+     with other H or I: NVFP4_ERR_UNSUPPORTED).  The results are the same
+     either way up to the fp32 summation order inside the GEMMs. */
   int32_t tile_rows;
 } nvfp4_moe_args;
 

@@ -162,7 +162,8 @@ struct MoeLayout {
 int64_t moe_tile_rows(const nvfp4_moe_args* a) {
   if (a->tile_rows) return a->tile_rows;
   const int64_t P = a->T * a->topk;
-  return P <= 16 * a->E ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
+  const bool fits = nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I);
+  return fits && P <= 16 * a->E ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
 }
 
 MoeLayout moe_layout(const nvfp4_moe_args* a) {
@@ -217,6 +218,11 @@ int moe_validate(const nvfp4_moe_args* a) {
       a->tile_rows != nvfp4::gemm_tile_rows())
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: tile_rows must be 0, %d or %d",
                 nvfp4::skinny_tile_rows(), nvfp4::gemm_tile_rows());
+  if (a->tile_rows == nvfp4::skinny_tile_rows() &&
+      !(nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I)))
+    return fail(NVFP4_ERR_UNSUPPORTED,
+                "moe_expert_ffn_nvfp4: tile_rows %d needs H and I multiples of 256 (or 128)",
+                nvfp4::skinny_tile_rows());
   if (a->T > 0 && (!a->x || !a->topk_ids || !a->topk_w || !a->w1_q || !a->w1_sf || !a->w1_gs ||
                    !a->w2_q || !a->w2_sf || !a->w2_gs || !a->a2_gs || !a->out))
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: null required pointer");

@@ -51,17 +51,28 @@ struct SkOperands {
   const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
   uint32_t bq_row[2];   // byte offsets of this lane's column rows (tile rows 64 wave + 32 nt + lane % 32)
-  uint32_t bsf_row[2];  // and of their scale rows
+  uint32_t sf_dma[4];   // scale-row offsets of the tile rows 64 wave + 16 i + lane / 4 (i < 4)
+  int sf_tr[4];         // those tile rows
   int g;                // lane half
 };
 
-// One super-step of weights in a lane: for each column tile nt, the 16 B of
-// nibbles of each MFMA step j and the scale bytes (two per step: step j's
-// pair is bits 16 (j & 1) of s[nt][j >> 1]).
+// The nibbles of one super-step in a lane: for each column tile nt, the 16 B
+// of each MFMA step j.
 struct SkB {
   uint4 q[2][kSkSteps];
-  uint32_t s[2][2];
 };
+
+// Scales in LDS.  Every 256 K (one super-step) a weight row has 16 scale
+// bytes.  The scales of four whole super-steps (a macro-step: 64 B per row,
+// 16 KiB per tile) are brought in with one direct load per lane and wave for
+// each quarter of the rows, 4 lanes per row, so each scale line is fetched by
+// loads issued together.  Row tr keeps its 16 B chunk c (super-step c of the
+// macro-step) at position c ^ ((tr >> 2) & 3), which spreads the 32 rows one
+// read instruction touches over distinct banks.  The 8 scale bytes of a K
+// tail of 128 go to a separate 2 KiB area (row tr at bytes 8 tr).
+constexpr int kSkSfMacro = kTileN * 64;  // bytes
+constexpr int kSkSfTail = kTileN * 8;
+__device__ __forceinline__ int sk_sf_swz(int tr) { return (tr >> 2) & 3; }
 
 // Steps of super-step ss (nfull whole super-steps, then a tail of 2 steps if
 // the K steps are not a multiple of 4).
@@ -76,30 +87,72 @@ __device__ __forceinline__ void sk_load_a(f16x8* buf, const SkOperands& op, int 
   for (int j = 0; j < kSkSteps; ++j) dma16(buf + j * kSkAStage + wave * 64, src + 64 * (j & (m - 1)));
 }
 
-// Weights of super-step ss: four 16 B loads of consecutive addresses per
-// column tile (one 128 B line for the two lanes of a column) and its scale
-// bytes; a tail super-step repeats its two steps.
+// Nibbles of super-step ss: four 16 B loads of consecutive addresses per
+// column tile (one 128 B line for the two lanes of a column); a tail
+// super-step repeats its two steps.
 __device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int ss, int m) {
   SkB b;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const uint8_t* q = op.bq + (size_t)ss * (kSkSteps * kStepK / 2) + op.bq_row[nt] + 16 * m * op.g;
-    const uint8_t* sf = op.bsf + (size_t)ss * (kSkSteps * kStepK / 16) + op.bsf_row[nt] + 2 * m * op.g;
 #pragma unroll
     for (int j = 0; j < kSkSteps; ++j) b.q[nt][j] = *reinterpret_cast<const uint4*>(q + 16 * (j & (m - 1)));
-    b.s[nt][0] = *reinterpret_cast<const uint32_t*>(sf);
-    b.s[nt][1] = *reinterpret_cast<const uint32_t*>(sf + (m == kSkSteps ? 4 : 0));
   }
   return b;
 }
 
-// The MFMAs of step j from A buffer buf and weights W.
-__device__ __forceinline__ void sk_step(const f16x8* buf, const int (&ra)[4], const SkB& W, int j,
-                                        f32x16 (&acc)[2]) {
+// Direct loads of the scales of macro-step mac (super-steps 4 mac .. 4 mac
+// + 3; chunks past the last whole super-step re-read it and are not used).
+__device__ __forceinline__ void sk_load_sf_macro(uint8_t* sfbuf, const SkOperands& op, int mac, int nfull,
+                                                 int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (lane & 3) ^ sk_sf_swz(op.sf_tr[i]);
+    const int ssrc = min(4 * mac + c, nfull - 1);
+    dma16(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf + op.sf_dma[i] + 16 * ssrc);
+  }
+}
+
+// Direct loads of the 8 tail scale bytes of every tile row (dword d of the
+// area holds half d & 1 of row d >> 1); row_of maps a tile row to its scale
+// row offset.
+template <class RowOf>
+__device__ __forceinline__ void sk_load_sf_tail(uint8_t* sftail, const SkOperands& op, int nfull, int wave,
+                                                int lane, RowOf row_of) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int d = 256 * i + 64 * wave + lane;
+    dma4(reinterpret_cast<uint32_t*>(sftail + 1024 * i + 256 * wave),
+         op.bsf + row_of(d >> 1) + 16 * nfull + 4 * (d & 1));
+  }
+}
+
+// This lane's scale words of super-step ss for its two column tiles: step j's
+// pair of block scales is bits 16 (j & 1) of s[nt][j >> 1].
+__device__ __forceinline__ void sk_read_sf(const uint8_t* sfbuf, const uint8_t* sftail, int ss, int nfull,
+                                           int wave, int lane, uint32_t (&s)[2][2]) {
+  const int g = lane >> 5;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int tr = 64 * wave + 32 * nt + (lane & 31);
+    if (ss < nfull) {
+      const uint2 v = *reinterpret_cast<const uint2*>(sfbuf + 64 * tr + 16 * ((ss & 3) ^ sk_sf_swz(tr)) + 8 * g);
+      s[nt][0] = v.x;
+      s[nt][1] = v.y;
+    } else {
+      s[nt][0] = *reinterpret_cast<const uint32_t*>(sftail + 8 * tr + 4 * g);
+      s[nt][1] = 0;
+    }
+  }
+}
+
+// The MFMAs of step j from A buffer buf, nibbles W and scale words sw.
+__device__ __forceinline__ void sk_step(const f16x8* buf, const int (&ra)[4], const SkB& W,
+                                        const uint32_t (&sw)[2][2], int j, f32x16 (&acc)[2]) {
   f16x2 lo[2], hi[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(W.s[nt][j >> 1] >> (16 * (j & 1)), 1.0f, false);
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[nt][j >> 1] >> (16 * (j & 1)), 1.0f, false);
     lo[nt] = f16x2{sc[0], sc[0]};
     hi[nt] = f16x2{sc[1], sc[1]};
   }
@@ -115,41 +168,63 @@ __device__ __forceinline__ void sk_step(const f16x8* buf, const int (&ra)[4], co
   SCHED_FENCE();  // keeps each step's fragments from being hoisted into the previous one
 }
 
+struct SkLds {
+  f16x8* a;        // two A buffers of one super-step
+  uint8_t* sf;     // scales of one macro-step
+  uint8_t* sftail; // scales of the K tail
+};
+
 // Super-step ss on A buffer BUF and register set W[BUF]: wait for its loads
-// (issued one super-step earlier) and publish A with a barrier (which also
-// tells every wave that buffer BUF ^ 1 is no longer read), issue the loads of
-// super-step ss + 1 (A first, then B; past the end they repeat the last
-// super-step and are not used), then run its MFMAs.
-template <int BUF>
-__device__ __forceinline__ void sk_super(f16x8* lds_a, const int (&ra)[4], SkB (&W)[2], const SkOperands& op,
-                                         int ss, int nss, int nfull, int wave, f32x16 (&acc)[2]) {
+// (issued one super-step earlier) and publish them with a barrier (which
+// also tells every wave that A buffer BUF ^ 1 is no longer read), read its
+// scale words; at the end of a macro-step, once every wave has read them,
+// fetch the next macro-step's scales; issue the loads of super-step ss + 1
+// (A first, then B; past the end they repeat the last super-step and are not
+// used, and the tail's scales with the tail), then run its MFMAs.
+template <int BUF, class RowOf>
+__device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB (&W)[2], const SkOperands& op,
+                                         int ss, int nss, int nfull, int wave, int lane, f32x16 (&acc)[2],
+                                         RowOf row_of) {
   wait_vmcnt<0>();
   lds_barrier();
+  uint32_t sw[2][2];
+  sk_read_sf(L.sf, L.sftail, ss, nfull, wave, lane, sw);
+  if ((ss & 3) == 3 && ss + 1 < nfull) {
+    lds_barrier();
+    sk_load_sf_macro(L.sf, op, (ss + 1) >> 2, nfull, wave, lane);
+  }
   const int nx = min(ss + 1, nss - 1);
   const int mx = sk_steps(nx, nfull);
-  sk_load_a(lds_a + (BUF ^ 1) * kSkABuf, op, nx, mx, wave);
+  sk_load_a(L.a + (BUF ^ 1) * kSkABuf, op, nx, mx, wave);
   W[BUF ^ 1] = sk_load_b(op, nx, mx);
+  if (ss + 1 == nfull && nss > nfull) sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
   SCHED_FENCE();
-  const f16x8* buf = lds_a + BUF * kSkABuf;
-  sk_step(buf, ra, W[BUF], 0, acc);
-  sk_step(buf, ra, W[BUF], 1, acc);
+  const f16x8* buf = L.a + BUF * kSkABuf;
+  sk_step(buf, ra, W[BUF], sw, 0, acc);
+  sk_step(buf, ra, W[BUF], sw, 1, acc);
   if (ss < nfull) {
-    sk_step(buf, ra, W[BUF], 2, acc);
-    sk_step(buf, ra, W[BUF], 3, acc);
+    sk_step(buf, ra, W[BUF], sw, 2, acc);
+    sk_step(buf, ra, W[BUF], sw, 3, acc);
   }
 }
 
 // The K loop over nk steps of 64 (nk even); ends with all loads landed and
-// every wave past its last LDS read.
-__device__ __forceinline__ void sk_mainloop(f16x8* lds_a, const SkOperands& op, int nk,
-                                            f32x16 (&acc)[2]) {
+// every wave past its last LDS read.  row_of(tr) is the byte offset of the
+// scale row of tile row tr within the expert's scales.
+template <class RowOf>
+__device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op, int nk, f32x16 (&acc)[2],
+                                            RowOf row_of) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r = lane & 31;
   const int nfull = nk / kSkSteps;
   const int nss = nfull + (nk % kSkSteps ? 1 : 0);
   SkB W[2];
-  sk_load_a(lds_a, op, 0, sk_steps(0, nfull), wave);
+  sk_load_a(L.a, op, 0, sk_steps(0, nfull), wave);
+  if (nfull > 0)
+    sk_load_sf_macro(L.sf, op, 0, nfull, wave, lane);
+  else
+    sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
   W[0] = sk_load_b(op, 0, sk_steps(0, nfull));
   // A fragment chunk of sub-step s: row r, logical chunk 4 g + s
   int ra[4];
@@ -158,31 +233,40 @@ __device__ __forceinline__ void sk_mainloop(f16x8* lds_a, const SkOperands& op, 
   acc[0] = f32x16{};
   acc[1] = f32x16{};
   for (int ss = 0; ss < nss; ss += 2) {
-    sk_super<0>(lds_a, ra, W, op, ss, nss, nfull, wave, acc);
-    if (ss + 1 < nss) sk_super<1>(lds_a, ra, W, op, ss + 1, nss, nfull, wave, acc);
+    sk_super<0>(L, ra, W, op, ss, nss, nfull, wave, lane, acc, row_of);
+    if (ss + 1 < nss) sk_super<1>(L, ra, W, op, ss + 1, nss, nfull, wave, lane, acc, row_of);
   }
   wait_vmcnt<0>();
   lds_barrier();
 }
 
 // Operand sources of this lane for a tile: A row `arow` (lane's tile row is
-// 8 wave + lane / 8), and the B rows (global weight rows) brow[0], brow[1].
-__device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64_t K, const uint32_t (&brow)[2],
-                                            int lane, int R) {
+// 8 wave + lane / 8); row_of(tr) gives the global weight row of tile row tr.
+template <class WRow>
+__device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64_t K, int wave, int lane, int R,
+                                            WRow wrow) {
   const int c = (lane & 7) ^ swz_key(R);
   op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)(c & 3);
   op.a_hi = 64u * (uint32_t)(c >> 2);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    op.bq_row[j] = brow[j] * (uint32_t)(K / 2);
-    op.bsf_row[j] = brow[j] * (uint32_t)(K / 16);
+  for (int j = 0; j < 2; ++j) op.bq_row[j] = (uint32_t)wrow(64 * wave + 32 * j + (lane & 31)) * (uint32_t)(K / 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    op.sf_tr[i] = 64 * wave + 16 * i + (lane >> 2);
+    op.sf_dma[i] = (uint32_t)wrow(op.sf_tr[i]) * (uint32_t)(K / 16);
   }
   op.g = lane >> 5;
 }
 
+#define SK_LDS_DECL                                              \
+  __shared__ f16x8 lds_a[2 * kSkABuf];                           \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sf[kSkSfMacro]; \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sft[kSkSfTail]; \
+  const SkLds L{lds_a, lds_sf, lds_sft}
+
 // ------------------------------------------------------------------ L1
 __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
-  __shared__ f16x8 lds_a[2 * kSkABuf];
+  SK_LDS_DECL;
   GemmTile t;
   int nt;
   if (!tile_of<kSkTileM>(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
@@ -192,6 +276,8 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     const int rr = r < t.nrows ? r : 0;
     return p.perm ? p.perm[t.row0 + rr] : t.row0 + rr;
   };
+  auto wrow = [&](int tr) { return l1_weight_row(nt, tr); };
+  auto sf_row = [&](int tr) { return (uint32_t)l1_weight_row(nt, tr) * (uint32_t)(p.K / 16); };
   SkOperands op;
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
   op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
@@ -200,13 +286,10 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     const int R = 8 * wave + (lane >> 3);
     const int o = out_row_of(R);
     const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
-    uint32_t brow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) brow[j] = (uint32_t)l1_weight_row(nt, 64 * wave + 32 * j + (lane & 31));
-    sk_operands(op, arow, p.K, brow, lane, R);
+    sk_operands(op, arow, p.K, wave, lane, R, wrow);
   }
   f32x16 acc[2];
-  sk_mainloop(lds_a, op, (int)(p.K / kStepK), acc);
+  sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
 
   // epilogue: SwiGLU -> bf16 tile (32 x 128) in LDS, then NVFP4 of its rows
   constexpr int kCStride = 136;
@@ -249,26 +332,22 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
 
 // ------------------------------------------------------------------ L2
 __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
-  __shared__ f16x8 lds_a[2 * kSkABuf];
+  SK_LDS_DECL;
   GemmTile t;
   int nt;
   if (!tile_of<kSkTileM>(p.tiles, p.ntiles, 0, p.n_ntiles, &t, &nt)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto pair_of = [&](int r) -> int { return p.perm[t.row0 + (r < t.nrows ? r : 0)]; };
+  auto wrow = [&](int tr) { return nt * kTileN + tr; };
+  auto sf_row = [&](int tr) { return (uint32_t)(nt * kTileN + tr) * (uint32_t)(p.K / 16); };
   SkOperands op;
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
-  {
-    const int R = 8 * wave + (lane >> 3);
-    uint32_t brow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) brow[j] = (uint32_t)(nt * kTileN + 64 * wave + 32 * j + (lane & 31));
-    sk_operands(op, (uint32_t)pair_of(R), p.K, brow, lane, R);
-  }
+  sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), wrow);
   f32x16 acc[2];
-  sk_mainloop(lds_a, op, (int)(p.K / kStepK), acc);
+  sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
   int* out_row = reinterpret_cast<int*>(lds_a);
   if (tid < kSkTileM) out_row[tid] = pair_of(tid);
   __syncthreads();
@@ -289,6 +368,10 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
 // ------------------------------------------------------------------ launchers
 int skinny_tile_rows() { return kSkTileM; }
 
+// K of whole super-steps (the scale rows then stay 16-byte aligned for the
+// direct loads), or a single tail super-step of 128.
+bool skinny_supports_k(int64_t K) { return K > 0 && (K % (kSkSteps * kStepK) == 0 || K == 2 * kStepK); }
+
 hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
@@ -298,7 +381,7 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
-  if (K % (2 * kStepK) != 0) return hipErrorInvalidValue;  // whole super-steps or a tail of 2 steps
+  if (!skinny_supports_k(K)) return hipErrorInvalidValue;
   l1_skinny_kernel<<<(unsigned)grid, kSkThreads, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -310,7 +393,7 @@ hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, tiles, ntiles, perm, (int)(N / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
-  if (K % (2 * kStepK) != 0) return hipErrorInvalidValue;  // whole super-steps or a tail of 2 steps
+  if (!skinny_supports_k(K)) return hipErrorInvalidValue;
   l2_skinny_kernel<<<(unsigned)grid, kSkThreads, 0, s>>>(p);
   return hipGetLastError();
 }

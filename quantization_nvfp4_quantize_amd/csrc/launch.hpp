@@ -36,6 +36,8 @@ hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* g
 int gemm_tile_rows();
 // Rows per tile of the few-rows-per-expert kernels (decode shape).
 int skinny_tile_rows();
+// Whether those kernels take a reduction length K (a multiple of 256, or 128).
+bool skinny_supports_k(int64_t K);
 // L1: c = SwiGLU(alpha * A @ W^T) -> bf16 (optional) and NVFP4 (c_q, c_sf).
 // tiles == nullptr: identity tiling of M rows with expert 0.  perm != nullptr:
 // tile rows are sorted positions, perm gives the pair id, the activation row
