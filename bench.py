@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 MoE expert-FFN hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dec,pre] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dec,pre] [--no-cpu] [--no-modes]
 
 Prints one JSON line.  `value` is the prefill-shaped MoE layer (T16384 H7168
 I2048 E256 top-8: activation global scale + quantize, grouping, L1 GEMM with
@@ -11,6 +11,10 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
             copies (> 256 MiB Infinity Cache); also dynamic scale, dequantize
   expert    single-expert L1 stage M4096 K7168 N 2x2048
   dec       decode-shaped layer T128 (Zipf routing; weight-streaming bound)
+  prefill_unfused / prefill_dynamic  the same prefill layer with the L1
+            output written as bf16 and quantized in a separate pass, with the
+            supplied scale (the fusion's saving) or with the dynamic
+            amax / 2688 scale (and y's distance from the fused run)
 Timing: W untimed warmups, then K timed steps.  quantize and expert replay a
 HIP graph of K launches between two events (no host gaps); the MoE legs run
 eagerly and the library records HIP events between its stages on the same
@@ -259,18 +263,24 @@ def moe_weights(nv, cfg):
     return w1q, w1sf, w1gs, w2q, w2sf, w2gs
 
 
-def bench_moe(nv, cfg, steps, warmup):
+def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
+    """One MoE layer config; mode "fused" (L1 output quantized in the GEMM
+    epilogue with the supplied scale), "unfused" (bf16 L1 output, separate
+    quantization pass, supplied scale) or "dynamic" (unfused, with the
+    dynamic amax / 2688 scale of the L1 output)."""
     import synth
     dev = torch.device("cuda:0")
-    w = moe_weights(nv, cfg)
+    if w is None:
+        w = moe_weights(nv, cfg)
     xb = synth.activations(cfg)
     x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
     ids, wts = synth.routing(cfg)
     ti = torch.from_numpy(ids).to(dev)
     tw = torch.from_numpy(wts).to(dev)
-    a2 = torch.tensor([cfg.a2_gs], dtype=torch.float32, device=dev)
+    a2 = None if mode == "dynamic" else torch.tensor([cfg.a2_gs], dtype=torch.float32, device=dev)
+    a2_out = torch.empty(1, dtype=torch.float32, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
-    args = nv.moe_args(x, ti, tw, *w, a2, out)
+    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out, l1_unfused=(mode == "unfused"))
     ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         nv.moe_expert_ffn_raw(args, dev, ws)
@@ -300,8 +310,8 @@ def bench_moe(nv, cfg, steps, warmup):
         stage_ms=stage_ms,
         l1_TFLOPs=l1_flops / stage_ms["l1_gemm_swiglu_quant"] / 1e9,
         l2_TFLOPs=l2_flops / stage_ms["l2_gemm"] / 1e9,
-        l1_flops=l1_flops, l2_flops=l2_flops,
-    ), (w, x, ids, wts)
+        l1_flops=l1_flops, l2_flops=l2_flops, mode=mode, a2_gs=float(a2_out.item()),
+    ), (w, x, ids, wts, out.float())
 
 
 def bench_expert(nv, steps, warmup):
@@ -385,6 +395,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--legs", default="quant,expert,dec,pre")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the unfused and dynamic-scale runs of the prefill layer")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                     help="print the markdown HBM-traffic summary of four rocprofv3 counter CSVs")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
@@ -421,9 +433,22 @@ def main():
     if "pre" in legs:
         res["prefill"], pre = bench_moe(nv, synth.PRE, args.steps, args.warmup)
         print("# prefill done", flush=True, file=sys.stderr)
+        if not args.no_modes:
+            # the pages' unfused flows on the same layer: the fusion's saving,
+            # and the dynamic L1-output scale against the supplied one
+            y_static = pre[4]
+            for mode in ("unfused", "dynamic"):
+                r, extra = bench_moe(nv, synth.PRE, max(3, args.steps // 3), args.warmup, w=pre[0], mode=mode)
+                r = {k: r[k] for k in ("ms_per_step", "TFLOPs", "stage_ms", "a2_gs")}
+                yd = extra[4]
+                r["y_rel_fro_vs_fused"] = float(torch.linalg.norm(yd - y_static) / torch.linalg.norm(y_static))
+                res["prefill_" + mode] = r
+            res["prefill_unfused"]["fusion_saving_ms"] = (res["prefill_unfused"]["ms_per_step"]
+                                                         - res["prefill"]["ms_per_step"])
+            print("# prefill modes done", flush=True, file=sys.stderr)
     cpu = None
     if not args.no_cpu and pre is not None:
-        _, xdev, ids, wts = pre
+        _, xdev, ids, wts, _ = pre
         xb = synth.activations(synth.PRE)
         cpu = cpu_baseline_moe(synth.PRE, xb, ids, wts, ntok=48)
         if "quantize" in res:

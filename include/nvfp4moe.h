@@ -131,7 +131,13 @@ typedef struct {
   const uint8_t *w2_q;      /* [E][H][I/2] */
   const uint8_t *w2_sf;     /* [E][H][I/16] */
   const float *w2_gs;       /* [E] */
-  const float *a2_gs;       /* device float: supplied global scale of the L1 output */
+  /* device float: supplied global scale of the L1 output, which is then
+     quantized in the L1 GEMM's epilogue (NVFP4-1.1_APPROACH_PART_2.md,
+     fp4_mode epilogue with an l2_global_scale input).  Nullable: the
+     dynamic scale amax(L1 output over the valid pairs) / 2688 is used instead
+     and the L1 output is quantized in a separate pass (DEBUG_LOG.md, "NVFP4
+     MoE Pipeline": stage_activation of the activated rows). */
+  const float *a2_gs;
   void *out;                /* [T][H] */
   int out_dtype;            /* 0 = bf16, 1 = fp32 */
   /* nullable outputs (pair order p = t*k + j) */
@@ -153,18 +159,29 @@ typedef struct {
      with other H or I: NVFP4_ERR_UNSUPPORTED).  The results are the same
      either way up to the fp32 summation order inside the GEMMs. */
   int32_t tile_rows;
+  /* nullable: receives the L1-output global scale used (1 float) */
+  float *a2_gs_out;
+  /* 1: with a supplied a2_gs, still write the bf16 L1 output and quantize
+     it in a separate pass (the unfused flow of NVFP4-1.1_APPROACH.md,
+     "Target flow"; same bytes as the fused epilogue); 0: fused.  Any other
+     value: NVFP4_ERR_INVALID_ARG. */
+  int32_t l1_unfused;
 } nvfp4_moe_args;
 
 /*
  * moe_expert_ffn_nvfp4 -- y[t] = sum_j w[t][j] * FFN_{ids[t][j]}(x[t]) with
  *   FFN_e(x) = L2_e(NVFP4(bf16(silu(gate) * up)))  and  (gate, up) = L1_e(NVFP4(x))
  * where L1_e carries alpha1 = x_gs * w1_gs[e], L2_e carries alpha2 =
- * a2_gs * w2_gs[e], the L1 output is quantized with the supplied a2_gs, and
- * the k terms of a token are summed in fixed order j = 0..k-1 in fp32.
+ * a2_gs * w2_gs[e], the L1 output is quantized with a2_gs (supplied, or the
+ * dynamic amax / 2688 of the bf16 L1 output of all valid pairs when a2_gs is
+ * NULL), and the k terms of a token are summed in fixed order j = 0..k-1 in
+ * fp32.
  * Requirements: T >= 0; H % 256 == 0, I % 128 == 0, E <= 512, k <= 32, and the
  * f16 GEMM operands T * H * 2, T * k * I * 2 and one expert's I * H nibble
- * bytes at most 4 GiB each (else NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.  Workspace: the query's bytes,
- * which include the fp32 per-pair rows [P][H] of the L2 output.
+ * bytes at most 4 GiB each (else NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.
+ * Workspace: the query's bytes, which include the fp32 per-pair rows [P][H]
+ * of the L2 output and, for the unfused flow without l1_c_bf16, the bf16 L1
+ * output [P][I].
  */
 size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);
 int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, void *stream);

@@ -226,6 +226,26 @@ class Oracle:
             out.update(c=c, a2_q=a2q, a2_sf=a2sf)
         return out
 
+    def moe_tokens_dynamic(self, x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs,
+                           tokens=None, x_gs=None, want_pairs=False, threads=None):
+        """MoE expert FFN with a dynamic global scale for the L1 output, as
+        in DEBUG_LOG.md "NVFP4 MoE Pipeline" (stage_activation of the
+        activated rows): the SwiGLU output c of every valid pair of every
+        token is formed first, its global scale is g2 = amax / 2688 by the
+        same rule as for the activations, and then the listed tokens are run
+        with g2 as the L1-output scale.  Returns moe_tokens' dict plus a2_gs."""
+        T = np.asarray(x).shape[0]
+        # c does not depend on the L1-output scale: any placeholder works here
+        allc = self.moe_tokens(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, 1.0,
+                               tokens=np.arange(T), x_gs=x_gs, want_pairs=True,
+                               threads=threads)["c"]
+        # pairs of skipped experts stay zero in c and do not change the amax
+        g2 = self.global_scale(allc.reshape(-1, allc.shape[-1]))
+        out = self.moe_tokens(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, g2,
+                              tokens=tokens, x_gs=x_gs, want_pairs=want_pairs, threads=threads)
+        out["a2_gs"] = np.float32(g2)
+        return out
+
 
 _default = None
 

@@ -38,6 +38,8 @@ class MoeArgs(ctypes.Structure):
         ("l1_c_bf16", _vp), ("l1_q", _vp), ("l1_sf", _vp), ("err_count", _vp),
         ("stage_events", ctypes.POINTER(_vp)),
         ("tile_rows", ctypes.c_int32),
+        ("a2_gs_out", _vp),
+        ("l1_unfused", ctypes.c_int32),
     ]
 
 
@@ -173,9 +175,11 @@ def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, 
 
 def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
              x_gs=None, xq=None, xsf=None, x_gs_out=None, l1_c=None, l1_q=None, l1_sf=None,
-             err_count=None, tile_rows=0):
+             err_count=None, tile_rows=0, a2_gs_out=None, l1_unfused=False):
     """Build the nvfp4_moe_args struct from tensors (keeps no references).
-    tile_rows: 0 lets the library choose the GEMM tiles, 32 or 256 forces."""
+    tile_rows: 0 lets the library choose the GEMM tiles, 32 or 256 forces.
+    a2_gs None: dynamic L1-output global scale (unfused flow); l1_unfused:
+    the unfused flow with the supplied a2_gs; a2_gs_out receives the scale."""
     _require(x, torch.bfloat16, "x")
     _require(topk_ids, torch.int32, "topk_ids")
     _require(topk_w, torch.float32, "topk_w")
@@ -188,6 +192,8 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
                 _p(out), code, _p(xq), _p(xsf), _p(x_gs_out), _p(l1_c), _p(l1_q), _p(l1_sf),
                 _p(err_count))
     a.tile_rows = int(tile_rows)
+    a.a2_gs_out = _p(a2_gs_out)
+    a.l1_unfused = 1 if l1_unfused else 0
     return a
 
 
@@ -205,10 +211,11 @@ def moe_expert_ffn_raw(args, device, ws=None):
 
 
 def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
-                   out_dtype=torch.bfloat16, x_gs=None, debug=False, tile_rows=0):
+                   out_dtype=torch.bfloat16, x_gs=None, debug=False, tile_rows=0, l1_unfused=False):
     """NVFP4 MoE expert FFN.  Returns y [T][H] (out_dtype), plus with
     debug=True a dict of the intermediate outputs (xq, xsf, x_gs, l1_c,
-    l1_q, l1_sf, err_count).  tile_rows: see moe_args."""
+    l1_q, l1_sf, err_count, a2_gs_out).  a2_gs None: dynamic L1-output
+    global scale.  tile_rows, l1_unfused: see moe_args."""
     T, H = x.shape
     I = w1_q.shape[1] // 2
     k = topk_ids.shape[1]
@@ -223,9 +230,10 @@ def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, 
                    l1_c=torch.zeros((P, I), dtype=torch.bfloat16, device=dev),
                    l1_q=torch.zeros((P, I // 2), dtype=torch.uint8, device=dev),
                    l1_sf=torch.zeros((P, I // 16), dtype=torch.uint8, device=dev),
-                   err_count=torch.zeros(1, dtype=torch.int32, device=dev))
+                   err_count=torch.zeros(1, dtype=torch.int32, device=dev),
+                   a2_gs_out=torch.empty(1, dtype=torch.float32, device=dev))
     args = moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
-                    x_gs=x_gs, tile_rows=tile_rows, **dbg)
+                    x_gs=x_gs, tile_rows=tile_rows, l1_unfused=l1_unfused, **dbg)
     moe_expert_ffn_raw(args, dev)
     if debug:
         return out, dbg

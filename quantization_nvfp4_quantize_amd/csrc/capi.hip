@@ -152,10 +152,14 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
 namespace {
 
 struct MoeLayout {
-  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, a2q, a2sf, a2_f16, o,
-      total;
+  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, a2_gs, c, a2q, a2sf,
+      a2_f16, o, total;
   int max_tiles;
 };
+
+// The L1 output is quantized in a separate pass (from its bf16 rows) when its
+// global scale is dynamic or the caller asks for the unfused flow.
+bool moe_unfused(const nvfp4_moe_args* a) { return a->a2_gs == nullptr || a->l1_unfused == 1; }
 
 // Rows per GEMM tile: 32-row tiles (weights streamed through registers) when
 // the experts get few rows each, else 256-row tiles (MFMA-bound).
@@ -187,6 +191,8 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.tiles = take(sizeof(nvfp4::GemmTile) * (size_t)L.max_tiles);
   L.ntiles = take(sizeof(int));
   L.err = take(sizeof(int));
+  L.a2_gs = take(sizeof(float));
+  L.c = take(moe_unfused(a) && !a->l1_c_bf16 ? sizeof(uint16_t) * (size_t)(P * I) : 0);
   L.a2q = take((size_t)(P * I / 2));
   L.a2sf = take((size_t)(P * I / 16));
   L.a2_f16 = take(sizeof(uint16_t) * (size_t)(P * I));
@@ -218,13 +224,15 @@ int moe_validate(const nvfp4_moe_args* a) {
       a->tile_rows != nvfp4::gemm_tile_rows())
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: tile_rows must be 0, %d or %d",
                 nvfp4::skinny_tile_rows(), nvfp4::gemm_tile_rows());
+  if (a->l1_unfused != 0 && a->l1_unfused != 1)
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: l1_unfused must be 0 or 1");
   if (a->tile_rows == nvfp4::skinny_tile_rows() &&
       !(nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I)))
     return fail(NVFP4_ERR_UNSUPPORTED,
                 "moe_expert_ffn_nvfp4: tile_rows %d needs H and I multiples of 256 (or 128)",
                 nvfp4::skinny_tile_rows());
   if (a->T > 0 && (!a->x || !a->topk_ids || !a->topk_w || !a->w1_q || !a->w1_sf || !a->w1_gs ||
-                   !a->w2_q || !a->w2_sf || !a->w2_gs || !a->a2_gs || !a->out))
+                   !a->w2_q || !a->w2_sf || !a->w2_gs || !a->out))
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: null required pointer");
   if (!aligned(a->x, 16) || !aligned(a->w1_q, 16) || !aligned(a->w2_q, 16) || !aligned(a->out, 16) ||
       !aligned(a->xq, 16) || !aligned(a->l1_q, 16) || !aligned(a->l1_c_bf16, 16) ||
@@ -293,20 +301,47 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
                        "route")))
     return st;
   mark(3);
-  // a4-a6: L1 GEMM + SwiGLU + compact bf16 + NVFP4
+  // a4-a6: L1 GEMM + SwiGLU + compact bf16 + NVFP4 (fused: in the GEMM's
+  // epilogue with the supplied scale; unfused: the GEMM writes the bf16 rows,
+  // then the scale (supplied, or the dynamic amax of the valid pairs' rows)
+  // and a separate quantization pass)
   uint8_t* a2q = a->l1_q ? a->l1_q : reinterpret_cast<uint8_t*>(w + L.a2q);
   uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
   uint16_t* a2_f16 = reinterpret_cast<uint16_t*>(w + L.a2_f16);
   auto l1 = skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1;
-  if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs, a->l1_c_bf16, a2q,
-                          a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s),
-                       "L1 GEMM")))
-    return st;
+  const float* a2_gs = a->a2_gs;
+  if (!moe_unfused(a)) {
+    if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs, a->l1_c_bf16, a2q,
+                            a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s),
+                         "L1 GEMM")))
+      return st;
+    if (a->a2_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a->a2_gs, a->a2_gs_out, s), "copy a2_gs")))
+      return st;
+  } else {
+    uint16_t* c = a->l1_c_bf16 ? a->l1_c_bf16 : reinterpret_cast<uint16_t*>(w + L.c);
+    if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, nullptr, c, nullptr,
+                            nullptr, nullptr, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s),
+                         "L1 GEMM")))
+      return st;
+    if (!a2_gs) {
+      float* g2 = a->a2_gs_out ? a->a2_gs_out : reinterpret_cast<float*>(w + L.a2_gs);
+      if ((st = hip_status(nvfp4::launch_global_scale_rows(c, P, I, a->topk_ids, (int)E,
+                                                           reinterpret_cast<float*>(w + L.partial), g2, s),
+                           "L1-output global scale")))
+        return st;
+      a2_gs = g2;
+    } else if (a->a2_gs_out &&
+               (st = hip_status(nvfp4::launch_copy_scalar(a2_gs, a->a2_gs_out, s), "copy a2_gs"))) {
+      return st;
+    }
+    if ((st = hip_status(nvfp4::launch_quantize(c, P * I, a2_gs, a2q, a2sf, a2_f16, s), "quantize L1 output")))
+      return st;
+  }
   mark(4);
   // a7: L2 GEMM, weighted by the routing weights
   float* o = reinterpret_cast<float*>(w + L.o);
   auto l2 = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
-  if ((st = hip_status(l2(a2_f16, a->a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
+  if ((st = hip_status(l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
                           L.max_tiles, perm, s),
                        "L2 GEMM")))
     return st;

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
       }
     }
   }
-  const float E2 = 1.0f / p.out_gs[0];
+  const float E2 = p.c_q ? 1.0f / p.out_gs[0] : 1.0f;  // no quantization without c_q
   fill_rtab(rtab, E2, tid);
   __syncthreads();
 
@@ -381,15 +381,17 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   for (int pass = 0; pass < npass; ++pass) {
     const int qrow = pass * (kGemmThreads / 16) + (tid >> 4);
     uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
-    uint32_t code;
-    uint32_t q = quantize_half_block(w, E2, rtab, &code);
+    uint32_t code = 0, q = 0;
+    if (p.c_q) q = quantize_half_block(w, E2, rtab, &code);  // tile-uniform branch
     if (qrow < t.nrows) {
       const int64_t o = out_row[qrow];
       const int64_t col0 = 128 * (int64_t)nt + 8 * hb;  // compact column of this lane's 8
-      reinterpret_cast<uint32_t*>(p.c_q + o * (I / 2))[col0 / 8] = q;
-      if ((hb & 1) == 0) p.c_sf[o * (I / 16) + col0 / 16] = (uint8_t)code;
+      if (p.c_q) {
+        reinterpret_cast<uint32_t*>(p.c_q + o * (I / 2))[col0 / 8] = q;
+        if ((hb & 1) == 0) p.c_sf[o * (I / 16) + col0 / 16] = (uint8_t)code;
+        if (p.c_f16) *reinterpret_cast<f16x8*>(p.c_f16 + o * I + col0) = dequant8(q, scale_pair(code));
+      }
       if (p.c_bf16) *reinterpret_cast<uint4*>(p.c_bf16 + o * I + col0) = w;
-      if (p.c_f16) *reinterpret_cast<f16x8*>(p.c_f16 + o * I + col0) = dequant8(q, scale_pair(code));
     }
   }
 }

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     const float c = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
     ctile[acc_row(i, lane) * kCStride + col] = __builtin_bit_cast(uint16_t, (__bf16)c);
   }
-  const float E2 = 1.0f / p.out_gs[0];
+  const float E2 = p.c_q ? 1.0f / p.out_gs[0] : 1.0f;  // no quantization without c_q
   fill_rtab(rtab, E2, tid);
   __syncthreads();
   const int64_t I = p.N2 / 2;
@@ -317,15 +317,17 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
   for (int pass = 0; pass < npass; ++pass) {
     const int qrow = pass * (kSkThreads / 16) + (tid >> 4);
     const uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
-    uint32_t code;
-    const uint32_t q = quantize_half_block(w, E2, rtab, &code);
+    uint32_t code = 0, q = 0;
+    if (p.c_q) q = quantize_half_block(w, E2, rtab, &code);  // tile-uniform branch
     if (qrow < t.nrows) {
       const int64_t o = out_row[qrow];
-      const int64_t col0 = 128 * (int64_t)nt + 8 * hb;
-      reinterpret_cast<uint32_t*>(p.c_q + o * (I / 2))[col0 / 8] = q;
-      if ((hb & 1) == 0) p.c_sf[o * (I / 16) + col0 / 16] = (uint8_t)code;
+      const int64_t col0 = 128 * (int64_t)nt + 8 * hb;  // compact column of this lane's 8
+      if (p.c_q) {
+        reinterpret_cast<uint32_t*>(p.c_q + o * (I / 2))[col0 / 8] = q;
+        if ((hb & 1) == 0) p.c_sf[o * (I / 16) + col0 / 16] = (uint8_t)code;
+        if (p.c_f16) *reinterpret_cast<f16x8*>(p.c_f16 + o * I + col0) = dequant8(q, scale_pair(code));
+      }
       if (p.c_bf16) *reinterpret_cast<uint4*>(p.c_bf16 + o * I + col0) = w;
-      if (p.c_f16) *reinterpret_cast<f16x8*>(p.c_f16 + o * I + col0) = dequant8(q, scale_pair(code));
     }
   }
 }

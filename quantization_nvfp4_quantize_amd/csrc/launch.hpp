@@ -21,6 +21,10 @@ size_t global_scale_workspace_bytes();
 // g = max|x| / 2688 (1 if all zero) over n bf16 values (n % 8 == 0) -> gs[0]
 hipError_t launch_global_scale(const uint16_t* x, int64_t n, float* partial, float* gs,
                                hipStream_t s);
+// The same over the rows of a [rows][cols] bf16 matrix whose row r is pair r
+// of a top-k routing, skipping rows whose expert id ids[r] is outside [0, E).
+hipError_t launch_global_scale_rows(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ids, int E,
+                                    float* partial, float* gs, hipStream_t s);
 hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s);
 // n bf16 values (n % 16 == 0) -> q [n/2], sf [n/16] with global scale gs[0];
 // f16out (nullable) [n]: exact f16 of e2m1 * block scale (the GEMM operand)

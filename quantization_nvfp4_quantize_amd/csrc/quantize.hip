@@ -48,6 +48,30 @@ __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint4* __
   }
 }
 
+// Pass 1 over the rows of a [rows][cols] matrix that belong to valid (token,
+// expert) pairs: row r counts when 0 <= ids[r] < E.  rc8 = cols / 8 chunks per
+// row; the chunk index stays below 2^32.
+__global__ __launch_bounds__(kQThreads) void amax_rows_partial_kernel(const uint4* __restrict__ x,
+                                                                      int64_t n8, uint32_t rc8,
+                                                                      const int32_t* __restrict__ ids,
+                                                                      int E, float* __restrict__ partial) {
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kQThreads) {
+    const int32_t e = ids[(uint32_t)i / rc8];
+    if (e >= 0 && e < E) m = fmaxf(m, abs_max8(load_nt(x + i)));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kQThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kQThreads / 64; ++w) r = fmaxf(r, red[w]);
+    partial[blockIdx.x] = r;
+  }
+}
+
 // Pass 2: one workgroup reduces the partials; g = amax / (6 * 448), or 1 when
 // the tensor is all zero (or empty).
 __global__ __launch_bounds__(1024) void amax_finalize_kernel(const float* __restrict__ partial,
@@ -170,6 +194,17 @@ hipError_t launch_global_scale(const uint16_t* x, int64_t n, float* partial, flo
   int64_t n8 = n / 8;
   int wg = amax_workgroups(n8);
   amax_partial_kernel<<<wg, kQThreads, 0, s>>>(reinterpret_cast<const uint4*>(x), n8, partial);
+  amax_finalize_kernel<<<1, 1024, 0, s>>>(partial, wg, gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_global_scale_rows(const uint16_t* x, int64_t rows, int64_t cols, const int32_t* ids, int E,
+                                    float* partial, float* gs, hipStream_t s) {
+  const int64_t n8 = rows * cols / 8;
+  if (cols % 8 != 0 || n8 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
+  const int wg = amax_workgroups(n8);
+  amax_rows_partial_kernel<<<wg, kQThreads, 0, s>>>(reinterpret_cast<const uint4*>(x), n8,
+                                                    (uint32_t)(cols / 8), ids, E, partial);
   amax_finalize_kernel<<<1, 1024, 0, s>>>(partial, wg, gs);
   return hipGetLastError();
 }

@@ -368,6 +368,73 @@ def pin_moe_dense(o):
     assert err < 1e-6, err
 
 
+def pin_moe_dynamic_all_ones(o):
+    """The all-ones case with the dynamic L1-output scale: c is the same
+    constant in every pair, so g2 = bf16(c) / 2688 exactly (the scale the
+    static all-ones pin supplies by hand) and y has the same closed form."""
+    T, H, I, E, k = 4, 64, 32, 2, 2
+    one = np.full((T, H), 0x3F80, np.uint16)
+    ids = np.array([[0, 1], [1, 0], [0, 1], [1, -1]], np.int32)
+    wts = np.array([[0.25, 0.75], [0.5, 0.5], [1.0, 0.0], [0.125, 0.875]], np.float32)
+    w1 = np.full((2 * I, H), 0x3F80, np.uint16)
+    w2 = np.full((H, I), 0x3F80, np.uint16)
+    g1, g2w = o.global_scale(w1), o.global_scale(w2)
+    q1, s1 = o.quantize(w1, g1)
+    q2, s2 = o.quantize(w2, g2w)
+    gx = np.float32(1.0) / np.float32(2688.0)
+    h = H * 2688.0 * 2688.0 * float(np.float32(gx * g1))
+    c_bf = float(bf16_round([h / (1 + math.exp(-h)) * h])[0])
+    out = o.moe_tokens_dynamic(one, ids, wts, np.stack([q1] * E), np.stack([s1] * E),
+                               np.float32([g1] * E), np.stack([q2] * E), np.stack([s2] * E),
+                               np.float32([g2w] * E))
+    assert out["a2_gs"] == np.float32(c_bf) / np.float32(2688.0)
+    alpha2 = float(np.float32(out["a2_gs"] * g2w))
+    for t in range(T):
+        valid = ids[t] >= 0
+        want = I * 2688.0 * 2688.0 * alpha2 * float(wts[t][valid].astype(np.float64).sum())
+        assert np.allclose(out["y"][t], np.float32(want), rtol=1e-6, atol=0), (t, out["y"][t][0], want)
+
+
+def pin_moe_dynamic_dense(o):
+    """Dynamic L1-output scale on the tiny workload with two skipped pairs:
+    g2 is the largest bf16-rounded SwiGLU value of the valid pairs (brute
+    force, fp64 matmuls) / 2688, and y follows with g2 as the scale."""
+    cfg = synth.TINY
+    w = _oracle_weights(o, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ids = ids.copy()
+    ids[3, 0], ids[5, 1] = -1, cfg.E
+    out = o.moe_tokens_dynamic(x, ids, wts, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"],
+                               w["w2gs"])
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.topk
+    gx = o.global_scale(x)
+    xq, xsf = o.quantize(x, gx)
+    xa = o.dequantize(xq, xsf, 1.0).astype(np.float64)
+    w1a = [o.dequantize(w["w1q"][e], w["w1sf"][e], 1.0).astype(np.float64) for e in range(cfg.E)]
+    w2a = [o.dequantize(w["w2q"][e], w["w2sf"][e], 1.0).astype(np.float64) for e in range(cfg.E)]
+    cs = {}
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            if not 0 <= e < cfg.E:
+                continue
+            hh = ((w1a[e] @ xa[t]) * float(np.float32(gx * w["w1gs"][e]))).reshape(I // 8, 2, 8)
+            gate, up = hh[:, 0, :].reshape(-1), hh[:, 1, :].reshape(-1)
+            cs[t, j] = synth.bf16_bits((gate / (1.0 + np.exp(-gate)) * up).astype(np.float32))
+    amax = max(float(np.abs(synth.bf16_values(c)).max()) for c in cs.values())
+    g2 = np.float32(np.float32(amax) / np.float32(2688.0))
+    assert out["a2_gs"] == g2, (out["a2_gs"], g2)
+    y = np.zeros((T, H))
+    for (t, j), c in cs.items():
+        e = ids[t, j]
+        cq, csf = o.quantize(c[None, :], g2)
+        a2 = o.dequantize(cq, csf, 1.0).astype(np.float64)[0]
+        y[t] += float(wts[t, j]) * (w2a[e] @ a2) * float(np.float32(g2 * w["w2gs"][e]))
+    err = np.linalg.norm(out["y"] - y) / np.linalg.norm(y)
+    assert err < 1e-6, err
+
+
 def pin_l1_rows_dense(o):
     """Single-expert L1 + SwiGLU rows against a dense fp64 matmul."""
     rng = np.random.Generator(np.random.PCG64(5))
@@ -396,6 +463,7 @@ def pin_l1_rows_dense(o):
 ALL_PINS = [
     pin_e4m3_worked, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e2m1_worked,
     pin_e2m1_grid, pin_crafted_blocks, pin_global_scale, pin_dequant_exhaustive,
-    pin_moe_all_ones, pin_l1_rows_dense, pin_moe_dense, pin_quantize_invariants,
+    pin_moe_all_ones, pin_moe_dynamic_all_ones, pin_l1_rows_dense, pin_moe_dense,
+    pin_moe_dynamic_dense, pin_quantize_invariants,
     pin_e4m3_encode_vs_pages_procedure, pin_e4m3_encode_vs_torch,
 ]

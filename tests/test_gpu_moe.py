@@ -14,7 +14,7 @@ import torch
 
 import synth
 from gpu_util import cosine, dev_bf16, dev_f32, host, host_bits, rel_fro
-from moe_util import gpu_weights, oracle_tokens
+from moe_util import gpu_weights, oracle_tokens, oracle_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -28,13 +28,15 @@ def nv():
 TILES = [32, 256]  # both GEMM tile modes (32: weights streamed, 256: MFMA-bound)
 
 
-def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32, tile_rows=0):
+def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32, tile_rows=0, dynamic=False,
+             l1_unfused=False):
     x = dev_bf16(x_bits)
     ti = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     tw = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).cuda()
+    a2 = None if dynamic else dev_f32(cfg.a2_gs)
     y, dbg = nv.moe_expert_ffn(x, ti, tw, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"],
-                               w["w2gs"], dev_f32(cfg.a2_gs), out_dtype=out_dtype, debug=True,
-                               tile_rows=tile_rows)
+                               w["w2gs"], a2, out_dtype=out_dtype, debug=True,
+                               tile_rows=tile_rows, l1_unfused=l1_unfused)
     torch.cuda.synchronize()
     return y, dbg
 
@@ -155,6 +157,64 @@ def test_moe_skinny_k_schedules(nv, orc, H, I):
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
     print(f"H{H} I{I}: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
     _gate(*res[:4])
+
+
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_unfused_static_matches_fused(nv, tile_rows):
+    """The unfused flow (bf16 L1 output, then a separate quantization pass)
+    with the supplied scale produces the fused epilogue's bytes exactly."""
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ya, da = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
+    yb, db = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows, l1_unfused=True)
+    assert host(db["a2_gs_out"])[0] == np.float32(cfg.a2_gs)
+    assert host(da["a2_gs_out"])[0] == np.float32(cfg.a2_gs)
+    assert np.array_equal(host_bits(da["l1_c"]), host_bits(db["l1_c"]))
+    for key in ("l1_q", "l1_sf"):
+        assert np.array_equal(host(da[key]), host(db[key])), key
+    assert np.array_equal(host(ya).view(np.uint32), host(yb).view(np.uint32))
+
+
+@pytest.mark.parametrize("tile_rows", TILES)
+@pytest.mark.parametrize("shape", ["tiny", "mid"])
+def test_moe_dynamic_l1_scale(nv, orc, tile_rows, shape):
+    """Dynamic L1-output global scale (a2_gs NULL: amax of the valid pairs'
+    bf16 SwiGLU rows / 2688, then a separate quantization pass) against the
+    oracle's dynamic flow, with two skipped pairs whose rows must not count."""
+    import dataclasses
+    cfg = synth.TINY if shape == "tiny" else dataclasses.replace(synth.TINY, T=40, H=1280, I=768, E=4,
+                                                                 name="mid1280x768")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ids = ids.copy()
+    ids[3, 0], ids[5, 1] = -1, cfg.E
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows, dynamic=True)
+    used = sorted(set(int(e) for e in ids.reshape(-1) if 0 <= e < cfg.E))
+    ow = oracle_weights(orc, cfg, used)
+    remap = {e: i for i, e in enumerate(used)}
+    ids_r = np.vectorize(lambda e: remap.get(int(e), -1))(ids).astype(np.int32)
+    ref = orc.moe_tokens_dynamic(x, ids_r, wts, ow["w1q"], ow["w1sf"], ow["w1gs"], ow["w2q"], ow["w2sf"],
+                                 ow["w2gs"])
+    g_gpu = host(dbg["a2_gs_out"])[0]
+    rel = abs(float(g_gpu) / float(ref["a2_gs"]) - 1.0)
+    print(f"{shape}: dynamic a2_gs gpu {g_gpu!r} oracle {ref['a2_gs']!r} (rel {rel:.2e})")
+    assert rel <= 2.0 ** -8
+    # the GPU's scale is its own valid rows' amax / 2688, by its own quantizer
+    valid = ((ids >= 0) & (ids < cfg.E)).reshape(-1)
+    c_valid = dbg["l1_c"][torch.from_numpy(np.nonzero(valid)[0]).cuda()]
+    _, _, g_self = nv.quantize(c_valid.contiguous())
+    assert host(g_self)[0] == g_gpu
+    cq, csf, _ = nv.quantize(dbg["l1_c"], dbg["a2_gs_out"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dbg["l1_q"])[valid], host(cq)[valid])
+    assert np.array_equal(host(dbg["l1_sf"])[valid], host(csf)[valid])
+    yg = host(y)
+    err, cos = rel_fro(yg, ref["y"]), cosine(yg, ref["y"])
+    print(f"{shape}: y rel_fro {err:.3e} cos {cos:.7f}")
+    assert err <= 1e-3 and cos >= 0.9999
 
 
 @pytest.mark.parametrize("tile_rows", TILES)
