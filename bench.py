@@ -11,10 +11,13 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
             copies (> 256 MiB Infinity Cache); also dynamic scale, dequantize
   expert    single-expert L1 stage M4096 K7168 N 2x2048
   dec       decode-shaped layer T128 (Zipf routing; weight-streaming bound)
-  prefill_unfused / prefill_dynamic  the same prefill layer with the L1
-            output written as bf16 and quantized in a separate pass, with the
-            supplied scale (the fusion's saving) or with the dynamic
-            amax / 2688 scale (and y's distance from the fused run)
+  prefill_unfused / prefill_interleaved / prefill_dynamic  the same prefill
+            layer with the L1 output written as bf16 and quantized in a
+            separate pass: compact with the supplied scale (the fusion's
+            saving), interleaved [SiLU(gate), SwiGLU] groups with a
+            deinterleave + quantize pass (the pages' earlier flow), or
+            compact with the dynamic amax / 2688 scale (and y's distance from
+            the fused run)
 Timing: W untimed warmups, then K timed steps.  quantize and expert replay a
 HIP graph of K launches between two events (no host gaps); the MoE legs run
 eagerly and the library records HIP events between its stages on the same
@@ -265,9 +268,10 @@ def moe_weights(nv, cfg):
 
 def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     """One MoE layer config; mode "fused" (L1 output quantized in the GEMM
-    epilogue with the supplied scale), "unfused" (bf16 L1 output, separate
-    quantization pass, supplied scale) or "dynamic" (unfused, with the
-    dynamic amax / 2688 scale of the L1 output)."""
+    epilogue with the supplied scale), "unfused" (compact bf16 L1 output,
+    separate quantization pass, supplied scale), "interleaved" (interleaved
+    [SiLU(gate), SwiGLU] bf16 output, deinterleave + quantize pass) or
+    "dynamic" (unfused, with the dynamic amax / 2688 scale)."""
     import synth
     dev = torch.device("cuda:0")
     if w is None:
@@ -280,7 +284,8 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     a2 = None if mode == "dynamic" else torch.tensor([cfg.a2_gs], dtype=torch.float32, device=dev)
     a2_out = torch.empty(1, dtype=torch.float32, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
-    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out, l1_unfused=(mode == "unfused"))
+    flow = {"fused": 0, "unfused": 1, "interleaved": 2, "dynamic": 0}[mode]
+    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out, l1_unfused=flow)
     ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         nv.moe_expert_ffn_raw(args, dev, ws)
@@ -437,14 +442,15 @@ def main():
             # the pages' unfused flows on the same layer: the fusion's saving,
             # and the dynamic L1-output scale against the supplied one
             y_static = pre[4]
-            for mode in ("unfused", "dynamic"):
+            for mode in ("unfused", "interleaved", "dynamic"):
                 r, extra = bench_moe(nv, synth.PRE, max(3, args.steps // 3), args.warmup, w=pre[0], mode=mode)
                 r = {k: r[k] for k in ("ms_per_step", "TFLOPs", "stage_ms", "a2_gs")}
                 yd = extra[4]
                 r["y_rel_fro_vs_fused"] = float(torch.linalg.norm(yd - y_static) / torch.linalg.norm(y_static))
                 res["prefill_" + mode] = r
-            res["prefill_unfused"]["fusion_saving_ms"] = (res["prefill_unfused"]["ms_per_step"]
-                                                         - res["prefill"]["ms_per_step"])
+            for mode in ("unfused", "interleaved"):
+                res["prefill_" + mode]["fusion_saving_ms"] = (res["prefill_" + mode]["ms_per_step"]
+                                                             - res["prefill"]["ms_per_step"])
             print("# prefill modes done", flush=True, file=sys.stderr)
     cpu = None
     if not args.no_cpu and pre is not None:

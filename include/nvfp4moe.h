@@ -161,10 +161,15 @@ typedef struct {
   int32_t tile_rows;
   /* nullable: receives the L1-output global scale used (1 float) */
   float *a2_gs_out;
-  /* 1: with a supplied a2_gs, still write the bf16 L1 output and quantize
-     it in a separate pass (the unfused flow of NVFP4-1.1_APPROACH.md,
-     "Target flow"; same bytes as the fused epilogue); 0: fused.  Any other
-     value: NVFP4_ERR_INVALID_ARG. */
+  /* 0: fused.  1: with a supplied a2_gs, still write the compact bf16 L1
+     output and quantize it in a separate pass (the unfused flow of
+     NVFP4-1.1_APPROACH.md, "Target flow").  2: the pages' earlier flow
+     (NVFP4-1.1_APPROACH_PART_2.md, the current MoE forward): the L1 GEMM
+     writes an interleaved bf16 [P][2I] output, groups of 8 columns
+     alternating SiLU(gate) and SiLU(gate) * up, and a separate pass
+     deinterleaves and quantizes the SwiGLU groups; needs a supplied a2_gs.
+     1 and 2 give the fused flow's bytes.  Any other value:
+     NVFP4_ERR_INVALID_ARG. */
   int32_t l1_unfused;
 } nvfp4_moe_args;
 

@@ -179,7 +179,8 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
     """Build the nvfp4_moe_args struct from tensors (keeps no references).
     tile_rows: 0 lets the library choose the GEMM tiles, 32 or 256 forces.
     a2_gs None: dynamic L1-output global scale (unfused flow); l1_unfused:
-    the unfused flow with the supplied a2_gs; a2_gs_out receives the scale."""
+    True / 1 the unfused flow with the supplied a2_gs, "interleaved" / 2 the
+    interleaved-output flow; a2_gs_out receives the scale."""
     _require(x, torch.bfloat16, "x")
     _require(topk_ids, torch.int32, "topk_ids")
     _require(topk_w, torch.float32, "topk_w")
@@ -193,7 +194,7 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
                 _p(err_count))
     a.tile_rows = int(tile_rows)
     a.a2_gs_out = _p(a2_gs_out)
-    a.l1_unfused = 1 if l1_unfused else 0
+    a.l1_unfused = {False: 0, True: 1, 0: 0, 1: 1, 2: 2, "interleaved": 2}[l1_unfused]
     return a
 
 

@@ -158,8 +158,10 @@ struct MoeLayout {
 };
 
 // The L1 output is quantized in a separate pass (from its bf16 rows) when its
-// global scale is dynamic or the caller asks for the unfused flow.
+// global scale is dynamic or the caller asks for the unfused flow; flow 2 is
+// the pages' earlier one (interleaved bf16 output, deinterleave + quantize).
 bool moe_unfused(const nvfp4_moe_args* a) { return a->a2_gs == nullptr || a->l1_unfused == 1; }
+bool moe_interleaved(const nvfp4_moe_args* a) { return a->l1_unfused == 2; }
 
 // Rows per GEMM tile: 32-row tiles (weights streamed through registers) when
 // the experts get few rows each, else 256-row tiles (MFMA-bound).
@@ -192,7 +194,8 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.ntiles = take(sizeof(int));
   L.err = take(sizeof(int));
   L.a2_gs = take(sizeof(float));
-  L.c = take(moe_unfused(a) && !a->l1_c_bf16 ? sizeof(uint16_t) * (size_t)(P * I) : 0);
+  L.c = take(moe_interleaved(a) ? sizeof(uint16_t) * (size_t)(2 * P * I)
+             : moe_unfused(a) && !a->l1_c_bf16 ? sizeof(uint16_t) * (size_t)(P * I) : 0);
   L.a2q = take((size_t)(P * I / 2));
   L.a2sf = take((size_t)(P * I / 16));
   L.a2_f16 = take(sizeof(uint16_t) * (size_t)(P * I));
@@ -224,8 +227,10 @@ int moe_validate(const nvfp4_moe_args* a) {
       a->tile_rows != nvfp4::gemm_tile_rows())
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: tile_rows must be 0, %d or %d",
                 nvfp4::skinny_tile_rows(), nvfp4::gemm_tile_rows());
-  if (a->l1_unfused != 0 && a->l1_unfused != 1)
-    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: l1_unfused must be 0 or 1");
+  if (a->l1_unfused < 0 || a->l1_unfused > 2)
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: l1_unfused must be 0, 1 or 2");
+  if (a->l1_unfused == 2 && !a->a2_gs)
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: the interleaved flow needs a supplied a2_gs");
   if (a->tile_rows == nvfp4::skinny_tile_rows() &&
       !(nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I)))
     return fail(NVFP4_ERR_UNSUPPORTED,
@@ -310,9 +315,20 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   uint16_t* a2_f16 = reinterpret_cast<uint16_t*>(w + L.a2_f16);
   auto l1 = skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1;
   const float* a2_gs = a->a2_gs;
-  if (!moe_unfused(a)) {
+  if (moe_interleaved(a)) {
+    uint16_t* c_il = reinterpret_cast<uint16_t*>(w + L.c);
+    if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, nullptr, a->l1_c_bf16, nullptr,
+                            nullptr, nullptr, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, c_il),
+                         "L1 GEMM")))
+      return st;
+    if (a->a2_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a2_gs, a->a2_gs_out, s), "copy a2_gs")))
+      return st;
+    if ((st = hip_status(nvfp4::launch_quantize_interleaved(c_il, P, I, a2_gs, a2q, a2sf, a2_f16, s),
+                         "deinterleave + quantize L1 output")))
+      return st;
+  } else if (!moe_unfused(a)) {
     if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs, a->l1_c_bf16, a2q,
-                            a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s),
+                            a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, nullptr),
                          "L1 GEMM")))
       return st;
     if (a->a2_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a->a2_gs, a->a2_gs_out, s), "copy a2_gs")))
@@ -320,7 +336,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   } else {
     uint16_t* c = a->l1_c_bf16 ? a->l1_c_bf16 : reinterpret_cast<uint16_t*>(w + L.c);
     if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, nullptr, c, nullptr,
-                            nullptr, nullptr, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s),
+                            nullptr, nullptr, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, nullptr),
                          "L1 GEMM")))
       return st;
     if (!a2_gs) {

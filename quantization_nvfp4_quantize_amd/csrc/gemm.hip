@@ -356,28 +356,47 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   const int col = 32 * wn + (lane & 31);
   // only the row groups holding valid rows (rows past nrows are never stored)
   const int nmt = __builtin_amdgcn_readfirstlane(active_groups(t.nrows, wm));
+  const int64_t I = p.N2 / 2;
+  const int hb = tid & 15;
+  const int npass = (t.nrows + kGemmThreads / 16 - 1) / (kGemmThreads / 16);
+  // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS
+  auto fill_ctile = [&](bool gate_only) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    if (mt < nmt) {
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt < nmt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float gate = acc[mt][0][i] * alpha;
-        float up = acc[mt][1][i] * alpha;
-        float c = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
-        __bf16 b = (__bf16)c;
-        ctile[(wm * 128 + mt * 32 + acc_row(i, lane)) * kCStride + col] = __builtin_bit_cast(uint16_t, b);
+        for (int i = 0; i < 16; ++i) {
+          const float gate = acc[mt][0][i] * alpha;
+          const float sg = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
+          const float c = gate_only ? sg : sg * (acc[mt][1][i] * alpha);
+          ctile[(wm * 128 + mt * 32 + acc_row(i, lane)) * kCStride + col] =
+              __builtin_bit_cast(uint16_t, (__bf16)c);
+        }
       }
     }
+  };
+  if (p.c_il) {
+    // interleaved output: the SiLU(gate) groups first (16 lanes per row, 8
+    // columns each, 32 rows per pass)
+    fill_ctile(true);
+    __syncthreads();
+    for (int pass = 0; pass < npass; ++pass) {
+      const int qrow = pass * (kGemmThreads / 16) + (tid >> 4);
+      if (qrow < t.nrows) {
+        const uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
+        const int64_t g8 = 16 * (int64_t)nt + hb;  // group of 8 compact columns
+        *reinterpret_cast<uint4*>(p.c_il + (int64_t)out_row[qrow] * p.N2 + 16 * g8) = w;
+      }
+    }
+    __syncthreads();
   }
+  fill_ctile(false);
   const float E2 = p.c_q ? 1.0f / p.out_gs[0] : 1.0f;  // no quantization without c_q
   fill_rtab(rtab, E2, tid);
   __syncthreads();
 
   // ---- quantize the bf16 tile: 16 lanes per row (8 blocks, two halves
   // each), 32 rows per pass, passes up to the last valid row
-  const int64_t I = p.N2 / 2;
-  const int hb = tid & 15;
-  const int npass = (t.nrows + kGemmThreads / 16 - 1) / (kGemmThreads / 16);
   for (int pass = 0; pass < npass; ++pass) {
     const int qrow = pass * (kGemmThreads / 16) + (tid >> 4);
     uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
@@ -392,6 +411,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
         if (p.c_f16) *reinterpret_cast<f16x8*>(p.c_f16 + o * I + col0) = dequant8(q, scale_pair(code));
       }
       if (p.c_bf16) *reinterpret_cast<uint4*>(p.c_bf16 + o * I + col0) = w;
+      if (p.c_il) *reinterpret_cast<uint4*>(p.c_il + o * p.N2 + 2 * col0 + 8) = w;
     }
   }
 }
@@ -450,8 +470,8 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                      uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                     const int* perm, int topk, hipStream_t s) {
-  L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16,
+                     const int* perm, int topk, hipStream_t s, uint16_t* c_il) {
+  L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16, c_il,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
   int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;

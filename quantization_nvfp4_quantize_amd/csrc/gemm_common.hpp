@@ -171,6 +171,8 @@ struct L1Params {
   uint8_t* c_q;         // [out rows][N2/4]
   uint8_t* c_sf;        // [out rows][N2/32]
   uint16_t* c_f16;      // nullable [out rows][N2/2]: exact f16 of the quantized values
+  uint16_t* c_il;       // nullable [out rows][N2]: the interleaved bf16 output of the pages'
+                        // earlier flow (groups of 8: SiLU(gate), then SiLU(gate) * up)
   const GemmTile* tiles;  // nullable: identity tiling of M rows, expert 0
   const int* ntiles;
   int64_t M;            // rows when tiles == nullptr

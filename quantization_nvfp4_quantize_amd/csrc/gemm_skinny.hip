@@ -301,19 +301,37 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
   if (tid < kSkTileM) out_row[tid] = out_row_of(tid);
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
   const int col = 32 * wave + (lane & 31);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float gate = acc[0][i] * alpha;
-    const float up = acc[1][i] * alpha;
-    const float c = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
-    ctile[acc_row(i, lane) * kCStride + col] = __builtin_bit_cast(uint16_t, (__bf16)c);
-  }
-  const float E2 = p.c_q ? 1.0f / p.out_gs[0] : 1.0f;  // no quantization without c_q
-  fill_rtab(rtab, E2, tid);
-  __syncthreads();
   const int64_t I = p.N2 / 2;
   const int hb = tid & 15;
   const int npass = (t.nrows + kSkThreads / 16 - 1) / (kSkThreads / 16);
+  // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS
+  auto fill_ctile = [&](bool gate_only) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float gate = acc[0][i] * alpha;
+      const float sg = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
+      const float c = gate_only ? sg : sg * (acc[1][i] * alpha);
+      ctile[acc_row(i, lane) * kCStride + col] = __builtin_bit_cast(uint16_t, (__bf16)c);
+    }
+  };
+  if (p.c_il) {
+    // interleaved output: the SiLU(gate) groups first
+    fill_ctile(true);
+    __syncthreads();
+    for (int pass = 0; pass < npass; ++pass) {
+      const int qrow = pass * (kSkThreads / 16) + (tid >> 4);
+      if (qrow < t.nrows) {
+        const uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
+        const int64_t g8 = 16 * (int64_t)nt + hb;
+        *reinterpret_cast<uint4*>(p.c_il + (int64_t)out_row[qrow] * p.N2 + 16 * g8) = w;
+      }
+    }
+    __syncthreads();
+  }
+  fill_ctile(false);
+  const float E2 = p.c_q ? 1.0f / p.out_gs[0] : 1.0f;  // no quantization without c_q
+  fill_rtab(rtab, E2, tid);
+  __syncthreads();
   for (int pass = 0; pass < npass; ++pass) {
     const int qrow = pass * (kSkThreads / 16) + (tid >> 4);
     const uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
@@ -328,6 +346,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
         if (p.c_f16) *reinterpret_cast<f16x8*>(p.c_f16 + o * I + col0) = dequant8(q, scale_pair(code));
       }
       if (p.c_bf16) *reinterpret_cast<uint4*>(p.c_bf16 + o * I + col0) = w;
+      if (p.c_il) *reinterpret_cast<uint4*>(p.c_il + o * p.N2 + 2 * col0 + 8) = w;
     }
   }
 }
@@ -378,8 +397,8 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                            const int* perm, int topk, hipStream_t s) {
-  L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16,
+                            const int* perm, int topk, hipStream_t s, uint16_t* c_il) {
+  L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16, c_il,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;

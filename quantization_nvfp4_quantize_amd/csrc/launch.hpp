@@ -30,6 +30,11 @@ hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s);
 // f16out (nullable) [n]: exact f16 of e2m1 * block scale (the GEMM operand)
 hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_t* q, uint8_t* sf,
                            uint16_t* f16out, hipStream_t s);
+// The same for the SwiGLU columns of an interleaved [rows][2I] bf16 matrix
+// (groups of 8 columns alternating SiLU(gate), SiLU(gate) * up): the compact
+// [rows][I] values are quantized (rows * I / 8 < 2^32).
+hipError_t launch_quantize_interleaved(const uint16_t* x_il, int64_t rows, int64_t I, const float* gs,
+                                       uint8_t* q, uint8_t* sf, uint16_t* f16out, hipStream_t s);
 // NVFP4 (n values) -> exact f16 of e2m1 * block scale
 hipError_t launch_dequantize_f16(const uint8_t* q, const uint8_t* sf, int64_t n, uint16_t* out,
                                  hipStream_t s);
@@ -52,7 +57,7 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                      uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                     const int* perm, int topk, hipStream_t s);
+                     const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr);
 // L2: o[pair] = alpha * row_w[pair] * (A[pair] @ W_e^T) in fp32.
 hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
@@ -67,7 +72,7 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                            const int* perm, int topk, hipStream_t s);
+                            const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr);
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,

@@ -96,12 +96,16 @@ __global__ void copy_scalar_kernel(const float* __restrict__ src, float* __restr
 // ------------------------------------------------------------------ quantize
 // F16OUT: also write the exact f16 of each quantized value (e2m1 * block
 // scale, without the global scale) -- the GEMM operand form of the tensor.
-template <bool F16OUT>
+// IL: the input is an interleaved [rows][2 * 8 il8] matrix whose 8-column
+// groups alternate SiLU(gate) and SwiGLU values; chunk i of the compact
+// [rows][8 il8] tensor is its row's group 2 (i % il8) + 1.
+template <bool F16OUT, bool IL = false>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t n8,
                                                              const float* __restrict__ gs,
                                                              uint32_t* __restrict__ q,
                                                              uint8_t* __restrict__ sf,
-                                                             f16x8* __restrict__ f16out) {
+                                                             f16x8* __restrict__ f16out,
+                                                             uint32_t il8 = 0) {
   __shared__ float rtab[128];
   const float E = 1.0f / gs[0];
   fill_rtab(rtab, E, threadIdx.x);
@@ -110,7 +114,12 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
 #pragma unroll
   for (int u = 0; u < kQUnroll; ++u) {
     int64_t i = base + u * kQThreads;
-    w[u] = (i < n8) ? load_nt(x + i) : make_uint4(0, 0, 0, 0);
+    int64_t src = i;
+    if (IL) {
+      const uint32_t r = (uint32_t)i / il8, c = (uint32_t)i - r * il8;
+      src = 2 * (int64_t)r * il8 + 2 * c + 1;
+    }
+    w[u] = (i < n8) ? load_nt(x + src) : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();
 #pragma unroll
@@ -226,6 +235,18 @@ hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_
   else
     quantize_kernel<false><<<(unsigned)wg, kQThreads, 0, s>>>(
         reinterpret_cast<const uint4*>(x), n8, gs, reinterpret_cast<uint32_t*>(q), sf, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_interleaved(const uint16_t* x_il, int64_t rows, int64_t I, const float* gs,
+                                       uint8_t* q, uint8_t* sf, uint16_t* f16out, hipStream_t s) {
+  const int64_t n8 = rows * I / 8;
+  if (n8 == 0) return hipSuccess;
+  if (I % 16 != 0 || n8 >= ((int64_t)1 << 32) || !f16out) return hipErrorInvalidValue;
+  const int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
+  quantize_kernel<true, true><<<(unsigned)wg, kQThreads, 0, s>>>(
+      reinterpret_cast<const uint4*>(x_il), n8, gs, reinterpret_cast<uint32_t*>(q), sf,
+      reinterpret_cast<f16x8*>(f16out), (uint32_t)(I / 8));
   return hipGetLastError();
 }
 

@@ -160,15 +160,18 @@ def test_moe_skinny_k_schedules(nv, orc, H, I):
 
 
 @pytest.mark.parametrize("tile_rows", TILES)
-def test_moe_unfused_static_matches_fused(nv, tile_rows):
-    """The unfused flow (bf16 L1 output, then a separate quantization pass)
-    with the supplied scale produces the fused epilogue's bytes exactly."""
+@pytest.mark.parametrize("flow", [1, "interleaved"])
+def test_moe_unfused_static_matches_fused(nv, tile_rows, flow):
+    """The unfused flows with the supplied scale -- compact bf16 L1 output
+    then a separate quantization pass, or the interleaved [SiLU(gate),
+    SwiGLU] output then a deinterleave + quantize pass -- produce the fused
+    epilogue's bytes exactly."""
     cfg = synth.TINY
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
     ya, da = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
-    yb, db = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows, l1_unfused=True)
+    yb, db = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows, l1_unfused=flow)
     assert host(db["a2_gs_out"])[0] == np.float32(cfg.a2_gs)
     assert host(da["a2_gs_out"])[0] == np.float32(cfg.a2_gs)
     assert np.array_equal(host_bits(da["l1_c"]), host_bits(db["l1_c"]))
