@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 MoE expert-FFN hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dec,pre] [--no-cpu] [--no-modes]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dense,dec,pre] [--no-cpu] [--no-modes]
 
 Prints one JSON line.  `value` is the prefill-shaped MoE layer (T16384 H7168
 I2048 E256 top-8: activation global scale + quantize, grouping, L1 GEMM with
@@ -10,6 +10,7 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
             2.5625 algorithmic bytes per element), inputs rotated over five
             copies (> 256 MiB Infinity Cache); also dynamic scale, dequantize
   expert    single-expert L1 stage M4096 K7168 N 2x2048
+  dense     dense NVFP4 linear M4096 K4096 N16384 (quantize x + GEMM, bf16 out)
   dec       decode-shaped layer T128 (Zipf routing; weight-streaming bound)
   prefill_unfused / prefill_interleaved / prefill_dynamic  the same prefill
             layer with the L1 output written as bf16 and quantized in a
@@ -337,6 +338,24 @@ def bench_expert(nv, steps, warmup):
                 frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
 
 
+def bench_dense(nv, steps, warmup):
+    """Dense NVFP4 linear M4096 K4096 N16384 (activation global scale +
+    quantization + GEMM per call), bf16 output, graph-timed."""
+    import synth
+    dev = torch.device("cuda:0")
+    M, K, N = synth.DENSE_SHAPE["M"], synth.DENSE_SHAPE["K"], synth.DENSE_SHAPE["N"]
+    xb, w = synth.dense_problem(device=dev)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, wsf, wg = nv.quantize(w)
+    del w
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = nv.linear_workspace(M, K, N, dev)
+    ms = graph_time(lambda i: nv.linear(x, wq, wsf, wg, out=out, ws=ws), steps, warmup)
+    flops = 2.0 * M * N * K
+    return dict(workload=f"M{M} K{K} N{N}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
+                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline_moe(cfg, x_bits, ids, wts, ntok=8):
     """The oracle on a bounded sample of the prefill layer: ntok tokens (all
@@ -398,7 +417,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="quant,expert,dec,pre")
+    ap.add_argument("--legs", default="quant,expert,dense,dec,pre")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the unfused and dynamic-scale runs of the prefill layer")
@@ -430,6 +449,9 @@ def main():
     if "expert" in legs:
         res["expert_l1"] = bench_expert(nv, args.steps, args.warmup)
         print("# expert done", flush=True, file=sys.stderr)
+    if "dense" in legs:
+        res["dense_linear"] = bench_dense(nv, args.steps, args.warmup)
+        print("# dense done", flush=True, file=sys.stderr)
     if "dec" in legs:
         res["decode"], _ = bench_moe(nv, synth.DEC, args.steps, args.warmup)
         print("# decode done", flush=True, file=sys.stderr)

@@ -115,6 +115,27 @@ int nvfp4_gemm_swiglu_quant(const uint8_t *a_q, const uint8_t *a_sf, const float
                             uint8_t *c_sf, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * nvfp4_linear -- dense NVFP4 linear layer: the MoE's activation quantization
+ * and GEMM without routing, for the checkpoint's NVFP4 projections
+ * (DEBUG_LOG.md, "Checkpoint Layers": o_b_proj, q_a_proj, q_b_proj, kv_proj
+ * are NVFP4; the o_a_proj BF16 -> NVFP4 question of "Next Steps").
+ *   y[m][n] = f32(x_gs * w_gs) * sum_k deq(xq)[m][k] * deq(w)[n][k]
+ * with xq = NVFP4(x) under x_gs (supplied, or the dynamic amax / 2688), both
+ * operands exact (e2m1 * E4M3 block scale), fp32 accumulation.
+ *   x bf16 [M][K] (16-byte aligned); x_gs_in nullable (device float)
+ *   w_q [N][K/2], w_sf [N][K/16] (16-byte aligned), w_gs (device float)
+ *   out [M][N]: bf16 (out_dtype 0) or fp32 (1)
+ *   x_gs_out nullable (1 float): the activation global scale used
+ *   M >= 0; K % 64 == 0; N % 256 == 0; M * K * 2 and N * K / 2 at most 4 GiB
+ *   (else NVFP4_ERR_UNSUPPORTED).  Workspace: nvfp4_linear_workspace_size
+ *   bytes (the NVFP4 and exact-f16 copies of x), 256-byte aligned.
+ */
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t K, int64_t N);
+int nvfp4_linear(const uint16_t *x, int64_t M, int64_t K, const float *x_gs_in, const uint8_t *w_q,
+                 const uint8_t *w_sf, const float *w_gs, int64_t N, int out_dtype, void *out,
+                 float *x_gs_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * MoE expert FFN (DEBUG_LOG.md, "NVFP4 MoE Pipeline"), T tokens, hidden H,
  * intermediate I, E experts, top-k routing; P = T * k (token, expert) pairs,
  * pair p = t * k + j.

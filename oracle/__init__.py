@@ -226,6 +226,23 @@ class Oracle:
             out.update(c=c, a2_q=a2q, a2_sf=a2sf)
         return out
 
+    def linear(self, x_bf16, w_q, w_sf, w_gs, x_gs=None, rows=None, cols=None):
+        """Dense NVFP4 linear (the MoE's activation quantization and GEMM
+        without routing, DEBUG_LOG.md "NVFP4 MoE Pipeline"): x is quantized
+        with g = x_gs or the global scale of the whole x, both operands are
+        dequantized exactly (e2m1 * block scale, no global scale) and
+        y = f32(g * w_gs) * (A @ W^T) in fp64, returned as fp32 for the
+        listed rows and output columns (all by default), with g."""
+        x = np.ascontiguousarray(x_bf16, np.uint16)
+        g = self.global_scale(x) if x_gs is None else np.float32(x_gs)
+        rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows, np.int64)
+        cols = np.arange(w_q.shape[0]) if cols is None else np.asarray(cols, np.int64)
+        xq, xsf = self.quantize(x[rows], g)  # rows are independent given g
+        a = self.dequantize(xq, xsf, 1.0).astype(np.float64)
+        b = self.dequantize(np.asarray(w_q)[cols], np.asarray(w_sf)[cols], 1.0).astype(np.float64)
+        alpha = float(np.float32(np.float32(g) * np.float32(w_gs)))
+        return ((a @ b.T) * alpha).astype(np.float32), np.float32(g)
+
     def moe_tokens_dynamic(self, x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs,
                            tokens=None, x_gs=None, want_pairs=False, threads=None):
         """MoE expert FFN with a dynamic global scale for the L1 output, as

@@ -53,6 +53,9 @@ _SIG = {
     "nvfp4_gemm_swiglu_quant_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nvfp4_gemm_swiglu_quant": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64,
                                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, ctypes.c_int, _vp, _vp,
+                                    _vp, _sz, _vp]),
     "moe_expert_ffn_nvfp4_workspace_size": (_sz, [ctypes.POINTER(MoeArgs)]),
     "moe_expert_ffn_nvfp4": (ctypes.c_int, [ctypes.POINTER(MoeArgs), _vp, _sz, _vp]),
 }
@@ -171,6 +174,34 @@ def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, 
                                         N2, _p(out_gs), _p(c), _p(cq), _p(csf), _p(ws), ws.numel(),
                                         _stream(dev)), "nvfp4_gemm_swiglu_quant")
     return c, cq, csf
+
+
+def linear(x, w_q, w_sf, w_gs, out_dtype=torch.bfloat16, x_gs=None, x_gs_out=None, out=None, ws=None):
+    """Dense NVFP4 linear: y [M][N] = alpha * NVFP4(x) @ W^T (out_dtype bf16 or
+    float32).  x bf16 [M][K]; w_q [N][K/2], w_sf [N][K/16], w_gs float32 [1];
+    x_gs: supplied activation global scale (float32 [1]) or None (dynamic);
+    x_gs_out: float32 [1] that receives the scale used."""
+    _require(x, torch.bfloat16, "x")
+    for t, n, d in ((w_q, "w_q", torch.uint8), (w_sf, "w_sf", torch.uint8), (w_gs, "w_gs", torch.float32),
+                    (x_gs, "x_gs", torch.float32), (x_gs_out, "x_gs_out", torch.float32)):
+        _require(t, d, n)
+    M, K = x.shape
+    N = w_q.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    code = {torch.bfloat16: 0, torch.float32: 1}[out.dtype]
+    if ws is None:
+        ws = _workspace(_lib.nvfp4_linear_workspace_size(M, K, N), dev)
+    _check(_lib.nvfp4_linear(_p(x), M, K, _p(x_gs), _p(w_q), _p(w_sf), _p(w_gs), N, code, _p(out),
+                             _p(x_gs_out), _p(ws), ws.numel(), _stream(dev)), "nvfp4_linear")
+    return out
+
+
+def linear_workspace(M, K, N, device):
+    """A dedicated workspace for nvfp4_linear (e.g. for graph capture)."""
+    return torch.empty(max(int(_lib.nvfp4_linear_workspace_size(M, K, N)), 256), dtype=torch.uint8,
+                       device=device)
 
 
 def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,

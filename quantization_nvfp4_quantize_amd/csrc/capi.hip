@@ -148,6 +148,95 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
                     "nvfp4_gemm_swiglu_quant");
 }
 
+// ------------------------------------------------------------------ dense linear
+namespace {
+
+struct LinearLayout {
+  size_t partial, gs, xq, xsf, x_f16, total;
+};
+
+LinearLayout linear_layout(int64_t M, int64_t K) {
+  LinearLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = off;
+    off = round_up(off + bytes, 256);
+    return r;
+  };
+  L.partial = take(nvfp4::global_scale_workspace_bytes());
+  L.gs = take(sizeof(float));
+  L.xq = take((size_t)(M * K / 2));
+  L.xsf = take((size_t)(M * K / 16));
+  L.x_f16 = take(sizeof(uint16_t) * (size_t)(M * K));
+  L.total = off;
+  return L;
+}
+
+// Rows up to which the 32-row kernels (weights streamed) take the linear.
+constexpr int64_t kLinearSkinnyRows = 64;
+
+}  // namespace
+
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t K, int64_t N) {
+  (void)N;
+  if (M < 0 || K <= 0) return 0;
+  return linear_layout(M, K).total;
+}
+
+int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, const uint8_t* w_q,
+                 const uint8_t* w_sf, const float* w_gs, int64_t N, int out_dtype, void* out,
+                 float* x_gs_out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || K <= 0 || N <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: need M >= 0, K > 0, N > 0");
+  if (out_dtype != 0 && out_dtype != 1)
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (K % 64 != 0 || N % 256 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_linear: need K %% 64 == 0 and N %% 256 == 0 (K=%lld N=%lld)",
+                (long long)K, (long long)N);
+  if (M > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_linear: M too large");
+  if ((__int128)M * K * 2 > kMaxOperandBytes || (__int128)N * (K / 2) > kMaxOperandBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_linear: an operand exceeds 4 GiB");
+  if (M == 0) return NVFP4_OK;
+  if (!x || !w_q || !w_sf || !w_gs || !out)
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: null pointer");
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_sf, 16) || !aligned(out, 4) ||
+      !aligned(x_gs_in, 4) || !aligned(x_gs_out, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: misaligned pointer");
+  const LinearLayout L = linear_layout(M, K);
+  if (!ws || ws_bytes < L.total)
+    return fail(NVFP4_ERR_WORKSPACE, "nvfp4_linear: workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (!aligned(ws, 256)) return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: ws must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int st;
+  const float* gs = x_gs_in;
+  if (!gs) {
+    float* g = x_gs_out ? x_gs_out : reinterpret_cast<float*>(w + L.gs);
+    if ((st = hip_status(nvfp4::launch_global_scale(x, M * K, reinterpret_cast<float*>(w + L.partial), g, s),
+                         "nvfp4_linear (global scale)")))
+      return st;
+    gs = g;
+  } else if (x_gs_out &&
+             (st = hip_status(nvfp4::launch_copy_scalar(x_gs_in, x_gs_out, s), "nvfp4_linear (copy scale)"))) {
+    return st;
+  }
+  uint16_t* x_f16 = reinterpret_cast<uint16_t*>(w + L.x_f16);
+  if ((st = hip_status(nvfp4::launch_quantize(x, M * K, gs, reinterpret_cast<uint8_t*>(w + L.xq),
+                                              reinterpret_cast<uint8_t*>(w + L.xsf), x_f16, s),
+                       "nvfp4_linear (quantize x)")))
+    return st;
+  const bool skinny = M <= kLinearSkinnyRows && nvfp4::skinny_supports_k(K);
+  const int64_t tm = skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
+  const int tiles = (int)((M + tm - 1) / tm);
+  auto gemm = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
+  float* o32 = out_dtype == 1 ? static_cast<float*>(out) : nullptr;
+  uint16_t* o16 = out_dtype == 0 ? static_cast<uint16_t*>(out) : nullptr;
+  return hip_status(gemm(x_f16, gs, K, w_q, w_sf, w_gs, N, nullptr, o32, nullptr, nullptr, tiles, nullptr,
+                         s, M, o16),
+                    "nvfp4_linear");
+}
+
 // ------------------------------------------------------------------ MoE
 namespace {
 
@@ -358,7 +447,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   float* o = reinterpret_cast<float*>(w + L.o);
   auto l2 = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
   if ((st = hip_status(l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
-                          L.max_tiles, perm, s),
+                          L.max_tiles, perm, s, 0, nullptr),
                        "L2 GEMM")))
     return st;
   mark(5);

@@ -193,20 +193,32 @@ __device__ __forceinline__ int l1_weight_row(int nt, int rb) {
   return up ? gate + 8 : gate;
 }
 
+// The L2 down GEMM, and without routing (tiles == nullptr, perm == nullptr,
+// row_w == nullptr) the dense NVFP4 linear y = alpha * A @ W^T.
 struct L2Params {
-  const uint16_t* a_f16;  // exact f16 of the quantized L1 output [P][K], pair order
+  const uint16_t* a_f16;  // exact f16 of the quantized A rows [rows][K] (pair order for L2)
   const float* a_gs;
   int64_t K;            // I
   const uint8_t* w_q;   // [E][N][K/2]
   const uint8_t* w_sf;
   const float* w_gs;
   int64_t N;            // H
-  const float* row_w;   // [P] routing weight of each pair
-  float* o;             // [P][N] fp32
-  const GemmTile* tiles;
+  const float* row_w;   // nullable [P]: routing weight of each pair (1 without)
+  float* o;             // [rows][N] fp32 (used when o_bf16 is null)
+  uint16_t* o_bf16;     // nullable [rows][N] bf16 output
+  const GemmTile* tiles;  // nullable: identity tiling of M rows, expert 0
   const int* ntiles;
-  const int* perm;
+  int64_t M;            // rows when tiles == nullptr
+  const int* perm;      // nullable: sorted position -> pair id
   int n_ntiles;
 };
+
+// One output value of the L2 / linear epilogue.
+__device__ __forceinline__ void l2_store(const L2Params& p, int64_t idx, float v) {
+  if (p.o_bf16)
+    p.o_bf16[idx] = __builtin_bit_cast(uint16_t, (__bf16)v);
+  else
+    p.o[idx] = v;
+}
 
 }  // namespace nvfp4

@@ -356,10 +356,13 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   SK_LDS_DECL;
   GemmTile t;
   int nt;
-  if (!tile_of<kSkTileM>(p.tiles, p.ntiles, 0, p.n_ntiles, &t, &nt)) return;
+  if (!tile_of<kSkTileM>(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  auto pair_of = [&](int r) -> int { return p.perm[t.row0 + (r < t.nrows ? r : 0)]; };
+  auto pair_of = [&](int r) -> int {
+    const int rr = t.row0 + (r < t.nrows ? r : 0);
+    return p.perm ? p.perm[rr] : rr;
+  };
   auto wrow = [&](int tr) { return nt * kTileN + tr; };
   auto sf_row = [&](int tr) { return (uint32_t)(nt * kTileN + tr) * (uint32_t)(p.K / 16); };
   SkOperands op;
@@ -378,10 +381,10 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
     const int orw = acc_row(i, lane);
     if (orw < t.nrows) {
       const int64_t pr = out_row[orw];
-      const float s = alpha * p.row_w[pr];
-      float* orow = p.o + pr * p.N + (int64_t)nt * kTileN + wave * 64 + (lane & 31);
-      orow[0] = acc[0][i] * s;
-      orow[32] = acc[1][i] * s;
+      const float s = p.row_w ? alpha * p.row_w[pr] : alpha;
+      const int64_t idx = pr * p.N + (int64_t)nt * kTileN + wave * 64 + (lane & 31);
+      l2_store(p, idx, acc[0][i] * s);
+      l2_store(p, idx + 32, acc[1][i] * s);
     }
   }
 }
@@ -410,8 +413,8 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
-                            const int* perm, hipStream_t s) {
-  L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, tiles, ntiles, perm, (int)(N / kTileN)};
+                            const int* perm, hipStream_t s, int64_t M, uint16_t* o_bf16) {
+  L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
   if (!skinny_supports_k(K)) return hipErrorInvalidValue;

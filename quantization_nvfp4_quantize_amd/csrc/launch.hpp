@@ -58,11 +58,13 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
                      const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr);
-// L2: o[pair] = alpha * row_w[pair] * (A[pair] @ W_e^T) in fp32.
+// L2: o[pair] = alpha * w[pair] * (A @ W_e^T) for the routed rows (fp32), or
+// without routing (tiles, perm, row_w null) over M rows of expert 0, into o
+// (fp32) or o_bf16 (bf16) when that is non-null.
 hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, const int* perm,
-                     hipStream_t s);
+                     hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr);
 
 // ---- moe.hip
 size_t route_lds_bytes(int E);
@@ -76,7 +78,7 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
-                            const int* perm, hipStream_t s);
+                            const int* perm, hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr);
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
                         GemmTile* tiles, int* ntiles, int* err_count, hipStream_t s);
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,

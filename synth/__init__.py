@@ -11,6 +11,7 @@ the "nvfp4-megamoe-kernel" pages; no public dataset is involved):
   expert single expert M4096 K7168 N 2x2048 (gate/up interleaved by 8)
   dec   T128 H7168 I2048 E256 top-8, Zipf(1.1)-skewed routing
   pre   T16384 H7168 I2048 E256 top-8, uniform routing
+  dense NVFP4 linear M4096 K4096 N16384
 Activations are bf16 N(0,1); weights bf16 N(0, 0.02).
 
 Generators: numpy PCG64 with a fixed draw order for host tensors; expert
@@ -83,6 +84,9 @@ PRE = MoeConfig("pre", 16384, 7168, 2048, 256, 8, "normal", 4, 64.0 / 2688.0)
 MOE_CONFIGS = {c.name: c for c in (TINY, DEC, PRE)}
 
 QUANT_SHAPE = (8192, 7168)
+# dense NVFP4 linear: 4096 tokens through a projection with the (16384, 4096)
+# weight shape the pages list for o_a_proj (out features x in features)
+DENSE_SHAPE = dict(M=4096, K=4096, N=16384)
 EXPERT_SHAPE = dict(M=4096, K=7168, I=2048)
 EXPERT_A2_GS = 64.0 / 2688.0
 
@@ -161,6 +165,17 @@ def expert_problem(M=EXPERT_SHAPE["M"], K=EXPERT_SHAPE["K"], I=EXPERT_SHAPE["I"]
     gen.manual_seed(seed * 1_000_003)
     w1 = torch.randn(2 * I, K, generator=gen, device=dev, dtype=torch.float32) * 0.02
     return x, interleave_gate_up(w1.to(torch.bfloat16)).contiguous()
+
+
+def dense_problem(M=DENSE_SHAPE["M"], K=DENSE_SHAPE["K"], N=DENSE_SHAPE["N"], seed=5, device="cpu"):
+    """Dense linear: activations bf16 bits [M][K] (numpy, N(0,1)) and the
+    weight [N][K] (bf16 torch tensor on `device`, N(0, 0.02))."""
+    x = normal_bf16((M, K), seed * 1000 + 1)
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 1_000_003)
+    w = torch.randn(N, K, generator=gen, device=dev, dtype=torch.float32) * 0.02
+    return x, w.to(torch.bfloat16).contiguous()
 
 
 def torch_bits(t: torch.Tensor) -> np.ndarray:

@@ -435,6 +435,52 @@ def pin_moe_dynamic_dense(o):
     assert err < 1e-6, err
 
 
+def pin_linear_bruteforce(o):
+    """Dense linear on a tiny shape against triple loops over values decoded
+    here from the bytes: nibbles by the E2M1 definition, scale bytes by
+    torch's float8_e4m3fn (both independent of the oracle's decoders)."""
+    rng = np.random.Generator(np.random.PCG64(9))
+    M, K, N = 3, 48, 5
+    x = synth.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    gw = o.global_scale(w)
+    wq, wsf = o.quantize(w, gw)
+    y, gx = o.linear(x, wq, wsf, gw)
+    assert gx == o.global_scale(x)
+    xq, xsf = o.quantize(x, gx)
+    sfdec = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+
+    def value(q, sf, r, k):
+        nib = (int(q[r, k // 2]) >> (4 * (k % 2))) & 15
+        mag = _e2m1_magnitude(nib & 7)
+        return (-mag if nib & 8 else mag) * float(sfdec[sf[r, k // 16]])
+
+    alpha = float(np.float32(gx * gw))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += value(xq, xsf, m, k) * value(wq, wsf, n, k)
+            want = acc * alpha
+            assert abs(float(y[m, n]) - want) <= abs(want) * 2.0 ** -23 + 1e-30, (m, n, y[m, n], want)
+    # rows and columns subsets are the same numbers
+    ys, _ = o.linear(x, wq, wsf, gw, rows=[2, 0], cols=[4, 1])
+    assert np.array_equal(ys, y[[2, 0]][:, [4, 1]])
+
+
+def pin_linear_all_ones(o):
+    """All-ones x and W: every operand dequantizes to 2688 before its global
+    scale, so y = K * 2688^2 * f32(g_x * g_w) = K * f32(1/2688 * 1/2688) * 2688^2."""
+    M, K, N = 2, 64, 3
+    one_x = np.full((M, K), 0x3F80, np.uint16)
+    one_w = np.full((N, K), 0x3F80, np.uint16)
+    gw = o.global_scale(one_w)
+    wq, wsf = o.quantize(one_w, gw)
+    y, gx = o.linear(one_x, wq, wsf, gw)
+    want = K * 2688.0 * 2688.0 * float(np.float32(gx * gw))
+    assert np.all(y == np.float32(want)), (y, want)
+
+
 def pin_l1_rows_dense(o):
     """Single-expert L1 + SwiGLU rows against a dense fp64 matmul."""
     rng = np.random.Generator(np.random.PCG64(5))
@@ -464,6 +510,6 @@ ALL_PINS = [
     pin_e4m3_worked, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e2m1_worked,
     pin_e2m1_grid, pin_crafted_blocks, pin_global_scale, pin_dequant_exhaustive,
     pin_moe_all_ones, pin_moe_dynamic_all_ones, pin_l1_rows_dense, pin_moe_dense,
-    pin_moe_dynamic_dense, pin_quantize_invariants,
+    pin_moe_dynamic_dense, pin_linear_all_ones, pin_linear_bruteforce, pin_quantize_invariants,
     pin_e4m3_encode_vs_pages_procedure, pin_e4m3_encode_vs_torch,
 ]

@@ -135,3 +135,20 @@ def test_moe_rejects(lib):
     assert lib.moe_expert_ffn_nvfp4(by(a), FAKE, need - 1, None) == -3
     assert b"workspace" in lib.nvfp4_last_error()
     del q
+
+
+def test_linear_rejects(lib):
+    # shape checks come before any pointer is used
+    assert lib.nvfp4_linear(FAKE, 4, 48, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE, 1 << 30, None) == -2
+    assert lib.nvfp4_linear(FAKE, 4, 64, None, FAKE, FAKE, FAKE, 200, 0, FAKE, None, FAKE, 1 << 30, None) == -2
+    assert lib.nvfp4_linear(FAKE, -1, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.nvfp4_linear(FAKE, 4, 64, None, FAKE, FAKE, FAKE, 256, 2, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.nvfp4_linear(None, 4, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.nvfp4_linear(ctypes.c_void_p(0x10008), 4, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE,
+                            1 << 30, None) == -1
+    need = lib.nvfp4_linear_workspace_size(4, 64, 256)
+    assert need > 0
+    assert lib.nvfp4_linear(FAKE, 4, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE, need - 1, None) == -3
+    assert b"workspace" in lib.nvfp4_last_error()
+    # an empty batch is a no-op
+    assert lib.nvfp4_linear(None, 0, 64, None, None, None, None, 256, 0, None, None, None, 0, None) == 0
