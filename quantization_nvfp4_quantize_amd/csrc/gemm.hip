@@ -49,6 +49,8 @@
 //     L2 operand).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "gemm_common.hpp"
 
 namespace nvfp4 {
@@ -249,18 +251,11 @@ __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRa
   if (rem > 2) gemm_step<2, 0, FULL>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
 }
 
-// The whole K loop over nk steps of 64 (operand sources in `op`; the tile has
-// nrows valid rows).  The prologue brings A steps 0..2 and B steps 0..2 with
-// their scales into LDS, then reads the raw B and scales of step 0 and
-// dequantizes its sub-step 0 fragments.  Ends with every load
-// landed and all waves past the last LDS read, so the caller may reuse the
-// LDS.
-__device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, int nk, int nrows,
-                                              f32x16 (&acc)[4][2]) {
-  const int tid = threadIdx.x, lane = tid & 63;
+// The prologue of a tile's K loop: the direct loads of A steps 0..2 and B
+// steps 0..2 with their scales into LDS stages 0..2.  The LDS stages must be
+// free (every wave past its last read of them).
+__device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, int nk, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave_m(wave), wn = wave_n(wave), g = lane >> 5;
-  const int nmt = __builtin_amdgcn_readfirstlane(active_groups(nrows, wm));  // tile-uniform
   const int last = nk - 1;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
@@ -276,6 +271,20 @@ __device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, 
       dma4(L.s + j * kBScale * 4 + (wave & 3) * 64,
            op.bsf + (size_t)min(j, last) * (kStepK / 16) + op.bsf_off);
   }
+}
+
+// The rest of the K loop over nk steps of 64 (operand sources in `op`; the
+// tile has nrows valid rows), after gemm_prologue: waits for the prologue's
+// loads (and any earlier memory operation of the wave), reads the raw B and
+// scales of step 0 and dequantizes its sub-step 0 fragments, then runs the
+// steps.  Ends with every load landed and all waves past the last LDS read,
+// so the caller may reuse the LDS.
+__device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int nk, int nrows,
+                                          f32x16 (&acc)[4][2], int tid) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave_m(wave), wn = wave_n(wave), g = lane >> 5;
+  const int nmt = __builtin_amdgcn_readfirstlane(active_groups(nrows, wm));  // tile-uniform
   const ReadPtrs rp = read_ptrs(L, wm, wn, lane);
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -302,6 +311,40 @@ __device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, 
     gemm_steps<false>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   wait_vmcnt<0>();
   lds_barrier();
+}
+
+// The whole K loop of one tile.
+__device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, int nk, int nrows,
+                                              f32x16 (&acc)[4][2]) {
+  gemm_prologue(L, op, nk, threadIdx.x);
+  gemm_body(L, op, nk, nrows, acc, threadIdx.x);
+}
+
+// threadIdx.x behind an empty asm statement: values derived from it inside a
+// persistent loop are recomputed per item instead of being hoisted out of the
+// loop (which would hold dozens of per-lane addresses across the K loop).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// ------------------------------------------------------------------ persistent grid
+// The L2 GEMM runs one workgroup per CU (a multiple of 8) over W (row tile,
+// column tile) items, row-tile-major.  The XCD x = b % 8 of workgroup b owns
+// the contiguous range of items work_item would deal it, and its workgroups
+// take them in turn, so the workgroups running together on one XCD work on
+// neighbouring items.  The next item's operand offsets and prologue loads are
+// issued before the current item's epilogue, so its load latency, the
+// epilogue and the absent workgroup launch overlap.
+struct Items {
+  int item, end, stride;
+};
+
+__device__ __forceinline__ Items persistent_items(int W) {
+  const int x = blockIdx.x & 7, q = W >> 3, r = W & 7;
+  const int start = x * q + min(x, r);
+  return {start + (int)(blockIdx.x >> 3), start + q + (x < r ? 1 : 0), (int)(gridDim.x >> 3)};
 }
 
 // ------------------------------------------------------------------ L1
@@ -417,57 +460,115 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
 }
 
 // ------------------------------------------------------------------ L2
+// Persistent (its K loop is short, so the per-item prologue, epilogue and
+// workgroup launch were a large share of its time); the epilogue needs only
+// the output rows and scales, which live outside the operand stages.  The
+// L1 GEMM (K = H) stays one workgroup per item: in a persistent loop its
+// larger epilogue state pushed the K loop into register spills.
 __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   __shared__ f16x8 lds_a[kAStages * kLdsOperand];
   __shared__ f16x8 lds_b[kBStages * kBRaw];
   __shared__ uint32_t lds_s[kBStages * kBScale * 4];
+  __shared__ int out_row[kTileM];
+  __shared__ float out_scale[kTileM];
   const Lds L{lds_a, lds_b, lds_s};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mtiles = p.tiles ? *p.ntiles : (int)((p.M + kTileM - 1) / kTileM);
+  Items its = persistent_items(mtiles * p.n_ntiles);
+  const int end = its.end, stride = its.stride;
+  int item = its.item;
+  if (item >= end) return;
+  const int nk = (int)(p.K / kStepK);
+
+  // tile, column tile and this lane's operand sources of an item
+  auto setup = [&](int it, GemmTile& t, int& nt, Operands& op, int tid_s) {
+    const int lane = tid_s & 63, wave = tid_s >> 6;
+    const int ti = it / p.n_ntiles;
+    nt = it % p.n_ntiles;
+    if (p.tiles) {
+      t = p.tiles[ti];
+    } else {
+      const int64_t r0 = (int64_t)ti * kTileM;
+      t.expert = 0;
+      t.row0 = (int)r0;
+      t.nrows = (int)((p.M - r0) < kTileM ? (p.M - r0) : kTileM);
+      t.pad = 0;
+    }
+    op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int R = 32 * wave + 8 * u + (lane >> 3);
+      const int rr = t.row0 + (R < t.nrows ? R : 0);  // padding rows repeat the first row
+      const int pr = p.perm ? p.perm[rr] : rr;
+      op.a_off[u] = (uint32_t)pr * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
+    }
+    op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
+    op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
+    op.bq_off = (uint32_t)(nt * kTileN + 32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) +
+                16u * ((lane ^ (lane >> 4)) & 1);
+    op.bsf_off = (uint32_t)(nt * kTileN + 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
+  };
+
   GemmTile t;
   int nt;
-  if (!tile_of<kTileM>(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // pair id of tile row r (padding rows repeat the first row, never stored)
-  auto pair_of = [&](int r) -> int {
-    const int rr = t.row0 + (r < t.nrows ? r : 0);
-    return p.perm ? p.perm[rr] : rr;
-  };
   Operands op;
-  op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
+  setup(item, t, nt, op, tid);
+  gemm_prologue(L, op, nk, tid);
+  int tid_i = tid;
+  for (;;) {
+    asm volatile("" : "+v"(tid_i));  // see opaque_tid: keeps per-lane addresses inside the loop
+    const int lane_i = tid_i & 63;
+    f32x16 acc[4][2];
+    gemm_body(L, op, nk, t.nrows, acc, tid_i);
+    // output row (pair id) and scale alpha * routing weight of every tile row
+    if (tid_i < t.nrows) {
+      const int pr = p.perm ? p.perm[t.row0 + tid_i] : t.row0 + tid_i;
+      const float alpha = p.a_gs[0] * p.w_gs[t.expert];
+      out_row[tid_i] = pr;
+      out_scale[tid_i] = p.row_w ? alpha * p.row_w[pr] : alpha;
+    }
+    const int next = item + stride;
+    const bool more = next < end;  // workgroup-uniform
+    GemmTile tn = t;
+    int ntn = nt;
+    if (more) {
+      setup(next, tn, ntn, op, tid_i);  // op now describes the next item
+      gemm_prologue(L, op, nk, tid_i);  // the stages are free: gemm_body ended with a barrier
+    }
+    __syncthreads();
+    const int wm = wave_m(tid_i >> 6), wn = wave_n(tid_i >> 6);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int R = 32 * wave + 8 * u + (lane >> 3);
-    op.a_off[u] = (uint32_t)pair_of(R) * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
-  }
-  op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
-  op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
-  op.bq_off = (uint32_t)(nt * kTileN + 32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) +
-              16u * ((lane ^ (lane >> 4)) & 1);
-  op.bsf_off = (uint32_t)(nt * kTileN + 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
-  f32x16 acc[4][2];
-  gemm_mainloop(L, op, (int)(p.K / kStepK), t.nrows, acc);
-  int* out_row = reinterpret_cast<int*>(lds_a);
-  if (tid < kTileM) out_row[tid] = pair_of(tid);
-  __syncthreads();
-  const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  const int wm = wave_m(wave), wn = wave_n(wave);
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int orw = wm * 128 + mt * 32 + acc_row(i, lane);
-      if (orw < t.nrows) {
-        const int64_t pr = out_row[orw];
-        const float s = p.row_w ? alpha * p.row_w[pr] : alpha;
-        const int64_t idx = pr * p.N + (int64_t)nt * kTileN + wn * 64 + (lane & 31);
-        l2_store(p, idx, acc[mt][0][i] * s);
-        l2_store(p, idx + 32, acc[mt][1][i] * s);
+      for (int i = 0; i < 16; ++i) {
+        const int orw = wm * 128 + mt * 32 + acc_row(i, lane_i);
+        if (orw < t.nrows) {
+          const int64_t idx = (int64_t)out_row[orw] * p.N + (int64_t)nt * kTileN + wn * 64 + (lane_i & 31);
+          const float sc = out_scale[orw];
+          l2_store(p, idx, acc[mt][0][i] * sc);
+          l2_store(p, idx + 32, acc[mt][1][i] * sc);
+        }
       }
     }
+    if (!more) break;
+    item = next;
+    t = tn;
+    nt = ntn;
   }
 }
 
 // ------------------------------------------------------------------ launchers
 int gemm_tile_rows() { return kTileM; }
+
+// Persistent grid for up to `items` items: one workgroup per CU of the
+// current device, a multiple of 8 (the XCDs), no more than the items need.
+static unsigned persistent_grid(int64_t items) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  return (unsigned)std::min<int64_t>((items + 7) / 8 * 8, (int64_t)(cus / 8 * 8));
+}
 
 hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
@@ -487,9 +588,9 @@ hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      const GemmTile* tiles, const int* ntiles, int max_tiles, const int* perm,
                      hipStream_t s, int64_t M, uint16_t* o_bf16) {
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN)};
-  int64_t grid = (int64_t)max_tiles * p.n_ntiles;
-  if (grid == 0) return hipSuccess;
-  l2_gemm_kernel<<<(unsigned)grid, kGemmThreads, 0, s>>>(p);
+  const int64_t items = (int64_t)max_tiles * p.n_ntiles;
+  if (items == 0) return hipSuccess;
+  l2_gemm_kernel<<<persistent_grid(items), kGemmThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
