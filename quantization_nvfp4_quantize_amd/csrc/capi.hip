@@ -241,7 +241,7 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
 namespace {
 
 struct MoeLayout {
-  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, a2_gs, c, a2q, a2sf,
+  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, route, a2_gs, c, a2q, a2sf,
       a2_f16, o, total;
   int max_tiles;
 };
@@ -282,6 +282,7 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.tiles = take(sizeof(nvfp4::GemmTile) * (size_t)L.max_tiles);
   L.ntiles = take(sizeof(int));
   L.err = take(sizeof(int));
+  L.route = take(nvfp4::route_workspace_bytes(P, (int)E));
   L.a2_gs = take(sizeof(float));
   L.c = take(moe_interleaved(a) ? sizeof(uint16_t) * (size_t)(2 * P * I)
              : moe_unfused(a) && !a->l1_c_bf16 ? sizeof(uint16_t) * (size_t)(P * I) : 0);
@@ -391,7 +392,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
   const bool skinny = moe_tile_rows(a) == nvfp4::skinny_tile_rows();
   if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, (int)moe_tile_rows(a), offsets, perm,
-                                           tiles, ntiles, err, s),
+                                           tiles, ntiles, err, reinterpret_cast<int*>(w + L.route), s),
                        "route")))
     return st;
   mark(3);

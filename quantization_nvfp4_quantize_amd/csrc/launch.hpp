@@ -79,8 +79,10 @@ hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
                             const int* perm, hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr);
+// Scratch (ints) of the many-workgroup grouping for P pairs and E experts.
+size_t route_workspace_bytes(int64_t P, int E);
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
-                        GemmTile* tiles, int* ntiles, int* err_count, hipStream_t s);
+                        GemmTile* tiles, int* ntiles, int* err_count, int* ws, hipStream_t s);
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,
                           bool bf16_out, void* out, hipStream_t s);
 

@@ -16,6 +16,9 @@
 // bits, so positions follow pair order without atomics on the output.
 // Expert ids outside [0, E) are skipped and counted.
 //
+// For many pairs the same grouping runs over many workgroups (count, scan,
+// place; below), with the same result.
+//
 // combine_kernel: y[t] = sum over j of o[t*k + j] in fixed order j = 0..k-1
 // (each o row already carries alpha2 * routing weight).
 #include <hip/hip_runtime.h>
@@ -143,6 +146,154 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
 }
 
+// ---- the same grouping over many workgroups (large P).  Workgroup g of G
+// owns pairs [P g / G, P (g + 1) / G).  route_count_kernel counts each
+// workgroup's pairs per expert; route_scan_kernel turns the counts into each
+// workgroup's first position per expert (experts in order, workgroups in
+// order inside an expert), the offsets and the tile list;
+// route_place_kernel places each workgroup's pairs as the single-workgroup
+// kernel does, so perm is the same stable order.
+
+__global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_t* __restrict__ ids,
+                                                                    int64_t P, int E,
+                                                                    int* __restrict__ gcount,
+                                                                    int* __restrict__ gerr) {
+  extern __shared__ int cnt[];  // [E]
+  __shared__ int s_err;
+  const int tid = threadIdx.x, G = gridDim.x, g = blockIdx.x;
+  for (int e = tid; e < E; e += kRouteThreads) cnt[e] = 0;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+  const int64_t p0 = P * g / G, p1 = P * (g + 1) / G;
+  for (int64_t p = p0 + tid; p < p1; p += kRouteThreads) {
+    const int e = ids[p];
+    if (e >= 0 && e < E)
+      atomicAdd(&cnt[e], 1);
+    else
+      atomicAdd(&s_err, 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kRouteThreads) gcount[(int64_t)g * E + e] = cnt[e];
+  if (tid == 0) gerr[g] = s_err;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int G, int E, int tile_rows,
+                                                                   int* __restrict__ gcount,
+                                                                   const int* __restrict__ gerr,
+                                                                   int* __restrict__ offsets,
+                                                                   GemmTile* __restrict__ tiles,
+                                                                   int* __restrict__ ntiles,
+                                                                   int* __restrict__ err_count) {
+  __shared__ int scan[kRouteThreads];
+  const int tid = threadIdx.x;
+  int base_pairs = 0, base_tiles = 0;
+  for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
+    const int e = e0 + tid;
+    // this expert's pairs per workgroup -> exclusive starts within the expert
+    int np = 0;
+    if (e < E)
+      for (int g = 0; g < G; ++g) {
+        const int c = gcount[(int64_t)g * E + e];
+        gcount[(int64_t)g * E + e] = np;
+        np += c;
+      }
+    const int nt = (np + tile_rows - 1) / tile_rows;
+    scan[tid] = np;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+      int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl_p = scan[tid];
+    const int chunk_p = scan[kRouteThreads - 1];
+    __syncthreads();
+    scan[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < kRouteThreads; off <<= 1) {
+      int v = (tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int incl_t = scan[tid];
+    const int chunk_t = scan[kRouteThreads - 1];
+    __syncthreads();
+    if (e < E) {
+      const int start = base_pairs + incl_p - np;
+      offsets[e] = start;
+      for (int g = 0; g < G; ++g) gcount[(int64_t)g * E + e] += start;
+      const int tb = base_tiles + incl_t - nt;
+      for (int k = 0; k < nt; ++k) {
+        GemmTile t;
+        t.expert = e;
+        t.row0 = start + k * tile_rows;
+        t.nrows = min(tile_rows, np - k * tile_rows);
+        t.pad = 0;
+        tiles[tb + k] = t;
+      }
+    }
+    base_pairs += chunk_p;
+    base_tiles += chunk_t;
+  }
+  if (tid == 0) {
+    offsets[E] = base_pairs;
+    *ntiles = base_tiles;
+    int err = 0;
+    for (int g = 0; g < G; ++g) err += gerr[g];
+    if (err_count) *err_count = err;
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_t* __restrict__ ids,
+                                                                    int64_t P, int E,
+                                                                    const int* __restrict__ gcount,
+                                                                    int* __restrict__ perm) {
+  extern __shared__ int cnt[];  // [waves][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, G = gridDim.x, g = blockIdx.x;
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
+  __syncthreads();
+  const int64_t q0 = P * g / G, q1 = P * (g + 1) / G, n = q1 - q0;
+  const int64_t p0 = q0 + n * wave / kRouteWaves, p1 = q0 + n * (wave + 1) / kRouteWaves;
+  int* mycnt = cnt + wave * E;
+  for (int64_t p = p0 + lane; p < p1; p += 64) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&mycnt[e], 1);
+  }
+  __syncthreads();
+  // each wave's first position per expert: the workgroup's start plus the
+  // pairs of the earlier waves
+  for (int e = tid; e < E; e += kRouteThreads) {
+    int run = gcount[(int64_t)g * E + e];
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t b = p0; b < p1; b += 64) {
+    const int64_t p = b + lane;
+    const int e = (p < p1) ? ids[p] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+      match &= ((e >> bit) & 1) ? ones : ~ones;
+    }
+    if (valid) {
+      const int rank = __popcll(match & lt_mask);
+      const int pos = mycnt[e] + rank;
+      perm[pos] = (int)p;
+      if ((match & lt_mask) == 0) mycnt[e] = pos - rank + __popcll(match);
+    }
+  }
+}
+
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ ids, int E,
@@ -175,11 +326,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 size_t route_lds_bytes(int E) { return sizeof(int) * ((size_t)kRouteWaves * E + E + kRouteThreads); }
 
+// Pairs per workgroup of the many-workgroup grouping, and the most workgroups.
+constexpr int64_t kRouteChunk = 4096;
+constexpr int kRouteMaxGroups = 256;
+
+int route_groups(int64_t P) {
+  const int64_t g = (P + kRouteChunk - 1) / kRouteChunk;
+  return (int)(g < 1 ? 1 : g > kRouteMaxGroups ? kRouteMaxGroups : g);
+}
+
+size_t route_workspace_bytes(int64_t P, int E) {
+  const int G = route_groups(P);
+  return sizeof(int) * ((size_t)G * E + G);
+}
+
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
-                        GemmTile* tiles, int* ntiles, int* err_count, hipStream_t s) {
-  size_t lds = route_lds_bytes(E);
-  route_kernel<<<1, kRouteThreads, lds, s>>>(ids, P, E, tile_rows, offsets, perm, tiles, ntiles,
-                                             err_count);
+                        GemmTile* tiles, int* ntiles, int* err_count, int* ws, hipStream_t s) {
+  const int G = route_groups(P);
+  if (G == 1 || !ws) {
+    route_kernel<<<1, kRouteThreads, route_lds_bytes(E), s>>>(ids, P, E, tile_rows, offsets, perm, tiles,
+                                                              ntiles, err_count);
+    return hipGetLastError();
+  }
+  int* gcount = ws;
+  int* gerr = ws + (size_t)G * E;
+  route_count_kernel<<<G, kRouteThreads, sizeof(int) * E, s>>>(ids, P, E, gcount, gerr);
+  route_scan_kernel<<<1, kRouteThreads, 0, s>>>(G, E, tile_rows, gcount, gerr, offsets, tiles, ntiles,
+                                                 err_count);
+  route_place_kernel<<<G, kRouteThreads, sizeof(int) * kRouteWaves * E, s>>>(ids, P, E, gcount, perm);
   return hipGetLastError();
 }
 

@@ -221,6 +221,24 @@ def test_moe_dynamic_l1_scale(nv, orc, tile_rows, shape):
 
 
 @pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_many_route_groups(nv, orc, tile_rows):
+    """Enough pairs (P = 9000) for the grouping to run over several
+    workgroups (3 x 4096 pairs), with skipped ids spread over them, against
+    the oracle on every token."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=4500, name="tiny4500")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ids = ids.copy()
+    ids[[5, 2100, 4400], [0, 1, 0]] = [-1, cfg.E, 77]
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
+    assert host(dbg["err_count"])[0] == 3
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    _gate(*res[:4])
+
+
+@pytest.mark.parametrize("tile_rows", TILES)
 def test_moe_deterministic(nv, tile_rows):
     cfg = synth.TINY
     w = gpu_weights(nv, cfg)
