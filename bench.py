@@ -127,6 +127,9 @@ KERNEL_SOURCES = {
     "quantize_kernel": ["quantize.hip", "nvfp4_device.hpp", "launch.hpp"],
     "dequantize_kernel": ["quantize.hip", "nvfp4_device.hpp", "launch.hpp"],
     "combine_kernel": ["moe.hip", "launch.hpp"],
+    "amax_partial_kernel": ["quantize.hip", "nvfp4_device.hpp", "launch.hpp"],
+    "l1_skinny_kernel": ["gemm_skinny.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
+    "l2_skinny_kernel": ["gemm_skinny.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
@@ -140,8 +143,8 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, grid):
-    """HBM bytes per launch of `kernel` at grid size `grid` from the
+def load_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` in the bench leg `workload` from the
     committed counter summary, or None when absent or when the kernel's
     sources changed since the counters were taken."""
     try:
@@ -152,7 +155,7 @@ def load_traffic(kernel, grid):
     for line in text.splitlines():
         if line.startswith("traffic-json: "):
             d = json.loads(line[len("traffic-json: "):])
-            if d["kernel"] == kernel and d["grid"] == grid and d["src"] == source_hash(kernel):
+            if d.get("kernel") == kernel and d.get("workload") == workload and d.get("src") == source_hash(kernel):
                 return d["bytes_per_launch"]
     return None
 
@@ -189,10 +192,20 @@ def _read_counters(path, counter):
     return rows
 
 
-def traffic_summary(copy_fetch, copy_write, fetch, write, cmds):
-    """Markdown summary of two counter runs (FETCH_SIZE, WRITE_SIZE in KiB
-    per dispatch), each scaled by what the same counter reads for the 512 MiB
-    copy of known size; one traffic-json line per (kernel, grid)."""
+def _split_legs(items):
+    """'leg=path' arguments -> [(leg, path)]."""
+    out = []
+    for it in items:
+        leg, _, path = it.partition("=")
+        out.append((leg, path))
+    return out
+
+
+def traffic_summary(copy_fetch, copy_write, legs, cmds):
+    """Markdown summary of counter runs (FETCH_SIZE and WRITE_SIZE in KiB per
+    dispatch, one pair of runs per bench leg: legs = [(leg, fetch_csv,
+    write_csv)]), each scaled by what the same counter reads for the 512 MiB
+    copy of known size; one traffic-json line per (leg, kernel, grid)."""
     import collections
     n_copy = 512 << 20
     cf = [v for k, g, v in _read_counters(copy_fetch, "FETCH_SIZE") if k == "__amd_rocclr_copyBuffer"]
@@ -200,27 +213,29 @@ def traffic_summary(copy_fetch, copy_write, fetch, write, cmds):
     f_fac = n_copy / (np.median(cf) * 1024.0)
     w_fac = n_copy / (np.median(cw) * 1024.0)
     agg = collections.defaultdict(lambda: [[], []])
-    for i, (path, ctr) in enumerate(((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE"))):
-        for k, g, v in _read_counters(path, ctr):
-            if k in KERNEL_SOURCES:
-                agg[(k, g)][i].append(v)
+    for leg, fetch, write in legs:
+        for i, (path, ctr) in enumerate(((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE"))):
+            for k, g, v in _read_counters(path, ctr):
+                if k in KERNEL_SOURCES:
+                    agg[(leg, k, g)][i].append(v)
     out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
-           "Commands (from the repository root, on one MI355X; R = repository root):", ""]
+           "Commands (from the repository root, on one MI355X; R = repository root; LEG is each of the",
+           "bench legs listed in the table, one pair of counter runs per leg):", ""]
     out += ["    " + c for c in cmds]
     out += ["",
             f"Calibration: a 512 MiB device copy reads FETCH_SIZE {np.median(cf):.0f} KiB and "
             f"WRITE_SIZE {np.median(cw):.0f} KiB per dispatch (median of {len(cf)}, {len(cw)}), "
             f"so the scale factors are {f_fac:.4f} (fetch) and {w_fac:.4f} (write).", "",
-            "| kernel | grid | dispatches | FETCH KiB | WRITE KiB | HBM bytes per launch (scaled) |",
-            "|---|---|---|---|---|---|"]
+            "| leg | kernel | grid | dispatches | FETCH KiB | WRITE KiB | HBM bytes per launch (scaled) |",
+            "|---|---|---|---|---|---|---|"]
     js = []
-    for (k, g), (fv, wv) in sorted(agg.items()):
+    for (leg, k, g), (fv, wv) in sorted(agg.items()):
         if not fv or not wv:
             continue
         fk, wk = float(np.mean(fv)), float(np.mean(wv))
         b = fk * 1024 * f_fac + wk * 1024 * w_fac
-        out.append(f"| {k} | {g} | {len(fv)} | {fk:.0f} | {wk:.0f} | {b / 1e6:.2f} MB |")
-        js.append("traffic-json: " + json.dumps({"kernel": k, "grid": g, "src": source_hash(k),
+        out.append(f"| {leg} | {k} | {g} | {len(fv)} | {fk:.0f} | {wk:.0f} | {b / 1e6:.2f} MB |")
+        js.append("traffic-json: " + json.dumps({"kernel": k, "workload": leg, "grid": g, "src": source_hash(k),
                                                  "bytes_per_launch": b, "fetch_bytes": fk * 1024 * f_fac,
                                                  "write_bytes": wk * 1024 * w_fac}))
     out += ["", "Machine-readable lines (bench.py reads these; src = hash of the kernel's sources):", ""]
@@ -228,22 +243,33 @@ def traffic_summary(copy_fetch, copy_write, fetch, write, cmds):
     return "\n".join(out) + "\n"
 
 
-def trace_summary(trace_csv, cmd):
-    """Markdown table of a rocprofv3 kernel trace: dispatches and average
-    duration per (kernel, grid)."""
+def trace_summary(legs, cmd):
+    """Markdown table of rocprofv3 kernel traces, one per bench leg (legs =
+    [(leg, kernel_trace_csv)]): dispatches and average duration per (leg,
+    kernel, grid)."""
     import collections
     import csv
     agg = collections.defaultdict(list)
-    with open(trace_csv) as fh:
-        for r in csv.DictReader(fh):
-            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-            agg[(_short_name(r["Kernel_Name"]), grid)].append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-    out = ["# Kernel trace (rocprofv3 --kernel-trace --stats)", "", "Command (from the repository root, on one "
-           "MI355X; R = repository root):", "", "    " + cmd, "",
-           "| kernel | grid (work-items) | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
-    for (k, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        out.append(f"| {k} | {g} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
+    for leg, path in legs:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                agg[(leg, _short_name(r["Kernel_Name"]), grid)].append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    out = ["# Kernel trace (rocprofv3 --kernel-trace --stats), per bench leg", "",
+           "Command (from the repository root, on one MI355X; R = repository root; LEG is each bench leg",
+           "in the table):", "", "    " + cmd, "",
+           "Kernels of the library (and the runtime's copy) only; torch's own kernels (weight generation)",
+           "are left out.", "",
+           "| leg | kernel | grid (work-items) | dispatches | avg us | min us | max us |",
+           "|---|---|---|---|---|---|---|"]
+    mine = set(KERNEL_SOURCES) | {"amax_rows_partial_kernel", "amax_finalize_kernel", "copy_scalar_kernel",
+                                  "dequantize_f16_kernel", "route_kernel", "route_count_kernel",
+                                  "route_scan_kernel", "route_place_kernel", "l1_skinny_kernel",
+                                  "l2_skinny_kernel", "__amd_rocclr_copyBuffer"}
+    for (leg, k, g), v in sorted(agg.items(), key=lambda kv: (kv[0][0], -sum(kv[1]))):
+        if k in mine:
+            out.append(f"| {leg} | {k} | {g} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -421,17 +447,21 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the unfused and dynamic-scale runs of the prefill layer")
-    ap.add_argument("--traffic-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
-                    help="print the markdown HBM-traffic summary of four rocprofv3 counter CSVs")
-    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
-                    help="print the markdown summary of a rocprofv3 kernel trace")
+    ap.add_argument("--traffic-summary", nargs="+", metavar="CSV",
+                    help="print the markdown HBM-traffic summary of rocprofv3 counter CSVs: COPY_FETCH "
+                         "COPY_WRITE, then LEG=FETCH_CSV LEG=WRITE_CSV pairs")
+    ap.add_argument("--trace-summary", nargs="+", metavar="LEG=KERNEL_TRACE_CSV",
+                    help="print the markdown summary of rocprofv3 kernel traces, one per bench leg")
     ap.add_argument("--cmd", action="append", default=[], help="command lines quoted in a summary")
     args = ap.parse_args()
     if args.traffic_summary:
-        sys.stdout.write(traffic_summary(*args.traffic_summary, args.cmd))
+        cf, cw, *rest = args.traffic_summary
+        pairs = _split_legs(rest)
+        legs = [(pairs[i][0], pairs[i][1], pairs[i + 1][1]) for i in range(0, len(pairs), 2)]
+        sys.stdout.write(traffic_summary(cf, cw, legs, args.cmd))
         return
     if args.trace_summary:
-        sys.stdout.write(trace_summary(args.trace_summary, " ".join(args.cmd)))
+        sys.stdout.write(trace_summary(_split_legs(args.trace_summary), " ".join(args.cmd)))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -484,11 +514,7 @@ def main():
     p = res.get("prefill")
     traffic = None
     if p:
-        cfg = synth.PRE
-        # the library's L1 launch: (ceil(P / 256) + E) row tiles x 2I / 256
-        # column tiles, 512 threads each
-        grid = ((cfg.P + 255) // 256 + cfg.E) * (2 * cfg.I // 256) * 512
-        traffic = load_traffic("l1_gemm_swiglu_quant_kernel", grid)
+        traffic = load_traffic("l1_gemm_swiglu_quant_kernel", "pre")
     line = {
         "metric": "MoE expert-FFN TFLOP/s + quantize GB/s, % of MI355X roofline (1 GPU)",
         "value": p["TFLOPs"] if p else None,

@@ -127,16 +127,18 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     int64_t i = base + u * kQThreads;  // i and i^1 hold the two halves of block i/2
     uint32_t code;
     uint32_t p = quantize_half_block(w[u], E, rtab, &code);
-    if (i < n8) {
-      q[i] = p;
-      if ((i & 1) == 0) sf[i >> 1] = (uint8_t)code;
+    if (i < n8) {  // the NVFP4 bytes are not read back by this pass: streaming stores
+      __builtin_nontemporal_store(p, q + i);
+      if ((i & 1) == 0) __builtin_nontemporal_store((uint8_t)code, sf + (i >> 1));
       if (F16OUT) f16out[i] = dequant8(p, scale_pair(code));
     }
   }
 }
 
 // ------------------------------------------------------------------ dequantize
-// Each lane handles 8 elements: one dword of nibbles and its block scale.
+// Each lane handles kQUnroll chunks of 8 elements (one dword of nibbles and
+// its block scale each, loaded together before any is converted); the bf16
+// output is written with streaming stores.
 // x = f32(f32(e2m1 * sfd) * g); the gfx950 FP4 -> f32 conversion gives the
 // exact E2M1 values, the product with the E4M3 scale is exact in fp32.
 template <bool BF16_OUT>
@@ -145,10 +147,21 @@ __global__ __launch_bounds__(kQThreads) void dequantize_kernel(const uint32_t* _
                                                                const float* __restrict__ gs,
                                                                int64_t n8, void* __restrict__ out) {
   const float g = gs[0];
-  for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < n8;
-       i += (int64_t)gridDim.x * kQThreads) {
-    uint32_t p = q[i];
-    float sfd = e4m3_decode_signed(sf[i >> 1]);
+  const int64_t base = (int64_t)blockIdx.x * kQChunksPerWG + threadIdx.x;
+  uint32_t pq[kQUnroll];
+  uint32_t cs[kQUnroll];
+#pragma unroll
+  for (int u = 0; u < kQUnroll; ++u) {
+    const int64_t i = base + u * kQThreads;
+    pq[u] = (i < n8) ? __builtin_nontemporal_load(q + i) : 0u;
+    cs[u] = (i < n8) ? sf[i >> 1] : 0u;
+  }
+#pragma unroll
+  for (int u = 0; u < kQUnroll; ++u) {
+    const int64_t i = base + u * kQThreads;
+    if (i >= n8) break;
+    const uint32_t p = pq[u];
+    const float sfd = e4m3_decode_signed(cs[u]);
     float v[8];
     auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
     auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
@@ -163,12 +176,12 @@ __global__ __launch_bounds__(kQThreads) void dequantize_kernel(const uint32_t* _
     v[6] = (f3[0] * sfd) * g;
     v[7] = (f3[1] * sfd) * g;
     if (BF16_OUT) {
-      uint4 o;
       __bf16 h[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) h[k] = (__bf16)v[k];
+      u32x4 o;
       __builtin_memcpy(&o, h, 16);
-      reinterpret_cast<uint4*>(out)[i] = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + i);
     } else {
       float4* o = reinterpret_cast<float4*>(out) + 2 * i;
       o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -265,8 +278,7 @@ hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* g
                              bool bf16_out, void* out, hipStream_t s) {
   int64_t n8 = n / 8;
   if (n8 == 0) return hipSuccess;
-  int64_t wg = (n8 + kQThreads - 1) / kQThreads;
-  if (wg > 65536) wg = 65536;
+  int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
   if (bf16_out)
     dequantize_kernel<true><<<(unsigned)wg, kQThreads, 0, s>>>(
         reinterpret_cast<const uint32_t*>(q), sf, gs, n8, out);
