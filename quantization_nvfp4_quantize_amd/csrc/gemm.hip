@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "gemm_common.hpp"
 
@@ -562,11 +563,19 @@ int gemm_tile_rows() { return kTileM; }
 
 // Persistent grid for up to `items` items: one workgroup per CU of the
 // current device, a multiple of 8 (the XCDs), no more than the items need.
+// The CU count is queried once per device.
 static unsigned persistent_grid(int64_t items) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-    cus = 256;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cu_count[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  int cus = dev >= 0 ? cu_count[dev].load(std::memory_order_relaxed) : 0;
+  if (cus == 0) {
+    if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 8)
+      cus = 256;
+    if (dev >= 0) cu_count[dev].store(cus, std::memory_order_relaxed);
+  }
   return (unsigned)std::min<int64_t>((items + 7) / 8 * 8, (int64_t)(cus / 8 * 8));
 }
 
