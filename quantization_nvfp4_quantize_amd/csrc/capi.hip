@@ -233,7 +233,7 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
   float* o32 = out_dtype == 1 ? static_cast<float*>(out) : nullptr;
   uint16_t* o16 = out_dtype == 0 ? static_cast<uint16_t*>(out) : nullptr;
   return hip_status(gemm(x_f16, gs, K, w_q, w_sf, w_gs, N, nullptr, o32, nullptr, nullptr, tiles, nullptr,
-                         s, M, o16),
+                         s, M, o16, nullptr),
                     "nvfp4_linear");
 }
 
@@ -241,8 +241,8 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
 namespace {
 
 struct MoeLayout {
-  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, route, a2_gs, c, a2q, a2sf,
-      a2_f16, o, total;
+  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, route, sched, a2_gs, c, a2q,
+      a2sf, a2_f16, o, total;
   int max_tiles;
 };
 
@@ -283,6 +283,7 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.ntiles = take(sizeof(int));
   L.err = take(sizeof(int));
   L.route = take(nvfp4::route_workspace_bytes(P, (int)E));
+  L.sched = take(16 * sizeof(int));
   L.a2_gs = take(sizeof(float));
   L.c = take(moe_interleaved(a) ? sizeof(uint16_t) * (size_t)(2 * P * I)
              : moe_unfused(a) && !a->l1_c_bf16 ? sizeof(uint16_t) * (size_t)(P * I) : 0);
@@ -392,7 +393,8 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
   const bool skinny = moe_tile_rows(a) == nvfp4::skinny_tile_rows();
   if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, (int)moe_tile_rows(a), offsets, perm,
-                                           tiles, ntiles, err, reinterpret_cast<int*>(w + L.route), s),
+                                           tiles, ntiles, err, reinterpret_cast<int*>(w + L.route),
+                                           reinterpret_cast<int*>(w + L.sched), s),
                        "route")))
     return st;
   mark(3);
@@ -448,7 +450,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   float* o = reinterpret_cast<float*>(w + L.o);
   auto l2 = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
   if ((st = hip_status(l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
-                          L.max_tiles, perm, s, 0, nullptr),
+                          L.max_tiles, perm, s, 0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8),
                        "L2 GEMM")))
     return st;
   mark(5);

@@ -348,6 +348,20 @@ __device__ __forceinline__ Items persistent_items(int W) {
   return {start + (int)(blockIdx.x >> 3), start + q + (x < r ? 1 : 0), (int)(gridDim.x >> 3)};
 }
 
+// The items of XCD x are start .. end - 1.  With work counters (sched), the
+// workgroups of an XCD claim its items one at a time in order (item = start +
+// the counter's old value), so a workgroup that drew short items (an expert's
+// last few rows) takes more of them; without, they take them in turn.
+struct XcdRange {
+  int start, end;
+};
+
+__device__ __forceinline__ XcdRange xcd_range(int W) {
+  const int x = blockIdx.x & 7, q = W >> 3, r = W & 7;
+  const int start = x * q + min(x, r);
+  return {start, start + q + (x < r ? 1 : 0)};
+}
+
 // ------------------------------------------------------------------ L1
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
   __shared__ f16x8 lds_a[kAStages * kLdsOperand];
@@ -473,12 +487,26 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   __shared__ int out_row[kTileM];
   __shared__ float out_scale[kTileM];
   const Lds L{lds_a, lds_b, lds_s};
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_claim[2];
+  const int tid = threadIdx.x;
   const int mtiles = p.tiles ? *p.ntiles : (int)((p.M + kTileM - 1) / kTileM);
-  Items its = persistent_items(mtiles * p.n_ntiles);
-  const int end = its.end, stride = its.stride;
-  int item = its.item;
-  if (item >= end) return;
+  const XcdRange xr = xcd_range(mtiles * p.n_ntiles);
+  int* const counter = p.sched ? p.sched + (blockIdx.x & 7) : nullptr;
+  // the first two items of this workgroup (claimed, or in turn)
+  int item, next;
+  if (counter) {
+    if (tid == 0) {
+      s_claim[0] = xr.start + atomicAdd(counter, 1);
+      s_claim[1] = xr.start + atomicAdd(counter, 1);
+    }
+    __syncthreads();
+    item = s_claim[0];
+    next = s_claim[1];
+  } else {
+    item = xr.start + (int)(blockIdx.x >> 3);
+    next = item + (int)(gridDim.x >> 3);
+  }
+  if (item >= xr.end) return;
   const int nk = (int)(p.K / kStepK);
 
   // tile, column tile and this lane's operand sources of an item
@@ -519,8 +547,13 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   for (;;) {
     asm volatile("" : "+v"(tid_i));  // see opaque_tid: keeps per-lane addresses inside the loop
     const int lane_i = tid_i & 63;
+    // claim the item after `next` now; its index is needed only after this
+    // item's epilogue, when the loads before it have landed anyway
+    int claimed = 0;
+    if (counter && tid_i == 0) claimed = atomicAdd(counter, 1);
     f32x16 acc[4][2];
     gemm_body(L, op, nk, t.nrows, acc, tid_i);
+    if (counter && tid_i == 0) s_claim[0] = xr.start + claimed;  // published by the epilogue's barrier
     // output row (pair id) and scale alpha * routing weight of every tile row
     if (tid_i < t.nrows) {
       const int pr = p.perm ? p.perm[t.row0 + tid_i] : t.row0 + tid_i;
@@ -528,8 +561,7 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
       out_row[tid_i] = pr;
       out_scale[tid_i] = p.row_w ? alpha * p.row_w[pr] : alpha;
     }
-    const int next = item + stride;
-    const bool more = next < end;  // workgroup-uniform
+    const bool more = next < xr.end;  // workgroup-uniform
     GemmTile tn = t;
     int ntn = nt;
     if (more) {
@@ -537,6 +569,7 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
       gemm_prologue(L, op, nk, tid_i);  // the stages are free: gemm_body ended with a barrier
     }
     __syncthreads();
+    const int after = counter ? s_claim[0] : next + (int)(gridDim.x >> 3);
     const int wm = wave_m(tid_i >> 6), wn = wave_n(tid_i >> 6);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -553,6 +586,7 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     }
     if (!more) break;
     item = next;
+    next = after;
     t = tn;
     nt = ntn;
   }
@@ -595,8 +629,9 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
 hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, const int* perm,
-                     hipStream_t s, int64_t M, uint16_t* o_bf16) {
-  L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN)};
+                     hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched) {
+  L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN),
+             sched};
   const int64_t items = (int64_t)max_tiles * p.n_ntiles;
   if (items == 0) return hipSuccess;
   l2_gemm_kernel<<<persistent_grid(items), kGemmThreads, 0, s>>>(p);

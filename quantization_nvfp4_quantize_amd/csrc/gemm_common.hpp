@@ -211,6 +211,7 @@ struct L2Params {
   int64_t M;            // rows when tiles == nullptr
   const int* perm;      // nullable: sorted position -> pair id
   int n_ntiles;
+  int* sched;           // nullable: 8 zeroed work counters (one per XCD) for dynamic item claiming
 };
 
 // One output value of the L2 / linear epilogue.

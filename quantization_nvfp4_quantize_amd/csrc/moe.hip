@@ -28,6 +28,7 @@
 namespace nvfp4 {
 
 constexpr int kRouteThreads = 1024;
+constexpr int kSchedCounters = 16;  // the GEMMs' work counters, zeroed with the grouping
 constexpr int kRouteWaves = kRouteThreads / 64;
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
@@ -36,7 +37,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
                                                               int* __restrict__ perm,
                                                               GemmTile* __restrict__ tiles,
                                                               int* __restrict__ ntiles,
-                                                              int* __restrict__ err_count) {
+                                                              int* __restrict__ err_count,
+                                                              int* __restrict__ sched) {
   extern __shared__ int sm[];
   int* cnt = sm;                            // [waves][E]: pass-1 counts, then running positions
   int* total = cnt + kRouteWaves * E;       // [E]
@@ -123,6 +125,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
     *ntiles = base_tiles;
     if (err_count) *err_count = s_err;
   }
+  if (sched && tid < kSchedCounters) sched[tid] = 0;
 
   // pass 2: stable placement, 64 pairs per step, ranks by ballot matching
   int nbits = 1;
@@ -183,7 +186,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int G, int E,
                                                                    int* __restrict__ offsets,
                                                                    GemmTile* __restrict__ tiles,
                                                                    int* __restrict__ ntiles,
-                                                                   int* __restrict__ err_count) {
+                                                                   int* __restrict__ err_count,
+                                                                   int* __restrict__ sched) {
   __shared__ int scan[kRouteThreads];
   const int tid = threadIdx.x;
   int base_pairs = 0, base_tiles = 0;
@@ -244,6 +248,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int G, int E,
     for (int g = 0; g < G; ++g) err += gerr[g];
     if (err_count) *err_count = err;
   }
+  if (sched && tid < kSchedCounters) sched[tid] = 0;
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_t* __restrict__ ids,
@@ -341,18 +346,18 @@ size_t route_workspace_bytes(int64_t P, int E) {
 }
 
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
-                        GemmTile* tiles, int* ntiles, int* err_count, int* ws, hipStream_t s) {
+                        GemmTile* tiles, int* ntiles, int* err_count, int* ws, int* sched, hipStream_t s) {
   const int G = route_groups(P);
   if (G == 1 || !ws) {
     route_kernel<<<1, kRouteThreads, route_lds_bytes(E), s>>>(ids, P, E, tile_rows, offsets, perm, tiles,
-                                                              ntiles, err_count);
+                                                              ntiles, err_count, sched);
     return hipGetLastError();
   }
   int* gcount = ws;
   int* gerr = ws + (size_t)G * E;
   route_count_kernel<<<G, kRouteThreads, sizeof(int) * E, s>>>(ids, P, E, gcount, gerr);
   route_scan_kernel<<<1, kRouteThreads, 0, s>>>(G, E, tile_rows, gcount, gerr, offsets, tiles, ntiles,
-                                                 err_count);
+                                                 err_count, sched);
   route_place_kernel<<<G, kRouteThreads, sizeof(int) * kRouteWaves * E, s>>>(ids, P, E, gcount, perm);
   return hipGetLastError();
 }
