@@ -321,37 +321,17 @@ __device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, 
   gemm_body(L, op, nk, nrows, acc, threadIdx.x);
 }
 
-// threadIdx.x behind an empty asm statement: values derived from it inside a
-// persistent loop are recomputed per item instead of being hoisted out of the
-// loop (which would hold dozens of per-lane addresses across the K loop).
-__device__ __forceinline__ int opaque_tid() {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
-
 // ------------------------------------------------------------------ persistent grid
 // The L2 GEMM runs one workgroup per CU (a multiple of 8) over W (row tile,
 // column tile) items, row-tile-major.  The XCD x = b % 8 of workgroup b owns
-// the contiguous range of items work_item would deal it, and its workgroups
-// take them in turn, so the workgroups running together on one XCD work on
-// neighbouring items.  The next item's operand offsets and prologue loads are
-// issued before the current item's epilogue, so its load latency, the
-// epilogue and the absent workgroup launch overlap.
-struct Items {
-  int item, end, stride;
-};
-
-__device__ __forceinline__ Items persistent_items(int W) {
-  const int x = blockIdx.x & 7, q = W >> 3, r = W & 7;
-  const int start = x * q + min(x, r);
-  return {start + (int)(blockIdx.x >> 3), start + q + (x < r ? 1 : 0), (int)(gridDim.x >> 3)};
-}
-
-// The items of XCD x are start .. end - 1.  With work counters (sched), the
-// workgroups of an XCD claim its items one at a time in order (item = start +
-// the counter's old value), so a workgroup that drew short items (an expert's
-// last few rows) takes more of them; without, they take them in turn.
+// the contiguous range start .. end - 1 of items that work_item would deal
+// it, so the workgroups running together on one XCD work on neighbouring
+// items.  With work counters (sched), the workgroups of an XCD claim its
+// items one at a time in order (item = start + the counter's old value), so
+// a workgroup that drew short items (an expert's last few rows) takes more
+// of them; without, they take them in turn.  The next item's operand offsets
+// and prologue loads are issued before the current item's epilogue, so its
+// load latency, the epilogue and the absent workgroup launch overlap.
 struct XcdRange {
   int start, end;
 };
@@ -545,7 +525,10 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   gemm_prologue(L, op, nk, tid);
   int tid_i = tid;
   for (;;) {
-    asm volatile("" : "+v"(tid_i));  // see opaque_tid: keeps per-lane addresses inside the loop
+    // threadIdx.x behind an empty asm statement: the per-lane addresses
+    // derived from it are recomputed per item instead of being hoisted out of
+    // the loop (which would hold dozens of them across the K loop)
+    asm volatile("" : "+v"(tid_i));
     const int lane_i = tid_i & 63;
     // claim the item after `next` now; its index is needed only after this
     // item's epilogue, when the loads before it have landed anyway
