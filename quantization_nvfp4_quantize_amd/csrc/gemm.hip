@@ -214,10 +214,10 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
           S[KB ^ 1].w[0] = s_next[0];
           S[KB ^ 1].w[1] = s_next[32];
         }
-        dma16(b_dst, b_src + op.bq_off);
-        if (scales) dma4(s_dst, s_src + op.bsf_off);
+        dma16s(b_dst, b_src, op.bq_off);
+        if (scales) dma4s(s_dst, s_src, op.bsf_off);
       }
-      if (slot >= 1 && slot < 5) dma16(a_dst + (slot - 1) * 64, a_src + op.a_off[slot - 1]);
+      if (slot >= 1 && slot < 5) dma16s(a_dst + (slot - 1) * 64, a_src, op.a_off[slot - 1]);
       SCHED_FENCE();
     }
   }
@@ -263,14 +263,13 @@ __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, 
     const uint8_t* a_src = op.a + (size_t)min(j, last) * (kStepK * 2);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      dma16(L.a + j * kLdsOperand + (4 * wave + u) * 64, a_src + op.a_off[u]);
+      dma16s(L.a + j * kLdsOperand + (4 * wave + u) * 64, a_src, op.a_off[u]);
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    dma16(L.b + j * kBRaw + wave * 64, op.bq + (size_t)min(j, last) * (kStepK / 2) + op.bq_off);
+    dma16s(L.b + j * kBRaw + wave * 64, op.bq + (size_t)min(j, last) * (kStepK / 2), op.bq_off);
     if ((wave >> 2) == (j & 1))
-      dma4(L.s + j * kBScale * 4 + (wave & 3) * 64,
-           op.bsf + (size_t)min(j, last) * (kStepK / 16) + op.bsf_off);
+      dma4s(L.s + j * kBScale * 4 + (wave & 3) * 64, op.bsf + (size_t)min(j, last) * (kStepK / 16), op.bsf_off);
   }
 }
 

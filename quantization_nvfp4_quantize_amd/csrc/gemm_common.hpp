@@ -83,6 +83,33 @@ __device__ __forceinline__ void dma16(f16x8* dst, const uint8_t* src) {
       : "memory");
 }
 
+// The same with a wave-uniform base address (held in scalar registers) and a
+// 32-bit per-lane byte offset: one VGPR per lane instead of a 64-bit
+// address, and no per-lane 64-bit add.
+__device__ __forceinline__ void dma16s(f16x8* dst, const uint8_t* base, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(dst)), "v"(off), "s"(base)
+      : "memory");
+}
+
+__device__ __forceinline__ void dma4s(uint32_t* dst, const uint8_t* base, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(dst)), "v"(off), "s"(base)
+      : "memory");
+}
+
 // 256 B: lane i writes dword i of `dst` (wave-uniform) with the 4 B at src.
 __device__ __forceinline__ void dma4(uint32_t* dst, const uint8_t* src) {
   uint32_t saved;

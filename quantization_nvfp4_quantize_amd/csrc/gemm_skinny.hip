@@ -82,9 +82,10 @@ __device__ __forceinline__ int sk_steps(int ss, int nfull) { return ss < nfull ?
 // wave w fetches rows 8 w .. 8 w + 7 (1 KiB per step).  A tail super-step
 // loads its two steps twice (the second copy is not read).
 __device__ __forceinline__ void sk_load_a(f16x8* buf, const SkOperands& op, int ss, int m, int wave) {
-  const uint8_t* src = op.a + (size_t)ss * (kSkSteps * kStepK * 2) + op.a_hi * (uint32_t)m + op.a_base;
+  const uint8_t* base = op.a + (size_t)ss * (kSkSteps * kStepK * 2);
+  const uint32_t off = op.a_hi * (uint32_t)m + op.a_base;
 #pragma unroll
-  for (int j = 0; j < kSkSteps; ++j) dma16(buf + j * kSkAStage + wave * 64, src + 64 * (j & (m - 1)));
+  for (int j = 0; j < kSkSteps; ++j) dma16s(buf + j * kSkAStage + wave * 64, base, off + 64u * (j & (m - 1)));
 }
 
 // Nibbles of super-step ss: four 16 B loads of consecutive addresses per
@@ -109,7 +110,7 @@ __device__ __forceinline__ void sk_load_sf_macro(uint8_t* sfbuf, const SkOperand
   for (int i = 0; i < 4; ++i) {
     const int c = (lane & 3) ^ sk_sf_swz(op.sf_tr[i]);
     const int ssrc = min(4 * mac + c, nfull - 1);
-    dma16(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf + op.sf_dma[i] + 16 * ssrc);
+    dma16s(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf, op.sf_dma[i] + 16u * ssrc);
   }
 }
 
