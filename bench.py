@@ -360,8 +360,21 @@ def bench_expert(nv, steps, warmup):
             torch.empty((M, I // 16), dtype=torch.uint8, device=dev))
     ms = graph_time(lambda i: nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, out=outs), steps, warmup)
     flops = 2.0 * M * K * 2 * I
-    return dict(workload=f"M{M} K{K} N2x{I}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
-                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
+    res = dict(workload=f"M{M} K{K} N2x{I}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
+               frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
+    # Context, not the product path: the vendor library's plain f16 GEMM
+    # (torch -> hipBLASLt) on the same operand values, A [M][K] @ B^T with B
+    # [2I][K] already dequantized (e2m1 * block scale, global scales left
+    # out, so every value is exact in f16).  It reads 4x the weight bytes and
+    # has no dequantization, SwiGLU or output quantization to do.
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    a16 = nv.dequantize(xq, xsf, one).to(torch.float16)
+    b16 = nv.dequantize(wq, wsf, one).to(torch.float16).t().contiguous()  # [K][2I]
+    c16 = torch.empty((M, 2 * I), dtype=torch.float16, device=dev)
+    ms_v = graph_time(lambda i: torch.matmul(a16, b16, out=c16), steps, warmup)
+    res["vendor_f16_gemm"] = dict(ms=ms_v, TFLOPs=flops / ms_v / 1e9,
+                                  library="torch.matmul (hipBLASLt), f16 in/out, B pre-dequantized")
+    return res
 
 
 def bench_dense(nv, steps, warmup):

@@ -233,7 +233,7 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
   float* o32 = out_dtype == 1 ? static_cast<float*>(out) : nullptr;
   uint16_t* o16 = out_dtype == 0 ? static_cast<uint16_t*>(out) : nullptr;
   return hip_status(gemm(x_f16, gs, K, w_q, w_sf, w_gs, N, nullptr, o32, nullptr, nullptr, tiles, nullptr,
-                         s, M, o16, nullptr),
+                         s, M, o16, nullptr, nullptr, nullptr),
                     "nvfp4_linear");
 }
 
@@ -242,7 +242,7 @@ namespace {
 
 struct MoeLayout {
   size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, route, sched, a2_gs, c, a2q,
-      a2sf, a2_f16, o, total;
+      a2sf, a2_f16, o, oexp, total;
   int max_tiles;
 };
 
@@ -251,6 +251,12 @@ struct MoeLayout {
 // the pages' earlier one (interleaved bf16 output, deinterleave + quantize).
 bool moe_unfused(const nvfp4_moe_args* a) { return a->a2_gs == nullptr || a->l1_unfused == 1; }
 bool moe_interleaved(const nvfp4_moe_args* a) { return a->l1_unfused == 2; }
+
+// With a bf16 output the L2 GEMM writes its per-pair rows in f16 with one
+// power-of-two exponent per (pair, 64 columns) (relative error <= 2^-11 per
+// value, 4x below the bf16 rounding of y), which halves the bytes written and
+// read back by the combine; an fp32 output keeps fp32 rows.
+bool moe_f16_rows(const nvfp4_moe_args* a) { return a->out_dtype == 0; }
 
 // Rows per GEMM tile: 32-row tiles (weights streamed through registers) when
 // the experts get few rows each, else 256-row tiles (MFMA-bound).
@@ -290,7 +296,8 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.a2q = take((size_t)(P * I / 2));
   L.a2sf = take((size_t)(P * I / 16));
   L.a2_f16 = take(sizeof(uint16_t) * (size_t)(P * I));
-  L.o = take(sizeof(float) * (size_t)(P * H));
+  L.o = take((moe_f16_rows(a) ? sizeof(uint16_t) : sizeof(float)) * (size_t)(P * H));
+  L.oexp = take(moe_f16_rows(a) ? (size_t)(P * H / 64) : 0);
   L.total = off;
   return L;
 }
@@ -447,15 +454,19 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   }
   mark(4);
   // a7: L2 GEMM, weighted by the routing weights
-  float* o = reinterpret_cast<float*>(w + L.o);
+  const bool f16_rows = moe_f16_rows(a);
+  float* o = f16_rows ? nullptr : reinterpret_cast<float*>(w + L.o);
+  uint16_t* o16 = f16_rows ? reinterpret_cast<uint16_t*>(w + L.o) : nullptr;
+  int8_t* oexp = f16_rows ? reinterpret_cast<int8_t*>(w + L.oexp) : nullptr;
   auto l2 = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
   if ((st = hip_status(l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
-                          L.max_tiles, perm, s, 0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8),
+                          L.max_tiles, perm, s, 0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp),
                        "L2 GEMM")))
     return st;
   mark(5);
   // a8: combine the k rows of every token
-  if ((st = hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s),
+  if ((st = hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s,
+                                             o16, oexp),
                        "combine")))
     return st;
   mark(6);

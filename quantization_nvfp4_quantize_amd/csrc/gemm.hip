@@ -553,16 +553,26 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     __syncthreads();
     const int after = counter ? s_claim[0] : next + (int)(gridDim.x >> 3);
     const int wm = wave_m(tid_i >> 6), wn = wave_n(tid_i >> 6);
+    if (p.o_f16) {
+      const int64_t col0 = (int64_t)nt * kTileN + wn * 64;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < 4; ++mt) {
+        if (wm * 128 + mt * 32 >= t.nrows) break;  // wave-uniform
+        store_f16_rows(p, acc[mt][0], acc[mt][1], wm * 128 + mt * 32, t.nrows, col0, lane_i,
+                       [&](int r) { return out_row[r]; }, [&](int r) { return out_scale[r]; });
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int orw = wm * 128 + mt * 32 + acc_row(i, lane_i);
-        if (orw < t.nrows) {
-          const int64_t idx = (int64_t)out_row[orw] * p.N + (int64_t)nt * kTileN + wn * 64 + (lane_i & 31);
-          const float sc = out_scale[orw];
-          l2_store(p, idx, acc[mt][0][i] * sc);
-          l2_store(p, idx + 32, acc[mt][1][i] * sc);
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int orw = wm * 128 + mt * 32 + acc_row(i, lane_i);
+          if (orw < t.nrows) {
+            const int64_t idx = (int64_t)out_row[orw] * p.N + (int64_t)nt * kTileN + wn * 64 + (lane_i & 31);
+            const float sc = out_scale[orw];
+            l2_store(p, idx, acc[mt][0][i] * sc);
+            l2_store(p, idx + 32, acc[mt][1][i] * sc);
+          }
         }
       }
     }
@@ -611,9 +621,10 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
 hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, const int* perm,
-                     hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched) {
+                     hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched, uint16_t* o_f16,
+                     int8_t* o_exp) {
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN),
-             sched};
+             sched, o_f16, o_exp};
   const int64_t items = (int64_t)max_tiles * p.n_ntiles;
   if (items == 0) return hipSuccess;
   l2_gemm_kernel<<<persistent_grid(items), kGemmThreads, 0, s>>>(p);

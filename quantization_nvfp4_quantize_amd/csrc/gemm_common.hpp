@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -239,7 +241,76 @@ struct L2Params {
   const int* perm;      // nullable: sorted position -> pair id
   int n_ntiles;
   int* sched;           // nullable: 8 zeroed work counters (one per XCD) for dynamic item claiming
+  uint16_t* o_f16;      // nullable [rows][N] f16 output (used with o_exp instead of o):
+  int8_t* o_exp;        // value = o_f16 * 2^o_exp, one exponent per (row, 64-column block) [rows][N/64]
 };
+
+// Exponent for storing the values of one (row, 64-column block) in f16:
+// with m the block's largest magnitude, m * 2^-s lies in [2^14, 2^15), so no
+// value overflows and values down to 2^-28 of the block maximum stay normal
+// f16 numbers (full 11-bit precision).  s is clamped to [-128, 114] (int8): zero,
+// subnormal, infinite or NaN maxima only need a value that keeps the rest
+// finite.
+__device__ __forceinline__ int f16_block_exp(float m) {
+  const int ex = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+  return max(ex - 14, -128);
+}
+
+// Largest value over the 32 lanes of each half of the wave, for N values at
+// once (independent chains, so their latencies overlap): DPP inside each
+// 16-lane row, then a swap of the two rows of each half.
+template <int N>
+__device__ __forceinline__ void half_wave_max(float (&m)[N]) {
+  auto step = [&](auto ctrl) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      m[i] = fmaxf(m[i], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m[i]), decltype(ctrl)::value,
+                                                                  0xF, 0xF, false)));
+  };
+  step(std::integral_constant<int, 0xB1>{});   // lane ^ 1
+  step(std::integral_constant<int, 0x4E>{});   // lane ^ 2
+  step(std::integral_constant<int, 0x124>{});  // row_ror 4
+  step(std::integral_constant<int, 0x128>{});  // row_ror 8
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m[i]), __float_as_uint(m[i]), false, false);
+    m[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
+// One wave's 32-row x 64-column block of L2 outputs in the f16 form: rows
+// r0 + acc_row(i, lane) (those below nrows are valid) of the MFMA tiles a0
+// (columns col0 + lane % 32) and a1 (columns + 32); row_of(r) gives the
+// output row and scale_of(r) the factor of tile row r.  Every lane of the
+// wave must take part (cross-lane maxima); the exponent of the row of value i
+// is stored by lane i of each half-wave.
+template <class RowOf, class ScaleOf>
+__device__ __forceinline__ void store_f16_rows(const L2Params& p, const f32x16& a0, const f32x16& a1,
+                                               int r0, int nrows, int64_t col0, int lane, RowOf row_of,
+                                               ScaleOf scale_of) {
+  float sc[16], m[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + acc_row(i, lane);
+    sc[i] = r < nrows ? scale_of(r) : 0.0f;
+    m[i] = fmaxf(fabsf(a0[i] * sc[i]), fabsf(a1[i] * sc[i]));
+  }
+  half_wave_max(m);
+  int my_exp = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + acc_row(i, lane);
+    const int e = f16_block_exp(m[i]);
+    if ((lane & 31) == i) my_exp = e;
+    if (r < nrows) {
+      const int64_t idx = (int64_t)row_of(r) * p.N + col0 + (lane & 31);
+      p.o_f16[idx] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(a0[i] * sc[i], -e));
+      p.o_f16[idx + 32] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(a1[i] * sc[i], -e));
+    }
+  }
+  const int r = r0 + acc_row(lane & 15, lane);
+  if ((lane & 31) < 16 && r < nrows) p.o_exp[(int64_t)row_of(r) * (p.N / 64) + col0 / 64] = (int8_t)my_exp;
+}
 
 // One output value of the L2 / linear epilogue.
 __device__ __forceinline__ void l2_store(const L2Params& p, int64_t idx, float v) {

@@ -377,6 +377,12 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   if (tid < kSkTileM) out_row[tid] = pair_of(tid);
   __syncthreads();
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
+  if (p.o_f16) {
+    store_f16_rows(p, acc[0], acc[1], 0, t.nrows, (int64_t)nt * kTileN + wave * 64, lane,
+                   [&](int r) { return out_row[r]; },
+                   [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int orw = acc_row(i, lane);
@@ -414,10 +420,11 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
-                            const int* perm, hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched) {
+                            const int* perm, hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched,
+                            uint16_t* o_f16, int8_t* o_exp) {
   (void)sched;  // one workgroup per item here
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN),
-             nullptr};
+             nullptr, o_f16, o_exp};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
   if (!skinny_supports_k(K)) return hipErrorInvalidValue;

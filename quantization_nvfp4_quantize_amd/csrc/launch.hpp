@@ -60,12 +60,15 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr);
 // L2: o[pair] = alpha * w[pair] * (A @ W_e^T) for the routed rows (fp32), or
 // without routing (tiles, perm, row_w null) over M rows of expert 0, into o
-// (fp32) or o_bf16 (bf16) when that is non-null.  sched (nullable): 8 work
-// counters, zero at launch, that let the workgroups claim items dynamically.
+// (fp32), o_bf16 (bf16) when that is non-null, or o_f16 with o_exp (f16
+// values times a power of two per row and 64-column block, N % 64 == 0) when
+// those are non-null.  sched (nullable): 8 work counters, zero at launch, that
+// let the workgroups claim items dynamically.
 hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, const int* perm,
-                     hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr, int* sched = nullptr);
+                     hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr, int* sched = nullptr,
+                     uint16_t* o_f16 = nullptr, int8_t* o_exp = nullptr);
 
 // ---- moe.hip
 size_t route_lds_bytes(int E);
@@ -79,13 +82,17 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
-                            const int* perm, hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr, int* sched = nullptr);
+                            const int* perm, hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr, int* sched = nullptr,
+                            uint16_t* o_f16 = nullptr, int8_t* o_exp = nullptr);
 // Scratch (ints) of the many-workgroup grouping for P pairs and E experts.
 size_t route_workspace_bytes(int64_t P, int E);
 // Also zeroes sched[0 .. 16) (nullable): the GEMMs' work counters.
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
                         GemmTile* tiles, int* ntiles, int* err_count, int* ws, int* sched, hipStream_t s);
+// y[t] = sum over the k rows of token t of o (fp32), or of the f16 form
+// o_f16 * 2^o_exp when o_f16 is non-null (H % 64 == 0).
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,
-                          bool bf16_out, void* out, hipStream_t s);
+                          bool bf16_out, void* out, hipStream_t s, const uint16_t* o_f16 = nullptr,
+                          const int8_t* o_exp = nullptr);
 
 }  // namespace nvfp4

@@ -23,6 +23,8 @@
 // (each o row already carries alpha2 * routing weight).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 
 namespace nvfp4 {
@@ -329,6 +331,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// The same sum over the f16 form of o: o16[r][c] * 2^oexp[r][c / 64] (exact
+// in fp32), 8 columns per thread.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __restrict__ o16,
+                                                          const int8_t* __restrict__ oexp,
+                                                          const int32_t* __restrict__ ids, int E,
+                                                          int64_t T, int k, int64_t H,
+                                                          void* __restrict__ out) {
+  const int64_t n8 = H / 8, nb = H / 64;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * n8;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / n8, c = (i % n8) * 8;
+    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int64_t r = t * k + j;
+      const int e = ids[r];
+      if (e < 0 || e >= E) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(o16 + r * H + c);
+      const int s = oexp[r * nb + c / 64];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        y[2 * q] += ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu)), s);
+        y[2 * q + 1] += ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16)), s);
+      }
+    }
+    if (BF16_OUT) {
+      __bf16 h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h[q] = (__bf16)y[q];
+      uint4 u;
+      __builtin_memcpy(&u, h, 16);
+      reinterpret_cast<uint4*>(out)[(t * H + c) / 8] = u;
+    } else {
+      float4* dst = reinterpret_cast<float4*>(out) + (t * H + c) / 4;
+      dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+      dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  }
+}
+
 size_t route_lds_bytes(int E) { return sizeof(int) * ((size_t)kRouteWaves * E + E + kRouteThreads); }
 
 // Pairs per workgroup of the many-workgroup grouping, and the most workgroups.
@@ -363,7 +406,18 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int
 }
 
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,
-                          bool bf16_out, void* out, hipStream_t s) {
+                          bool bf16_out, void* out, hipStream_t s, const uint16_t* o_f16,
+                          const int8_t* o_exp) {
+  if (o_f16) {
+    const int64_t n = T * (H / 8);
+    if (n == 0) return hipSuccess;
+    const int64_t wg = std::min<int64_t>((n + 255) / 256, 65536);
+    if (bf16_out)
+      combine_f16_kernel<true><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+    else
+      combine_f16_kernel<false><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+    return hipGetLastError();
+  }
   int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
   int64_t wg = (n + 255) / 256;

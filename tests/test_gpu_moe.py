@@ -6,8 +6,9 @@ Gates (fp32-output mode): relative Frobenius error <= 1e-3 and cosine >=
 global scale) is bit-exact; the L1 SwiGLU output meets the same tolerance;
 the fused NVFP4 bytes of the L1 output equal the GPU's standalone quantizer
 on the GPU's own bf16 output.  bf16-output mode is compared with the oracle's
-y rounded to bf16 (reported, bounded loosely: bf16 rounding alone costs
-~1.7e-3)."""
+y rounded to bf16 (bounded loosely: bf16 rounding alone costs ~1.7e-3) and
+with the fp32-output run of the same layer (its per-pair L2 rows go through
+f16 with a power-of-two per row and 64 columns)."""
 import numpy as np
 import pytest
 import torch
@@ -84,18 +85,62 @@ def test_moe_tiny_full(nv, orc, tile_rows):
     assert host(dbg["err_count"])[0] == 0
 
 
-def test_moe_tiny_bf16_output(nv, orc):
-    cfg = synth.TINY
+def _check_bf16_vs_fp32(yb_dev, y32_dev):
+    """A bf16-output run against the fp32-output run of the same layer: the
+    bf16 path stores the per-pair L2 rows in f16 (relative error <= 2^-11
+    each) before the combine, then rounds y to bf16 (<= 2^-9)."""
+    yb = synth.bf16_values(host_bits(yb_dev))
+    y32 = host(y32_dev)
+    err = rel_fro(yb, y32)
+    assert err <= 2e-3, err
+    assert np.abs(yb - y32).max() <= 2.0 ** -8 * np.abs(y32).max()
+    return err
+
+
+@pytest.mark.parametrize("tile_rows", TILES)
+@pytest.mark.parametrize("T", [64, 257])
+def test_moe_bf16_output(nv, orc, tile_rows, T):
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=T, name=f"tiny{T}")
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
-    y, _ = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16)
+    y, _ = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16, tile_rows=tile_rows)
+    y32, _ = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
     ref = oracle_tokens(orc, cfg, x, ids, wts, np.arange(cfg.T), device="cuda:0")
     yb = synth.bf16_values(host_bits(y))
     yo = synth.bf16_values(synth.bf16_bits(ref["y"]))
     err, cos = rel_fro(yb, yo), cosine(yb, yo)
-    print(f"tiny bf16 output vs bf16(oracle): rel_fro {err:.3e} cos {cos:.7f}")
+    e32 = _check_bf16_vs_fp32(y, y32)
+    print(f"T{T} tiles {tile_rows}: bf16 output vs bf16(oracle) rel_fro {err:.3e} cos {cos:.7f}; "
+          f"vs the fp32-output run {e32:.3e}")
     assert err <= 5e-3 and cos >= 0.9999
+
+
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_bf16_rows_extreme_weights(nv, tile_rows):
+    """Routing weights from 2^-100 to 2^100 (and one token with all-zero
+    weights), so that rows of one tile differ by up to 2^200: every row keeps
+    its own f16 exponent, so every token of the bf16-output run matches the
+    fp32-output run to bf16 precision."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=257, name="tiny257")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    exps = np.array([-100, -60, -20, 0, 20, 60, 100])
+    wts = (wts * np.exp2(exps[np.arange(cfg.T) % len(exps)])[:, None]).astype(np.float32)
+    wts[5] = 0.0
+    yb, _ = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16, tile_rows=tile_rows)
+    y32, _ = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
+    yb = synth.bf16_values(host_bits(yb)).astype(np.float64)
+    y32 = host(y32).astype(np.float64)
+    assert np.all(yb[5] == 0.0) and np.all(y32[5] == 0.0)
+    num = np.linalg.norm(yb - y32, axis=1)
+    den = np.linalg.norm(y32, axis=1)
+    rel = num[den > 0] / den[den > 0]
+    print(f"tiles {tile_rows}: worst per-token rel error {rel.max():.3e}")
+    assert rel.max() <= 4e-3
 
 
 @pytest.mark.parametrize("tile_rows", TILES)
@@ -294,6 +339,11 @@ def test_moe_prefill_config_sampled(nv, orc):
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, y, dbg, device="cuda:0")
     print("prefill: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
     _gate(*res[:4])
+    del dbg
+    # the bench's configuration: bf16 output (f16 pair rows), every token
+    # against this fp32-output run
+    yb, _ = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16)
+    print("prefill bf16 output vs the fp32-output run: rel_fro %.3e" % _check_bf16_vs_fp32(yb, y))
 
 
 def test_moe_empty(nv):
