@@ -201,13 +201,17 @@ typedef struct {
  * a2_gs * w2_gs[e], the L1 output is quantized with a2_gs (supplied, or the
  * dynamic amax / 2688 of the bf16 L1 output of all valid pairs when a2_gs is
  * NULL), and the k terms of a token are summed in fixed order j = 0..k-1 in
- * fp32.
+ * fp32.  With out_dtype 0 (bf16) the per-pair L2 rows are held in f16 with
+ * one power-of-two scale per (pair, 64 columns) before that sum (relative
+ * error <= 2^-11 per term, a quarter of the bf16 rounding of y); with
+ * out_dtype 1 they stay fp32.
  * Requirements: T >= 0; H % 256 == 0, I % 128 == 0, E <= 512, k <= 32, and the
  * f16 GEMM operands T * H * 2, T * k * I * 2 and one expert's I * H nibble
  * bytes at most 4 GiB each (else NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.
- * Workspace: the query's bytes, which include the fp32 per-pair rows [P][H]
- * of the L2 output and, for the unfused flow without l1_c_bf16, the bf16 L1
- * output [P][I].
+ * Workspace: the query's bytes, which include the per-pair rows [P][H] of
+ * the L2 output (fp32, or f16 plus [P][H/64] exponent bytes for a bf16
+ * output) and, for the unfused flow without l1_c_bf16, the bf16 L1 output
+ * [P][I].
  */
 size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);
 int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, void *stream);
