@@ -173,12 +173,14 @@ typedef struct {
      `stream` before the global scale, then after the global scale, the
      activation quantization, the grouping, L1, L2 and the combine. */
   void *const *stage_events;
-  /* GEMM tile height: 0 chooses from the routing shape (32-row tiles that
-     stream the weights when there are at most 16 pairs per expert on
-     average and H and I are multiples of 256 or equal 128, else 256-row
-     tiles); 32 or 256 forces one (other values: NVFP4_ERR_INVALID_ARG; 32
-     with other H or I: NVFP4_ERR_UNSUPPORTED).  The results are the same
-     either way up to the fp32 summation order inside the GEMMs. */
+  /* GEMM tiling.  32: 32-row tiles that stream the weights.  256: 256-row
+     MFMA tiles.  288 (mixed): 256-row tiles, except that each expert's last
+     block of at most 32 rows goes on a 32-row tile.  0 chooses from the
+     routing shape: 32 when there are at most 16 pairs per expert on average,
+     else 288; 256 when H or I is not a multiple of 256 (or equal to 128),
+     which 32 and 288 need (NVFP4_ERR_UNSUPPORTED).  Other values:
+     NVFP4_ERR_INVALID_ARG.  The results are the same either way up to the
+     fp32 summation order inside the GEMMs. */
   int32_t tile_rows;
   /* nullable: receives the L1-output global scale used (1 float) */
   float *a2_gs_out;

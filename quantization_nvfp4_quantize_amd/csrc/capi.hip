@@ -241,8 +241,8 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
 namespace {
 
 struct MoeLayout {
-  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, err, route, sched, a2_gs, c, a2q,
-      a2sf, a2_f16, o, oexp, total;
+  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, small, nsmall, err, route, sched, a2_gs,
+      c, a2q, a2sf, a2_f16, o, oexp, total;
   int max_tiles;
 };
 
@@ -258,19 +258,29 @@ bool moe_interleaved(const nvfp4_moe_args* a) { return a->l1_unfused == 2; }
 // read back by the combine; an fp32 output keeps fp32 rows.
 bool moe_f16_rows(const nvfp4_moe_args* a) { return a->out_dtype == 0; }
 
-// Rows per GEMM tile: 32-row tiles (weights streamed through registers) when
-// the experts get few rows each, else 256-row tiles (MFMA-bound).
+// GEMM tiling: 32-row tiles (weights streamed through registers) when the
+// experts get few rows each; else 256-row tiles (MFMA-bound), each expert's
+// last block of at most 32 rows on a 32-row tile of its own when the 32-row
+// kernels take H and I (mixed, tile_rows 256 + 32: such a short block would
+// cost a 256-row tile most of a full tile's time).
+int kMixedTileRows() { return nvfp4::gemm_tile_rows() + nvfp4::skinny_tile_rows(); }
+
+bool moe_skinny_fits(const nvfp4_moe_args* a) {
+  return nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I);
+}
+
 int64_t moe_tile_rows(const nvfp4_moe_args* a) {
   if (a->tile_rows) return a->tile_rows;
   const int64_t P = a->T * a->topk;
-  const bool fits = nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I);
-  return fits && P <= 16 * a->E ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
+  if (!moe_skinny_fits(a)) return nvfp4::gemm_tile_rows();
+  return P <= 16 * a->E ? nvfp4::skinny_tile_rows() : kMixedTileRows();
 }
 
 MoeLayout moe_layout(const nvfp4_moe_args* a) {
   MoeLayout L;
   const int64_t T = a->T, H = a->H, I = a->I, E = a->E, P = a->T * a->topk;
-  const int64_t bm = moe_tile_rows(a);
+  const int64_t bm = moe_tile_rows(a) == nvfp4::skinny_tile_rows() ? nvfp4::skinny_tile_rows()
+                                                                    : nvfp4::gemm_tile_rows();
   L.max_tiles = (int)((P + bm - 1) / bm + E);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -287,6 +297,8 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.perm = take(sizeof(int) * (size_t)(P > 0 ? P : 1));
   L.tiles = take(sizeof(nvfp4::GemmTile) * (size_t)L.max_tiles);
   L.ntiles = take(sizeof(int));
+  L.small = take(sizeof(nvfp4::GemmTile) * (size_t)E);
+  L.nsmall = take(sizeof(int));
   L.err = take(sizeof(int));
   L.route = take(nvfp4::route_workspace_bytes(P, (int)E));
   L.sched = take(16 * sizeof(int));
@@ -322,18 +334,16 @@ int moe_validate(const nvfp4_moe_args* a) {
   if (a->out_dtype != 0 && a->out_dtype != 1)
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: out_dtype must be 0 (bf16) or 1 (fp32)");
   if (a->tile_rows != 0 && a->tile_rows != nvfp4::skinny_tile_rows() &&
-      a->tile_rows != nvfp4::gemm_tile_rows())
-    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: tile_rows must be 0, %d or %d",
-                nvfp4::skinny_tile_rows(), nvfp4::gemm_tile_rows());
+      a->tile_rows != nvfp4::gemm_tile_rows() && a->tile_rows != kMixedTileRows())
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: tile_rows must be 0, %d, %d or %d",
+                nvfp4::skinny_tile_rows(), nvfp4::gemm_tile_rows(), kMixedTileRows());
   if (a->l1_unfused < 0 || a->l1_unfused > 2)
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: l1_unfused must be 0, 1 or 2");
   if (a->l1_unfused == 2 && !a->a2_gs)
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: the interleaved flow needs a supplied a2_gs");
-  if (a->tile_rows == nvfp4::skinny_tile_rows() &&
-      !(nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I)))
+  if ((a->tile_rows == nvfp4::skinny_tile_rows() || a->tile_rows == kMixedTileRows()) && !moe_skinny_fits(a))
     return fail(NVFP4_ERR_UNSUPPORTED,
-                "moe_expert_ffn_nvfp4: tile_rows %d needs H and I multiples of 256 (or 128)",
-                nvfp4::skinny_tile_rows());
+                "moe_expert_ffn_nvfp4: tile_rows %d needs H and I multiples of 256 (or 128)", a->tile_rows);
   if (a->T > 0 && (!a->x || !a->topk_ids || !a->topk_w || !a->w1_q || !a->w1_sf || !a->w1_gs ||
                    !a->w2_q || !a->w2_sf || !a->w2_gs || !a->out))
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: null required pointer");
@@ -398,9 +408,14 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   nvfp4::GemmTile* tiles = reinterpret_cast<nvfp4::GemmTile*>(w + L.tiles);
   int* ntiles = reinterpret_cast<int*>(w + L.ntiles);
   int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
-  const bool skinny = moe_tile_rows(a) == nvfp4::skinny_tile_rows();
-  if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, (int)moe_tile_rows(a), offsets, perm,
-                                           tiles, ntiles, err, reinterpret_cast<int*>(w + L.route),
+  const int64_t mode = moe_tile_rows(a);
+  const bool skinny = mode == nvfp4::skinny_tile_rows(), mixed = mode == kMixedTileRows();
+  nvfp4::GemmTile* small = reinterpret_cast<nvfp4::GemmTile*>(w + L.small);
+  int* nsmall = reinterpret_cast<int*>(w + L.nsmall);
+  if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E,
+                                           skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows(),
+                                           mixed ? nvfp4::skinny_tile_rows() : 0, offsets, perm, tiles, ntiles,
+                                           small, nsmall, err, reinterpret_cast<int*>(w + L.route),
                                            reinterpret_cast<int*>(w + L.sched), s),
                        "route")))
     return st;
@@ -412,32 +427,33 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   uint8_t* a2q = a->l1_q ? a->l1_q : reinterpret_cast<uint8_t*>(w + L.a2q);
   uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
   uint16_t* a2_f16 = reinterpret_cast<uint16_t*>(w + L.a2_f16);
-  auto l1 = skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1;
+  // the L1 GEMM over the tile list (and the short tiles of the mixed tiling)
+  auto l1 = [&](const float* out_gs, uint16_t* c_bf16, uint8_t* cq, uint8_t* csf, uint16_t* cf16,
+                uint16_t* c_il) {
+    hipError_t e = (skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1)(
+        x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf, cf16, tiles, ntiles,
+        L.max_tiles, 0, perm, (int)k, s, c_il);
+    if (e == hipSuccess && mixed)
+      e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
+                                  cf16, small, nsmall, (int)E, 0, perm, (int)k, s, c_il);
+    return hip_status(e, "L1 GEMM");
+  };
   const float* a2_gs = a->a2_gs;
   if (moe_interleaved(a)) {
     uint16_t* c_il = reinterpret_cast<uint16_t*>(w + L.c);
-    if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, nullptr, a->l1_c_bf16, nullptr,
-                            nullptr, nullptr, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, c_il),
-                         "L1 GEMM")))
-      return st;
+    if ((st = l1(nullptr, a->l1_c_bf16, nullptr, nullptr, nullptr, c_il))) return st;
     if (a->a2_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a2_gs, a->a2_gs_out, s), "copy a2_gs")))
       return st;
     if ((st = hip_status(nvfp4::launch_quantize_interleaved(c_il, P, I, a2_gs, a2q, a2sf, a2_f16, s),
                          "deinterleave + quantize L1 output")))
       return st;
   } else if (!moe_unfused(a)) {
-    if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, a->a2_gs, a->l1_c_bf16, a2q,
-                            a2sf, a2_f16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, nullptr),
-                         "L1 GEMM")))
-      return st;
+    if ((st = l1(a->a2_gs, a->l1_c_bf16, a2q, a2sf, a2_f16, nullptr))) return st;
     if (a->a2_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a->a2_gs, a->a2_gs_out, s), "copy a2_gs")))
       return st;
   } else {
     uint16_t* c = a->l1_c_bf16 ? a->l1_c_bf16 : reinterpret_cast<uint16_t*>(w + L.c);
-    if ((st = hip_status(l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, nullptr, c, nullptr,
-                            nullptr, nullptr, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, nullptr),
-                         "L1 GEMM")))
-      return st;
+    if ((st = l1(nullptr, c, nullptr, nullptr, nullptr, nullptr))) return st;
     if (!a2_gs) {
       float* g2 = a->a2_gs_out ? a->a2_gs_out : reinterpret_cast<float*>(w + L.a2_gs);
       if ((st = hip_status(nvfp4::launch_global_scale_rows(c, P, I, a->topk_ids, (int)E,
@@ -458,11 +474,15 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   float* o = f16_rows ? nullptr : reinterpret_cast<float*>(w + L.o);
   uint16_t* o16 = f16_rows ? reinterpret_cast<uint16_t*>(w + L.o) : nullptr;
   int8_t* oexp = f16_rows ? reinterpret_cast<int8_t*>(w + L.oexp) : nullptr;
-  auto l2 = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
-  if ((st = hip_status(l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
-                          L.max_tiles, perm, s, 0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp),
-                       "L2 GEMM")))
-    return st;
+  {
+    hipError_t e = (skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2)(
+        a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles, L.max_tiles, perm, s, 0,
+        nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp);
+    if (e == hipSuccess && mixed)
+      e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, small, nsmall,
+                                  (int)E, perm, s, 0, nullptr, nullptr, o16, oexp);
+    if ((st = hip_status(e, "L2 GEMM"))) return st;
+  }
   mark(5);
   // a8: combine the k rows of every token
   if ((st = hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s,

@@ -86,9 +86,13 @@ hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             uint16_t* o_f16 = nullptr, int8_t* o_exp = nullptr);
 // Scratch (ints) of the many-workgroup grouping for P pairs and E experts.
 size_t route_workspace_bytes(int64_t P, int E);
-// Also zeroes sched[0 .. 16) (nullable): the GEMMs' work counters.
-hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
-                        GemmTile* tiles, int* ntiles, int* err_count, int* ws, int* sched, hipStream_t s);
+// Groups the pairs by expert into tiles of tile_rows rows; with small_rows
+// > 0 each expert's last block of at most small_rows rows is listed in
+// small / *nsmall (at most E entries) instead of tiles.  Also zeroes
+// sched[0 .. 16) (nullable): the GEMMs' work counters.
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int* offsets,
+                        int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
+                        int* ws, int* sched, hipStream_t s);
 // y[t] = sum over the k rows of token t of o (fp32), or of the f16 form
 // o_f16 * 2^o_exp when o_f16 is non-null (H % 64 == 0).
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,

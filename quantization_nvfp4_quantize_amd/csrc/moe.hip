@@ -8,7 +8,10 @@
 //                 increasing pair id inside each expert (stable, so the result
 //                 is deterministic),
 //   tiles[]       (expert, first sorted position, rows) for every block of up
-//                 to `tile_rows` rows of one expert, and their count.
+//                 to `tile_rows` rows of one expert, and their count; with
+//                 small_rows > 0, an expert's last block of at most
+//                 small_rows rows goes to a second list (small[], *nsmall)
+//                 for the GEMMs with short tiles instead.
 // Each wave owns a contiguous range of pairs.  Pass 1 counts its pairs per
 // expert in LDS; a prefix over (expert, wave) gives every wave its own
 // starting position per expert; pass 2 re-reads the range 64 pairs at a time
@@ -33,12 +36,85 @@ constexpr int kRouteThreads = 1024;
 constexpr int kSchedCounters = 16;  // the GEMMs' work counters, zeroed with the grouping
 constexpr int kRouteWaves = kRouteThreads / 64;
 
+// Exclusive prefix of v over the threads of the workgroup (one value per
+// thread, kRouteThreads threads, scratch of as many ints); *total receives
+// the sum.  Every thread must call it.
+__device__ __forceinline__ int block_exclusive_scan(int* scan, int v, int* total) {
+  const int tid = threadIdx.x;
+  scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int u = (tid >= off) ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += u;
+    __syncthreads();
+  }
+  const int incl = scan[tid];
+  *total = scan[kRouteThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Tiles of an expert with np rows: blocks of tile_rows rows; with
+// small_rows > 0, a last block of at most small_rows rows goes on a small
+// tile of its own instead (big: 0.., small: 0 or 1).
+struct TileCounts {
+  int big, small;
+};
+__device__ __forceinline__ TileCounts tile_counts(int np, int tile_rows, int small_rows) {
+  if (small_rows > 0) {
+    const int r = np % tile_rows;
+    return {np / tile_rows + (r > small_rows ? 1 : 0), (r > 0 && r <= small_rows) ? 1 : 0};
+  }
+  return {(np + tile_rows - 1) / tile_rows, 0};
+}
+
+// Offsets, tile list and small-tile list of all experts, 1024 experts per
+// chunk: count_of(e) gives expert e's pairs, on_start(e, start) hears its
+// first sorted position.  Every thread must call it.
+template <class CountOf, class OnStart>
+__device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows, int* scan,
+                                            int* offsets, GemmTile* tiles, int* ntiles,
+                                            GemmTile* small, int* nsmall, CountOf count_of,
+                                            OnStart on_start) {
+  const int tid = threadIdx.x;
+  int base_p = 0, base_t = 0, base_s = 0;
+  for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
+    const int e = e0 + tid;
+    const int np = (e < E) ? count_of(e) : 0;
+    const TileCounts c = tile_counts(np, tile_rows, small_rows);
+    int chunk_p, chunk_t, chunk_s;
+    const int xp = block_exclusive_scan(scan, np, &chunk_p);
+    const int xt = block_exclusive_scan(scan, c.big, &chunk_t);
+    const int xs = block_exclusive_scan(scan, c.small, &chunk_s);
+    if (e < E) {
+      const int start = base_p + xp;
+      offsets[e] = start;
+      on_start(e, start);
+      for (int k = 0; k < c.big; ++k)
+        tiles[base_t + xt + k] = GemmTile{e, start + k * tile_rows, min(tile_rows, np - k * tile_rows), 0};
+      if (c.small) small[base_s + xs] = GemmTile{e, start + c.big * tile_rows, np - c.big * tile_rows, 0};
+    }
+    base_p += chunk_p;
+    base_t += chunk_t;
+    base_s += chunk_s;
+  }
+  if (tid == 0) {
+    offsets[E] = base_p;
+    *ntiles = base_t;
+    if (nsmall) *nsmall = base_s;
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int64_t P, int E, int tile_rows,
+                                                              int small_rows,
                                                               int* __restrict__ offsets,
                                                               int* __restrict__ perm,
                                                               GemmTile* __restrict__ tiles,
                                                               int* __restrict__ ntiles,
+                                                              GemmTile* __restrict__ small,
+                                                              int* __restrict__ nsmall,
                                                               int* __restrict__ err_count,
                                                               int* __restrict__ sched) {
   extern __shared__ int sm[];
@@ -75,58 +151,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
   __syncthreads();
 
-  // exclusive scans over experts of (pairs, tiles), 1024 experts per chunk
-  int base_pairs = 0, base_tiles = 0;
-  for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
-    const int e = e0 + tid;
-    const int np = (e < E) ? total[e] : 0;
-    const int nt = (np + tile_rows - 1) / tile_rows;
-    // inclusive scan of np and nt packed in one int64-free pass: two scans
-    scan[tid] = np;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-      int v = (tid >= off) ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int incl_p = scan[tid];
-    const int chunk_p = scan[kRouteThreads - 1];
-    __syncthreads();
-    scan[tid] = nt;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-      int v = (tid >= off) ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int incl_t = scan[tid];
-    const int chunk_t = scan[kRouteThreads - 1];
-    __syncthreads();
-    if (e < E) {
-      const int start = base_pairs + incl_p - np;
-      offsets[e] = start;
-      for (int w = 0; w < kRouteWaves; ++w) cnt[w * E + e] += start;
-      int tb = base_tiles + incl_t - nt;
-      for (int k = 0; k < nt; ++k) {
-        GemmTile t;
-        t.expert = e;
-        t.row0 = start + k * tile_rows;
-        t.nrows = min(tile_rows, np - k * tile_rows);
-        t.pad = 0;
-        tiles[tb + k] = t;
-      }
-    }
-    base_pairs += chunk_p;
-    base_tiles += chunk_t;
-  }
+  group_tiles(E, tile_rows, small_rows, scan, offsets, tiles, ntiles, small, nsmall,
+              [&](int e) { return total[e]; },
+              [&](int e, int start) {
+                for (int w = 0; w < kRouteWaves; ++w) cnt[w * E + e] += start;
+              });
   __syncthreads();
-  if (tid == 0) {
-    offsets[E] = base_pairs;
-    *ntiles = base_tiles;
-    if (err_count) *err_count = s_err;
-  }
+  if (tid == 0 && err_count) *err_count = s_err;
   if (sched && tid < kSchedCounters) sched[tid] = 0;
 
   // pass 2: stable placement, 64 pairs per step, ranks by ballot matching
@@ -183,69 +214,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int G, int E, int tile_rows,
+                                                                   int small_rows,
                                                                    int* __restrict__ gcount,
                                                                    const int* __restrict__ gerr,
                                                                    int* __restrict__ offsets,
                                                                    GemmTile* __restrict__ tiles,
                                                                    int* __restrict__ ntiles,
+                                                                   GemmTile* __restrict__ small,
+                                                                   int* __restrict__ nsmall,
                                                                    int* __restrict__ err_count,
                                                                    int* __restrict__ sched) {
   __shared__ int scan[kRouteThreads];
   const int tid = threadIdx.x;
-  int base_pairs = 0, base_tiles = 0;
-  for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
-    const int e = e0 + tid;
-    // this expert's pairs per workgroup -> exclusive starts within the expert
-    int np = 0;
-    if (e < E)
-      for (int g = 0; g < G; ++g) {
-        const int c = gcount[(int64_t)g * E + e];
-        gcount[(int64_t)g * E + e] = np;
-        np += c;
-      }
-    const int nt = (np + tile_rows - 1) / tile_rows;
-    scan[tid] = np;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-      int v = (tid >= off) ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int incl_p = scan[tid];
-    const int chunk_p = scan[kRouteThreads - 1];
-    __syncthreads();
-    scan[tid] = nt;
-    __syncthreads();
-    for (int off = 1; off < kRouteThreads; off <<= 1) {
-      int v = (tid >= off) ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int incl_t = scan[tid];
-    const int chunk_t = scan[kRouteThreads - 1];
-    __syncthreads();
-    if (e < E) {
-      const int start = base_pairs + incl_p - np;
-      offsets[e] = start;
-      for (int g = 0; g < G; ++g) gcount[(int64_t)g * E + e] += start;
-      const int tb = base_tiles + incl_t - nt;
-      for (int k = 0; k < nt; ++k) {
-        GemmTile t;
-        t.expert = e;
-        t.row0 = start + k * tile_rows;
-        t.nrows = min(tile_rows, np - k * tile_rows);
-        t.pad = 0;
-        tiles[tb + k] = t;
-      }
-    }
-    base_pairs += chunk_p;
-    base_tiles += chunk_t;
-  }
+  // each expert's pairs per workgroup -> exclusive starts within the expert,
+  // then (with the expert's start) the workgroup's first position per expert
+  group_tiles(E, tile_rows, small_rows, scan, offsets, tiles, ntiles, small, nsmall,
+              [&](int e) {
+                int np = 0;
+                for (int g = 0; g < G; ++g) {
+                  const int c = gcount[(int64_t)g * E + e];
+                  gcount[(int64_t)g * E + e] = np;
+                  np += c;
+                }
+                return np;
+              },
+              [&](int e, int start) {
+                for (int g = 0; g < G; ++g) gcount[(int64_t)g * E + e] += start;
+              });
   if (tid == 0) {
-    offsets[E] = base_pairs;
-    *ntiles = base_tiles;
     int err = 0;
     for (int g = 0; g < G; ++g) err += gerr[g];
     if (err_count) *err_count = err;
@@ -388,19 +384,20 @@ size_t route_workspace_bytes(int64_t P, int E) {
   return sizeof(int) * ((size_t)G * E + G);
 }
 
-hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int* offsets, int* perm,
-                        GemmTile* tiles, int* ntiles, int* err_count, int* ws, int* sched, hipStream_t s) {
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int* offsets,
+                        int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
+                        int* ws, int* sched, hipStream_t s) {
   const int G = route_groups(P);
   if (G == 1 || !ws) {
-    route_kernel<<<1, kRouteThreads, route_lds_bytes(E), s>>>(ids, P, E, tile_rows, offsets, perm, tiles,
-                                                              ntiles, err_count, sched);
+    route_kernel<<<1, kRouteThreads, route_lds_bytes(E), s>>>(ids, P, E, tile_rows, small_rows, offsets, perm,
+                                                              tiles, ntiles, small, nsmall, err_count, sched);
     return hipGetLastError();
   }
   int* gcount = ws;
   int* gerr = ws + (size_t)G * E;
   route_count_kernel<<<G, kRouteThreads, sizeof(int) * E, s>>>(ids, P, E, gcount, gerr);
-  route_scan_kernel<<<1, kRouteThreads, 0, s>>>(G, E, tile_rows, gcount, gerr, offsets, tiles, ntiles,
-                                                 err_count, sched);
+  route_scan_kernel<<<1, kRouteThreads, 0, s>>>(G, E, tile_rows, small_rows, gcount, gerr, offsets, tiles, ntiles,
+                                                 small, nsmall, err_count, sched);
   route_place_kernel<<<G, kRouteThreads, sizeof(int) * kRouteWaves * E, s>>>(ids, P, E, gcount, perm);
   return hipGetLastError();
 }

@@ -114,12 +114,13 @@ def test_moe_rejects(lib):
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(out_dtype=3)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w2_gs=None)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(x=0x10008)), FAKE, 1 << 30, None) == -1
-    # GEMM tile height: 0 (automatic), 32 or 256 only
+    # GEMM tiling: 0 (automatic), 32, 256 or 288 (mixed) only
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(tile_rows=64)), FAKE, 1 << 30, None) == -1
     assert b"tile_rows" in lib.nvfp4_last_error()
-    # 32-row tiles need H and I multiples of 256 (or 128)
-    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(I=384, tile_rows=32)), FAKE, 1 << 30, None) == -2
-    assert b"multiples of 256" in lib.nvfp4_last_error()
+    # 32-row tiles (alone or in the mixed tiling) need H and I multiples of 256 (or 128)
+    for tr in (32, 288):
+        assert lib.moe_expert_ffn_nvfp4(by(_moe_args(I=384, tile_rows=tr)), FAKE, 1 << 30, None) == -2
+        assert b"multiples of 256" in lib.nvfp4_last_error()
     # the workspace follows the tile height (the tile list is sized per tile)
     small = lib.moe_expert_ffn_nvfp4_workspace_size(by(_moe_args(T=4096, tile_rows=32)))
     large = lib.moe_expert_ffn_nvfp4_workspace_size(by(_moe_args(T=4096, tile_rows=256)))

@@ -26,7 +26,9 @@ def nv():
     return nv
 
 
-TILES = [32, 256]  # both GEMM tile modes (32: weights streamed, 256: MFMA-bound)
+# GEMM tilings: 32 (weights streamed), 256 (MFMA-bound), 288 (256-row tiles,
+# each expert's last <= 32 rows on a 32-row tile)
+TILES = [32, 256, 288]
 
 
 def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32, tile_rows=0, dynamic=False,
@@ -295,7 +297,7 @@ def test_moe_deterministic(nv, tile_rows):
 
 
 def test_moe_tile_modes_agree(nv):
-    """The 32-row and the 256-row GEMM tiles group K differently inside their
+    """The 32-row, the 256-row and the mixed GEMM tiles group K differently inside their
     MFMAs, but on this workload the fp32 sums of the exact NVFP4 products do
     not round (the products share a fine grid and the sums stay within 24
     significant bits), so their results are bit-identical (decode shape: every
@@ -305,11 +307,35 @@ def test_moe_tile_modes_agree(nv):
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
     ya, da = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=32)
+    for tr in (256, 288):
+        yb, db = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tr)
+        assert np.array_equal(host_bits(da["l1_c"]), host_bits(db["l1_c"])), tr
+        for key in ("l1_q", "l1_sf"):
+            assert np.array_equal(host(da[key]), host(db[key])), (tr, key)
+        assert np.array_equal(host(ya).view(np.uint32), host(yb).view(np.uint32)), tr
+
+
+def test_moe_mixed_tiles_remainders(nv, orc):
+    """The mixed tiling on expert row counts chosen around its boundaries:
+    256 + 10 (one 256-row tile and a 10-row short tile), 512 + 32 (two and a
+    32-row short tile), 256 + 33 (a 33-row block stays on a 256-row tile),
+    255 and 32 (one tile each), 0 (no tile): every token against the oracle,
+    and bit-identical to the 256-row tiling."""
+    import dataclasses
+    counts = [266, 544, 289, 255, 32, 0]
+    cfg = dataclasses.replace(synth.TINY, T=sum(counts), E=len(counts), topk=1, name="mixed")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    rng = np.random.default_rng(7)
+    ids = rng.permutation(np.repeat(np.arange(cfg.E), counts)).astype(np.int32)[:, None]
+    wts = rng.uniform(0.5, 1.5, size=(cfg.T, 1)).astype(np.float32)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=288)
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    print("mixed: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
     yb, db = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=256)
-    assert np.array_equal(host_bits(da["l1_c"]), host_bits(db["l1_c"]))
-    for key in ("l1_q", "l1_sf"):
-        assert np.array_equal(host(da[key]), host(db[key])), key
-    assert np.array_equal(host(ya).view(np.uint32), host(yb).view(np.uint32))
+    assert np.array_equal(host_bits(dbg["l1_c"]), host_bits(db["l1_c"]))
+    assert np.array_equal(host(y).view(np.uint32), host(yb).view(np.uint32))
 
 
 @pytest.mark.parametrize("tile_rows", TILES)
