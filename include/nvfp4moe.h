@@ -169,9 +169,13 @@ typedef struct {
   uint8_t *l1_q;            /* [P][I/2] */
   uint8_t *l1_sf;           /* [P][I/16] */
   int32_t *err_count;       /* 1 int: number of skipped pairs (written, not added) */
-  /* nullable, for profiling: 7 hipEvent_t created by the caller, recorded on
+  /* nullable, for profiling: 9 hipEvent_t created by the caller, recorded on
      `stream` before the global scale, then after the global scale, the
-     activation quantization, the grouping, L1, L2 and the combine. */
+     activation quantization, the grouping, the L1 GEMM's main tile list
+     (256-row tiles, or the 32-row tiles of tiling 32), the whole L1 stage
+     (with the short tiles of the mixed tiling and any separate quantization
+     pass), the L2 GEMM's main tile list, the whole L2 stage and the
+     combine. */
   void *const *stage_events;
   /* GEMM tiling.  32: 32-row tiles that stream the weights.  256: 256-row
      MFMA tiles.  288 (mixed): 256-row tiles, except that each expert's last
@@ -204,14 +208,14 @@ typedef struct {
  * dynamic amax / 2688 of the bf16 L1 output of all valid pairs when a2_gs is
  * NULL), and the k terms of a token are summed in fixed order j = 0..k-1 in
  * fp32.  With out_dtype 0 (bf16) the per-pair L2 rows are held in f16 with
- * one power-of-two scale per (pair, 64 columns) before that sum (relative
+ * one power-of-two scale per (pair, 32 columns) before that sum (relative
  * error <= 2^-11 per term, a quarter of the bf16 rounding of y); with
  * out_dtype 1 they stay fp32.
  * Requirements: T >= 0; H % 256 == 0, I % 128 == 0, E <= 512, k <= 32, and the
  * f16 GEMM operands T * H * 2, T * k * I * 2 and one expert's I * H nibble
  * bytes at most 4 GiB each (else NVFP4_ERR_UNSUPPORTED); E >= 1, k >= 1.
  * Workspace: the query's bytes, which include the per-pair rows [P][H] of
- * the L2 output (fp32, or f16 plus [P][H/64] exponent bytes for a bf16
+ * the L2 output (fp32, or f16 plus [P][H/32] exponent bytes for a bf16
  * output) and, for the unfused flow without l1_c_bf16, the bf16 L1 output
  * [P][I].
  */

@@ -253,7 +253,7 @@ bool moe_unfused(const nvfp4_moe_args* a) { return a->a2_gs == nullptr || a->l1_
 bool moe_interleaved(const nvfp4_moe_args* a) { return a->l1_unfused == 2; }
 
 // With a bf16 output the L2 GEMM writes its per-pair rows in f16 with one
-// power-of-two exponent per (pair, 64 columns) (relative error <= 2^-11 per
+// power-of-two exponent per (pair, 32 columns) (relative error <= 2^-11 per
 // value, 4x below the bf16 rounding of y), which halves the bytes written and
 // read back by the combine; an fp32 output keeps fp32 rows.
 bool moe_f16_rows(const nvfp4_moe_args* a) { return a->out_dtype == 0; }
@@ -309,7 +309,7 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.a2sf = take((size_t)(P * I / 16));
   L.a2_f16 = take(sizeof(uint16_t) * (size_t)(P * I));
   L.o = take((moe_f16_rows(a) ? sizeof(uint16_t) : sizeof(float)) * (size_t)(P * H));
-  L.oexp = take(moe_f16_rows(a) ? (size_t)(P * H / 64) : 0);
+  L.oexp = take(moe_f16_rows(a) ? (size_t)(P * H / 32) : 0);
   L.total = off;
   return L;
 }
@@ -392,7 +392,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   }
   mark(1);
   if (T == 0) {
-    for (int i = 2; i < 7; ++i) mark(i);
+    for (int i = 2; i < 9; ++i) mark(i);
     return NVFP4_OK;
   }
   // a2: quantize the activations
@@ -433,6 +433,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     hipError_t e = (skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1)(
         x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf, cf16, tiles, ntiles,
         L.max_tiles, 0, perm, (int)k, s, c_il);
+    mark(4);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
                                   cf16, small, nsmall, (int)E, 0, perm, (int)k, s, c_il);
@@ -468,7 +469,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     if ((st = hip_status(nvfp4::launch_quantize(c, P * I, a2_gs, a2q, a2sf, a2_f16, s), "quantize L1 output")))
       return st;
   }
-  mark(4);
+  mark(5);
   // a7: L2 GEMM, weighted by the routing weights
   const bool f16_rows = moe_f16_rows(a);
   float* o = f16_rows ? nullptr : reinterpret_cast<float*>(w + L.o);
@@ -478,18 +479,19 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     hipError_t e = (skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2)(
         a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles, L.max_tiles, perm, s, 0,
         nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp);
+    mark(6);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, small, nsmall,
                                   (int)E, perm, s, 0, nullptr, nullptr, o16, oexp);
     if ((st = hip_status(e, "L2 GEMM"))) return st;
   }
-  mark(5);
+  mark(7);
   // a8: combine the k rows of every token
   if ((st = hip_status(nvfp4::launch_combine(o, a->topk_ids, (int)E, T, (int)k, H, a->out_dtype == 0, a->out, s,
                                              o16, oexp),
                        "combine")))
     return st;
-  mark(6);
+  mark(8);
   return NVFP4_OK;
 }
 

@@ -553,28 +553,15 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     __syncthreads();
     const int after = counter ? s_claim[0] : next + (int)(gridDim.x >> 3);
     const int wm = wave_m(tid_i >> 6), wn = wave_n(tid_i >> 6);
-    if (p.o_f16) {
-      const int64_t col0 = (int64_t)nt * kTileN + wn * 64;
+    // A stage 3 is free here (the next item's prologue fills stages 0..2):
+    // 4 KiB of it per wave for the epilogue's transposition
+    float* const scratch = reinterpret_cast<float*>(lds_a + 3 * kLdsOperand) + (tid_i >> 6) * 1024;
+    const int64_t col0 = (int64_t)nt * kTileN + wn * 64;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (wm * 128 + mt * 32 >= t.nrows) break;  // wave-uniform
-        store_f16_rows(p, acc[mt][0], acc[mt][1], wm * 128 + mt * 32, t.nrows, col0, lane_i,
-                       [&](int r) { return out_row[r]; }, [&](int r) { return out_scale[r]; });
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int orw = wm * 128 + mt * 32 + acc_row(i, lane_i);
-          if (orw < t.nrows) {
-            const int64_t idx = (int64_t)out_row[orw] * p.N + (int64_t)nt * kTileN + wn * 64 + (lane_i & 31);
-            const float sc = out_scale[orw];
-            l2_store(p, idx, acc[mt][0][i] * sc);
-            l2_store(p, idx + 32, acc[mt][1][i] * sc);
-          }
-        }
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      if (wm * 128 + mt * 32 >= t.nrows) break;  // wave-uniform
+      l2_store_block(p, acc[mt][0], acc[mt][1], scratch, wm * 128 + mt * 32, t.nrows, col0, lane_i,
+                     [&](int r) { return out_row[r]; }, [&](int r) { return out_scale[r]; });
     }
     if (!more) break;
     item = next;

@@ -7,8 +7,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -242,82 +240,99 @@ struct L2Params {
   int n_ntiles;
   int* sched;           // nullable: 8 zeroed work counters (one per XCD) for dynamic item claiming
   uint16_t* o_f16;      // nullable [rows][N] f16 output (used with o_exp instead of o):
-  int8_t* o_exp;        // value = o_f16 * 2^o_exp, one exponent per (row, 64-column block) [rows][N/64]
+  int8_t* o_exp;        // value = o_f16 * 2^o_exp, one exponent per (row, 32-column block) [rows][N/32]
 };
 
-// Exponent for storing the values of one (row, 64-column block) in f16:
+// Exponent for storing the values of one (row, 32-column block) in f16:
 // with m the block's largest magnitude, m * 2^-s lies in [2^14, 2^15), so no
 // value overflows and values down to 2^-28 of the block maximum stay normal
-// f16 numbers (full 11-bit precision).  s is clamped to [-128, 114] (int8): zero,
-// subnormal, infinite or NaN maxima only need a value that keeps the rest
-// finite.
+// f16 numbers (full 11-bit precision).  s is clamped to [-128, 114] (int8):
+// zero, subnormal, infinite or NaN maxima only need a value that keeps the
+// rest finite.
 __device__ __forceinline__ int f16_block_exp(float m) {
   const int ex = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
   return max(ex - 14, -128);
 }
 
-// Largest value over the 32 lanes of each half of the wave, for N values at
-// once (independent chains, so their latencies overlap): DPP inside each
-// 16-lane row, then a swap of the two rows of each half.
-template <int N>
-__device__ __forceinline__ void half_wave_max(float (&m)[N]) {
-  auto step = [&](auto ctrl) {
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      m[i] = fmaxf(m[i], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m[i]), decltype(ctrl)::value,
-                                                                  0xF, 0xF, false)));
-  };
-  step(std::integral_constant<int, 0xB1>{});   // lane ^ 1
-  step(std::integral_constant<int, 0x4E>{});   // lane ^ 2
-  step(std::integral_constant<int, 0x124>{});  // row_ror 4
-  step(std::integral_constant<int, 0x128>{});  // row_ror 8
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m[i]), __float_as_uint(m[i]), false, false);
-    m[i] = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  }
-}
-
-// One wave's 32-row x 64-column block of L2 outputs in the f16 form: rows
-// r0 + acc_row(i, lane) (those below nrows are valid) of the MFMA tiles a0
-// (columns col0 + lane % 32) and a1 (columns + 32); row_of(r) gives the
-// output row and scale_of(r) the factor of tile row r.  Every lane of the
-// wave must take part (cross-lane maxima); the exponent of the row of value i
-// is stored by lane i of each half-wave.
+// Epilogue writer of the L2 / linear GEMMs for one wave's 32-row x 64-column
+// output block: the MFMA tiles a0 (columns col0 + lane % 32) and a1 (columns
+// col0 + 32 + lane % 32) hold rows r0 + acc_row(i, lane), of which those
+// below nrows are valid; row_of(r) gives the output row of tile row r and
+// scale_of(r) its factor.  Each 32 x 32 half goes through the wave's 4 KiB
+// LDS scratch (row r stored at r ^ ((r >> 2) & 1), so that the two row
+// groups a write instruction covers land in different bank halves); then
+// lane l holds the 16 consecutive values 16 (l & 1) .. of row l / 2 and
+// stores them with 16 B writes: fp32 (o), bf16 (o_bf16), or f16 with one
+// exponent per (row, 32 columns) (o_f16, o_exp; the row's maximum is the
+// maximum over the lane pair).  Every lane of the wave must take part.
 template <class RowOf, class ScaleOf>
-__device__ __forceinline__ void store_f16_rows(const L2Params& p, const f32x16& a0, const f32x16& a1,
-                                               int r0, int nrows, int64_t col0, int lane, RowOf row_of,
-                                               ScaleOf scale_of) {
-  float sc[16], m[16];
+__device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& a0, const f32x16& a1,
+                                               float* scratch, int r0, int nrows, int64_t col0, int lane,
+                                               RowOf row_of, ScaleOf scale_of) {
+  float sc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = r0 + acc_row(i, lane);
     sc[i] = r < nrows ? scale_of(r) : 0.0f;
-    m[i] = fmaxf(fabsf(a0[i] * sc[i]), fabsf(a1[i] * sc[i]));
   }
-  half_wave_max(m);
-  int my_exp = 0;
+  const int rr = lane >> 1, h = lane & 1;
+  const bool valid = r0 + rr < nrows;
+  const int64_t orow = valid ? (int64_t)row_of(r0 + rr) : 0;
+  const float* src = scratch + 32 * (rr ^ ((rr >> 2) & 1)) + 16 * h;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + acc_row(i, lane);
-    const int e = f16_block_exp(m[i]);
-    if ((lane & 31) == i) my_exp = e;
-    if (r < nrows) {
-      const int64_t idx = (int64_t)row_of(r) * p.N + col0 + (lane & 31);
-      p.o_f16[idx] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(a0[i] * sc[i], -e));
-      p.o_f16[idx + 32] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(a1[i] * sc[i], -e));
+  for (int half = 0; half < 2; ++half) {
+    const f32x16& a = half ? a1 : a0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = acc_row(i, lane);
+      scratch[32 * (r ^ ((r >> 2) & 1)) + (lane & 31)] = a[i] * sc[i];
+    }
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 w = *reinterpret_cast<const float4*>(src + 4 * q);
+      v[4 * q] = w.x;
+      v[4 * q + 1] = w.y;
+      v[4 * q + 2] = w.z;
+      v[4 * q + 3] = w.w;
+    }
+    const int64_t col = col0 + 32 * half + 16 * h;
+    if (p.o_f16) {
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(v[q]));
+      m = fmaxf(m, pair_swap(m));
+      const int e = f16_block_exp(m);
+      if (valid) {
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const f16x2 hv{(_Float16)ldexpf(v[2 * q], -e), (_Float16)ldexpf(v[2 * q + 1], -e)};
+          w[q] = __builtin_bit_cast(uint32_t, hv);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(p.o_f16 + orow * p.N + col);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        if (h == 0) p.o_exp[orow * (p.N / 32) + col / 32] = (int8_t)e;
+      }
+    } else if (p.o_bf16) {
+      if (valid) {
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q + 1]) << 16);
+        uint4* dst = reinterpret_cast<uint4*>(p.o_bf16 + orow * p.N + col);
+        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+    } else if (valid) {
+      float4* dst = reinterpret_cast<float4*>(p.o + orow * p.N + col);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
   }
-  const int r = r0 + acc_row(lane & 15, lane);
-  if ((lane & 31) < 16 && r < nrows) p.o_exp[(int64_t)row_of(r) * (p.N / 64) + col0 / 64] = (int8_t)my_exp;
 }
 
-// One output value of the L2 / linear epilogue.
-__device__ __forceinline__ void l2_store(const L2Params& p, int64_t idx, float v) {
-  if (p.o_bf16)
-    p.o_bf16[idx] = __builtin_bit_cast(uint16_t, (__bf16)v);
-  else
-    p.o[idx] = v;
-}
 
 }  // namespace nvfp4

@@ -373,27 +373,16 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), wrow);
   f32x16 acc[2];
   sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
-  int* out_row = reinterpret_cast<int*>(lds_a);
+  // the scales' LDS holds the output rows, the A buffers each wave's
+  // 4 KiB transposition scratch
+  int* out_row = reinterpret_cast<int*>(lds_sf);
   if (tid < kSkTileM) out_row[tid] = pair_of(tid);
   __syncthreads();
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  if (p.o_f16) {
-    store_f16_rows(p, acc[0], acc[1], 0, t.nrows, (int64_t)nt * kTileN + wave * 64, lane,
-                   [&](int r) { return out_row[r]; },
-                   [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int orw = acc_row(i, lane);
-    if (orw < t.nrows) {
-      const int64_t pr = out_row[orw];
-      const float s = p.row_w ? alpha * p.row_w[pr] : alpha;
-      const int64_t idx = pr * p.N + (int64_t)nt * kTileN + wave * 64 + (lane & 31);
-      l2_store(p, idx, acc[0][i] * s);
-      l2_store(p, idx + 32, acc[1][i] * s);
-    }
-  }
+  float* const scratch = reinterpret_cast<float*>(lds_a) + wave * 1024;
+  l2_store_block(p, acc[0], acc[1], scratch, 0, t.nrows, (int64_t)nt * kTileN + wave * 64, lane,
+                 [&](int r) { return out_row[r]; },
+                 [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
 }
 
 // ------------------------------------------------------------------ launchers

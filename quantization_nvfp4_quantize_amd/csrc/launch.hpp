@@ -61,8 +61,8 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
 // L2: o[pair] = alpha * w[pair] * (A @ W_e^T) for the routed rows (fp32), or
 // without routing (tiles, perm, row_w null) over M rows of expert 0, into o
 // (fp32), o_bf16 (bf16) when that is non-null, or o_f16 with o_exp (f16
-// values times a power of two per row and 64-column block, N % 64 == 0) when
-// those are non-null.  sched (nullable): 8 work counters, zero at launch, that
+// values times a power of two per row and 32-column block) when those are
+// non-null.  sched (nullable): 8 work counters, zero at launch, that
 // let the workgroups claim items dynamically.
 hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                      const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w, float* o,
@@ -94,7 +94,7 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int
                         int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
                         int* ws, int* sched, hipStream_t s);
 // y[t] = sum over the k rows of token t of o (fp32), or of the f16 form
-// o_f16 * 2^o_exp when o_f16 is non-null (H % 64 == 0).
+// o_f16 * 2^o_exp when o_f16 is non-null (one exponent per 32 columns).
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,
                           bool bf16_out, void* out, hipStream_t s, const uint16_t* o_f16 = nullptr,
                           const int8_t* o_exp = nullptr);

@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-// The same sum over the f16 form of o: o16[r][c] * 2^oexp[r][c / 64] (exact
+// The same sum over the f16 form of o: o16[r][c] * 2^oexp[r][c / 32] (exact
 // in fp32), 8 columns per thread.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __restrict__ o16,
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ ids, int E,
                                                           int64_t T, int k, int64_t H,
                                                           void* __restrict__ out) {
-  const int64_t n8 = H / 8, nb = H / 64;
+  const int64_t n8 = H / 8, nb = H / 32;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < T * n8;
        i += (int64_t)gridDim.x * 256) {
     const int64_t t = i / n8, c = (i % n8) * 8;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __rest
       const int e = ids[r];
       if (e < 0 || e >= E) continue;
       const uint4 v = *reinterpret_cast<const uint4*>(o16 + r * H + c);
-      const int s = oexp[r * nb + c / 64];
+      const int s = oexp[r * nb + c / 32];
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

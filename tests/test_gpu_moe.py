@@ -8,7 +8,7 @@ the fused NVFP4 bytes of the L1 output equal the GPU's standalone quantizer
 on the GPU's own bf16 output.  bf16-output mode is compared with the oracle's
 y rounded to bf16 (bounded loosely: bf16 rounding alone costs ~1.7e-3) and
 with the fp32-output run of the same layer (its per-pair L2 rows go through
-f16 with a power-of-two per row and 64 columns)."""
+f16 with a power-of-two per row and 32 columns)."""
 import numpy as np
 import pytest
 import torch
