@@ -261,23 +261,22 @@ __device__ __forceinline__ int f16_block_exp(float m) {
 // scale_of(r) its factor.  Each 32 x 32 half goes through the wave's 4 KiB
 // LDS scratch (row r stored at r ^ ((r >> 2) & 1), so that the two row
 // groups a write instruction covers land in different bank halves); then
-// lane l holds the 16 consecutive values 16 (l & 1) .. of row l / 2 and
-// stores them with 16 B writes: fp32 (o), bf16 (o_bf16), or f16 with one
-// exponent per (row, 32 columns) (o_f16, o_exp; the row's maximum is the
-// maximum over the lane pair).  Every lane of the wave must take part.
+// lane l holds the 16 consecutive values 16 (l & 1) .. of row l / 2, scales
+// them and stores them with 16 B writes: fp32 (o), bf16 (o_bf16), or f16
+// with one exponent per (row, 32 columns) (o_f16, o_exp).  For the f16 form
+// the row factor sc is applied as sc * 2^-e: rounding is monotonic, so the
+// largest |a * sc| of the block is max |a| * |sc|, and a * (sc * 2^-e) equals
+// (a * sc) * 2^-e.  (The accumulators are sums of exact products of NVFP4
+// values, so a nonzero max |a| is at least 2^-20 and sc * 2^-e stays
+// finite.)  Every lane of the wave must take part.
 template <class RowOf, class ScaleOf>
 __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& a0, const f32x16& a1,
                                                float* scratch, int r0, int nrows, int64_t col0, int lane,
                                                RowOf row_of, ScaleOf scale_of) {
-  float sc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = r0 + acc_row(i, lane);
-    sc[i] = r < nrows ? scale_of(r) : 0.0f;
-  }
   const int rr = lane >> 1, h = lane & 1;
   const bool valid = r0 + rr < nrows;
   const int64_t orow = valid ? (int64_t)row_of(r0 + rr) : 0;
+  const float sc = valid ? scale_of(r0 + rr) : 0.0f;
   const float* src = scratch + 32 * (rr ^ ((rr >> 2) & 1)) + 16 * h;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -285,7 +284,7 @@ __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& 
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = acc_row(i, lane);
-      scratch[32 * (r ^ ((r >> 2) & 1)) + (lane & 31)] = a[i] * sc[i];
+      scratch[32 * (r ^ ((r >> 2) & 1)) + (lane & 31)] = a[i];
     }
     float v[16];
 #pragma unroll
@@ -301,13 +300,14 @@ __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& 
       float m = 0.0f;
 #pragma unroll
       for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(v[q]));
-      m = fmaxf(m, pair_swap(m));
+      m = fmaxf(m, pair_swap(m)) * fabsf(sc);
       const int e = f16_block_exp(m);
+      const float s2 = m > 0.0f ? ldexpf(sc, -e) : 0.0f;
       if (valid) {
         uint32_t w[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const f16x2 hv{(_Float16)ldexpf(v[2 * q], -e), (_Float16)ldexpf(v[2 * q + 1], -e)};
+          const f16x2 hv{(_Float16)(v[2 * q] * s2), (_Float16)(v[2 * q + 1] * s2)};
           w[q] = __builtin_bit_cast(uint32_t, hv);
         }
         uint4* dst = reinterpret_cast<uint4*>(p.o_f16 + orow * p.N + col);
@@ -320,8 +320,8 @@ __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& 
         uint32_t w[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * q + 1]) << 16);
+          w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[2 * q] * sc)) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(v[2 * q + 1] * sc)) << 16);
         uint4* dst = reinterpret_cast<uint4*>(p.o_bf16 + orow * p.N + col);
         dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
         dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -329,7 +329,8 @@ __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& 
     } else if (valid) {
       float4* dst = reinterpret_cast<float4*>(p.o + orow * p.N + col);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      for (int q = 0; q < 4; ++q)
+        dst[q] = make_float4(v[4 * q] * sc, v[4 * q + 1] * sc, v[4 * q + 2] * sc, v[4 * q + 3] * sc);
     }
   }
 }
