@@ -279,6 +279,77 @@ def trace_summary(legs, cmd):
     return "\n".join(out) + "\n"
 
 
+# ------------------------------------------------------------------ MFMA utilisation
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.md")
+XCDS, SIMDS = 8, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def mfma_summary(legs, cmd):
+    """Markdown table of rocprofv3 counter runs (SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_F16) for the GEMM kernels, one
+    run per bench leg (legs = [(leg, counter_csv)]).  Per dispatch: MFMA
+    busy fraction = busy cycles summed over the SIMDs / (active cycles of one
+    XCD x 1024 SIMDs), effective clock = active cycles of one XCD / duration,
+    and the f16 MFMA flops the counter reports (512 per MOP)."""
+    import collections
+    import csv
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for leg, path in legs:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                k = _short_name(r["Kernel_Name"])
+                if "gemm" not in k and "skinny" not in k and not k.startswith("Cijk"):
+                    continue
+                key = (leg, k if not k.startswith("Cijk") else "hipBLASLt f16 GEMM (torch.matmul)",
+                       int(r["Grid_Size"]))
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+                agg[key][r["Counter_Name"]].append((float(r["Counter_Value"]), dur))
+    out = ["# MFMA utilisation of the GEMM kernels (rocprofv3 counters), per bench leg", "",
+           "Command (from the repository root, on one MI355X; R = repository root; LEG is each bench leg",
+           "in the table):", "", "    " + cmd, "",
+           f"Per dispatch: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs)",
+           f"(rocprofv3 reports GRBM_GUI_ACTIVE summed over the {XCDS} XCDs); clock = GRBM_GUI_ACTIVE / {XCDS} /",
+           "duration; MFMA TFLOP/s = 512 x SQ_INSTS_VALU_MFMA_MOPS_F16 / duration.  Durations are those of the",
+           "counter runs.", "",
+           "| leg | kernel | grid | dispatches | avg us | clock GHz | MFMA busy | MFMA TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|"]
+    js = []
+    for (leg, k, g), c in sorted(agg.items()):
+        need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16")
+        if not all(n in c for n in need):
+            continue
+        n = len(c["GRBM_GUI_ACTIVE"])
+        busy = np.mean([x for x, _ in c["SQ_VALU_MFMA_BUSY_CYCLES"]])
+        gui = np.mean([x for x, _ in c["GRBM_GUI_ACTIVE"]]) / XCDS
+        dur = np.mean([d for _, d in c["GRBM_GUI_ACTIVE"]])
+        flops = 512.0 * np.mean([x for x, _ in c["SQ_INSTS_VALU_MFMA_MOPS_F16"]])
+        util, clk = busy / (gui * SIMDS), gui / dur / 1e9
+        out.append(f"| {leg} | {k} | {g} | {n} | {dur * 1e6:.1f} | {clk:.2f} | {100 * util:.1f} % | "
+                   f"{flops / dur / 1e12:.0f} |")
+        if k in KERNEL_SOURCES:
+            js.append(json.dumps({"kernel": k, "workload": leg, "grid": g, "src": source_hash(k),
+                                  "mfma_busy": util, "clock_ghz": clk, "mfma_flops": flops}))
+    out += ["", "Machine-readable lines (bench.py reads these; src = hash of the kernel's sources):", ""]
+    out += ["mfma-json: " + j for j in js]
+    return "\n".join(out) + "\n"
+
+
+def load_mfma(kernel, workload):
+    """MFMA busy fraction and clock of `kernel` in bench leg `workload` from
+    the committed counter summary, or None when absent or stale."""
+    try:
+        with open(MFMA_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("mfma-json: "):
+            d = json.loads(line[len("mfma-json: "):])
+            if d.get("kernel") == kernel and d.get("workload") == workload and d.get("src") == source_hash(kernel):
+                return {"mfma_busy": d["mfma_busy"], "clock_ghz": d["clock_ghz"]}
+    return None
+
+
 # ------------------------------------------------------------------ MoE
 def moe_weights(nv, cfg):
     """All experts' NVFP4 weights on the GPU (model preparation, untimed)."""
@@ -483,6 +554,8 @@ def main():
                          "COPY_WRITE, then LEG=FETCH_CSV LEG=WRITE_CSV pairs")
     ap.add_argument("--trace-summary", nargs="+", metavar="LEG=KERNEL_TRACE_CSV",
                     help="print the markdown summary of rocprofv3 kernel traces, one per bench leg")
+    ap.add_argument("--mfma-summary", nargs="+", metavar="LEG=COUNTER_CSV",
+                    help="print the markdown MFMA-utilisation summary of rocprofv3 counter runs, one per bench leg")
     ap.add_argument("--cmd", action="append", default=[], help="command lines quoted in a summary")
     args = ap.parse_args()
     if args.traffic_summary:
@@ -493,6 +566,9 @@ def main():
         return
     if args.trace_summary:
         sys.stdout.write(trace_summary(_split_legs(args.trace_summary), " ".join(args.cmd)))
+        return
+    if args.mfma_summary:
+        sys.stdout.write(mfma_summary(_split_legs(args.mfma_summary), " ".join(args.cmd)))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -543,9 +619,10 @@ def main():
         if "quantize" in res:
             res["quantize"]["cpu_baseline"] = cpu_baseline_quantize()
     p = res.get("prefill")
-    traffic = None
+    traffic = mfma = None
     if p:
         traffic = load_traffic("l1_gemm_swiglu_quant_kernel", "pre")
+        mfma = load_mfma("l1_gemm_swiglu_quant_kernel", "pre")
     line = {
         "metric": "MoE expert-FFN TFLOP/s + quantize GB/s, % of MI355X roofline (1 GPU)",
         "value": p["TFLOPs"] if p else None,
@@ -561,7 +638,10 @@ def main():
                       "achieved": p["l1_main_TFLOPs"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": p["l1_main_TFLOPs"] / F16_PEAK_TFLOPS, "traffic": traffic,
                       "traffic_unit": "bytes per launch (HBM, rocprofv3)",
-                      "algorithmic_flops_per_launch": p["l1_main_flops"]} if p else None),
+                      "algorithmic_flops_per_launch": p["l1_main_flops"],
+                      # rocprofv3 counters of the same kernel: MFMA-busy fraction of the SIMD
+                      # cycles and the clock it ran at (the 2.5 PFLOP/s peak assumes 2.4 GHz)
+                      "counters": mfma} if p else None),
         "cpu_baseline": cpu,
     }
     line.update(res)
