@@ -140,12 +140,21 @@ KERNEL_SOURCES = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace collapsed, so that a
+    comment-only edit does not mark a profile stale."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "quantization_nvfp4_quantize_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantization_nvfp4_quantize_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -26,19 +26,23 @@
 //   * Workgroups are dealt to the 8 XCDs in turn; work items are assigned so
 //     that each XCD takes one contiguous range of (M tile, N tile) items,
 //     M-tile-major, and the N tiles of an M tile share one XCD's L2.
-//   * K steps of 64.  A goes from global memory straight into LDS
-//     (global_load_lds_dwordx4: 8 lanes fetch one 128 B row, so every request
-//     uses whole cache lines and no VGPRs or LDS write instructions are
-//     spent on it) through three stages, issued two steps ahead.  B moves
-//     through registers: thread t loads half a row of nibbles and its two
-//     block scales two steps ahead, dequantizes them with the gfx950 FP4 -> f16
-//     and FP8 -> f16 conversions and one packed f16 multiply per pair, and
-//     writes the next step's B stage (two stages).  The conversions and the A
-//     loads are spread over the 8 MFMA groups of a step (scheduling fences
-//     keep the order); MFMA operand fragments are read one sub-step ahead.
-//   * LDS rows are 64 f16 = 8 chunks of 16 B, chunk c stored at
-//     c ^ ((row ^ row >> 3) & 7), which keeps the B writes and the MFMA
-//     operand reads free of bank conflicts (16-lane groups on 64 banks).
+//   * K steps of 64.  A (f16), the raw B nibbles and their block scales go
+//     from global memory straight into LDS (global_load_lds: 8 lanes fetch
+//     one 128 B row, so every request uses whole cache lines and no VGPRs or
+//     LDS write instructions are spent on them), issued three steps ahead
+//     into four A stages and three B / scale stages, each load addressed as
+//     a wave-uniform base plus a 32-bit lane offset.  Their completion is
+//     waited for with explicit load counts before the one LDS-only barrier
+//     per step.  Each wave reads the raw nibbles and scales of its columns
+//     from LDS and dequantizes them in registers with the gfx950 FP4 -> f16
+//     and FP8 -> f16 conversions and one packed f16 multiply per pair; the
+//     conversions, the A fragment reads and the direct loads are spread over
+//     the 8 MFMA groups of a step (scheduling fences keep the order), and
+//     operand fragments are read one sub-step ahead.
+//   * LDS rows of A are 64 f16 = 8 chunks of 16 B, chunk c stored at
+//     c ^ ((row ^ row >> 3) & 7); raw B half-rows alternate with
+//     (row >> 3) & 1.  Both keep the 16-lane groups of the fragment reads on
+//     distinct banks.
 //   * The K order inside a 64-chunk is permuted identically for A and B (lane
 //     half g reads physical chunk 4g + s at MFMA step s).
 //   * L1: the 256 B rows of a tile are the gate/up rows of 128 compact SwiGLU
@@ -47,6 +51,10 @@
 //     LDS, quantizes it with lane pairs (one 16-element block per pair), and
 //     writes the NVFP4 bytes plus the exact f16 of the quantized values (the
 //     L2 operand).
+//   * L2: persistent (one workgroup per CU claiming items per XCD), with
+//     the next item's first loads issued before the current item's epilogue;
+//     the epilogue transposes each wave's block through LDS and writes whole
+//     row segments (l2_store_block).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
