@@ -19,6 +19,8 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
             deinterleave + quantize pass (the pages' earlier flow), or
             compact with the dynamic amax / 2688 scale (and y's distance from
             the fused run)
+  prefill_aux  the fused prefill layer with the mixed tiling's 32-row short
+            tiles on a second stream, alongside the 256-row tiles
 Timing: W untimed warmups, then K timed steps.  quantize and expert replay a
 HIP graph of K launches between two events (no host gaps); the MoE legs run
 eagerly and the library records HIP events between its stages on the same
@@ -383,8 +385,10 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     """One MoE layer config; mode "fused" (L1 output quantized in the GEMM
     epilogue with the supplied scale), "unfused" (compact bf16 L1 output,
     separate quantization pass, supplied scale), "interleaved" (interleaved
-    [SiLU(gate), SwiGLU] bf16 output, deinterleave + quantize pass) or
-    "dynamic" (unfused, with the dynamic amax / 2688 scale)."""
+    [SiLU(gate), SwiGLU] bf16 output, deinterleave + quantize pass),
+    "dynamic" (unfused, with the dynamic amax / 2688 scale) or "aux" (fused,
+    with the mixed tiling's short tiles on a second stream alongside the
+    256-row tiles)."""
     import synth
     dev = torch.device("cuda:0")
     if w is None:
@@ -397,8 +401,14 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     a2 = None if mode == "dynamic" else torch.tensor([cfg.a2_gs], dtype=torch.float32, device=dev)
     a2_out = torch.empty(1, dtype=torch.float32, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
-    flow = {"fused": 0, "unfused": 1, "interleaved": 2, "dynamic": 0}[mode]
-    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out, l1_unfused=flow)
+    flow = {"fused": 0, "unfused": 1, "interleaved": 2, "dynamic": 0, "aux": 0}[mode]
+    aux = None
+    if mode == "aux":
+        # the library forks the short tiles onto this stream and joins it back
+        aux = (torch.cuda.Stream(), (torch.cuda.Event(), torch.cuda.Event()))
+        for e in aux[1]:
+            e.record()
+    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out, l1_unfused=flow, aux=aux)
     ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         nv.moe_expert_ffn_raw(args, dev, ws)
@@ -610,7 +620,7 @@ def main():
             # the pages' unfused flows on the same layer: the fusion's saving,
             # and the dynamic L1-output scale against the supplied one
             y_static = pre[4]
-            for mode in ("unfused", "interleaved", "dynamic"):
+            for mode in ("unfused", "interleaved", "dynamic", "aux"):
                 r, extra = bench_moe(nv, synth.PRE, max(3, args.steps // 3), args.warmup, w=pre[0], mode=mode)
                 r = {k: r[k] for k in ("ms_per_step", "TFLOPs", "stage_ms", "a2_gs")}
                 yd = extra[4]

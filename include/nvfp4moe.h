@@ -198,6 +198,18 @@ typedef struct {
      1 and 2 give the fused flow's bytes.  Any other value:
      NVFP4_ERR_INVALID_ARG. */
   int32_t l1_unfused;
+  /* nullable: a second stream (hipStream_t) and two events (hipEvent_t,
+     aux_events[0] and [1]), all created by the caller, on which the 32-row
+     short tiles of the mixed tiling run concurrently with the 256-row
+     tiles.  For each GEMM the library records aux_events[0] on `stream`,
+     makes aux_stream wait for it, launches the short tiles on aux_stream,
+     records aux_events[1] there and makes `stream` wait for it before the
+     next stage, so the call still completes in `stream` order (and can be
+     captured in a graph).  Without it, or in the other tilings, everything
+     runs on `stream`; the results are the same.  aux_stream without
+     aux_events: NVFP4_ERR_INVALID_ARG. */
+  void *aux_stream;
+  void *const *aux_events;
 } nvfp4_moe_args;
 
 /*

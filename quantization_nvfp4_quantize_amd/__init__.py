@@ -40,6 +40,8 @@ class MoeArgs(ctypes.Structure):
         ("tile_rows", ctypes.c_int32),
         ("a2_gs_out", _vp),
         ("l1_unfused", ctypes.c_int32),
+        ("aux_stream", _vp),
+        ("aux_events", ctypes.POINTER(_vp)),
     ]
 
 
@@ -206,14 +208,18 @@ def linear_workspace(M, K, N, device):
 
 def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
              x_gs=None, xq=None, xsf=None, x_gs_out=None, l1_c=None, l1_q=None, l1_sf=None,
-             err_count=None, tile_rows=0, a2_gs_out=None, l1_unfused=False):
+             err_count=None, tile_rows=0, a2_gs_out=None, l1_unfused=False, aux=None):
     """Build the nvfp4_moe_args struct from tensors (keeps no references).
     tile_rows: 0 lets the library choose the GEMM tiles; 32 or 256 forces
     one tile height, 288 the mixed tiling (256-row tiles, each expert's last
     block of at most 32 rows on a 32-row tile).
     a2_gs None: dynamic L1-output global scale (unfused flow); l1_unfused:
     True / 1 the unfused flow with the supplied a2_gs, "interleaved" / 2 the
-    interleaved-output flow; a2_gs_out receives the scale."""
+    interleaved-output flow; a2_gs_out receives the scale.  aux: None, or
+    (torch.cuda.Stream, (torch.cuda.Event, torch.cuda.Event)) on which the
+    short tiles of the mixed tiling run concurrently (the events must have
+    been recorded once, so that they exist); the struct then holds the event
+    handle array, which the caller keeps alive with the struct."""
     _require(x, torch.bfloat16, "x")
     _require(topk_ids, torch.int32, "topk_ids")
     _require(topk_w, torch.float32, "topk_w")
@@ -228,6 +234,11 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
     a.tile_rows = int(tile_rows)
     a.a2_gs_out = _p(a2_gs_out)
     a.l1_unfused = {False: 0, True: 1, 0: 0, 1: 1, 2: 2, "interleaved": 2}[l1_unfused]
+    if aux is not None:
+        stream, (ev0, ev1) = aux
+        a._aux_events = (ctypes.c_void_p * 2)(ev0.cuda_event, ev1.cuda_event)
+        a.aux_stream = stream.cuda_stream
+        a.aux_events = ctypes.cast(a._aux_events, ctypes.POINTER(ctypes.c_void_p))
     return a
 
 
@@ -245,11 +256,12 @@ def moe_expert_ffn_raw(args, device, ws=None):
 
 
 def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
-                   out_dtype=torch.bfloat16, x_gs=None, debug=False, tile_rows=0, l1_unfused=False):
+                   out_dtype=torch.bfloat16, x_gs=None, debug=False, tile_rows=0, l1_unfused=False,
+                   aux=None):
     """NVFP4 MoE expert FFN.  Returns y [T][H] (out_dtype), plus with
     debug=True a dict of the intermediate outputs (xq, xsf, x_gs, l1_c,
     l1_q, l1_sf, err_count, a2_gs_out).  a2_gs None: dynamic L1-output
-    global scale.  tile_rows, l1_unfused: see moe_args."""
+    global scale.  tile_rows, l1_unfused, aux: see moe_args."""
     T, H = x.shape
     I = w1_q.shape[1] // 2
     k = topk_ids.shape[1]
@@ -267,7 +279,7 @@ def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, 
                    err_count=torch.zeros(1, dtype=torch.int32, device=dev),
                    a2_gs_out=torch.empty(1, dtype=torch.float32, device=dev))
     args = moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
-                    x_gs=x_gs, tile_rows=tile_rows, l1_unfused=l1_unfused, **dbg)
+                    x_gs=x_gs, tile_rows=tile_rows, l1_unfused=l1_unfused, aux=aux, **dbg)
     moe_expert_ffn_raw(args, dev)
     if debug:
         return out, dbg

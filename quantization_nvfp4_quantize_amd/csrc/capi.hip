@@ -341,6 +341,8 @@ int moe_validate(const nvfp4_moe_args* a) {
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: l1_unfused must be 0, 1 or 2");
   if (a->l1_unfused == 2 && !a->a2_gs)
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: the interleaved flow needs a supplied a2_gs");
+  if (a->aux_stream && (!a->aux_events || !a->aux_events[0] || !a->aux_events[1]))
+    return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: aux_stream needs two aux_events");
   if ((a->tile_rows == nvfp4::skinny_tile_rows() || a->tile_rows == kMixedTileRows()) && !moe_skinny_fits(a))
     return fail(NVFP4_ERR_UNSUPPORTED,
                 "moe_expert_ffn_nvfp4: tile_rows %d needs H and I multiples of 256 (or 128)", a->tile_rows);
@@ -412,6 +414,23 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   const bool skinny = mode == nvfp4::skinny_tile_rows(), mixed = mode == kMixedTileRows();
   nvfp4::GemmTile* small = reinterpret_cast<nvfp4::GemmTile*>(w + L.small);
   int* nsmall = reinterpret_cast<int*>(w + L.nsmall);
+  // the short tiles of the mixed tiling run on the caller's second stream
+  // when it gave one: fork after the work they depend on, join before the
+  // work that depends on them
+  const bool concurrent = mixed && a->aux_stream;
+  hipStream_t aux = concurrent ? reinterpret_cast<hipStream_t>(a->aux_stream) : s;
+  auto fork = [&]() -> hipError_t {
+    if (!concurrent) return hipSuccess;
+    hipEvent_t ev = reinterpret_cast<hipEvent_t>(a->aux_events[0]);
+    hipError_t e = hipEventRecord(ev, s);
+    return e == hipSuccess ? hipStreamWaitEvent(aux, ev, 0) : e;
+  };
+  auto join = [&]() -> hipError_t {
+    if (!concurrent) return hipSuccess;
+    hipEvent_t ev = reinterpret_cast<hipEvent_t>(a->aux_events[1]);
+    hipError_t e = hipEventRecord(ev, aux);
+    return e == hipSuccess ? hipStreamWaitEvent(s, ev, 0) : e;
+  };
   if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E,
                                            skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows(),
                                            mixed ? nvfp4::skinny_tile_rows() : 0, offsets, perm, tiles, ntiles,
@@ -430,13 +449,16 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   // the L1 GEMM over the tile list (and the short tiles of the mixed tiling)
   auto l1 = [&](const float* out_gs, uint16_t* c_bf16, uint8_t* cq, uint8_t* csf, uint16_t* cf16,
                 uint16_t* c_il) {
-    hipError_t e = (skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1)(
-        x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf, cf16, tiles, ntiles,
-        L.max_tiles, 0, perm, (int)k, s, c_il);
+    hipError_t e = fork();
+    if (e == hipSuccess)
+      e = (skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1)(
+          x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf, cf16, tiles, ntiles,
+          L.max_tiles, 0, perm, (int)k, s, c_il);
     mark(4);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
-                                  cf16, small, nsmall, (int)E, 0, perm, (int)k, s, c_il);
+                                  cf16, small, nsmall, (int)E, 0, perm, (int)k, aux, c_il);
+    if (e == hipSuccess) e = join();
     return hip_status(e, "L1 GEMM");
   };
   const float* a2_gs = a->a2_gs;
@@ -476,13 +498,16 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   uint16_t* o16 = f16_rows ? reinterpret_cast<uint16_t*>(w + L.o) : nullptr;
   int8_t* oexp = f16_rows ? reinterpret_cast<int8_t*>(w + L.oexp) : nullptr;
   {
-    hipError_t e = (skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2)(
-        a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles, L.max_tiles, perm, s, 0,
-        nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp);
+    hipError_t e = fork();
+    if (e == hipSuccess)
+      e = (skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2)(
+          a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles, L.max_tiles, perm, s,
+          0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp);
     mark(6);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, small, nsmall,
-                                  (int)E, perm, s, 0, nullptr, nullptr, o16, oexp);
+                                  (int)E, perm, aux, 0, nullptr, nullptr, o16, oexp);
+    if (e == hipSuccess) e = join();
     if ((st = hip_status(e, "L2 GEMM"))) return st;
   }
   mark(7);

@@ -117,6 +117,9 @@ def test_moe_rejects(lib):
     # GEMM tiling: 0 (automatic), 32, 256 or 288 (mixed) only
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(tile_rows=64)), FAKE, 1 << 30, None) == -1
     assert b"tile_rows" in lib.nvfp4_last_error()
+    # a second stream needs its two events
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(aux_stream=0x1234)), FAKE, 1 << 30, None) == -1
+    assert b"aux_events" in lib.nvfp4_last_error()
     # 32-row tiles (alone or in the mixed tiling) need H and I multiples of 256 (or 128)
     for tr in (32, 288):
         assert lib.moe_expert_ffn_nvfp4(by(_moe_args(I=384, tile_rows=tr)), FAKE, 1 << 30, None) == -2

@@ -67,3 +67,41 @@ def test_moe_graph_replays(nv):
         torch.cuda.synchronize()
         assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
         _ = nv.moe_expert_ffn(x, ti, tw, *wl, a2)
+
+
+def test_moe_graph_replays_aux_stream(nv):
+    """A captured MoE layer whose mixed tiling forks its short tiles onto a
+    second stream and joins them back: every replay equals the eager run."""
+    import dataclasses
+    counts = [266, 40, 289, 20]
+    cfg = dataclasses.replace(synth.TINY, T=sum(counts), E=len(counts), topk=1, name="mixed")
+    w = gpu_weights(nv, cfg)
+    x = dev_bf16(synth.activations(cfg))
+    rng = np.random.default_rng(5)
+    ids = rng.permutation(np.repeat(np.arange(cfg.E), counts)).astype(np.int32)[:, None]
+    ti = torch.from_numpy(ids).cuda()
+    tw = torch.from_numpy(rng.uniform(0.5, 1.5, size=(cfg.T, 1)).astype(np.float32)).cuda()
+    a2 = dev_f32(cfg.a2_gs)
+    wl = (w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"], w["w2gs"])
+    ref = host(nv.moe_expert_ffn(x, ti, tw, *wl, a2, out_dtype=torch.float32, tile_rows=288))
+    stream = torch.cuda.Stream()
+    evs = (torch.cuda.Event(), torch.cuda.Event())
+    for e in evs:
+        e.record()
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda:0")
+    args = nv.moe_args(x, ti, tw, *wl, a2, out, tile_rows=288, aux=(stream, evs))
+    ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device="cuda:0")
+    nv.moe_expert_ffn_raw(args, x.device, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.moe_expert_ffn_raw(args, x.device, ws)
+    for _ in range(4):
+        out.zero_()
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
+        _ = nv.moe_expert_ffn(x, ti, tw, *wl, a2, tile_rows=288)

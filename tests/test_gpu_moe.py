@@ -315,6 +315,45 @@ def test_moe_tile_modes_agree(nv):
         assert np.array_equal(host(ya).view(np.uint32), host(yb).view(np.uint32)), tr
 
 
+def _aux():
+    stream = torch.cuda.Stream()
+    evs = (torch.cuda.Event(), torch.cuda.Event())
+    for e in evs:
+        e.record()  # creates the underlying event
+    return stream, evs
+
+
+@pytest.mark.parametrize("flow", ["fused", "unfused", "interleaved", "dynamic"])
+def test_moe_mixed_aux_stream(nv, flow):
+    """The mixed tiling with the short tiles on a second stream gives the
+    same bytes as on one stream, in every flow."""
+    import dataclasses
+    counts = [266, 544, 289, 255, 32, 0]
+    cfg = dataclasses.replace(synth.TINY, T=sum(counts), E=len(counts), topk=1, name="mixed")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    rng = np.random.default_rng(11)
+    ids = rng.permutation(np.repeat(np.arange(cfg.E), counts)).astype(np.int32)[:, None]
+    wts = rng.uniform(0.5, 1.5, size=(cfg.T, 1)).astype(np.float32)
+    xd = dev_bf16(x)
+    ti = torch.from_numpy(ids).cuda()
+    tw = torch.from_numpy(wts).cuda()
+    a2 = None if flow == "dynamic" else dev_f32(cfg.a2_gs)
+    unf = {"fused": False, "unfused": 1, "interleaved": 2, "dynamic": False}[flow]
+    wl = (w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"], w["w2gs"])
+    for out_dtype in (torch.float32, torch.bfloat16):
+        ya, da = nv.moe_expert_ffn(xd, ti, tw, *wl, a2, out_dtype=out_dtype, debug=True, tile_rows=288,
+                                   l1_unfused=unf)
+        yb, db = nv.moe_expert_ffn(xd, ti, tw, *wl, a2, out_dtype=out_dtype, debug=True, tile_rows=288,
+                                   l1_unfused=unf, aux=_aux())
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(da["l1_c"]), host_bits(db["l1_c"])), (flow, out_dtype)
+        for key in ("l1_q", "l1_sf", "a2_gs_out"):
+            assert np.array_equal(host(da[key]), host(db[key])), (flow, out_dtype, key)
+        assert np.array_equal(host_bits(ya) if out_dtype == torch.bfloat16 else host(ya).view(np.uint32),
+                              host_bits(yb) if out_dtype == torch.bfloat16 else host(yb).view(np.uint32))
+
+
 def test_moe_mixed_tiles_remainders(nv, orc):
     """The mixed tiling on expert row counts chosen around its boundaries:
     256 + 10 (one 256-row tile and a 10-row short tile), 512 + 32 (two and a
