@@ -190,6 +190,22 @@ def test_moe_ragged_token_counts(nv, orc, tile_rows):
         _gate(*res[:4])
 
 
+@pytest.mark.parametrize("tile_rows", TILES)
+def test_moe_largest_expert_count_and_topk(nv, orc, tile_rows):
+    """The largest supported routing: E = 512 experts and top-32, every token
+    against the oracle."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=40, E=512, topk=32, name="e512k32")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows)
+    assert host(dbg["err_count"])[0] == 0
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    print("E512 top-32: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
+
+
 @pytest.mark.parametrize("H,I", [(1280, 768), (1024, 512), (256, 1280)])
 def test_moe_skinny_k_schedules(nv, orc, H, I):
     """32-row tiles with reduction lengths whose 256-K super-steps leave a
