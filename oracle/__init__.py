@@ -14,6 +14,7 @@ mutated builds to show that the pins catch plausible mistakes); the module
 level functions use the default build next to this file.
 """
 import ctypes
+import importlib
 import os
 
 import numpy as np
@@ -82,7 +83,9 @@ class Oracle:
 
     def __init__(self, path=DEFAULT_LIB):
         if path == DEFAULT_LIB and not os.path.exists(path):
-            from . import build as _b
+            # import the submodule explicitly: a from-import would first look the
+            # name up through this module's __getattr__ and recurse into here
+            _b = importlib.import_module(__name__ + ".build")
             _b.build()
         self.path = path
         L = ctypes.CDLL(path)
@@ -274,8 +277,13 @@ def default():
     return _default
 
 
+_SUBMODULES = ("build",)
+
+
 def __getattr__(name):
     # module-level access to the default build's methods: oracle.quantize(...)
     if name.startswith("_"):
         raise AttributeError(name)
+    if name in _SUBMODULES:
+        return importlib.import_module(__name__ + "." + name)
     return getattr(default(), name)

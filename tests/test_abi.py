@@ -156,3 +156,21 @@ def test_linear_rejects(lib):
     assert b"workspace" in lib.nvfp4_last_error()
     # an empty batch is a no-op
     assert lib.nvfp4_linear(None, 0, 64, None, None, None, None, 256, 0, None, None, None, 0, None) == 0
+
+
+def test_build_scripts_need_no_built_library(tmp_path):
+    """build() must work on a fresh checkout, before any .so exists: the
+    oracle's build submodule resolves without loading the default oracle, and
+    both build scripts load by path without importing their packages."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import importlib, sys; sys.path.insert(0, %r); "
+            "import oracle; m = oracle.build; "
+            "assert m.__name__ == 'oracle.build', m; "
+            "assert oracle._default is None; "
+            "import __graft_entry__ as g; "
+            "h = g._load_script('quantization_nvfp4_quantize_amd/build.py', '_t'); "
+            "assert callable(h.build); "
+            "assert 'quantization_nvfp4_quantize_amd' not in sys.modules") % root
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=str(tmp_path))
