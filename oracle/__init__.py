@@ -4,10 +4,13 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its Python binding) never imports it, and the two share no code.
 
-Thin numpy/ctypes wrapper around ``nvfp4_oracle.c``: argument marshalling
-only; every step of the arithmetic lives in the C file, which cites the pages
-("nvfp4-megamoe-kernel": NVFP4-1.1_APPROACH_PART_2.md, NVFP4-1.1_APPROACH.md,
-DEBUG_LOG.md "NVFP4 MoE Pipeline") it follows.
+Thin numpy/ctypes wrapper around ``nvfp4_oracle.c`` and ``mxfp4_oracle.c``:
+argument marshalling only; every step of the arithmetic lives in the C
+files.  ``nvfp4_oracle.c`` cites the pages ("nvfp4-megamoe-kernel":
+NVFP4-1.1_APPROACH_PART_2.md, NVFP4-1.1_APPROACH.md, DEBUG_LOG.md "NVFP4 MoE
+Pipeline") it follows; ``mxfp4_oracle.c`` follows the OCP Microscaling
+Formats (MX) Specification v1.0, which defines the MXFP4 format of the
+separately labelled scaled-MFMA variant (the pages do not define it).
 
 ``Oracle(path)`` wraps one build of the library (tests also load deliberately
 mutated builds to show that the pins catch plausible mistakes); the module
@@ -62,6 +65,15 @@ _SIGNATURES = {
     "orc_l1_swiglu_rows": (None, [_u8p, _u8p, ctypes.c_float, ctypes.c_int64, _u8p, _u8p,
                                   ctypes.c_float, ctypes.c_int64, _i64p, ctypes.c_int64, _f64p,
                                   _u16p, ctypes.c_int]),
+    "orc_mx_scale_value": (ctypes.c_double, [ctypes.c_uint32]),
+    "orc_mx_scale_code": (ctypes.c_uint32, [ctypes.c_double]),
+    "orc_mx_e2m1_value": (ctypes.c_double, [ctypes.c_uint32]),
+    "orc_mx_e2m1_nibble": (ctypes.c_uint32, [ctypes.c_double]),
+    "orc_mx_quantize_block": (ctypes.c_uint32, [_u16p, _u8p]),
+    "orc_mx_quantize": (None, [_u16p, ctypes.c_int64, ctypes.c_int64, _u8p, _u8p]),
+    "orc_mx_dequantize": (None, [_u8p, _u8p, ctypes.c_int64, ctypes.c_int64, _f64p]),
+    "orc_mx_linear": (None, [_u8p, _u8p, ctypes.c_int64, ctypes.c_int64, _u8p, _u8p, ctypes.c_int64,
+                             _f64p, ctypes.c_int]),
     "orc_moe_tokens": (ctypes.c_float, [ctypes.POINTER(MoeProblem), _i64p, ctypes.c_int64,
                                         _f32p, _u16p, _u8p, _u8p, ctypes.c_int]),
 }
@@ -265,6 +277,65 @@ class Oracle:
                               tokens=tokens, x_gs=x_gs, want_pairs=want_pairs, threads=threads)
         out["a2_gs"] = np.float32(g2)
         return out
+
+
+    # ------------------------------------------------------------ MXFP4
+    # The OCP MX v1.0 format (E8M0 scale per 32 elements), mxfp4_oracle.c.
+    def mx_scale_value(self, code):
+        return self.L.orc_mx_scale_value(int(code))
+
+    def mx_scale_code(self, amax):
+        return int(self.L.orc_mx_scale_code(float(amax)))
+
+    def mx_e2m1_value(self, nibble):
+        return self.L.orc_mx_e2m1_value(int(nibble))
+
+    def mx_e2m1_nibble(self, v):
+        return int(self.L.orc_mx_e2m1_nibble(float(v)))
+
+    def mx_quantize_block(self, xb_bf16):
+        xb = np.ascontiguousarray(xb_bf16, dtype=np.uint16)
+        assert xb.size == 32
+        q = np.zeros(16, np.uint8)
+        code = self.L.orc_mx_quantize_block(_ptr(xb, _u16p), _ptr(q, _u8p))
+        return q, int(code)
+
+    def mx_quantize(self, x_bf16):
+        """x_bf16: uint16 [M][K] bf16 bit patterns, K % 32 == 0.
+        Returns (q uint8 [M][K/2], scale codes uint8 [M][K/32])."""
+        x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+        M, K = x.shape
+        assert K % 32 == 0
+        q = np.zeros((M, K // 2), np.uint8)
+        sc = np.zeros((M, K // 32), np.uint8)
+        if M:
+            self.L.orc_mx_quantize(_ptr(x, _u16p), M, K, _ptr(q, _u8p), _ptr(sc, _u8p))
+        return q, sc
+
+    def mx_dequantize(self, q, sc):
+        """Exact values (float64) of an MXFP4 matrix."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        sc = np.ascontiguousarray(sc, dtype=np.uint8)
+        M, K2 = q.shape
+        K = 2 * K2
+        assert sc.shape == (M, K // 32)
+        out = np.zeros((M, K), np.float64)
+        if M:
+            self.L.orc_mx_dequantize(_ptr(q, _u8p), _ptr(sc, _u8p), M, K, _ptr(out, _f64p))
+        return out
+
+    def mx_linear(self, aq, asc, wq, wsc, threads=None):
+        """y [M][N] = A @ W^T in float64 for MXFP4 A [M][K], W [N][K]."""
+        aq, asc = np.ascontiguousarray(aq, np.uint8), np.ascontiguousarray(asc, np.uint8)
+        wq, wsc = np.ascontiguousarray(wq, np.uint8), np.ascontiguousarray(wsc, np.uint8)
+        M, K = aq.shape[0], aq.shape[1] * 2
+        N = wq.shape[0]
+        assert wq.shape[1] * 2 == K and asc.shape == (M, K // 32) and wsc.shape == (N, K // 32)
+        y = np.zeros((M, N), np.float64)
+        if M and N:
+            self.L.orc_mx_linear(_ptr(aq, _u8p), _ptr(asc, _u8p), M, K, _ptr(wq, _u8p), _ptr(wsc, _u8p), N,
+                                 _ptr(y, _f64p), threads or default_threads())
+        return y
 
 
 _default = None

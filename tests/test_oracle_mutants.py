@@ -54,7 +54,8 @@ def _build_mutant(tmp_path, name, edits):
     lib = tmp_path / f"lib_{name}.so"
     inc = os.path.dirname(SRC)
     subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
-                    "-I", inc, "-o", str(lib), str(cpath), "-lm"], check=True)
+                    "-I", inc, "-o", str(lib), str(cpath), os.path.join(inc, "mxfp4_oracle.c"), "-lm"],
+                   check=True)
     return str(lib)
 
 
