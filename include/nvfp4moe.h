@@ -234,6 +234,41 @@ typedef struct {
 size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);
 int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * MXFP4 -- a separately labelled format, NOT the pages' NVFP4: the Open
+ * Compute Project "Microscaling Formats (MX) Specification" v1.0 format
+ * that gfx950's scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) consumes,
+ * for measuring the FP4 matrix-core headroom next to the NVFP4 path.  Blocks
+ * of 32 consecutive elements along K share one E8M0 scale code c (the value
+ * 2^(c - 127), section 5.4); each element is E2M1 (section 5.3.3); there is
+ * no tensor scale.  Quantization follows section 6.3: code = floor(log2(max
+ * |x| of the block)) - 2 + 127, clamped to [0, 254] (0 for an all-zero
+ * block), element = x / 2^(code - 127) rounded to the nearest E2M1 value,
+ * ties to even, saturating at 6; the nibble sign is the sign bit of x.
+ * Layout of a logical [R][K] MXFP4 matrix (K % 32 == 0):
+ *   q     uint8 [R][K/2]   element 2i in the low nibble of byte i
+ *   scale uint8 [R][K/32]  E8M0 codes
+ *
+ * mxfp4_quantize: x bf16 [M][K] (16-byte aligned) -> q (4-byte aligned),
+ *   scale.  M >= 0, K % 32 == 0 (else NVFP4_ERR_INVALID_ARG).
+ * mxfp4_dequantize: q, scale -> out [M][K] = e2m1 * 2^(code - 127), bf16
+ *   (out_dtype 0, rounded to nearest even) or fp32 (1, exact); out 16-byte
+ *   aligned.
+ * mxfp4_linear: y[m][n] = sum_k deq(MXFP4(x))[m][k] * deq(w)[n][k], exact
+ *   products, fp32 accumulation; x bf16 [M][K]; w_q [N][K/2] (16-byte
+ *   aligned), w_scale [N][K/32] (4-byte aligned); out [M][N] bf16 (out_dtype
+ *   0) or fp32 (1), 16-byte aligned.  K % 128 == 0 and N % 256 == 0, M * K / 2
+ *   and N * K / 2 at most 4 GiB (else NVFP4_ERR_UNSUPPORTED).  Workspace:
+ *   mxfp4_linear_workspace_size bytes (the MXFP4 copy of x), 256-byte
+ *   aligned.
+ */
+int mxfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *q, uint8_t *scale, void *stream);
+int mxfp4_dequantize(const uint8_t *q, const uint8_t *scale, int64_t M, int64_t K, int out_dtype, void *out,
+                     void *stream);
+size_t mxfp4_linear_workspace_size(int64_t M, int64_t K, int64_t N);
+int mxfp4_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *w_q, const uint8_t *w_scale, int64_t N,
+                 int out_dtype, void *out, void *ws, size_t ws_bytes, void *stream);
+
 /* Helpers. */
 const char *nvfp4_status_string(int status);
 const char *nvfp4_last_error(void);

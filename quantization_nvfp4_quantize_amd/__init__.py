@@ -58,6 +58,10 @@ _SIG = {
     "nvfp4_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nvfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _i64, ctypes.c_int, _vp, _vp,
                                     _vp, _sz, _vp]),
+    "mxfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "mxfp4_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
+    "mxfp4_linear_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "mxfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, ctypes.c_int, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_nvfp4_workspace_size": (_sz, [ctypes.POINTER(MoeArgs)]),
     "moe_expert_ffn_nvfp4": (ctypes.c_int, [ctypes.POINTER(MoeArgs), _vp, _sz, _vp]),
 }
@@ -203,6 +207,57 @@ def linear(x, w_q, w_sf, w_gs, out_dtype=torch.bfloat16, x_gs=None, x_gs_out=Non
 def linear_workspace(M, K, N, device):
     """A dedicated workspace for nvfp4_linear (e.g. for graph capture)."""
     return torch.empty(max(int(_lib.nvfp4_linear_workspace_size(M, K, N)), 256), dtype=torch.uint8,
+                       device=device)
+
+
+# ------------------------------------------------------------------ MXFP4
+# The separately labelled OCP MX v1.0 format (E8M0 scale per 32 elements) on
+# the scaled FP4 MFMA; not the NVFP4 of the functions above.
+def mx_quantize(x, out=None):
+    """bf16 [M][K] (K % 32 == 0) -> (q uint8 [M][K/2], scale codes uint8 [M][K/32])."""
+    _require(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if out is None:
+        out = (torch.empty((M, K // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((M, K // 32), dtype=torch.uint8, device=x.device))
+    q, sc = out
+    _check(_lib.mxfp4_quantize(_p(x), M, K, _p(q), _p(sc), _stream(x.device)), "mxfp4_quantize")
+    return q, sc
+
+
+def mx_dequantize(q, sc, out_dtype=torch.bfloat16, out=None):
+    """MXFP4 -> bf16 or float32 [M][K]."""
+    _require(q, torch.uint8, "q")
+    _require(sc, torch.uint8, "scale")
+    M, K = q.shape[0], 2 * q.shape[1]
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=q.device)
+    code = {torch.bfloat16: 0, torch.float32: 1}[out.dtype]
+    _check(_lib.mxfp4_dequantize(_p(q), _p(sc), M, K, code, _p(out), _stream(q.device)), "mxfp4_dequantize")
+    return out
+
+
+def mx_linear(x, w_q, w_sc, out_dtype=torch.bfloat16, out=None, ws=None):
+    """Dense MXFP4 linear: y [M][N] = MXFP4(x) @ W^T with W MXFP4 [N][K]."""
+    _require(x, torch.bfloat16, "x")
+    _require(w_q, torch.uint8, "w_q")
+    _require(w_sc, torch.uint8, "w_scale")
+    M, K = x.shape
+    N = w_q.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    code = {torch.bfloat16: 0, torch.float32: 1}[out.dtype]
+    if ws is None:
+        ws = _workspace(_lib.mxfp4_linear_workspace_size(M, K, N), dev)
+    _check(_lib.mxfp4_linear(_p(x), M, K, _p(w_q), _p(w_sc), N, code, _p(out), _p(ws), ws.numel(),
+                             _stream(dev)), "mxfp4_linear")
+    return out
+
+
+def mx_linear_workspace(M, K, N, device):
+    """A dedicated workspace for mxfp4_linear (e.g. for graph capture)."""
+    return torch.empty(max(int(_lib.mxfp4_linear_workspace_size(M, K, N)), 256), dtype=torch.uint8,
                        device=device)
 
 

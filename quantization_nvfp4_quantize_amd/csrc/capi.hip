@@ -237,6 +237,89 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
                     "nvfp4_linear");
 }
 
+// ------------------------------------------------------------------ MXFP4
+// The separately labelled OCP MX v1.0 format (E8M0 scale per 32 elements)
+// on gfx950's scaled FP4 MFMA.
+int mxfp4_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* scale, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || K <= 0 || K % 32 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_quantize: need M >= 0, K > 0, K %% 32 == 0 (M=%lld K=%lld)",
+                (long long)M, (long long)K);
+  if (M == 0) return NVFP4_OK;
+  if (!x || !q || !scale) return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_quantize: x, q and scale must be non-null");
+  if (!aligned(x, 16) || !aligned(q, 4))
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_quantize: x must be 16-byte and q 4-byte aligned");
+  return hip_status(nvfp4::launch_mx_quantize(x, M * K, q, scale, reinterpret_cast<hipStream_t>(stream)),
+                    "mxfp4_quantize");
+}
+
+int mxfp4_dequantize(const uint8_t* q, const uint8_t* scale, int64_t M, int64_t K, int out_dtype, void* out,
+                     void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || K <= 0 || K % 32 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_dequantize: need M >= 0, K > 0, K %% 32 == 0");
+  if (out_dtype != 0 && out_dtype != 1)
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_dequantize: out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (M == 0) return NVFP4_OK;
+  if (!q || !scale || !out) return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_dequantize: null pointer");
+  if (!aligned(q, 4) || !aligned(out, 16))
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_dequantize: q must be 4-byte and out 16-byte aligned");
+  return hip_status(nvfp4::launch_mx_dequantize(q, scale, M * K, out_dtype == 0, out,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "mxfp4_dequantize");
+}
+
+namespace {
+struct MxLayout {
+  size_t xq, xsc, total;
+};
+MxLayout mx_layout(int64_t M, int64_t K) {
+  MxLayout L;
+  L.xq = 0;
+  L.xsc = round_up((size_t)(M * K / 2), 256);
+  L.total = round_up(L.xsc + (size_t)(M * K / 32), 256);
+  return L;
+}
+}  // namespace
+
+size_t mxfp4_linear_workspace_size(int64_t M, int64_t K, int64_t N) {
+  (void)N;
+  if (M < 0 || K <= 0) return 0;
+  return mx_layout(M, K).total;
+}
+
+int mxfp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w_q, const uint8_t* w_scale, int64_t N,
+                 int out_dtype, void* out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || K <= 0 || N <= 0) return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_linear: need M >= 0, K > 0, N > 0");
+  if (out_dtype != 0 && out_dtype != 1)
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_linear: out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (K % nvfp4::mx_gemm_step_k() != 0 || N % nvfp4::mx_gemm_tile() != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED, "mxfp4_linear: need K %% %d == 0 and N %% %d == 0 (K=%lld N=%lld)",
+                nvfp4::mx_gemm_step_k(), nvfp4::mx_gemm_tile(), (long long)K, (long long)N);
+  if (M > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "mxfp4_linear: M too large");
+  if ((__int128)M * (K / 2) > kMaxOperandBytes || (__int128)N * (K / 2) > kMaxOperandBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "mxfp4_linear: an operand exceeds 4 GiB");
+  if (M == 0) return NVFP4_OK;
+  if (!x || !w_q || !w_scale || !out) return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_linear: null pointer");
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_scale, 4) || !aligned(out, 16))
+    return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_linear: misaligned pointer");
+  const MxLayout L = mx_layout(M, K);
+  if (!ws || ws_bytes < L.total)
+    return fail(NVFP4_ERR_WORKSPACE, "mxfp4_linear: workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (!aligned(ws, 256)) return fail(NVFP4_ERR_INVALID_ARG, "mxfp4_linear: ws must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(w + L.xq);
+  uint8_t* xsc = reinterpret_cast<uint8_t*>(w + L.xsc);
+  int st;
+  if ((st = hip_status(nvfp4::launch_mx_quantize(x, M * K, xq, xsc, s), "mxfp4_linear (quantize x)"))) return st;
+  return hip_status(nvfp4::launch_mx_gemm(xq, xsc, M, K, w_q, w_scale, N,
+                                          out_dtype == 1 ? static_cast<float*>(out) : nullptr,
+                                          out_dtype == 0 ? static_cast<uint16_t*>(out) : nullptr, s),
+                    "mxfp4_linear");
+}
+
 // ------------------------------------------------------------------ MoE
 namespace {
 

@@ -99,4 +99,18 @@ hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, 
                           bool bf16_out, void* out, hipStream_t s, const uint16_t* o_f16 = nullptr,
                           const int8_t* o_exp = nullptr);
 
+// ---- mxfp4.hip (OCP MX v1.0 MXFP4: E8M0 scale per 32 elements, E2M1 elements)
+// n bf16 values (n % 32 == 0) -> q [n/2] (element 2i in the low nibble of
+// byte i), sc [n/32] E8M0 codes
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t n, uint8_t* q, uint8_t* sc, hipStream_t s);
+hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* sc, int64_t n, bool bf16_out, void* out,
+                                hipStream_t s);
+// Tile size (rows and columns) and K step of the MXFP4 GEMM.
+int mx_gemm_tile();
+int mx_gemm_step_k();
+// y [M][N] = A @ W^T for MXFP4 A [M][K], W [N][K] (K % mx_gemm_step_k() == 0,
+// N % mx_gemm_tile() == 0) into o (fp32) or o_bf16 when that is non-null.
+hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t M, int64_t K, const uint8_t* w_q,
+                          const uint8_t* w_sc, int64_t N, float* o, uint16_t* o_bf16, hipStream_t s);
+
 }  // namespace nvfp4

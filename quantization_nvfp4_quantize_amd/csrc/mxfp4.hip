@@ -1,0 +1,332 @@
+// MXFP4 quantize, dequantize and GEMM on gfx950: the separately labelled
+// scaled-MFMA variant next to the pages' NVFP4.  MXFP4 is the format of the
+// Open Compute Project "Microscaling Formats (MX) Specification" v1.0: 32
+// consecutive elements share one E8M0 scale (code c = 2^(c - 127), section
+// 5.4), each element is E2M1 (section 5.3.3), there is no tensor scale.  The
+// conversion of section 6.3 sets the shared exponent to floor(log2(max |V|))
+// - 2 and rounds V / 2^exp to nearest E2M1, ties to even, saturating at 6.
+// It is not NVFP4 (E4M3 scale per 16 elements, fp32 tensor scale, the pages'
+// two-stage E2M1 rounding): an NVFP4 block scale is not a power of two, so
+// NVFP4 operands cannot be fed to the scaled MFMA exactly, which is why the
+// NVFP4 GEMMs dequantize to f16.
+//
+// MI355X design:
+//   * Quantize: one lane per 8 elements (a 16 B load), the 4 lanes of a block
+//     take its maximum with two DPP steps; the shared exponent comes straight
+//     from the maximum's exponent bits (code = max(biased exponent - 2, 0):
+//     every subnormal or zero maximum clamps to code 0); the elements are
+//     scaled by the exact power of two 2^(127 - code) and converted with the
+//     gfx950 FP4 conversion, which rounds to nearest even on the E2M1 grid,
+//     saturates at 6 and keeps the sign of zero.
+//   * GEMM: v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 and one
+//     E8M0 scale per lane (row, 32-element K block): the operands go from
+//     HBM straight into LDS and from LDS straight into the MFMA -- no
+//     dequantization at all.  A workgroup of 8 wave64s owns a 256 x 256
+//     output tile, wave w rows 128 (w >> 2) .. +128 and columns 64 (w & 3)
+//     .. +64 as 4 x 2 MFMA tiles; K steps of 128 (two MFMA sub-steps of 64),
+//     operands and scales loaded three steps ahead into four LDS stages.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "gemm_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ quantize
+constexpr int kMxQThreads = 256;
+constexpr int kMxQUnroll = 4;
+constexpr int kMxQChunksPerWG = kMxQThreads * kMxQUnroll;
+
+// Maximum over the 4 lanes of a quad (quad_perm [1,0,3,2], then [2,3,0,1]).
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+}
+
+// E8M0 code of a block whose largest magnitude is m >= 0 (finite):
+// floor(log2(m)) - 2 + 127 = biased exponent - 2 for a normal m, clamped at
+// 0, which also covers subnormal and zero maxima (their exponent is below
+// -126, so the code would be negative).
+__device__ __forceinline__ uint32_t mx_scale_code(float m) {
+  const int ef = (int)(__float_as_uint(m) >> 23);
+  return (uint32_t)max(ef - 2, 0);
+}
+
+// n8 chunks of 8 bf16 (4 chunks per block, n8 % 4 == 0) -> q (one dword of
+// 8 nibbles per chunk, element 2i in the low nibble of byte i), sc (one code
+// per block).
+__global__ __launch_bounds__(kMxQThreads) void mx_quantize_kernel(const uint4* __restrict__ x, int64_t n8,
+                                                                  uint32_t* __restrict__ q,
+                                                                  uint8_t* __restrict__ sc) {
+  const int64_t base = (int64_t)blockIdx.x * kMxQChunksPerWG + threadIdx.x;
+  uint4 w[kMxQUnroll];
+#pragma unroll
+  for (int u = 0; u < kMxQUnroll; ++u) {
+    const int64_t i = base + u * kMxQThreads;
+    w[u] = (i < n8) ? *(x + i) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kMxQUnroll; ++u) {
+    const int64_t i = base + u * kMxQThreads;  // chunks 4b .. 4b + 3 of block b sit in one quad
+    const uint32_t code = mx_scale_code(quad_max(abs_max8(w[u])));
+    const float r = __uint_as_float((254u - code) << 23);  // 2^(127 - code), exact
+    uint32_t p = 0;
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].x) * r, bf16_hi(w[u].x) * r, 1.0f, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].y) * r, bf16_hi(w[u].y) * r, 1.0f, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].z) * r, bf16_hi(w[u].z) * r, 1.0f, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].w) * r, bf16_hi(w[u].w) * r, 1.0f, 3);
+    if (i < n8) {
+      q[i] = p;
+      if ((i & 3) == 0) sc[i >> 2] = (uint8_t)code;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dequantize
+// x = e2m1 * 2^(code - 127), exact (ldexp keeps subnormal results).
+template <bool BF16_OUT>
+__global__ __launch_bounds__(kMxQThreads) void mx_dequantize_kernel(const uint32_t* __restrict__ q,
+                                                                    const uint8_t* __restrict__ sc, int64_t n8,
+                                                                    void* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kMxQThreads + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * kMxQThreads) {
+    const uint32_t p = q[i];
+    const int e = (int)sc[i >> 2] - 127;
+    const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 0);
+    const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 1);
+    const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 2);
+    const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, 3);
+    const float v[8] = {ldexpf(f0[0], e), ldexpf(f0[1], e), ldexpf(f1[0], e), ldexpf(f1[1], e),
+                        ldexpf(f2[0], e), ldexpf(f2[1], e), ldexpf(f3[0], e), ldexpf(f3[1], e)};
+    if (BF16_OUT) {
+      uint32_t h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        h[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * j]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[2 * j + 1]) << 16);
+      reinterpret_cast<uint4*>(out)[i] = make_uint4(h[0], h[1], h[2], h[3]);
+    } else {
+      float4* o = reinterpret_cast<float4*>(out) + 2 * i;
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ GEMM
+constexpr int kMxTile = 256;          // rows and columns of a workgroup tile
+constexpr int kMxThreads = 512;
+constexpr int kMxStepK = 128;         // K per main-loop step
+constexpr int kMxStages = 4;
+constexpr int kMxOperand = kMxTile * (kMxStepK / 2) / 16;  // 16 B chunks of one operand stage (16 KiB)
+constexpr int kMxScales = kMxTile;                         // dwords of one scale stage (1 KiB)
+
+// LDS: A and B stages (256 rows of 64 B = 4 chunks of 32 E2M1 values, logical
+// chunk c of row r stored at c ^ ((r >> 2) & 3), so that the 16 rows a
+// fragment read covers per 16 lanes land on 16 distinct 16 B bank groups),
+// and per stage one dword of 4 scale codes per row.  136 KiB in all.
+struct MxLds {
+  uint4* a;      // kMxStages x kMxOperand
+  uint4* b;      // kMxStages x kMxOperand
+  uint32_t* sa;  // kMxStages x kMxScales
+  uint32_t* sb;
+};
+
+struct MxOperands {
+  const uint8_t* a;    // A nibbles [M][K/2], wave-uniform
+  uint32_t a_off[2];   // this lane's sources: tile rows 32 wave + 16 u + lane / 4
+  const uint8_t* b;    // W nibbles [N][K/2]
+  uint32_t b_off[2];
+  const uint8_t* s;    // scale source of this wave (A scales for waves 0..3, W scales for 4..7)
+  uint32_t s_off;      // this lane's scale row: 64 (wave & 3) + lane of the tile
+};
+
+// Direct loads of step j into stage st: A and B (2 x 1 KiB each per wave),
+// then the wave's 256 B of scales.
+__device__ __forceinline__ void mx_load_step(const MxLds& L, const MxOperands& op, int j, int st, int wave) {
+  const uint8_t* a_src = op.a + (size_t)j * (kMxStepK / 2);
+  const uint8_t* b_src = op.b + (size_t)j * (kMxStepK / 2);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    dma16s(reinterpret_cast<f16x8*>(L.a + st * kMxOperand + (32 * wave + 16 * u) * 4), a_src, op.a_off[u]);
+    dma16s(reinterpret_cast<f16x8*>(L.b + st * kMxOperand + (32 * wave + 16 * u) * 4), b_src, op.b_off[u]);
+  }
+  uint32_t* s_dst = ((wave >> 2) ? L.sb : L.sa) + st * kMxScales + 64 * (wave & 3);
+  dma4s(s_dst, op.s + (size_t)j * (kMxStepK / 32), op.s_off);
+}
+
+__device__ __forceinline__ i32x8 widen(const uint4& v) {
+  i32x4 w = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  return __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+struct MxParams {
+  const uint8_t* a_q;   // [M][K/2]
+  const uint8_t* a_sc;  // [M][K/32]
+  const uint8_t* w_q;   // [N][K/2]
+  const uint8_t* w_sc;  // [N][K/32]
+  int64_t M, K, N;
+  float* o;             // [M][N] fp32 (when o_bf16 is null)
+  uint16_t* o_bf16;     // nullable [M][N] bf16
+};
+
+__global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(MxParams p) {
+  __shared__ uint4 lds_a[kMxStages * kMxOperand];
+  __shared__ uint4 lds_b[kMxStages * kMxOperand];
+  __shared__ uint32_t lds_sa[kMxStages * kMxScales];
+  __shared__ uint32_t lds_sb[kMxStages * kMxScales];
+  const MxLds L{lds_a, lds_b, lds_sa, lds_sb};
+
+  const int ntn = (int)(p.N / kMxTile);
+  const int mtiles = (int)((p.M + kMxTile - 1) / kMxTile);
+  int item;
+  if (!work_item(mtiles * ntn, &item)) return;
+  const int tm = item / ntn, tn = item % ntn;
+  const int64_t m0 = (int64_t)tm * kMxTile, n0 = (int64_t)tn * kMxTile;
+  const int nrows = (int)min((int64_t)kMxTile, p.M - m0);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t K2 = (uint32_t)(p.K / 2), K32 = (uint32_t)(p.K / 32);
+  MxOperands op;
+  op.a = p.a_q + m0 * K2;
+  op.b = p.w_q + n0 * K2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int R = 32 * wave + 16 * u + (lane >> 2);  // tile row; its key (R >> 2) & 3 is (lane >> 4) & 3
+    const uint32_t chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    op.a_off[u] = (uint32_t)min(R, nrows - 1) * K2 + chunk;  // rows past M repeat the last one (never stored)
+    op.b_off[u] = (uint32_t)R * K2 + chunk;
+  }
+  const int srow = 64 * (wave & 3) + lane;
+  if (wave >> 2) {
+    op.s = p.w_sc + n0 * K32;
+    op.s_off = (uint32_t)srow * K32;
+  } else {
+    op.s = p.a_sc + m0 * K32;
+    op.s_off = (uint32_t)min(srow, nrows - 1) * K32;
+  }
+
+  const int nk = (int)(p.K / kMxStepK), last = nk - 1;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) mx_load_step(L, op, min(j, last), j, wave);
+
+  // fragment addresses: row r of the wave's row group mt (A) or column group
+  // nt (B) reads logical chunk 2 s + g at sub-step s; the XOR key of its row
+  // is (lane >> 2) & 3 (row groups start at multiples of 32)
+  const int wm = wave >> 2, wn = wave & 3, g = lane >> 5, r = lane & 31;
+  const int key = (lane >> 2) & 3;
+  const uint4* a_frag[2];
+  const uint4* b_frag[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    a_frag[s] = L.a + (128 * wm + r) * 4 + ((2 * s + g) ^ key);
+    b_frag[s] = L.b + (64 * wn + r) * 4 + ((2 * s + g) ^ key);
+  }
+  const uint32_t* a_scale = L.sa + 128 * wm + r;
+  const uint32_t* b_scale = L.sb + 64 * wn + r;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  for (int kb = 0; kb < nk; ++kb) {
+    const int st = kb & 3;
+    // the step's scales: byte 0 of (dword >> 8 g) is K block g (sub-step
+    // 0), byte 2 is K block 2 + g (sub-step 1)
+    uint32_t sa[4], sb[2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) sa[mt] = a_scale[st * kMxScales + 32 * mt] >> (8 * g);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) sb[nt] = b_scale[st * kMxScales + 32 * nt] >> (8 * g);
+    uint4 fa[2][4], fb[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) fa[s][mt] = a_frag[s][st * kMxOperand + 128 * mt];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) fb[s][nt] = b_frag[s][st * kMxOperand + 128 * nt];
+    }
+    // step kb + 3 into the stage read during step kb - 1
+    mx_load_step(L, op, min(kb + 3, last), (kb + 3) & 3, wave);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (s == 0)
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                widen(fa[0][mt]), widen(fb[0][nt]), acc[mt][nt], 4, 4, 0, (int)sa[mt], 0, (int)sb[nt]);
+          else
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                widen(fa[1][mt]), widen(fb[1][nt]), acc[mt][nt], 4, 4, 2, (int)sa[mt], 2, (int)sb[nt]);
+        }
+    // 5 loads per step: at most 10 outstanding means every load of step
+    // kb - 2 and earlier has landed, which includes step kb + 1
+    wait_vmcnt<10>();
+    lds_barrier();
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  // epilogue: each wave's 32 x 64 blocks through 4 KiB of LDS, rows of 16 B stores
+  L2Params ep{};
+  ep.N = p.N;
+  ep.o = p.o;
+  ep.o_bf16 = p.o_bf16;
+  float* const scratch = reinterpret_cast<float*>(lds_a) + wave * 1024;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (128 * wm + 32 * mt >= nrows) break;  // wave-uniform
+    l2_store_block(ep, acc[mt][0], acc[mt][1], scratch, 128 * wm + 32 * mt, nrows, n0 + 64 * wn, lane,
+                   [&](int rr) { return m0 + rr; }, [&](int) { return 1.0f; });
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_mx_quantize(const uint16_t* x, int64_t n, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t wg = (n8 + kMxQChunksPerWG - 1) / kMxQChunksPerWG;
+  mx_quantize_kernel<<<(unsigned)wg, kMxQThreads, 0, s>>>(reinterpret_cast<const uint4*>(x), n8,
+                                                          reinterpret_cast<uint32_t*>(q), sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_dequantize(const uint8_t* q, const uint8_t* sc, int64_t n, bool bf16_out, void* out,
+                                hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t wg = std::min<int64_t>((n8 + kMxQThreads - 1) / kMxQThreads, 65536);
+  if (bf16_out)
+    mx_dequantize_kernel<true><<<(unsigned)wg, kMxQThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(q), sc,
+                                                                    n8, out);
+  else
+    mx_dequantize_kernel<false><<<(unsigned)wg, kMxQThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(q), sc,
+                                                                     n8, out);
+  return hipGetLastError();
+}
+
+int mx_gemm_tile() { return kMxTile; }
+int mx_gemm_step_k() { return kMxStepK; }
+
+hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_sc, int64_t M, int64_t K, const uint8_t* w_q,
+                          const uint8_t* w_sc, int64_t N, float* o, uint16_t* o_bf16, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  MxParams p{a_q, a_sc, w_q, w_sc, M, K, N, o, o_bf16};
+  const int64_t items = ((M + kMxTile - 1) / kMxTile) * (N / kMxTile);
+  mx_gemm_kernel<<<(unsigned)((items + 7) / 8 * 8), kMxThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -174,3 +174,20 @@ def test_build_scripts_need_no_built_library(tmp_path):
             "assert callable(h.build); "
             "assert 'quantization_nvfp4_quantize_amd' not in sys.modules") % root
     subprocess.run([sys.executable, "-c", code], check=True, cwd=str(tmp_path))
+
+
+def test_mxfp4_rejects_bad_args(lib):
+    """The MXFP4 entry points validate before any launch."""
+    assert lib.mxfp4_quantize(FAKE, 4, 48, FAKE, FAKE, None) == -1  # K % 32
+    assert lib.mxfp4_quantize(None, 4, 64, FAKE, FAKE, None) == -1
+    assert lib.mxfp4_quantize(ctypes.c_void_p(0x10008), 4, 64, FAKE, FAKE, None) == -1  # x misaligned
+    assert lib.mxfp4_quantize(FAKE, 0, 64, None, None, None) == 0  # empty: nothing to do
+    assert lib.mxfp4_dequantize(FAKE, FAKE, 4, 64, 2, FAKE, None) == -1  # out_dtype
+    ws = lib.mxfp4_linear_workspace_size(4, 256, 256)
+    assert ws >= 4 * 256 // 2 + 4 * 256 // 32
+    assert lib.mxfp4_linear(FAKE, 4, 192, FAKE, FAKE, 256, 0, FAKE, FAKE, ws, None) == -2  # K % 128
+    assert lib.mxfp4_linear(FAKE, 4, 256, FAKE, FAKE, 128, 0, FAKE, FAKE, ws, None) == -2  # N % 256
+    assert lib.mxfp4_linear(FAKE, 4, 256, FAKE, FAKE, 256, 0, FAKE, FAKE, ws - 1, None) == -3
+    assert lib.mxfp4_linear(FAKE, 4, 256, None, FAKE, 256, 0, FAKE, FAKE, ws, None) == -1
+    assert lib.mxfp4_linear(FAKE, 4, 256, FAKE, FAKE, 256, 0, FAKE, ctypes.c_void_p(0x10010), ws, None) == -1
+    assert b"mxfp4_linear" in lib.nvfp4_last_error()
