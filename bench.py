@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 MoE expert-FFN hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dense,dec,pre] [--no-cpu] [--no-modes]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dense,mx,dec,pre] [--no-cpu] [--no-modes]
 
 Prints one JSON line.  `value` is the prefill-shaped MoE layer (T16384 H7168
 I2048 E256 top-8: activation global scale + quantize, grouping, L1 GEMM with
@@ -11,6 +11,10 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
             copies (> 256 MiB Infinity Cache); also dynamic scale, dequantize
   expert    single-expert L1 stage M4096 K7168 N 2x2048
   dense     dense NVFP4 linear M4096 K4096 N16384 (quantize x + GEMM, bf16 out)
+  mx        the separately labelled MXFP4 variant (OCP MX v1.0 format, E8M0
+            scale per 32 elements) on the scaled FP4 MFMA: quantize
+            8192 x 7168 and the dense linear M4096 K4096 N16384, against the
+            FP4 MFMA peak
   dec       decode-shaped layer T128 (Zipf routing; weight-streaming bound)
   prefill_unfused / prefill_interleaved / prefill_dynamic  the same prefill
             layer with the L1 output written as bf16 and quantized in a
@@ -42,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0  # dense FP4 (scaled f8f6f4) MFMA
 # intervals between the library's 9 stage events; l1_main / l2_main are the
 # GEMM launches over the main tile list (256-row tiles in the prefill), and
 # l1_rest / l2_rest the 32-row short tiles of the mixed tiling (and, in the
@@ -138,6 +143,8 @@ KERNEL_SOURCES = {
     "amax_partial_kernel": ["quantize.hip", "nvfp4_device.hpp", "launch.hpp"],
     "l1_skinny_kernel": ["gemm_skinny.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
     "l2_skinny_kernel": ["gemm_skinny.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
+    "mx_gemm_kernel": ["mxfp4.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
+    "mx_quantize_kernel": ["mxfp4.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
@@ -503,6 +510,39 @@ def bench_dense(nv, steps, warmup):
                 frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
 
 
+def bench_mx(nv, steps, warmup):
+    """The separately labelled MXFP4 variant (OCP MX v1.0: E8M0 scale per 32
+    elements) on the scaled FP4 MFMA: quantize 8192 x 7168 (inputs rotated
+    like the NVFP4 quantize leg) and the dense linear M4096 K4096 N16384
+    (activation quantization + GEMM, bf16 out), against the FP4 MFMA peak."""
+    import synth
+    dev = torch.device("cuda:0")
+    M, K = synth.QUANT_SHAPE
+    n = M * K
+    x0 = torch.from_numpy(synth.quant_tensor().view(np.int16)).view(torch.bfloat16).to(dev)
+    ncopy = 5
+    xs = [x0] + [x0.clone() for _ in range(ncopy - 1)]
+    outs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+             torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) for _ in range(ncopy)]
+    q_ms = graph_time(lambda i: nv.mx_quantize(xs[i % ncopy], out=outs[i % ncopy]), steps, warmup)
+    qbytes = 2 * n + n // 2 + n // 32
+    del xs, outs
+    Md, Kd, Nd = synth.DENSE_SHAPE["M"], synth.DENSE_SHAPE["K"], synth.DENSE_SHAPE["N"]
+    xb, w = synth.dense_problem(Md, Kd, Nd, device=dev)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, wsc = nv.mx_quantize(w)
+    del w
+    out = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+    ws = nv.mx_linear_workspace(Md, Kd, Nd, dev)
+    l_ms = graph_time(lambda i: nv.mx_linear(x, wq, wsc, out=out, ws=ws), steps, warmup)
+    flops = 2.0 * Md * Nd * Kd
+    return dict(format="MXFP4 (OCP MX v1.0, E8M0 scale per 32 elements; not NVFP4)",
+                quantize_shape=[M, K], quantize_algorithmic_bytes=qbytes, quantize_ms=q_ms,
+                quantize_GBps=qbytes / q_ms / 1e6, quantize_frac=qbytes / q_ms / 1e6 / HBM_PEAK_GBS,
+                linear_workload=f"M{Md} K{Kd} N{Nd}", linear_ms=l_ms, linear_TFLOPs=flops / l_ms / 1e9,
+                linear_algorithmic_flops=flops, linear_frac_fp4_peak=flops / l_ms / 1e9 / FP4_PEAK_TFLOPS)
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline_moe(cfg, x_bits, ids, wts, ntok=8):
     """The oracle on a bounded sample of the prefill layer: ntok tokens (all
@@ -564,7 +604,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="quant,expert,dense,dec,pre")
+    ap.add_argument("--legs", default="quant,expert,dense,mx,dec,pre")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the unfused and dynamic-scale runs of the prefill layer")
@@ -608,6 +648,10 @@ def main():
     if "dense" in legs:
         res["dense_linear"] = bench_dense(nv, args.steps, args.warmup)
         print("# dense done", flush=True, file=sys.stderr)
+    if "mx" in legs:
+        res["mxfp4"] = bench_mx(nv, args.steps, args.warmup)
+        print("# mxfp4 done", flush=True, file=sys.stderr)
+        torch.cuda.empty_cache()
     if "dec" in legs:
         res["decode"], _ = bench_moe(nv, synth.DEC, args.steps, args.warmup)
         print("# decode done", flush=True, file=sys.stderr)

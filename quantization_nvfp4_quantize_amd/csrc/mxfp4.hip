@@ -24,7 +24,9 @@
 //     dequantization at all.  A workgroup of 8 wave64s owns a 256 x 256
 //     output tile, wave w rows 128 (w >> 2) .. +128 and columns 64 (w & 3)
 //     .. +64 as 4 x 2 MFMA tiles; K steps of 128 (two MFMA sub-steps of 64),
-//     operands and scales loaded three steps ahead into four LDS stages.
+//     operands and scales loaded four steps ahead into four LDS stages, and
+//     each step's fragments read from LDS one step ahead into registers, so
+//     that the MFMAs never wait for LDS.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,6 +41,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------ quantize
 constexpr int kMxQThreads = 256;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load (non-temporal: the data is read once).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 constexpr int kMxQUnroll = 4;
 constexpr int kMxQChunksPerWG = kMxQThreads * kMxQUnroll;
 
@@ -68,7 +78,7 @@ __global__ __launch_bounds__(kMxQThreads) void mx_quantize_kernel(const uint4* _
 #pragma unroll
   for (int u = 0; u < kMxQUnroll; ++u) {
     const int64_t i = base + u * kMxQThreads;
-    w[u] = (i < n8) ? *(x + i) : make_uint4(0, 0, 0, 0);
+    w[u] = (i < n8) ? load_stream(x + i) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < kMxQUnroll; ++u) {
@@ -80,9 +90,9 @@ __global__ __launch_bounds__(kMxQThreads) void mx_quantize_kernel(const uint4* _
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].y) * r, bf16_hi(w[u].y) * r, 1.0f, 1);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].z) * r, bf16_hi(w[u].z) * r, 1.0f, 2);
     p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, bf16_lo(w[u].w) * r, bf16_hi(w[u].w) * r, 1.0f, 3);
-    if (i < n8) {
-      q[i] = p;
-      if ((i & 3) == 0) sc[i >> 2] = (uint8_t)code;
+    if (i < n8) {  // not read back by this pass: streaming stores
+      __builtin_nontemporal_store(p, q + i);
+      if ((i & 3) == 0) __builtin_nontemporal_store((uint8_t)code, sc + (i >> 2));
     }
   }
 }
@@ -125,6 +135,7 @@ constexpr int kMxStepK = 128;         // K per main-loop step
 constexpr int kMxStages = 4;
 constexpr int kMxOperand = kMxTile * (kMxStepK / 2) / 16;  // 16 B chunks of one operand stage (16 KiB)
 constexpr int kMxScales = kMxTile;                         // dwords of one scale stage (1 KiB)
+constexpr int kMxGroupRows = 4;                            // row tiles per group of the work order
 
 // LDS: A and B stages (256 rows of 64 B = 4 chunks of 32 E2M1 values, logical
 // chunk c of row r stored at c ^ ((r >> 2) & 3), so that the 16 rows a
@@ -186,7 +197,14 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(MxParams p) {
   const int mtiles = (int)((p.M + kMxTile - 1) / kMxTile);
   int item;
   if (!work_item(mtiles * ntn, &item)) return;
-  const int tm = item / ntn, tn = item % ntn;
+  // Items in groups of kMxGroupRows row tiles, row tile fastest inside a
+  // group: the 32 workgroups that run together on one XCD (contiguous items)
+  // then cover 4 row tiles x 8 column tiles, 12 operand tiles instead of the
+  // 33 of a row-major order, which keeps most of their loads in the XCD's L2.
+  const int group = item / (kMxGroupRows * ntn);
+  const int tm0 = group * kMxGroupRows, gm = min(kMxGroupRows, mtiles - tm0);
+  const int within = item - group * kMxGroupRows * ntn;
+  const int tm = tm0 + within % gm, tn = within / gm;
   const int64_t m0 = (int64_t)tm * kMxTile, n0 = (int64_t)tn * kMxTile;
   const int nrows = (int)min((int64_t)kMxTile, p.M - m0);
 
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(MxParams p) {
 
   const int nk = (int)(p.K / kMxStepK), last = nk - 1;
 #pragma unroll
-  for (int j = 0; j < 3; ++j) mx_load_step(L, op, min(j, last), j, wave);
+  for (int j = 0; j < kMxStages; ++j) mx_load_step(L, op, min(j, last), j, wave);
 
   // fragment addresses: row r of the wave's row group mt (A) or column group
   // nt (B) reads logical chunk 2 s + g at sub-step s; the XOR key of its row
@@ -236,45 +254,77 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(MxParams p) {
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
-  wait_vmcnt<0>();
-  lds_barrier();
 
-  for (int kb = 0; kb < nk; ++kb) {
-    const int st = kb & 3;
-    // the step's scales: byte 0 of (dword >> 8 g) is K block g (sub-step
-    // 0), byte 2 is K block 2 + g (sub-step 1)
-    uint32_t sa[4], sb[2];
+  // The sub-step s fragments of stage st, and the stage's scale dwords
+  // shifted so that byte 0 is the K block of sub-step 0 and byte 2 that of
+  // sub-step 1 for this lane's half g.
+  auto read_frags = [&](int st, int s, uint4 (&fa)[4], uint4 (&fb)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) fa[mt] = a_frag[s][st * kMxOperand + 128 * mt];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) fb[nt] = b_frag[s][st * kMxOperand + 128 * nt];
+  };
+  auto read_scales = [&](int st, uint32_t (&sa)[4], uint32_t (&sb)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) sa[mt] = a_scale[st * kMxScales + 32 * mt] >> (8 * g);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) sb[nt] = b_scale[st * kMxScales + 32 * nt] >> (8 * g);
-    uint4 fa[2][4], fb[2][2];
+  };
+  // the 8 MFMAs of one sub-step (OPSEL 0: sub-step 0, scale byte 0; 2:
+  // sub-step 1, scale byte 2)
+  auto mfmas0 = [&](const uint4 (&fa)[4], const uint4 (&fb)[2], const uint32_t (&sa)[4], const uint32_t (&sb)[2]) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) fa[s][mt] = a_frag[s][st * kMxOperand + 128 * mt];
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fa[mt]), widen(fb[nt]), acc[mt][nt],
+                                                                     4, 4, 0, (int)sa[mt], 0, (int)sb[nt]);
+  };
+  auto mfmas1 = [&](const uint4 (&fa)[4], const uint4 (&fb)[2], const uint32_t (&sa)[4], const uint32_t (&sb)[2]) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) fb[s][nt] = b_frag[s][st * kMxOperand + 128 * nt];
-    }
-    // step kb + 3 into the stage read during step kb - 1
-    mx_load_step(L, op, min(kb + 3, last), (kb + 3) & 3, wave);
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fa[mt]), widen(fb[nt]), acc[mt][nt],
+                                                                     4, 4, 2, (int)sa[mt], 2, (int)sb[nt]);
+  };
+
+  // Software pipeline, one step kb per iteration: c0 holds the step's
+  // sub-step 0 fragments (and sa, sb its scales), read during the previous
+  // iteration.  Read the sub-step 1 fragments c1 while the sub-step 0 MFMAs
+  // run; then the barrier, which ends every wave's reads of stage kb and
+  // publishes stage kb + 1; then read the sub-step 0 fragments and scales of
+  // step kb + 1 (a stale but valid stage in the last iteration), load step
+  // kb + 4 into the stage of step kb, and run the sub-step 1 MFMAs while
+  // those reads land.  The iteration is one basic block with scheduling
+  // fences between its phases, so the barrier stays between the two MFMA
+  // groups.  5 loads per step: at most 10 outstanding at the barrier means
+  // every load of step kb - 3 and earlier has landed, including step kb + 1.
+  uint4 c0a[4], c0b[2], c1a[4], c1b[2];
+  uint32_t sa[4], sb[2], sa1[4], sb1[2];
+  wait_vmcnt<0>();
+  lds_barrier();
+  read_scales(0, sa, sb);
+  read_frags(0, 0, c0a, c0b);
+  for (int kb = 0; kb < nk; ++kb) {
+    const int st = kb & 3;
+    read_frags(st, 1, c1a, c1b);
+    SCHED_FENCE();
+    mfmas0(c0a, c0b, sa, sb);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) sa1[mt] = sa[mt];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          if (s == 0)
-            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                widen(fa[0][mt]), widen(fb[0][nt]), acc[mt][nt], 4, 4, 0, (int)sa[mt], 0, (int)sb[nt]);
-          else
-            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                widen(fa[1][mt]), widen(fb[1][nt]), acc[mt][nt], 4, 4, 2, (int)sa[mt], 2, (int)sb[nt]);
-        }
-    // 5 loads per step: at most 10 outstanding means every load of step
-    // kb - 2 and earlier has landed, which includes step kb + 1
+    for (int nt = 0; nt < 2; ++nt) sb1[nt] = sb[nt];
+    SCHED_FENCE();
     wait_vmcnt<10>();
     lds_barrier();
+    SCHED_FENCE();
+    read_scales((kb + 1) & 3, sa, sb);
+    read_frags((kb + 1) & 3, 0, c0a, c0b);
+    mx_load_step(L, op, min(kb + kMxStages, last), st, wave);
+    SCHED_FENCE();
+    mfmas1(c1a, c1b, sa1, sb1);
+    SCHED_FENCE();
   }
   wait_vmcnt<0>();
   lds_barrier();
