@@ -499,8 +499,18 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   // tile, column tile and this lane's operand sources of an item
   auto setup = [&](int it, GemmTile& t, int& nt, Operands& op, int tid_s) {
     const int lane = tid_s & 63, wave = tid_s >> 6;
-    const int ti = it / p.n_ntiles;
-    nt = it % p.n_ntiles;
+    // Dense (unrouted) rows: items in groups of 4 row tiles, row tile
+    // fastest inside a group, so the workgroups running together on an XCD
+    // share 4 A tiles and 8 weight tiles in its L2 instead of 1 A tile and
+    // 32 weight tiles (-2 % on M4096 K4096 N16384).  Routed tiles keep the
+    // row-tile-major order: an expert's 2-3 row tiles already run together,
+    // and grouping them measured slower.
+    const int gr = p.tiles ? 1 : 4;
+    const int group = it / (gr * p.n_ntiles);
+    const int t0 = group * gr, gm = min(gr, mtiles - t0);
+    const int within = it - group * gr * p.n_ntiles;
+    const int ti = t0 + within % gm;
+    nt = within / gm;
     if (p.tiles) {
       t = p.tiles[ti];
     } else {
