@@ -300,15 +300,18 @@ def trace_summary(legs, cmd):
 # ------------------------------------------------------------------ MFMA utilisation
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.md")
 XCDS, SIMDS = 8, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+# MFMA operation counters (512 flops per MOP): f16 for the NVFP4 GEMMs, f6f4
+# for the MXFP4 GEMM's scaled FP4 MFMA
+MFMA_MOPS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
 
 
 def mfma_summary(legs, cmd):
     """Markdown table of rocprofv3 counter runs (SQ_VALU_MFMA_BUSY_CYCLES,
-    GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_F16) for the GEMM kernels, one
+    GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_F16 / _F6F4) for the GEMM kernels, one
     run per bench leg (legs = [(leg, counter_csv)]).  Per dispatch: MFMA
     busy fraction = busy cycles summed over the SIMDs / (active cycles of one
     XCD x 1024 SIMDs), effective clock = active cycles of one XCD / duration,
-    and the f16 MFMA flops the counter reports (512 per MOP)."""
+    and the MFMA flops the counters report (512 per MOP)."""
     import collections
     import csv
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
@@ -327,20 +330,21 @@ def mfma_summary(legs, cmd):
            "in the table):", "", "    " + cmd, "",
            f"Per dispatch: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs)",
            f"(rocprofv3 reports GRBM_GUI_ACTIVE summed over the {XCDS} XCDs); clock = GRBM_GUI_ACTIVE / {XCDS} /",
-           "duration; MFMA TFLOP/s = 512 x SQ_INSTS_VALU_MFMA_MOPS_F16 / duration.  Durations are those of the",
-           "counter runs.", "",
+           "duration; MFMA TFLOP/s = 512 x (SQ_INSTS_VALU_MFMA_MOPS_F16 + SQ_INSTS_VALU_MFMA_MOPS_F6F4) /",
+           "duration.  Durations are those of the counter runs.", "",
            "| leg | kernel | grid | dispatches | avg us | clock GHz | MFMA busy | MFMA TFLOP/s |",
            "|---|---|---|---|---|---|---|---|"]
     js = []
     for (leg, k, g), c in sorted(agg.items()):
-        need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_F16")
-        if not all(n in c for n in need):
+        need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+        mops = [m for m in MFMA_MOPS if m in c]
+        if not all(n in c for n in need) or not mops:
             continue
         n = len(c["GRBM_GUI_ACTIVE"])
         busy = np.mean([x for x, _ in c["SQ_VALU_MFMA_BUSY_CYCLES"]])
         gui = np.mean([x for x, _ in c["GRBM_GUI_ACTIVE"]]) / XCDS
         dur = np.mean([d for _, d in c["GRBM_GUI_ACTIVE"]])
-        flops = 512.0 * np.mean([x for x, _ in c["SQ_INSTS_VALU_MFMA_MOPS_F16"]])
+        flops = 512.0 * sum(np.mean([x for x, _ in c[m]]) for m in mops)
         util, clk = busy / (gui * SIMDS), gui / dur / 1e9
         out.append(f"| {leg} | {k} | {g} | {n} | {dur * 1e6:.1f} | {clk:.2f} | {100 * util:.1f} % | "
                    f"{flops / dur / 1e12:.0f} |")
