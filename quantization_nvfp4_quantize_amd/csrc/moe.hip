@@ -32,6 +32,8 @@
 
 namespace nvfp4 {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kRouteThreads = 1024;
 constexpr int kSchedCounters = 16;  // the GEMMs' work counters, zeroed with the grouping
 constexpr int kRouteWaves = kRouteThreads / 64;
@@ -328,8 +330,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // The same sum over the f16 form of o: o16[r][c] * 2^oexp[r][c / 32] (exact
-// in fp32), 8 columns per thread.
-template <bool BF16_OUT>
+// in fp32), 8 columns per thread.  With k <= KMAX the k expert ids and then
+// the k rows are all loaded before the first addition (streaming loads: each
+// row is read once), so a thread keeps k loads in flight; the sum still runs
+// in the fixed order j = 0 .. k - 1.  KMAX = 0: a plain loop for any k.
+template <bool BF16_OUT, int KMAX>
 __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __restrict__ o16,
                                                           const int8_t* __restrict__ oexp,
                                                           const int32_t* __restrict__ ids, int E,
@@ -340,26 +345,53 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __rest
        i += (int64_t)gridDim.x * 256) {
     const int64_t t = i / n8, c = (i % n8) * 8;
     float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int64_t r = t * k + j;
-      const int e = ids[r];
-      if (e < 0 || e >= E) continue;
-      const uint4 v = *reinterpret_cast<const uint4*>(o16 + r * H + c);
-      const int s = oexp[r * nb + c / 32];
+    auto add = [&](const uint4& v, int s) {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         y[2 * q] += ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] & 0xffffu)), s);
         y[2 * q + 1] += ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(w[q] >> 16)), s);
       }
+    };
+    if (KMAX > 0) {
+      bool ok[KMAX > 0 ? KMAX : 1];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const int e = j < k ? ids[t * k + j] : -1;
+        ok[j] = e >= 0 && e < E;
+      }
+      uint4 v[KMAX > 0 ? KMAX : 1];
+      int s[KMAX > 0 ? KMAX : 1];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        const int64_t r = t * k + j;
+        if (ok[j]) {
+          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o16 + r * H + c));
+          v[j] = make_uint4(x.x, x.y, x.z, x.w);
+          s[j] = oexp[r * nb + c / 32];
+        } else {
+          v[j] = make_uint4(0, 0, 0, 0);
+          s[j] = 0;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (ok[j]) add(v[j], s[j]);
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int64_t r = t * k + j;
+        const int e = ids[r];
+        if (e < 0 || e >= E) continue;
+        add(*reinterpret_cast<const uint4*>(o16 + r * H + c), oexp[r * nb + c / 32]);
+      }
     }
     if (BF16_OUT) {
       __bf16 h[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) h[q] = (__bf16)y[q];
-      uint4 u;
+      u32x4 u;
       __builtin_memcpy(&u, h, 16);
-      reinterpret_cast<uint4*>(out)[(t * H + c) / 8] = u;
+      __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(out) + (t * H + c) / 8);
     } else {
       float4* dst = reinterpret_cast<float4*>(out) + (t * H + c) / 4;
       dst[0] = make_float4(y[0], y[1], y[2], y[3]);
@@ -409,10 +441,16 @@ hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, 
     const int64_t n = T * (H / 8);
     if (n == 0) return hipSuccess;
     const int64_t wg = std::min<int64_t>((n + 255) / 256, 65536);
-    if (bf16_out)
-      combine_f16_kernel<true><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
-    else
-      combine_f16_kernel<false><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+    if (k <= 8) {
+      if (bf16_out)
+        combine_f16_kernel<true, 8><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+      else
+        combine_f16_kernel<false, 8><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+    } else if (bf16_out) {
+      combine_f16_kernel<true, 0><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+    } else {
+      combine_f16_kernel<false, 0><<<(unsigned)wg, 256, 0, s>>>(o_f16, o_exp, ids, E, T, k, H, out);
+    }
     return hipGetLastError();
   }
   int64_t n = T * (H / 4);
