@@ -206,6 +206,32 @@ def test_moe_largest_expert_count_and_topk(nv, orc, tile_rows):
     _gate(*res[:4])
 
 
+@pytest.mark.parametrize("topk", [2, 32])
+def test_moe_bf16_combine_skipped_pairs(nv, orc, topk):
+    """The bf16-output combine (f16 per-pair rows) with skipped pairs (invalid
+    expert ids) at top-2 (all k rows loaded before the sum) and at top-32
+    (the loop for k above 8): against the fp32-output run of the same
+    routing, and against the oracle."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=40, E=512 if topk == 32 else 8, topk=topk, name=f"bf16k{topk}")
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    ids = ids.copy()
+    ids[3, 0] = -1
+    ids[7, topk - 1] = cfg.E
+    ids[11, :] = -1  # a token without any valid pair: y = 0
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16)
+    y32, _ = _gpu_moe(nv, cfg, w, x, ids, wts)
+    assert host(dbg["err_count"])[0] == 2 + topk
+    assert np.all(host_bits(y)[11] == 0)
+    _check_bf16_vs_fp32(y, y32)
+    ref = oracle_tokens(orc, cfg, x, ids, wts, np.arange(cfg.T), device="cuda:0")
+    yb = synth.bf16_values(host_bits(y))
+    yo = synth.bf16_values(synth.bf16_bits(ref["y"]))
+    assert rel_fro(yb, yo) <= 5e-3 and cosine(yb, yo) >= 0.9999
+
+
 @pytest.mark.parametrize("H,I", [(1280, 768), (1024, 512), (256, 1280)])
 def test_moe_skinny_k_schedules(nv, orc, H, I):
     """32-row tiles with reduction lengths whose 256-K super-steps leave a
