@@ -13,6 +13,7 @@
 namespace nvfp4 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kStepK = 64;    // K per main-loop step (4 MFMA sub-steps of 16)
 constexpr int kTileN = 256;   // B rows (output columns of the GEMM) per workgroup
@@ -255,37 +256,33 @@ __device__ __forceinline__ int f16_block_exp(float m) {
 }
 
 // Epilogue writer of the L2 / linear GEMMs for one wave's 32-row x 64-column
-// output block: the MFMA tiles a0 (columns col0 + lane % 32) and a1 (columns
-// col0 + 32 + lane % 32) hold rows r0 + acc_row(i, lane), of which those
-// below nrows are valid; row_of(r) gives the output row of tile row r and
-// scale_of(r) its factor.  Each 32 x 32 half goes through the wave's 4 KiB
-// LDS scratch (row r stored at r ^ ((r >> 2) & 1), so that the two row
-// groups a write instruction covers land in different bank halves); then
-// lane l holds the 16 consecutive values 16 (l & 1) .. of row l / 2, scales
-// them and stores them with 16 B writes: fp32 (o), bf16 (o_bf16), or f16
-// with one exponent per (row, 32 columns) (o_f16, o_exp).  For the f16 form
-// the row factor sc is applied as sc * 2^-e: rounding is monotonic, so the
-// largest |a * sc| of the block is max |a| * |sc|, and a * (sc * 2^-e) equals
-// (a * sc) * 2^-e.  (The accumulators are sums of exact products of NVFP4
-// values, so a nonzero max |a| is at least 2^-20 and sc * 2^-e stays
-// finite.)  Every lane of the wave must take part.
-template <class RowOf, class ScaleOf>
-__device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& a0, const f32x16& a1,
-                                               float* scratch, int r0, int nrows, int64_t col0, int lane,
-                                               RowOf row_of, ScaleOf scale_of) {
+// output block of rows r0 + 0..31, of which those below nrows are valid;
+// row_of(r) gives the output row of tile row r and scale_of(r) its factor.
+// Each 32 x 32 half (columns col0 + 32 half ..) goes through the wave's 4 KiB
+// LDS scratch: fill(half, scratch) stores element (r, c) of the half at
+// scratch[32 (r ^ ((r >> 2) & 1)) + c] (the two row groups of an MFMA
+// accumulator write land in different bank halves); then lane l holds the
+// 16 consecutive values 16 (l & 1) .. of row l / 2, scales them and stores
+// them with 16 B writes: fp32 (o), bf16 (o_bf16), or f16 with one exponent
+// per (row, 32 columns) (o_f16, o_exp).  For the f16 form the row factor sc
+// is applied as sc * 2^-e: rounding is monotonic, so the largest |a * sc| of
+// the block is max |a| * |sc|, and a * (sc * 2^-e) equals (a * sc) * 2^-e.
+// (The accumulators are sums of exact products of NVFP4 values, so a nonzero
+// max |a| is at least 2^-20 and sc * 2^-e stays finite.)  Every lane of the
+// wave must take part.
+__device__ __forceinline__ int l2_scratch_index(int r, int c) { return 32 * (r ^ ((r >> 2) & 1)) + c; }
+
+template <class Fill, class RowOf, class ScaleOf>
+__device__ __forceinline__ void l2_store_rows(const L2Params& p, float* scratch, int r0, int nrows, int64_t col0,
+                                              int lane, Fill fill, RowOf row_of, ScaleOf scale_of) {
   const int rr = lane >> 1, h = lane & 1;
   const bool valid = r0 + rr < nrows;
   const int64_t orow = valid ? (int64_t)row_of(r0 + rr) : 0;
   const float sc = valid ? scale_of(r0 + rr) : 0.0f;
-  const float* src = scratch + 32 * (rr ^ ((rr >> 2) & 1)) + 16 * h;
+  const float* src = scratch + l2_scratch_index(rr, 16 * h);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const f32x16& a = half ? a1 : a0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = acc_row(i, lane);
-      scratch[32 * (r ^ ((r >> 2) & 1)) + (lane & 31)] = a[i];
-    }
+    fill(half, scratch);
     float v[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -333,6 +330,21 @@ __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& 
         dst[q] = make_float4(v[4 * q] * sc, v[4 * q + 1] * sc, v[4 * q + 2] * sc, v[4 * q + 3] * sc);
     }
   }
+}
+
+// The same for the accumulators of two 32 x 32 MFMA tiles: a0 holds columns
+// col0 + lane % 32 and a1 columns col0 + 32 + lane % 32, at rows
+// acc_row(i, lane).
+template <class RowOf, class ScaleOf>
+__device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& a0, const f32x16& a1,
+                                               float* scratch, int r0, int nrows, int64_t col0, int lane,
+                                               RowOf row_of, ScaleOf scale_of) {
+  auto fill = [&](int half, float* sc) {
+    const f32x16& a = half ? a1 : a0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[l2_scratch_index(acc_row(i, lane), lane & 31)] = a[i];
+  };
+  l2_store_rows(p, scratch, r0, nrows, col0, lane, fill, row_of, scale_of);
 }
 
 

@@ -9,24 +9,27 @@
 // bytes one CU keeps in flight are far below what HBM latency needs; with few
 // rows the MFMAs are idle anyway.  Here:
 //   * A workgroup of 4 waves owns 32 rows x 256 B rows (output columns); wave
-//     w owns B rows 64 w .. +64 as two 32-column MFMA tiles (for L1: the gate
-//     and the up rows of the same 32 SwiGLU columns, so SwiGLU stays within a
-//     lane), 32 fp32 accumulators per lane.
-//   * K advances in super-steps of 256 (four MFMA steps of 64).  The K order
-//     inside a super-step is permuted identically for A and B so that lane
-//     half g of a column holds the contiguous K range [128 g, 128 g + 128):
-//     the two lanes of a column read one whole 128 B line of nibbles with
-//     four back-to-back 16 B loads (plus 8 scale bytes), so every line of the
-//     weight stream is used by loads issued together instead of by loads one
-//     K step apart, which the L2 would have to keep the line for.
-//   * Weights never touch LDS: each lane loads its super-step of nibbles and
-//     scales straight into registers one super-step ahead (two register sets)
-//     and dequantizes them to exact f16 in registers (each weight once).
+//     w owns B rows 64 w .. +64 as four 16-column tiles of the 16x16x32 f16
+//     MFMA (for L1: gate columns 0..15, 16..31, then the up columns 0..15,
+//     16..31 of the same 32 SwiGLU columns, so SwiGLU stays within a lane),
+//     and both 16-row halves of the tile: 32 fp32 accumulators per lane.
+//   * Weights never touch LDS: each lane loads its 16 B pieces of nibbles
+//     straight into registers one super-step (256 K) ahead, two register
+//     sets, and dequantizes them to exact f16 in registers (each weight
+//     once).  The 16x16x32 operand layout (lane = column l % 16, four lanes
+//     per column) lets each load instruction cover 16 weight rows x 64
+//     contiguous bytes: loads that touch 32 rows each (the 32x32x16 operand
+//     layout) stream at ~5.2 TB/s on this part, 16-row loads at ~6.3 TB/s.
+//   * K order: in a super-step, lane group g = lane / 16 holds the nibbles
+//     of K [128 h + 32 g, +32) (h = 0, 1: its two loads), and MFMA step
+//     (h, s) takes K [128 h + 32 g + 8 s, +8) from it.  The activations use
+//     the same order.
 //   * The 32 activation rows (exact f16) of a super-step go to one of two LDS
-//     buffers with direct-to-LDS loads issued one super-step ahead; one
-//     LDS-only barrier per super-step.
-//   * 32 KiB of LDS and at most 168 VGPRs, so three workgroups (12 waves)
-//     share a CU.
+//     buffers with direct-to-LDS loads issued one super-step ahead (region j
+//     of a buffer holds K [64 j, 64 j + 64)); one LDS-only barrier per
+//     super-step.
+//   * 32 KiB of LDS for the activations plus 18 KiB of scales, and at most
+//     168 VGPRs, so three workgroups (12 waves) share a CU.
 #include <hip/hip_runtime.h>
 
 #include "gemm_common.hpp"
@@ -46,20 +49,21 @@ constexpr int kSkABuf = kSkSteps * kSkAStage;       // one super-step of A (16 K
 // q = 4 m g + 4 j + s, for A and for B alike.
 struct SkOperands {
   const uint8_t* a;     // A matrix (f16 rows of K), wave-uniform
-  uint32_t a_base;      // this lane's A row (tile row 8 wave + lane / 8) + 16 (c & 3)
-  uint32_t a_hi;        // 64 (c >> 2); c = (lane & 7) ^ key(row) is the logical chunk it fetches
+  uint32_t a_base;      // this lane's A row (tile row 8 wave + lane / 8) + 16 c, c = (lane & 7) ^ key(row)
   const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
-  uint32_t bq_row[2];   // byte offsets of this lane's column rows (tile rows 64 wave + 32 nt + lane % 32)
-  uint32_t sf_dma[4];   // scale-row offsets of the tile rows 64 wave + 16 i + lane / 4 (i < 4)
-  int sf_tr[4];         // those tile rows
-  int g;                // lane half
+  uint32_t bq_row[4];   // byte offsets of this lane's column rows (tile rows 64 wave + 16 ct + lane % 16)
+  uint32_t sf_dma;      // scale-row offset of the tile row 64 wave + lane / 4
+  uint32_t sf_step[4];  // wave-uniform: from it to the scale rows of the tile rows 64 wave + 16 i + lane / 4
+  int sf_c;             // the 16 B chunk (super-step) this lane fetches in those rows: (lane & 3) ^
+                        // sk_sf_swz(row), the same for the four rows (sk_sf_swz(row) = (lane >> 4) & 3)
+  int g;                // lane group (lane / 16)
 };
 
-// The nibbles of one super-step in a lane: for each column tile nt, the 16 B
-// of each MFMA step j.
+// The nibbles of one super-step in a lane: for each column tile ct, the
+// 16 B of K [128 h + 32 g, +32) (h = 0, 1; a K tail of 128 has h = 0 only).
 struct SkB {
-  uint4 q[2][kSkSteps];
+  uint4 q[4][2];
 };
 
 // Scales in LDS.  Every 256 K (one super-step) a weight row has 16 scale
@@ -78,26 +82,27 @@ __device__ __forceinline__ int sk_sf_swz(int tr) { return (tr >> 2) & 3; }
 // the K steps are not a multiple of 4).
 __device__ __forceinline__ int sk_steps(int ss, int nfull) { return ss < nfull ? kSkSteps : 2; }
 
-// Direct loads of A for super-step ss into buf: step j's 32 rows x 128 B;
-// wave w fetches rows 8 w .. 8 w + 7 (1 KiB per step).  A tail super-step
-// loads its two steps twice (the second copy is not read).
+// Direct loads of A for super-step ss into buf: region j holds K [64 j,
+// 64 j + 64) of the 32 rows (128 B each, 16 B chunk c at c ^ key(row)); wave
+// w fetches rows 8 w .. 8 w + 7 (1 KiB per region).  A tail super-step (m =
+// 2 steps) loads its two regions twice (the second copy is not read).
 __device__ __forceinline__ void sk_load_a(f16x8* buf, const SkOperands& op, int ss, int m, int wave) {
   const uint8_t* base = op.a + (size_t)ss * (kSkSteps * kStepK * 2);
-  const uint32_t off = op.a_hi * (uint32_t)m + op.a_base;
 #pragma unroll
-  for (int j = 0; j < kSkSteps; ++j) dma16s(buf + j * kSkAStage + wave * 64, base, off + 64u * (j & (m - 1)));
+  for (int j = 0; j < kSkSteps; ++j)
+    dma16s(buf + j * kSkAStage + wave * 64, base, op.a_base + 128u * (uint32_t)(j & (m - 1)));
 }
 
-// Nibbles of super-step ss: four 16 B loads of consecutive addresses per
-// column tile (one 128 B line for the two lanes of a column); a tail
-// super-step repeats its two steps.
+// Nibbles of super-step ss: per column tile, the 16 B of K [128 h + 32 g,
+// +32) for h = 0, 1 (h = 0 only in a tail super-step): each load covers 16
+// weight rows x 64 contiguous bytes.
 __device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int ss, int m) {
   SkB b;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const uint8_t* q = op.bq + (size_t)ss * (kSkSteps * kStepK / 2) + op.bq_row[nt] + 16 * m * op.g;
+  for (int ct = 0; ct < 4; ++ct) {
+    const uint8_t* q = op.bq + (size_t)ss * (kSkSteps * kStepK / 2) + op.bq_row[ct] + 16 * op.g;
 #pragma unroll
-    for (int j = 0; j < kSkSteps; ++j) b.q[nt][j] = *reinterpret_cast<const uint4*>(q + 16 * (j & (m - 1)));
+    for (int h = 0; h < 2; ++h) b.q[ct][h] = *reinterpret_cast<const uint4*>(q + 64 * (h & (m >> 2)));
   }
   return b;
 }
@@ -108,9 +113,8 @@ __device__ __forceinline__ void sk_load_sf_macro(uint8_t* sfbuf, const SkOperand
                                                  int wave, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = (lane & 3) ^ sk_sf_swz(op.sf_tr[i]);
-    const int ssrc = min(4 * mac + c, nfull - 1);
-    dma16s(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf, op.sf_dma[i] + 16u * ssrc);
+    const int ssrc = min(4 * mac + op.sf_c, nfull - 1);
+    dma16s(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf + op.sf_step[i], op.sf_dma + 16u * ssrc);
   }
 }
 
@@ -128,45 +132,52 @@ __device__ __forceinline__ void sk_load_sf_tail(uint8_t* sftail, const SkOperand
   }
 }
 
-// This lane's scale words of super-step ss for its two column tiles: step j's
-// pair of block scales is bits 16 (j & 1) of s[nt][j >> 1].
+// This lane's block-scale pairs of super-step ss for its four column tiles:
+// s[ct][h] holds, in its low 16 bits, the scales of the 16-K blocks 8 h + 2 g
+// and 8 h + 2 g + 1 (those of MFMA steps (h, 0..1) and (h, 2..3)).
 __device__ __forceinline__ void sk_read_sf(const uint8_t* sfbuf, const uint8_t* sftail, int ss, int nfull,
-                                           int wave, int lane, uint32_t (&s)[2][2]) {
-  const int g = lane >> 5;
+                                           int wave, int lane, uint32_t (&s)[4][2]) {
+  const int g = lane >> 4, sh = 16 * (g & 1);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int tr = 64 * wave + 32 * nt + (lane & 31);
+  for (int ct = 0; ct < 4; ++ct) {
+    const int tr = 64 * wave + 16 * ct + (lane & 15);
     if (ss < nfull) {
-      const uint2 v = *reinterpret_cast<const uint2*>(sfbuf + 64 * tr + 16 * ((ss & 3) ^ sk_sf_swz(tr)) + 8 * g);
-      s[nt][0] = v.x;
-      s[nt][1] = v.y;
+      const uint4 v = *reinterpret_cast<const uint4*>(sfbuf + 64 * tr + 16 * ((ss & 3) ^ sk_sf_swz(tr)));
+      s[ct][0] = word_of(v, g >> 1) >> sh;
+      s[ct][1] = word_of(v, 2 + (g >> 1)) >> sh;
     } else {
-      s[nt][0] = *reinterpret_cast<const uint32_t*>(sftail + 8 * tr + 4 * g);
-      s[nt][1] = 0;
+      s[ct][0] = *reinterpret_cast<const uint32_t*>(sftail + 8 * tr + 4 * (g >> 1)) >> sh;
+      s[ct][1] = 0;
     }
   }
 }
 
-// The MFMAs of step j from A buffer buf, nibbles W and scale words sw.
-__device__ __forceinline__ void sk_step(const f16x8* buf, const int (&ra)[4], const SkB& W,
-                                        const uint32_t (&sw)[2][2], int j, f32x16 (&acc)[2]) {
-  f16x2 lo[2], hi[2];
+// The MFMAs of K half h of a super-step (4 steps of 32) from A buffer buf,
+// nibbles W and scale pairs sw; ra[s] is this lane's A chunk of step (h = 0,
+// s) in row group 0 (row group 1: ra[s ^ 2] + 128, since key(r + 16) =
+// key(r) ^ 2 for r < 16).
+__device__ __forceinline__ void sk_half(const f16x8* buf, const int (&ra)[4], const SkB& W,
+                                        const uint32_t (&sw)[4][2], int h, f32x4 (&acc)[2][4]) {
+  f16x2 lo[4], hi[4];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[nt][j >> 1] >> (16 * (j & 1)), 1.0f, false);
-    lo[nt] = f16x2{sc[0], sc[0]};
-    hi[nt] = f16x2{sc[1], sc[1]};
+  for (int ct = 0; ct < 4; ++ct) {
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw[ct][h], 1.0f, false);
+    lo[ct] = f16x2{sc[0], sc[0]};
+    hi[ct] = f16x2{sc[1], sc[1]};
   }
-  const int off = j * kSkAStage;
+  const int off = 2 * h * kSkAStage;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const f16x8 fa = buf[ra[s] + off];
-    const f16x8 b0 = dequant8(word_of(W.q[0][j], s), s < 2 ? lo[0] : hi[0]);
-    const f16x8 b1 = dequant8(word_of(W.q[1][j], s), s < 2 ? lo[1] : hi[1]);
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, b0, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, b1, acc[1], 0, 0, 0);
+    const f16x8 a0 = buf[ra[s] + off];
+    const f16x8 a1 = buf[ra[s ^ 2] + off + 128];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f16x8 b = dequant8(word_of(W.q[ct][h], s), s < 2 ? lo[ct] : hi[ct]);
+      acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b, acc[0][ct], 0, 0, 0);
+      acc[1][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b, acc[1][ct], 0, 0, 0);
+    }
   }
-  SCHED_FENCE();  // keeps each step's fragments from being hoisted into the previous one
+  SCHED_FENCE();  // keeps each half's fragments from being hoisted into the previous one
 }
 
 struct SkLds {
@@ -184,11 +195,11 @@ struct SkLds {
 // used, and the tail's scales with the tail), then run its MFMAs.
 template <int BUF, class RowOf>
 __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB (&W)[2], const SkOperands& op,
-                                         int ss, int nss, int nfull, int wave, int lane, f32x16 (&acc)[2],
+                                         int ss, int nss, int nfull, int wave, int lane, f32x4 (&acc)[2][4],
                                          RowOf row_of) {
   wait_vmcnt<0>();
   lds_barrier();
-  uint32_t sw[2][2];
+  uint32_t sw[4][2];
   sk_read_sf(L.sf, L.sftail, ss, nfull, wave, lane, sw);
   if ((ss & 3) == 3 && ss + 1 < nfull) {
     lds_barrier();
@@ -201,23 +212,19 @@ __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB
   if (ss + 1 == nfull && nss > nfull) sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
   SCHED_FENCE();
   const f16x8* buf = L.a + BUF * kSkABuf;
-  sk_step(buf, ra, W[BUF], sw, 0, acc);
-  sk_step(buf, ra, W[BUF], sw, 1, acc);
-  if (ss < nfull) {
-    sk_step(buf, ra, W[BUF], sw, 2, acc);
-    sk_step(buf, ra, W[BUF], sw, 3, acc);
-  }
+  sk_half(buf, ra, W[BUF], sw, 0, acc);
+  if (ss < nfull) sk_half(buf, ra, W[BUF], sw, 1, acc);
 }
 
 // The K loop over nk steps of 64 (nk even); ends with all loads landed and
 // every wave past its last LDS read.  row_of(tr) is the byte offset of the
 // scale row of tile row tr within the expert's scales.
 template <class RowOf>
-__device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op, int nk, f32x16 (&acc)[2],
+__device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op, int nk, f32x4 (&acc)[2][4],
                                             RowOf row_of) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, r = lane & 31;
+  const int g = lane >> 4, r = lane & 15;
   const int nfull = nk / kSkSteps;
   const int nss = nfull + (nk % kSkSteps ? 1 : 0);
   SkB W[2];
@@ -227,12 +234,15 @@ __device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op
   else
     sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
   W[0] = sk_load_b(op, 0, sk_steps(0, nfull));
-  // A fragment chunk of sub-step s: row r, logical chunk 4 g + s
+  // A fragment of step (0, s) for row r (group 0): K [32 g + 8 s, +8) is
+  // chunk 4 (g & 1) + s of region g >> 1
   int ra[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) ra[s] = r * 8 + ((4 * g + s) ^ swz_key(r));
-  acc[0] = f32x16{};
-  acc[1] = f32x16{};
+  for (int s = 0; s < 4; ++s) ra[s] = (g >> 1) * kSkAStage + r * 8 + ((4 * (g & 1) + s) ^ swz_key(r));
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x4{};
   for (int ss = 0; ss < nss; ss += 2) {
     sk_super<0>(L, ra, W, op, ss, nss, nfull, wave, lane, acc, row_of);
     if (ss + 1 < nss) sk_super<1>(L, ra, W, op, ss + 1, nss, nfull, wave, lane, acc, row_of);
@@ -247,16 +257,19 @@ template <class WRow>
 __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64_t K, int wave, int lane, int R,
                                             WRow wrow) {
   const int c = (lane & 7) ^ swz_key(R);
-  op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)(c & 3);
-  op.a_hi = 64u * (uint32_t)(c >> 2);
+  op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)c;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) op.bq_row[j] = (uint32_t)wrow(64 * wave + 32 * j + (lane & 31)) * (uint32_t)(K / 2);
+  for (int ct = 0; ct < 4; ++ct) op.bq_row[ct] = (uint32_t)wrow(64 * wave + 16 * ct + (lane & 15)) * (uint32_t)(K / 2);
+  // the weight rows of tile rows 64 wave + 16 i + r (r < 16) lie the same
+  // number of rows after that of 64 wave + r for every r (plain order: 16 i;
+  // the L1 gate/up order: 32 (i & 1) + 8 (i >> 1)), so the steps are scalars
+  const int w0 = wrow(64 * wave + (lane >> 2));
+  op.sf_dma = (uint32_t)w0 * (uint32_t)(K / 16);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    op.sf_tr[i] = 64 * wave + 16 * i + (lane >> 2);
-    op.sf_dma[i] = (uint32_t)wrow(op.sf_tr[i]) * (uint32_t)(K / 16);
-  }
-  op.g = lane >> 5;
+  for (int i = 0; i < 4; ++i)
+    op.sf_step[i] = (uint32_t)__builtin_amdgcn_readfirstlane((wrow(64 * wave + 16 * i + (lane >> 2)) - w0) * (int)(K / 16));
+  op.sf_c = (lane & 3) ^ sk_sf_swz(64 * wave + (lane >> 2));
+  op.g = lane >> 4;
 }
 
 #define SK_LDS_DECL                                              \
@@ -289,7 +302,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
     sk_operands(op, arow, p.K, wave, lane, R, wrow);
   }
-  f32x16 acc[2];
+  f32x4 acc[2][4];
   sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
 
   // epilogue: SwiGLU -> bf16 tile (32 x 128) in LDS, then NVFP4 of its rows
@@ -301,19 +314,25 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
   int* out_row = reinterpret_cast<int*>(lds_a + kCTileChunks + 32);
   if (tid < kSkTileM) out_row[tid] = out_row_of(tid);
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
-  const int col = 32 * wave + (lane & 31);
   const int64_t I = p.N2 / 2;
   const int hb = tid & 15;
   const int npass = (t.nrows + kSkThreads / 16 - 1) / (kSkThreads / 16);
-  // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS
+  // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS: column
+  // tiles ct and ct + 2 (ct < 2) hold the gate and up values of SwiGLU
+  // columns 32 wave + 16 ct + lane % 16, at rows 16 mt + 4 (lane / 16) + i
   auto fill_ctile = [&](bool gate_only) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float gate = acc[0][i] * alpha;
-      const float sg = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
-      const float c = gate_only ? sg : sg * (acc[1][i] * alpha);
-      ctile[acc_row(i, lane) * kCStride + col] = __builtin_bit_cast(uint16_t, (__bf16)c);
-    }
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gate = acc[mt][ct][i] * alpha;
+          const float sg = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
+          const float c = gate_only ? sg : sg * (acc[mt][ct + 2][i] * alpha);
+          const int row = 16 * mt + 4 * (lane >> 4) + i, col = 32 * wave + 16 * ct + (lane & 15);
+          ctile[row * kCStride + col] = __builtin_bit_cast(uint16_t, (__bf16)c);
+        }
   };
   if (p.c_il) {
     // interleaved output: the SiLU(gate) groups first
@@ -371,7 +390,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
   sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), wrow);
-  f32x16 acc[2];
+  f32x4 acc[2][4];
   sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
   // the scales' LDS holds the output rows, the A buffers each wave's
   // 4 KiB transposition scratch
@@ -380,9 +399,19 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   __syncthreads();
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
   float* const scratch = reinterpret_cast<float*>(lds_a) + wave * 1024;
-  l2_store_block(p, acc[0], acc[1], scratch, 0, t.nrows, (int64_t)nt * kTileN + wave * 64, lane,
-                 [&](int r) { return out_row[r]; },
-                 [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
+  // half h of the wave's 64 columns is column tiles 2 h, 2 h + 1
+  auto fill = [&](int half, float* sc) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[l2_scratch_index(16 * mt + 4 * (lane >> 4) + i, 16 * c2 + (lane & 15))] = acc[mt][2 * half + c2][i];
+  };
+  l2_store_rows(p, scratch, 0, t.nrows, (int64_t)nt * kTileN + wave * 64, lane, fill,
+                [&](int r) { return out_row[r]; },
+                [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
 }
 
 // ------------------------------------------------------------------ launchers
