@@ -43,10 +43,9 @@ constexpr int kSkAStage = kSkTileM * (kStepK / 8);  // 16 B chunks of one A step
 constexpr int kSkABuf = kSkSteps * kSkAStage;       // one super-step of A (16 KiB)
 
 // Per-workgroup operand sources (32-bit byte offsets, as in the 256-row
-// kernels).  A super-step of m K steps (m = 4, or m = 2 for a K tail of 128)
-// starting at K step kb0 holds K chunks of 8 (physical index q within the
-// super-step) as follows: MFMA step j, sub-step s, lane half g uses
-// q = 4 m g + 4 j + s, for A and for B alike.
+// kernels).  Within a super-step (256 K, or a K tail of 128), MFMA step
+// (h, s) of lane group g = lane / 16 takes K [128 h + 32 g + 8 s, +8), for A
+// and for B alike.
 struct SkOperands {
   const uint8_t* a;     // A matrix (f16 rows of K), wave-uniform
   uint32_t a_base;      // this lane's A row (tile row 8 wave + lane / 8) + 16 c, c = (lane & 7) ^ key(row)
