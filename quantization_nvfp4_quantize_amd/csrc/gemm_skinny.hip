@@ -54,9 +54,8 @@ struct SkOperands {
   uint32_t bq_row[4];   // byte offsets of this lane's column rows (tile rows 64 wave + 16 ct + lane % 16)
   uint32_t sf_dma;      // scale-row offset of the tile row 64 wave + lane / 4
   uint32_t sf_step[4];  // wave-uniform: from it to the scale rows of the tile rows 64 wave + 16 i + lane / 4
-  int sf_c;             // the 16 B chunk (super-step) this lane fetches in those rows: (lane & 3) ^
-                        // sk_sf_swz(row), the same for the four rows (sk_sf_swz(row) = (lane >> 4) & 3)
   int g;                // lane group (lane / 16)
+  bool a_rows;          // wave-uniform: this wave's 8 A rows include a valid one
 };
 
 // The nibbles of one super-step in a lane: for each column tile ct, the
@@ -84,8 +83,12 @@ __device__ __forceinline__ int sk_steps(int ss, int nfull) { return ss < nfull ?
 // Direct loads of A for super-step ss into buf: region j holds K [64 j,
 // 64 j + 64) of the 32 rows (128 B each, 16 B chunk c at c ^ key(row)); wave
 // w fetches rows 8 w .. 8 w + 7 (1 KiB per region).  A tail super-step (m =
-// 2 steps) loads its two regions twice (the second copy is not read).
+// 2 steps) loads its two regions twice (the second copy is not read).  A wave
+// whose rows are all past the tile's valid rows loads nothing: those rows of
+// the buffer keep stale values, which reach only accumulator rows that are
+// never stored (an MFMA output row depends on its own A row alone).
 __device__ __forceinline__ void sk_load_a(f16x8* buf, const SkOperands& op, int ss, int m, int wave) {
+  if (!op.a_rows) return;
   const uint8_t* base = op.a + (size_t)ss * (kSkSteps * kStepK * 2);
 #pragma unroll
   for (int j = 0; j < kSkSteps; ++j)
@@ -110,9 +113,15 @@ __device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int ss, int m) {
 // + 3; chunks past the last whole super-step re-read it and are not used).
 __device__ __forceinline__ void sk_load_sf_macro(uint8_t* sfbuf, const SkOperands& op, int mac, int nfull,
                                                  int wave, int lane) {
+  // the lane writes position lane & 3 of its rows tr = 64 wave + 16 i +
+  // lane / 4, which holds chunk (lane & 3) ^ sk_sf_swz(tr) = (lane & 3) ^
+  // ((lane >> 4) & 3); recomputed here rather than held across the K loop
+  int l = lane;
+  asm volatile("" : "+v"(l));
+  const int sf_c = (l & 3) ^ ((l >> 4) & 3);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ssrc = min(4 * mac + op.sf_c, nfull - 1);
+    const int ssrc = min(4 * mac + sf_c, nfull - 1);
     dma16s(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf + op.sf_step[i], op.sf_dma + 16u * ssrc);
   }
 }
@@ -254,7 +263,7 @@ __device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op
 // 8 wave + lane / 8); row_of(tr) gives the global weight row of tile row tr.
 template <class WRow>
 __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64_t K, int wave, int lane, int R,
-                                            WRow wrow) {
+                                            int nrows, WRow wrow) {
   const int c = (lane & 7) ^ swz_key(R);
   op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)c;
 #pragma unroll
@@ -267,8 +276,8 @@ __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     op.sf_step[i] = (uint32_t)__builtin_amdgcn_readfirstlane((wrow(64 * wave + 16 * i + (lane >> 2)) - w0) * (int)(K / 16));
-  op.sf_c = (lane & 3) ^ sk_sf_swz(64 * wave + (lane >> 2));
   op.g = lane >> 4;
+  op.a_rows = __builtin_amdgcn_readfirstlane(8 * wave < nrows ? 1 : 0) != 0;
 }
 
 #define SK_LDS_DECL                                              \
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     const int R = 8 * wave + (lane >> 3);
     const int o = out_row_of(R);
     const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
-    sk_operands(op, arow, p.K, wave, lane, R, wrow);
+    sk_operands(op, arow, p.K, wave, lane, R, t.nrows, wrow);
   }
   f32x4 acc[2][4];
   sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
@@ -388,7 +397,8 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
-  sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), wrow);
+  sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), t.nrows,
+              wrow);
   f32x4 acc[2][4];
   sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
   // the scales' LDS holds the output rows, the A buffers each wave's
