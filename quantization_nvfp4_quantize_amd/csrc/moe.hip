@@ -39,22 +39,34 @@ constexpr int kSchedCounters = 16;  // the GEMMs' work counters, zeroed with the
 constexpr int kRouteWaves = kRouteThreads / 64;
 
 // Exclusive prefix of v over the threads of the workgroup (one value per
-// thread, kRouteThreads threads, scratch of as many ints); *total receives
-// the sum.  Every thread must call it.
+// thread, kRouteThreads threads, scratch of at least 2 kRouteWaves ints);
+// *total receives the sum.  Every thread must call it.  Each wave scans its
+// 64 values with shuffles, the first wave scans the wave totals, and every
+// thread adds its wave's offset: three barriers.
 __device__ __forceinline__ int block_exclusive_scan(int* scan, int v, int* total) {
-  const int tid = threadIdx.x;
-  scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    const int u = (tid >= off) ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += u;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  const int incl = scan[tid];
-  *total = scan[kRouteThreads - 1];
+  if (lane == 63) scan[wave] = x;
   __syncthreads();
-  return incl - v;
+  if (wave == 0) {
+    int t = lane < kRouteWaves ? scan[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kRouteWaves; off <<= 1) {
+      const int y = __shfl_up(t, off, 64);
+      if (lane >= off) t += y;
+    }
+    if (lane < kRouteWaves) scan[kRouteWaves + lane] = t;  // inclusive prefix of the wave totals
+  }
+  __syncthreads();
+  const int base = wave ? scan[kRouteWaves + wave - 1] : 0;
+  *total = scan[2 * kRouteWaves - 1];
+  __syncthreads();  // the scratch is reused by the next call
+  return base + x - v;
 }
 
 // Tiles of an expert with np rows: blocks of tile_rows rows; with
