@@ -124,7 +124,7 @@ int nvfp4_gemm_swiglu_quant(const uint8_t *a_q, const uint8_t *a_sf, const float
  * operands exact (e2m1 * E4M3 block scale), fp32 accumulation.
  *   x bf16 [M][K] (16-byte aligned); x_gs_in nullable (device float)
  *   w_q [N][K/2], w_sf [N][K/16] (16-byte aligned), w_gs (device float)
- *   out [M][N]: bf16 (out_dtype 0) or fp32 (1)
+ *   out [M][N]: bf16 (out_dtype 0) or fp32 (1), 16-byte aligned
  *   x_gs_out nullable (1 float): the activation global scale used
  *   M >= 0; K % 64 == 0; N % 256 == 0; M * K * 2 and N * K / 2 at most 4 GiB
  *   (else NVFP4_ERR_UNSUPPORTED).  Workspace: nvfp4_linear_workspace_size

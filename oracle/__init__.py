@@ -5,8 +5,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 its Python binding) never imports it, and the two share no code.
 
 Thin numpy/ctypes wrapper around ``nvfp4_oracle.c`` and ``mxfp4_oracle.c``:
-argument marshalling only; every step of the arithmetic lives in the C
-files.  ``nvfp4_oracle.c`` cites the pages ("nvfp4-megamoe-kernel":
+argument marshalling, and the composition of C calls in the pages' order
+(``moe_tokens_dynamic`` runs the C MoE once for the L1 outputs, takes their
+global scale with the C rule, then runs the C MoE with it); every arithmetic
+step lives in the C files.  ``nvfp4_oracle.c`` cites the pages ("nvfp4-megamoe-kernel":
 NVFP4-1.1_APPROACH_PART_2.md, NVFP4-1.1_APPROACH.md, DEBUG_LOG.md "NVFP4 MoE
 Pipeline") it follows; ``mxfp4_oracle.c`` follows the OCP Microscaling
 Formats (MX) Specification v1.0, which defines the MXFP4 format of the
@@ -74,6 +76,8 @@ _SIGNATURES = {
     "orc_mx_dequantize": (None, [_u8p, _u8p, ctypes.c_int64, ctypes.c_int64, _f64p]),
     "orc_mx_linear": (None, [_u8p, _u8p, ctypes.c_int64, ctypes.c_int64, _u8p, _u8p, ctypes.c_int64,
                              _f64p, ctypes.c_int]),
+    "orc_linear_rows": (None, [_u8p, _u8p, ctypes.c_float, ctypes.c_int64, _u8p, _u8p, ctypes.c_float, _i64p,
+                                ctypes.c_int64, _i64p, ctypes.c_int64, _f32p, ctypes.c_int]),
     "orc_moe_tokens": (ctypes.c_float, [ctypes.POINTER(MoeProblem), _i64p, ctypes.c_int64,
                                         _f32p, _u16p, _u8p, _u8p, ctypes.c_int]),
 }
@@ -241,22 +245,31 @@ class Oracle:
             out.update(c=c, a2_q=a2q, a2_sf=a2sf)
         return out
 
-    def linear(self, x_bf16, w_q, w_sf, w_gs, x_gs=None, rows=None, cols=None):
+    def linear(self, x_bf16, w_q, w_sf, w_gs, x_gs=None, rows=None, cols=None, threads=None):
         """Dense NVFP4 linear (the MoE's activation quantization and GEMM
         without routing, DEBUG_LOG.md "NVFP4 MoE Pipeline"): x is quantized
         with g = x_gs or the global scale of the whole x, both operands are
         dequantized exactly (e2m1 * block scale, no global scale) and
-        y = f32(g * w_gs) * (A @ W^T) in fp64, returned as fp32 for the
-        listed rows and output columns (all by default), with g."""
+        y = f32(g * w_gs) * (A @ W^T) in fp64 (orc_linear_rows), returned as
+        fp32 for the listed rows and output columns (all by default), with g."""
         x = np.ascontiguousarray(x_bf16, np.uint16)
         g = self.global_scale(x) if x_gs is None else np.float32(x_gs)
         rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows, np.int64)
         cols = np.arange(w_q.shape[0]) if cols is None else np.asarray(cols, np.int64)
         xq, xsf = self.quantize(x[rows], g)  # rows are independent given g
-        a = self.dequantize(xq, xsf, 1.0).astype(np.float64)
-        b = self.dequantize(np.asarray(w_q)[cols], np.asarray(w_sf)[cols], 1.0).astype(np.float64)
-        alpha = float(np.float32(np.float32(g) * np.float32(w_gs)))
-        return ((a @ b.T) * alpha).astype(np.float32), np.float32(g)
+        w_q = np.ascontiguousarray(w_q, np.uint8)
+        w_sf = np.ascontiguousarray(w_sf, np.uint8)
+        K = x.shape[1]
+        assert w_q.shape[1] * 2 == K and w_sf.shape[1] * 16 == K
+        loc = np.ascontiguousarray(np.arange(rows.size), np.int64)
+        cols = np.ascontiguousarray(cols, np.int64)
+        y = np.zeros((rows.size, cols.size), np.float32)
+        if rows.size and cols.size:
+            self.L.orc_linear_rows(_ptr(xq, _u8p), _ptr(xsf, _u8p), float(g), K, _ptr(w_q, _u8p),
+                                   _ptr(w_sf, _u8p), float(np.float32(w_gs)), _ptr(loc, _i64p), loc.size,
+                                   _ptr(cols, _i64p), cols.size, _ptr(y, _f32p),
+                                   threads or default_threads())
+        return y, np.float32(g)
 
     def moe_tokens_dynamic(self, x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs,
                            tokens=None, x_gs=None, want_pairs=False, threads=None):

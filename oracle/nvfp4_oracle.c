@@ -346,6 +346,69 @@ void orc_l1_swiglu_rows(const uint8_t *aq, const uint8_t *asf, float a_gs, int64
 }
 
 /* ---------------------------------------------------------------------- */
+/* Dense NVFP4 linear                                                      */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+  const uint8_t *aq, *asf, *wq, *wsf;
+  int64_t K;
+  double alpha;
+  const int64_t *rows, *cols;
+  int64_t ncols;
+  float *y;
+  int64_t i0, i1;
+} lin_job;
+
+static void *lin_worker(void *p) {
+  lin_job *j = (lin_job *)p;
+  double *arow = (double *)malloc(sizeof(double) * (size_t)j->K);
+  for (int64_t i = j->i0; i < j->i1; ++i) {
+    for (int64_t k = 0; k < j->K; ++k) arow[k] = deq_unscaled(j->aq, j->asf, j->K, j->rows[i], k);
+    for (int64_t c = 0; c < j->ncols; ++c) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < j->K; ++k) acc += arow[k] * deq_unscaled(j->wq, j->wsf, j->K, j->cols[c], k);
+      j->y[i * j->ncols + c] = (float)(acc * j->alpha);
+    }
+  }
+  free(arow);
+  return NULL;
+}
+
+/* The pipeline's activation quantization and GEMM without routing (DEBUG_LOG.md,
+ * "NVFP4 MoE Pipeline": the GEMM scales by alpha = input global scale times
+ * weight global scale; "Checkpoint Layers" lists NVFP4 linear projections).
+ * For the listed rows of the quantized activations aq/asf [.][K] and the
+ * listed weight rows (output features) of wq/wsf [.][K]:
+ *   y[i][c] = f32( f32(a_gs * w_gs) * sum_k a~[rows[i]][k] * w~[cols[c]][k] )
+ * with exactly dequantized operands (e2m1 * block scale) summed in fp64. */
+void orc_linear_rows(const uint8_t *aq, const uint8_t *asf, float a_gs, int64_t K, const uint8_t *wq,
+                     const uint8_t *wsf, float w_gs, const int64_t *rows, int64_t nrows, const int64_t *cols,
+                     int64_t ncols, float *y, int threads) {
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  float alpha = a_gs * w_gs;
+  pthread_t tid[256];
+  lin_job jobs[256];
+  for (int t = 0; t < threads; ++t) {
+    lin_job *j = &jobs[t];
+    j->aq = aq;
+    j->asf = asf;
+    j->wq = wq;
+    j->wsf = wsf;
+    j->K = K;
+    j->alpha = (double)alpha;
+    j->rows = rows;
+    j->cols = cols;
+    j->ncols = ncols;
+    j->y = y;
+    j->i0 = nrows * t / threads;
+    j->i1 = nrows * (t + 1) / threads;
+    pthread_create(&tid[t], NULL, lin_worker, j);
+  }
+  for (int t = 0; t < threads; ++t) pthread_join(tid[t], NULL);
+}
+
+/* ---------------------------------------------------------------------- */
 /* MoE expert FFN                                                          */
 /* ---------------------------------------------------------------------- */
 

@@ -44,6 +44,9 @@ void orc_l1_swiglu_rows(const uint8_t *aq, const uint8_t *asf, float a_gs, int64
                         const uint8_t *wq, const uint8_t *wsf, float w_gs, int64_t N2,
                         const int64_t *rows, int64_t nrows, double *h, uint16_t *c,
                         int threads);
+void orc_linear_rows(const uint8_t *aq, const uint8_t *asf, float a_gs, int64_t K, const uint8_t *wq,
+                     const uint8_t *wsf, float w_gs, const int64_t *rows, int64_t nrows, const int64_t *cols,
+                     int64_t ncols, float *y, int threads);
 float orc_moe_tokens(const orc_moe_problem *pb, const int64_t *tokens, int64_t ntok, float *y,
                      uint16_t *c_out, uint8_t *a2q_out, uint8_t *a2sf_out, int threads);
 #endif

@@ -104,17 +104,16 @@ def _require(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-_WS = {}
-
-
 def _workspace(nbytes, device):
-    """A cached device workspace of at least nbytes (per device)."""
-    key = torch.device(device).index
-    buf = _WS.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
-        _WS[key] = buf
-    return buf
+    """A fresh device workspace of at least nbytes for one call.
+
+    It comes from torch's caching allocator on the current stream, so a block
+    is handed out again only after the work queued on that stream has used
+    it: calls on different streams never share one, and a graph captured
+    around a call keeps its block in the graph's private pool for as long as
+    the graph lives.  (The allocator caches freed blocks, so a call of the
+    same size costs no device allocation.)"""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ API

@@ -200,9 +200,10 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
   if (M == 0) return NVFP4_OK;
   if (!x || !w_q || !w_sf || !w_gs || !out)
     return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: null pointer");
-  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_sf, 16) || !aligned(out, 4) ||
+  // the GEMM epilogues write out with 16-byte vector stores
+  if (!aligned(x, 16) || !aligned(w_q, 16) || !aligned(w_sf, 16) || !aligned(out, 16) ||
       !aligned(x_gs_in, 4) || !aligned(x_gs_out, 4))
-    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: misaligned pointer");
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_linear: misaligned pointer (x, w_q, w_sf and out need 16 bytes)");
   const LinearLayout L = linear_layout(M, K);
   if (!ws || ws_bytes < L.total)
     return fail(NVFP4_ERR_WORKSPACE, "nvfp4_linear: workspace %zu < %zu bytes", ws_bytes, L.total);

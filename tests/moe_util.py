@@ -58,3 +58,47 @@ def oracle_tokens(orc, cfg, x_bits, ids, wts, tokens, device="cuda:0", want_pair
     w = oracle_weights(orc, cfg, used, device=device)
     return orc.moe_tokens(x_bits, ids_r, wts, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"],
                           w["w2gs"], cfg.a2_gs, tokens=tokens, want_pairs=want_pairs)
+
+
+def expert_rows(ids, E):
+    """The stable grouping of (token, expert) pairs by expert: for expert e,
+    the pair ids p = t * k + j routed to it, in increasing order (its rows
+    0, 1, ... in the grouped GEMMs).  Pairs with an id outside [0, E) are
+    skipped.  Host-side test selection only."""
+    flat = np.asarray(ids).reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    fs = flat[order]
+    return {e: order[np.searchsorted(fs, e, "left"):np.searchsorted(fs, e, "right")] for e in range(E)}
+
+
+def boundary_tokens(ids, E, k, tile=256, short=32, n_edge_experts=8, seed=0, extra=()):
+    """Tokens chosen so that the oracle comparison reaches every kind of row
+    of the mixed tiling at full size: for each expert whose last block of at
+    most `short` rows goes on a short tile, the token of a seeded row of that
+    block (of its last row for every eighth such expert); for `n_edge_experts` experts with more than
+    `tile` + 1 rows, the tokens of rows tile - 1, tile and tile + 1; the
+    tokens of each expert's first row for experts with at most `short` rows
+    in all; plus `extra`.  Returns (sorted token ids, dict of what each
+    group holds)."""
+    rows = expert_rows(ids, E)
+    short_tok, edge_tok, small_tok, short_e = [], [], [], []
+    edge_experts = [e for e in range(E) if rows[e].size > tile + 1]
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if len(edge_experts) > n_edge_experts:
+        edge_experts = sorted(rng.choice(edge_experts, n_edge_experts, replace=False).tolist())
+    for e in range(E):
+        n = rows[e].size
+        rem = n % tile
+        if n > tile and 0 < rem <= short:
+            # a seeded row of the short block; its last row for every 8th expert
+            r = n - 1 if len(short_e) % 8 == 0 else n - rem + int(rng.integers(rem))
+            short_tok.append(rows[e][r] // k)
+            short_e.append(e)
+        if 0 < n <= short:
+            small_tok.append(rows[e][0] // k)
+    for e in edge_experts:
+        edge_tok += [rows[e][tile - 1] // k, rows[e][tile] // k, rows[e][tile + 1] // k]
+    toks = np.unique(np.array(list(short_tok) + list(edge_tok) + list(small_tok) + list(extra), np.int64))
+    info = dict(short=np.unique(short_tok), edge=np.unique(edge_tok), small=np.unique(small_tok),
+                edge_experts=edge_experts, short_experts=short_e)
+    return toks, info

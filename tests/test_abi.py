@@ -150,6 +150,11 @@ def test_linear_rejects(lib):
     assert lib.nvfp4_linear(None, 4, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE, 1 << 30, None) == -1
     assert lib.nvfp4_linear(ctypes.c_void_p(0x10008), 4, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE,
                             1 << 30, None) == -1
+    # out is written with 16-byte stores: an offset out pointer is rejected
+    for off in (4, 8):
+        assert lib.nvfp4_linear(FAKE, 4, 64, None, FAKE, FAKE, FAKE, 256, 1, ctypes.c_void_p(0x10000 + off), None,
+                                FAKE, 1 << 30, None) == -1
+        assert b"misaligned" in lib.nvfp4_last_error()
     need = lib.nvfp4_linear_workspace_size(4, 64, 256)
     assert need > 0
     assert lib.nvfp4_linear(FAKE, 4, 64, None, FAKE, FAKE, FAKE, 256, 0, FAKE, None, FAKE, need - 1, None) == -3

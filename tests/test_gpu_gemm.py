@@ -2,10 +2,11 @@
 GEMM + SwiGLU + compact bf16 + fused NVFP4, against the CPU oracle.
 
 Gates: compact bf16 SwiGLU output within relative Frobenius error 1e-3 and
-cosine >= 0.9999 of the oracle's; the fused NVFP4 bytes equal the GPU's own
-standalone quantizer applied to the GPU's bf16 output (that quantizer is
-bit-exact against the oracle), and differ from the oracle's bytes only where
-the bf16 inputs differ."""
+cosine >= 0.9999 of the oracle's; the fused NVFP4 bytes (nibbles and scale
+bytes) equal, bit for bit, the oracle's quantization of the GPU's own bf16
+output under the same supplied global scale, on every compared row.  The
+scale bytes that differ from the oracle's quantization of its own bf16 output
+(where the two GEMMs' bf16 roundings differ) are counted and reported."""
 import numpy as np
 import pytest
 import torch
@@ -35,8 +36,6 @@ def _run(nv, orc, x, w, out_gs, rows=None):
     xq, xsf, xg = nv.quantize(dev_bf16(x))
     wq, wsf, wg = nv.quantize(dev_bf16(w))
     c, cq, csf = nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, dev_f32(out_gs))
-    # the standalone quantizer on the GPU's own bf16 output
-    cq2, csf2, _ = nv.quantize(c, dev_f32(out_gs))
     torch.cuda.synchronize()
     gx, gw = orc.global_scale(x), orc.global_scale(w)
     oq, osf = orc.quantize(x, gx)
@@ -45,8 +44,7 @@ def _run(nv, orc, x, w, out_gs, rows=None):
     if rows is None:
         rows = np.arange(M)
     c_or, _ = orc.l1_swiglu_rows(oq, osf, gx, owq, owsf, gw, rows)
-    return dict(c=host_bits(c)[rows], cq=host(cq)[rows], csf=host(csf)[rows], cq2=host(cq2)[rows],
-                csf2=host(csf2)[rows], c_or=c_or, rows=rows)
+    return dict(c=host_bits(c)[rows], cq=host(cq)[rows], csf=host(csf)[rows], c_or=c_or, rows=rows)
 
 
 def _gate(r, orc, out_gs, tol=1e-3):
@@ -54,12 +52,18 @@ def _gate(r, orc, out_gs, tol=1e-3):
     co = synth.bf16_values(r["c_or"])
     err, cos = rel_fro(cg, co), cosine(cg, co)
     assert err <= tol and cos >= 0.9999, (err, cos)
-    # fused quantization == standalone quantization of the same bf16 values
-    assert np.array_equal(r["cq"], r["cq2"]) and np.array_equal(r["csf"], r["csf2"])
-    # and against the oracle's own bytes: mismatches only where c differs
-    oq, osf = orc.quantize(r["c_or"], out_gs)
-    same_rows_blocks = (r["c"].reshape(len(r["rows"]), -1, 16) == r["c_or"].reshape(len(r["rows"]), -1, 16)).all(-1)
-    assert np.array_equal(r["csf"][same_rows_blocks], osf[same_rows_blocks])
+    # the fused NVFP4 bytes == the oracle's quantization of the GPU's own bf16
+    # output under the same supplied scale, nibbles and scale bytes
+    gq, gsf = orc.quantize(r["c"], out_gs)
+    bad = np.nonzero(r["csf"] != gsf)
+    assert bad[0].size == 0, ("scale bytes", bad[0].size, r["csf"][bad][:8], gsf[bad][:8])
+    bad = np.nonzero(r["cq"] != gq)
+    assert bad[0].size == 0, ("nibbles", bad[0].size, r["cq"][bad][:8], gq[bad][:8])
+    # against the oracle's quantization of its own bf16 output: scale bytes
+    # may differ only in blocks whose bf16 values differ
+    _, osf = orc.quantize(r["c_or"], out_gs)
+    same = (r["c"].reshape(len(r["rows"]), -1, 16) == r["c_or"].reshape(len(r["rows"]), -1, 16)).all(-1)
+    assert np.array_equal(r["csf"][same], osf[same])
     return err, cos, float((r["csf"] != osf).mean())
 
 
@@ -89,10 +93,15 @@ def test_l1_stage_all_ones(nv, orc):
 
 def test_l1_stage_expert_config_sampled(nv, orc):
     """The single-expert workload M4096 K7168 N 2x2048, run in full on the
-    GPU, compared on sampled rows (tile edges included)."""
+    GPU, compared on 128 sampled rows (every tile edge included)."""
     x, w1 = synth.expert_problem()
     w = synth.torch_bits(w1)
-    rows = np.array([0, 1, 127, 128, 255, 256, 257, 1023, 2048, 3071, 4094, 4095])
+    # every 256-row tile boundary (rows 256 t - 1, 256 t, 256 t + 1) plus a
+    # seeded spread of interior rows: 128 rows in all
+    edges = np.array([r for t in range(17) for r in (256 * t - 1, 256 * t, 256 * t + 1) if 0 <= r < 4096])
+    rng = np.random.Generator(np.random.PCG64(41))
+    inner = rng.choice(np.setdiff1d(np.arange(4096), edges), size=128 - edges.size, replace=False)
+    rows = np.sort(np.concatenate([edges, inner]))
     r = _run(nv, orc, x, w, np.float32(synth.EXPERT_A2_GS), rows=rows)
     err, cos, flip = _gate(r, orc, np.float32(synth.EXPERT_A2_GS))
     print(f"expert config: rel_fro {err:.3e} cos {cos:.7f} scale-byte flips {flip:.2e}")

@@ -105,3 +105,51 @@ def test_moe_graph_replays_aux_stream(nv):
         torch.cuda.synchronize()
         assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32))
         _ = nv.moe_expert_ffn(x, ti, tw, *wl, a2, tile_rows=288)
+
+
+def test_graph_keeps_its_workspace(nv):
+    """A graph captured around calls that take their workspace from the
+    binding (the dynamic-scale quantize and the MoE layer) keeps that
+    workspace for itself: eager calls that need larger workspaces, and other
+    tensors allocated and filled between the replays, do not disturb it."""
+    x = dev_bf16(synth.quant_tensor(256, 7168, seed=12))
+    ref = [host(t) for t in nv.quantize(x)]
+    q = torch.empty(ref[0].shape, dtype=torch.uint8, device="cuda:0")
+    sf = torch.empty(ref[1].shape, dtype=torch.uint8, device="cuda:0")
+    g = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    xm = dev_bf16(synth.activations(cfg))
+    ids, wts = synth.routing(cfg)
+    ti, tw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    wl = (w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"], w["w2gs"])
+    a2 = dev_f32(cfg.a2_gs)
+    yref = host(nv.moe_expert_ffn(xm, ti, tw, *wl, a2, out_dtype=torch.float32))
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda:0")
+    nv.quantize(x, out=(q, sf, g))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.quantize(x, out=(q, sf, g))
+        args = nv.moe_args(xm, ti, tw, *wl, a2, y)
+        nv.moe_expert_ffn_raw(args, xm.device)
+    import dataclasses
+    for i in range(3):
+        big = dev_bf16(synth.quant_tensor(1024 * (i + 2), 7168, seed=20 + i))
+        nv.quantize(big)
+        cbig = dataclasses.replace(cfg, T=512 * (i + 2), name="tiny_big")
+        xb = dev_bf16(synth.activations(cbig))
+        ib, wb = synth.routing(cbig)
+        nv.moe_expert_ffn(xb, torch.from_numpy(ib).cuda(), torch.from_numpy(wb).cuda(), *wl, a2)
+        junk = torch.full((1 << 24,), float(i + 7), dtype=torch.float32, device="cuda:0")
+        q.zero_()
+        sf.zero_()
+        g.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q), ref[0]) and np.array_equal(host(sf), ref[1]), i
+        assert host(g)[0] == ref[2][0], i
+        assert np.array_equal(host(y).view(np.uint32), yref.view(np.uint32)), i
+        del junk, big, xb

@@ -66,14 +66,19 @@ def test_linear_supplied_scale(nv, orc):
 
 def test_linear_bench_shape_sampled(nv, orc):
     """M4096 K4096 N16384 (the bench's dense workload), oracle on sampled
-    rows and columns of y."""
+    rows and columns of y: the rows on both sides of every 256-row tile
+    edge, and 64 columns (the 256-column tile edges at both ends and in the
+    middle, plus seeded ones)."""
     s = synth.DENSE_SHAPE
     x, w = synth.dense_problem(device="cuda:0")
     wq, wsf, wg = nv.quantize(w)
     y = nv.linear(dev_bf16(x), wq, wsf, wg, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 2047, 4095])
-    cols = np.array([0, 255, 256, 8191, 16383])
+    rows = np.array(sorted({r for t in range(17) for r in (256 * t - 1, 256 * t) if 0 <= r < s["M"]}))
+    fixed = [0, 255, 256, 257, 8191, 8192, 16383]
+    rng = np.random.Generator(np.random.PCG64(17))
+    cols = np.sort(np.concatenate([fixed, rng.choice(np.setdiff1d(np.arange(s["N"]), fixed), 64 - len(fixed),
+                                                     replace=False)]))
     wb = synth.torch_bits(w[torch.from_numpy(cols).cuda()])
     gw = orc.global_scale(synth.torch_bits(w))
     oq, osf = orc.quantize(wb, gw)

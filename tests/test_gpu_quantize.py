@@ -163,3 +163,142 @@ def test_quantize_rejects_bad_args(nv):
     x = torch.zeros((4, 24), dtype=torch.bfloat16, device="cuda:0")
     with pytest.raises(nv.Nvfp4Error):
         nv.quantize(x)
+
+
+# ------------------------------------------------------------------ E4M3 sweep
+# The block-scale encoder (fp32 -> E4M3, nearest with ties to the even code,
+# saturating at 448) driven through nvfp4_quantize at chosen values.  The
+# pages' worked values (NVFP4-1.1_APPROACH_PART_2.md, FP8 E4M3 fixes: 0.001 ->
+# 0x01, 250 -> 0x78 by the mantissa carry, 448 -> 0x7e, no 0x7f) sit among the
+# targets; the expected bytes are the oracle's.
+def _bits_of(v):
+    return np.array([np.float32(v)], np.float32).view(np.uint32).astype(np.int64)[0]
+
+
+def _from_bits(b):
+    return np.array([b], np.uint32).view(np.float32)[0]
+
+
+def _e4m3_magnitudes():
+    """Magnitudes of the codes 0x00..0x7e, decoded by torch's float8_e4m3fn."""
+    return torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+
+
+def _scale_targets():
+    """Block-scale values bsf to drive the encoder with: every midpoint of
+    two neighbouring codes and its fp32 neighbours (+-1, +-2 ulp), every code
+    value +-1 ulp, the saturation range [448, 481] around the 464 tie, and
+    the pages' worked values."""
+    vals = _e4m3_magnitudes()
+    mids, out = [], []
+    for c in range(0x7E):
+        mid = np.float32((np.float64(vals[c]) + np.float64(vals[c + 1])) / 2)
+        assert np.float64(mid) == (np.float64(vals[c]) + np.float64(vals[c + 1])) / 2
+        mids.append(mid)
+        out += [_from_bits(_bits_of(mid) + d) for d in (-2, -1, 0, 1, 2)]
+    for c in range(1, 0x7F):
+        out += [_from_bits(_bits_of(vals[c]) + d) for d in (-1, 1)]
+    for v in (448, 450, 455.5, 456, 460, 463.75, 464, 464.25, 470, 479.5, 480, 481, 500, 1e4, 3e38,
+              0.001, 240, 248, 250, 256, 2.0 ** -10, 2.0 ** -11, 1e-30):
+        out += [_from_bits(_bits_of(v) + d) for d in (-1, 0, 1)]
+    return np.unique(np.array(out, np.float32)), np.array(mids, np.float32)
+
+
+def _g_with_reciprocal(E):
+    """A global scale g > 2^-117 whose fp32 reciprocal f32(1/g) is exactly E."""
+    E = np.float32(E)
+    b = _bits_of(np.float32(1.0) / E)
+    for d in range(8):
+        for s in (1, -1):
+            g = _from_bits(b + s * d)
+            if np.isfinite(g) and g > 2.0 ** -117 and np.float32(1.0) / g == E:
+                return g
+    return None
+
+
+def _bf16_exact(v):
+    return float(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).float()) == v
+
+
+def _block_for(v):
+    """(bmax, g) with bmax a bf16 value and f32(f32(bmax / 6) * f32(1 / g))
+    == v exactly: bmax = 6 c 2^k makes bmax / 6 = c 2^k exact, E = 1 / g is
+    searched next to v / (c 2^k), and g next to 1 / E."""
+    v = np.float32(v)
+    for c in (1.0, 1.5, 1.25, 1.75, 1.125, 1.375, 1.625, 1.875):
+        k = int(np.floor(np.log2(np.float64(v) / c)))
+        for kk in (k, k - 1, k + 1, k - 20, k + 20):
+            b = 6.0 * c * 2.0 ** kk
+            if not (1e-37 < b < 3e38) or not _bf16_exact(b):
+                continue
+            bmax = np.float32(b)
+            q = np.float32(bmax / np.float32(6.0))
+            if np.float64(q) != b / 6.0:
+                continue
+            base = _bits_of(np.float32(np.float64(v) / np.float64(q)))
+            for d in range(-3, 4):
+                E = _from_bits(base + d)
+                if not np.isfinite(E) or E <= 0 or np.float32(q * E) != v:
+                    continue
+                g = _g_with_reciprocal(E)
+                if g is not None and np.float32(q * (np.float32(1.0) / g)) == v:
+                    return float(bmax), g
+    return None
+
+
+def test_e4m3_encoder_sweep(nv, orc):
+    """Blocks whose scale product lands exactly on every E4M3 midpoint (ties
+    to the even code), on its fp32 neighbours, on every code +-1 ulp, across
+    the saturation range and on the pages' worked values: scale bytes and
+    nibbles bit-exact against the oracle."""
+    targets, mids = _scale_targets()
+    rng = np.random.Generator(np.random.PCG64(77))
+    jobs = []
+    for v in targets:
+        sol = _block_for(v)
+        if sol is None:
+            continue
+        bmax, g = sol
+        blk = np.float32(bmax) * rng.uniform(-1.0, 1.0, size=16).astype(np.float32)
+        blk[rng.integers(16)] = np.float32(bmax) * (1 if rng.integers(2) else -1)
+        bits = synth.bf16_bits(blk)[None, :]
+        assert np.abs(synth.bf16_values(bits)).max() == np.float32(bmax)
+        q, sf, _ = nv.quantize(dev_bf16(bits), dev_f32(g))
+        jobs.append((v, g, bits, q, sf))
+    solved = np.array([j[0] for j in jobs], np.float32)
+    # every midpoint and its +-1 ulp neighbours is driven, and almost all else
+    for m in mids:
+        for d in (-1, 0, 1):
+            assert _from_bits(_bits_of(m) + d) in solved, (m, d)
+    assert solved.size >= 0.99 * targets.size, (solved.size, targets.size)
+    torch.cuda.synchronize()
+    codes = {}
+    for v, g, bits, q, sf in jobs:
+        oq, osf = orc.quantize(bits, g)
+        assert host(sf)[0, 0] == osf[0, 0], (float(v), float(g), host(sf)[0, 0], osf[0, 0])
+        assert np.array_equal(host(q), oq), (float(v), float(g))
+        codes[float(v)] = int(osf[0, 0])
+    # the pages' worked values, reached through the whole quantizer
+    assert codes[float(np.float32(0.001))] == 0x01
+    assert codes[250.0] == 0x78 and codes[248.0] == 0x78 and codes[240.0] == 0x77
+    assert codes[448.0] == 0x7E and codes[464.0] == 0x7E and codes[480.0] == 0x7E
+    assert 0x7F not in codes.values()
+    print(f"E4M3 encoder: {solved.size} of {targets.size} target scales driven, all equal to the oracle")
+
+
+@pytest.mark.parametrize("g", [0.3, 1.0 / 3.7, 0.0123, 7.77, 3.14159e-3, 2.0 ** -20 * 1.37])
+def test_e4m3_encoder_dense_bf16_maxima(nv, orc, g):
+    """Every finite bf16 block maximum (in [bmax, bmax/2, -bmax/3, 0, ...]
+    blocks) under irregular supplied global scales: the products bsf fall
+    densely across the whole E4M3 range, not on a power-of-two grid."""
+    v = np.arange(0, 1 << 15, dtype=np.uint32).astype(np.uint16)
+    v = v[(v & 0x7F80) != 0x7F80]
+    vals = synth.bf16_values(v)
+    blocks = np.zeros((v.size, 16), np.float32)
+    blocks[:, 0] = vals
+    blocks[:, 1] = vals / 2
+    blocks[:, 2] = -vals / 3
+    blocks[:, 7] = vals * np.float32(0.77)
+    bits = synth.bf16_bits(blocks)
+    bits[:, 0] = v
+    _check(nv, orc, bits.reshape(-1, 128), g=g, what=f"dense maxima, g={g}")
