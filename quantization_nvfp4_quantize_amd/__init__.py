@@ -263,7 +263,10 @@ def mx_linear_workspace(M, K, N, device):
 def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
              x_gs=None, xq=None, xsf=None, x_gs_out=None, l1_c=None, l1_q=None, l1_sf=None,
              err_count=None, tile_rows=0, a2_gs_out=None, l1_unfused=False, aux=None):
-    """Build the nvfp4_moe_args struct from tensors (keeps no references).
+    """Build the nvfp4_moe_args struct from tensors.  The struct holds
+    references to every tensor it points at, so they stay allocated for as
+    long as the struct lives (a temporary passed here cannot be freed and its
+    memory reused while a launch still reads it).
     tile_rows: 0 lets the library choose the GEMM tiles; 32 or 256 forces
     one tile height, 288 the mixed tiling (256-row tiles, each expert's last
     block of at most 32 rows on a 32-row tile).
@@ -285,6 +288,8 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
                 _p(w1_q), _p(w1_sf), _p(w1_gs), _p(w2_q), _p(w2_sf), _p(w2_gs), _p(a2_gs),
                 _p(out), code, _p(xq), _p(xsf), _p(x_gs_out), _p(l1_c), _p(l1_q), _p(l1_sf),
                 _p(err_count))
+    a._refs = (x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out, x_gs, xq, xsf, x_gs_out,
+               l1_c, l1_q, l1_sf, err_count, a2_gs_out)
     a.tile_rows = int(tile_rows)
     a.a2_gs_out = _p(a2_gs_out)
     a.l1_unfused = {False: 0, True: 1, 0: 0, 1: 1, 2: 2, "interleaved": 2}[l1_unfused]

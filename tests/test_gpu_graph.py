@@ -153,3 +153,25 @@ def test_graph_keeps_its_workspace(nv):
         assert host(g)[0] == ref[2][0], i
         assert np.array_equal(host(y).view(np.uint32), yref.view(np.uint32)), i
         del junk, big, xb
+
+
+def test_moe_args_keep_their_tensors(nv):
+    """A struct built from temporaries keeps them alive: the scale passed as
+    a temporary is still the one the launch reads after other allocations
+    have run."""
+    import gc
+    cfg = synth.TINY
+    w = gpu_weights(nv, cfg)
+    x = dev_bf16(synth.activations(cfg))
+    ids, wts = synth.routing(cfg)
+    ti, tw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    wl = (w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"], w["w2gs"])
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda:0")
+    used = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    args = nv.moe_args(x, ti, tw, *wl, dev_f32(cfg.a2_gs), y, a2_gs_out=used)
+    gc.collect()
+    junk = [torch.full((64,), 4.0, dtype=torch.float32, device="cuda:0") for _ in range(64)]
+    nv.moe_expert_ffn_raw(args, x.device)
+    torch.cuda.synchronize()
+    assert host(used)[0] == np.float32(cfg.a2_gs)
+    del junk
