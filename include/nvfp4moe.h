@@ -235,6 +235,26 @@ size_t moe_expert_ffn_nvfp4_workspace_size(const nvfp4_moe_args *args);
 int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_expert_ffn_nvfp4_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): moe_expert_ffn_nvfp4 on the same arguments, computing
+ * the same results, with its workspace taken from a static buffer of
+ * NVFP4_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends.  The caller still passes every input and output.
+ * Calls whose workspace (moe_expert_ffn_nvfp4_workspace_size) exceeds that
+ * size are rejected with NVFP4_ERR_WORKSPACE before anything is enqueued;
+ * 64 MiB holds, e.g., the T128 H7168 I2048 k8 decode layer (21.6 MiB with a
+ * bf16 output, 35.4 MiB with fp32) and T256 with a bf16 output.  The first
+ * call on a device looks the buffer's device address up (no allocation);
+ * make that first call outside graph capture.  Every call on one GPU uses
+ * that GPU's one buffer: calls that overlap on the same GPU (two streams,
+ * two threads) race and must be serialized by the caller.  Nothing is
+ * allocated, freed or synchronized.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_expert_ffn_nvfp4_noalloc(const nvfp4_moe_args *args, void *stream);
+
+/*
  * MXFP4 -- a separately labelled format, NOT the pages' NVFP4: the Open
  * Compute Project "Microscaling Formats (MX) Specification" v1.0 format
  * that gfx950's scaled FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) consumes,

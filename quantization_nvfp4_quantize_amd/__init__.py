@@ -64,6 +64,7 @@ _SIG = {
     "mxfp4_linear": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, ctypes.c_int, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_nvfp4_workspace_size": (_sz, [ctypes.POINTER(MoeArgs)]),
     "moe_expert_ffn_nvfp4": (ctypes.c_int, [ctypes.POINTER(MoeArgs), _vp, _sz, _vp]),
+    "moe_expert_ffn_nvfp4_noalloc": (ctypes.c_int, [ctypes.POINTER(MoeArgs), _vp]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -312,6 +313,13 @@ def moe_expert_ffn_raw(args, device, ws=None):
         ws = _workspace(need, device)
     _check(_lib.moe_expert_ffn_nvfp4(ctypes.byref(args), _p(ws), ws.numel(), _stream(device)),
            "moe_expert_ffn_nvfp4")
+
+
+def moe_expert_ffn_noalloc(args, device):
+    """Launch with a prepared MoeArgs on the library's static per-GPU scratch
+    buffer (moe_expert_ffn_nvfp4_noalloc): no workspace is allocated here
+    or in the library.  Calls that overlap on one GPU race on that buffer."""
+    _check(_lib.moe_expert_ffn_nvfp4_noalloc(ctypes.byref(args), _stream(device)), "moe_expert_ffn_nvfp4_noalloc")
 
 
 def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,

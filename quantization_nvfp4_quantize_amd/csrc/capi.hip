@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4moe.h"
 #include "launch.hpp"
 
@@ -602,6 +604,59 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     return st;
   mark(8);
   return NVFP4_OK;
+}
+
+// ------------------------------------------------------------------ no-allocation MoE
+// The workspace of moe_expert_ffn_nvfp4_noalloc: a static device array, one
+// copy per GPU (each holds it until the process ends).  In host code the
+// name `scratch` is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch array.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "moe_expert_ffn_nvfp4_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_ERR_UNSUPPORTED, "moe_expert_ffn_nvfp4_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "moe_expert_ffn_nvfp4_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(NVFP4_ERR_HIP, "moe_expert_ffn_nvfp4_noalloc: no device address for the scratch buffer");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+int moe_expert_ffn_nvfp4_noalloc(const nvfp4_moe_args* a, void* stream) {
+  g_last_error[0] = 0;
+  int st = moe_validate(a);
+  if (st) return st;
+  const size_t need = moe_layout(a).total;
+  if (need > NVFP4_NOALLOC_SCRATCH_BYTES)
+    return fail(NVFP4_ERR_WORKSPACE,
+                "moe_expert_ffn_nvfp4_noalloc: this call needs %zu bytes of workspace, more than the %zu-byte "
+                "static buffer (use moe_expert_ffn_nvfp4 with a caller workspace)",
+                need, (size_t)NVFP4_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws))) return st;
+  // the launch sequence writes every workspace byte it reads (the grouping
+  // kernels zero their own counters), so the previous call's contents do
+  // not matter
+  return moe_expert_ffn_nvfp4(a, ws, NVFP4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -196,3 +196,19 @@ def test_mxfp4_rejects_bad_args(lib):
     assert lib.mxfp4_linear(FAKE, 4, 256, None, FAKE, 256, 0, FAKE, FAKE, ws, None) == -1
     assert lib.mxfp4_linear(FAKE, 4, 256, FAKE, FAKE, 256, 0, FAKE, ctypes.c_void_p(0x10010), ws, None) == -1
     assert b"mxfp4_linear" in lib.nvfp4_last_error()
+
+
+def test_moe_noalloc_rejects_before_any_launch(lib):
+    """The allocation-free MoE entry point validates like the workspace one
+    and rejects a call whose workspace exceeds its static buffer with
+    NVFP4_ERR_WORKSPACE, before touching the device."""
+    by = ctypes.byref
+    assert lib.moe_expert_ffn_nvfp4_noalloc(None, None) == -1
+    assert lib.moe_expert_ffn_nvfp4_noalloc(by(_moe_args(H=200)), None) == -2
+    big = _moe_args(T=16384, H=7168, I=2048, E=256, topk=8)
+    assert lib.moe_expert_ffn_nvfp4_workspace_size(by(big)) > 64 << 20
+    assert lib.moe_expert_ffn_nvfp4_noalloc(by(big), None) == -3
+    msg = lib.nvfp4_last_error()
+    assert b"noalloc" in msg and b"static buffer" in msg
+    dec = _moe_args(T=128, H=7168, I=2048, E=256, topk=8, out_dtype=1)
+    assert lib.moe_expert_ffn_nvfp4_workspace_size(by(dec)) <= 64 << 20
