@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 MoE expert-FFN hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dense,mx,dec,pre] [--no-cpu] [--no-modes]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs quant,expert,dense,mx,dec,pre,tiny] [--no-cpu] [--no-modes]
 
 Prints one JSON line.  `value` is the prefill-shaped MoE layer (T16384 H7168
 I2048 E256 top-8: activation global scale + quantize, grouping, L1 GEMM with
@@ -25,11 +25,19 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
             the fused run)
   prefill_aux  the fused prefill layer with the mixed tiling's 32-row short
             tiles on a second stream, alongside the 256-row tiles
-Timing: W untimed warmups, then K timed steps.  quantize and expert replay a
-HIP graph of K launches between two events (no host gaps); the MoE legs run
-eagerly and the library records HIP events between its stages on the same
-stream, which gives every stage's duration (the L1 GEMM's feeds `roofline`).
-cpu_baseline: the CPU oracle timed on a bounded sample of the prefill layer.
+  tiny      the small MoE layer T64 H256 I128 E8 top-2 (launch-latency bound)
+Timing: W untimed warmups, then K timed steps.  quantize, expert, dense and mx
+replay a HIP graph of K launches between two events (no host gaps), then 50
+more replays each between its own events for a median; the MoE legs run K
+layers eagerly between two events, then at least 10 (prefill) or 50 (decode,
+tiny) layers with an event between consecutive layers for a median, then K
+layers with the library's stage events (HIP events between its stages on the
+same stream), which give every stage's duration (the L1 GEMM's feeds
+`roofline.achieved`).
+cpu_baseline: the CPU oracle, timed in the same run on this host's cores
+(the CPUs this process may use, at most 16), on bounded samples: the prefill
+layer (top level, the unit of `value`), and per leg the decode layer, the
+quantize rows, the single-expert stage rows and the whole tiny layer.
 """
 import argparse
 import ctypes
@@ -61,8 +69,10 @@ def _ev():
     return e
 
 
-def graph_time(fn, steps, warmup):
-    """Mean ms per call of fn(i) from one replay of a graph of `steps` calls."""
+def graph_time(fn, steps, warmup, replays=50, stats=None):
+    """ms per call of fn(i): one replay of a graph of `steps` calls between
+    two events (the mean), then `replays` more replays each between its own
+    two events, whose median per-call time goes to stats["ms_median"]."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -78,7 +88,18 @@ def graph_time(fn, steps, warmup):
     g.replay()
     b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+    ms = a.elapsed_time(b) / steps
+    if stats is not None:
+        evs = [(_ev(), _ev()) for _ in range(replays)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        per = [e0.elapsed_time(e1) / steps for e0, e1 in evs]
+        stats.update(ms_median=float(np.median(per)), median_of=f"{replays} graph replays of {steps} calls")
+    return ms
 
 
 # ------------------------------------------------------------------ quantize
@@ -97,13 +118,15 @@ def bench_quantize(nv, steps, warmup):
     _, _, g = nv.quantize(x0)
     g = g.clone()
     deq = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(ncopy)]
-    q_ms = graph_time(lambda i: nv.quantize(xs[i % ncopy], g, out=outs[i % ncopy]), steps, warmup)
+    qst = {}
+    q_ms = graph_time(lambda i: nv.quantize(xs[i % ncopy], g, out=outs[i % ncopy]), steps, warmup, stats=qst)
     d_ms = graph_time(lambda i: nv.quantize(xs[i % ncopy], None, out=outs[i % ncopy]), steps, warmup)
     dq_ms = graph_time(lambda i: nv.dequantize(outs[i % ncopy][0], outs[i % ncopy][1], g,
                                                out=deq[i % ncopy]), steps, warmup)
     qbytes = 2 * n + n // 2 + n // 16
     return dict(shape=[M, K], algorithmic_bytes=qbytes, quantize_ms=q_ms,
                 quantize_GBps=qbytes / q_ms / 1e6, quantize_frac=qbytes / q_ms / 1e6 / HBM_PEAK_GBS,
+                quantize_ms_median=qst["ms_median"], median_of=qst["median_of"],
                 quantize_dynamic_ms=d_ms,
                 quantize_dynamic_GBps=(qbytes + 2 * n) / d_ms / 1e6,
                 dequantize_ms=dq_ms, dequantize_GBps=(n // 2 + n // 16 + 2 * n) / dq_ms / 1e6)
@@ -392,7 +415,7 @@ def moe_weights(nv, cfg):
     return w1q, w1sf, w1gs, w2q, w2sf, w2gs
 
 
-def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
+def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
     """One MoE layer config; mode "fused" (L1 output quantized in the GEMM
     epilogue with the supplied scale), "unfused" (compact bf16 L1 output,
     separate quantization pass, supplied scale), "interleaved" (interleaved
@@ -433,6 +456,16 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # per-layer times for a median: events between consecutive layers
+    iters = max(steps, median_iters)
+    bounds = [_ev() for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    bounds[0].record()
+    for i in range(iters):
+        nv.moe_expert_ffn_raw(args, dev, ws)
+        bounds[i + 1].record()
+    torch.cuda.synchronize()
+    per_layer = [bounds[i].elapsed_time(bounds[i + 1]) for i in range(iters)]
     # the stage breakdown: a second run with the library's stage events
     evs = [[_ev() for _ in range(STAGE_EVENTS)] for _ in range(steps)]
     handles = [(ctypes.c_void_p * STAGE_EVENTS)(*[e.cuda_event for e in row]) for row in evs]
@@ -445,6 +478,8 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     evented_ms = evs[0][0].elapsed_time(evs[-1][STAGE_EVENTS - 1]) / steps
     stage_ms = {name: float(np.mean([evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)]))
                 for s, name in enumerate(STAGES)}
+    stage_ms_median = {name: float(np.median([evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)]))
+                       for s, name in enumerate(STAGES)}
     stage_ms["l1_gemm_swiglu_quant"] = stage_ms["l1_main"] + stage_ms["l1_rest"]
     stage_ms["l2_gemm"] = stage_ms["l2_main"] + stage_ms["l2_rest"]
     flops = cfg.flops()
@@ -462,10 +497,11 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused"):
     l1_main_flops = 2.0 * main_rows * cfg.H * 2 * cfg.I
     return dict(
         workload=f"T{cfg.T} H{cfg.H} I{cfg.I} E{cfg.E} top{cfg.topk} ({cfg.routing} routing)",
-        ms_per_step=ms, ms_per_step_with_stage_events=evented_ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
+        ms_per_step=ms, ms_median=float(np.median(per_layer)), median_of=f"{iters} layers",
+        ms_per_step_with_stage_events=evented_ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
         experts_touched=int(used.size),
         weight_GBps=used.size * wbytes_per_expert / ms / 1e6,
-        stage_ms=stage_ms,
+        stage_ms=stage_ms, stage_ms_median=stage_ms_median,
         l1_TFLOPs=l1_flops / stage_ms["l1_gemm_swiglu_quant"] / 1e9,
         l2_TFLOPs=l2_flops / stage_ms["l2_gemm"] / 1e9,
         l1_main_rows=main_rows, l1_main_flops=l1_main_flops,
@@ -486,10 +522,12 @@ def bench_expert(nv, steps, warmup):
     outs = (torch.empty((M, I), dtype=torch.bfloat16, device=dev),
             torch.empty((M, I // 2), dtype=torch.uint8, device=dev),
             torch.empty((M, I // 16), dtype=torch.uint8, device=dev))
-    ms = graph_time(lambda i: nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, out=outs), steps, warmup)
+    st = {}
+    ms = graph_time(lambda i: nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, out=outs), steps, warmup, stats=st)
     flops = 2.0 * M * K * 2 * I
     res = dict(workload=f"M{M} K{K} N2x{I}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
-               frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
+               frac=flops / ms / 1e9 / F16_PEAK_TFLOPS, ms_median=st["ms_median"], median_of=st["median_of"],
+               frac_median=flops / st["ms_median"] / 1e9 / F16_PEAK_TFLOPS)
     # Context, not the product path: the vendor library's plain f16 GEMM
     # (torch -> hipBLASLt) on the same operand values, A [M][K] @ B^T with B
     # [2I][K] already dequantized (e2m1 * block scale, global scales left
@@ -517,10 +555,11 @@ def bench_dense(nv, steps, warmup):
     del w
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ws = nv.linear_workspace(M, K, N, dev)
-    ms = graph_time(lambda i: nv.linear(x, wq, wsf, wg, out=out, ws=ws), steps, warmup)
+    st = {}
+    ms = graph_time(lambda i: nv.linear(x, wq, wsf, wg, out=out, ws=ws), steps, warmup, stats=st)
     flops = 2.0 * M * N * K
     return dict(workload=f"M{M} K{K} N{N}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
-                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS)
+                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS, ms_median=st["ms_median"], median_of=st["median_of"])
 
 
 def bench_mx(nv, steps, warmup):
@@ -547,69 +586,149 @@ def bench_mx(nv, steps, warmup):
     del w
     out = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
     ws = nv.mx_linear_workspace(Md, Kd, Nd, dev)
-    l_ms = graph_time(lambda i: nv.mx_linear(x, wq, wsc, out=out, ws=ws), steps, warmup)
+    st = {}
+    l_ms = graph_time(lambda i: nv.mx_linear(x, wq, wsc, out=out, ws=ws), steps, warmup, stats=st)
     flops = 2.0 * Md * Nd * Kd
     return dict(format="MXFP4 (OCP MX v1.0, E8M0 scale per 32 elements; not NVFP4)",
                 quantize_shape=[M, K], quantize_algorithmic_bytes=qbytes, quantize_ms=q_ms,
                 quantize_GBps=qbytes / q_ms / 1e6, quantize_frac=qbytes / q_ms / 1e6 / HBM_PEAK_GBS,
                 linear_workload=f"M{Md} K{Kd} N{Nd}", linear_ms=l_ms, linear_TFLOPs=flops / l_ms / 1e9,
-                linear_algorithmic_flops=flops, linear_frac_fp4_peak=flops / l_ms / 1e9 / FP4_PEAK_TFLOPS)
+                linear_algorithmic_flops=flops, linear_frac_fp4_peak=flops / l_ms / 1e9 / FP4_PEAK_TFLOPS,
+                linear_ms_median=st["ms_median"], median_of=st["median_of"])
 
 
 # ------------------------------------------------------------------ CPU oracle
-def cpu_baseline_moe(cfg, x_bits, ids, wts, ntok=8):
-    """The oracle on a bounded sample of the prefill layer: ntok tokens (all
-    their top-k pairs), weights of the experts they use quantized by the
-    oracle beforehand (untimed, like the GPU's weight preparation)."""
-    import oracle
+# The oracle (plain C, fp64 GEMMs, never tuned) timed on this host's cores in
+# the same run, on bounded samples of each workload.  Threads: the CPUs this
+# process may run on, capped at 16 (one GPU's share of a shared host).
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return dict(cpu_model=model, host_logical_cpus=os.cpu_count(), cpus_available=avail,
+                threads=max(1, min(avail, 16)))
+
+
+def _median_runs(fn, runs):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), ts
+
+
+def _oracle_experts(orc, cfg, experts):
+    """Oracle-quantized weights of the listed experts (model preparation,
+    untimed like the GPU's), drawn on the GPU like the GPU path's."""
     import synth
-    orc = oracle.default()
-    tokens = np.linspace(0, cfg.T - 1, ntok).astype(np.int64)
-    used = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
-    remap = {e: i for i, e in enumerate(used)}
-    ids_r = np.full_like(ids, -1)
-    for t in tokens:
-        ids_r[t] = [remap[int(e)] for e in ids[t]]
-    n = len(used)
+    n = len(experts)
     W = dict(w1q=np.zeros((n, 2 * cfg.I, cfg.H // 2), np.uint8), w1sf=np.zeros((n, 2 * cfg.I, cfg.H // 16), np.uint8),
              w1gs=np.zeros(n, np.float32), w2q=np.zeros((n, cfg.H, cfg.I // 2), np.uint8),
              w2sf=np.zeros((n, cfg.H, cfg.I // 16), np.uint8), w2gs=np.zeros(n, np.float32))
-    for i, e in enumerate(used):
-        a, b = synth.expert_weights(cfg, e, device="cuda:0")
+    for i, e in enumerate(experts):
+        a, b = synth.expert_weights(cfg, int(e), device="cuda:0")
         a, b = synth.torch_bits(a), synth.torch_bits(b)
         W["w1gs"][i] = orc.global_scale(a)
         W["w1q"][i], W["w1sf"][i] = orc.quantize(a, W["w1gs"][i])
         W["w2gs"][i] = orc.global_scale(b)
         W["w2q"][i], W["w2sf"][i] = orc.quantize(b, W["w2gs"][i])
-    threads = min(oracle.default_threads(), ntok)
-    t0 = time.time()
-    orc.moe_tokens(x_bits, ids_r, wts, W["w1q"], W["w1sf"], W["w1gs"], W["w2q"], W["w2sf"], W["w2gs"],
-                   cfg.a2_gs, tokens=tokens, threads=threads)
-    dt = time.time() - t0
-    flops = 6.0 * ntok * cfg.topk * cfg.H * cfg.I
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{ntok} of the {cfg.T} prefill tokens ({ntok * cfg.topk} pairs, all stages "
-                      f"from activation quantization to the combine) in {dt:.1f} s; "
-                      f"oracle weight quantization of {n} experts excluded"}
+    return W
 
 
-def cpu_baseline_quantize(target_s=5.0):
+def _few_expert_tokens(ids, E, ntok, pool):
+    """ntok tokens from the first `pool` tokens, chosen greedily so that they
+    share experts (each next token adds the fewest experts not yet used):
+    the oracle's cost per pair does not depend on which experts, and fewer
+    distinct experts keep its untimed weight preparation short."""
+    used, chosen = set(), []
+    cand = list(range(min(pool, ids.shape[0])))
+    for _ in range(ntok):
+        best = min(cand, key=lambda t: len(set(int(e) for e in ids[t] if 0 <= e < E) - used))
+        cand.remove(best)
+        chosen.append(best)
+        used |= set(int(e) for e in ids[best] if 0 <= e < E)
+    return np.array(sorted(chosen), np.int64), sorted(used)
+
+
+def cpu_baseline_moe(cfg, ntok, runs, threads, pool=512):
+    """The oracle's MoE layer (activation quantization, L1 + SwiGLU, L1-output
+    quantization, L2, combine) on ntok tokens of the workload (all their
+    top-k pairs), median of `runs`; algorithmic TFLOP/s as for the GPU."""
     import oracle
     import synth
     orc = oracle.default()
-    threads = oracle.default_threads()
-    rows = 256
+    x_bits = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    if ntok >= cfg.T:
+        tokens, used = np.arange(cfg.T, dtype=np.int64), sorted(set(int(e) for e in ids.reshape(-1)))
+    else:
+        tokens, used = _few_expert_tokens(ids, cfg.E, ntok, pool)
+    remap = {e: i for i, e in enumerate(used)}
+    ids_r = np.vectorize(lambda e: remap.get(int(e), -1))(ids).astype(np.int32)
+    W = _oracle_experts(orc, cfg, used)
+    def run():  # the activation global scale spans all T tokens, as in the GPU layer
+        g = orc.global_scale(x_bits)
+        orc.moe_tokens(x_bits, ids_r, wts, W["w1q"], W["w1sf"], W["w1gs"], W["w2q"], W["w2sf"], W["w2gs"],
+                       cfg.a2_gs, tokens=tokens, x_gs=g, threads=threads)
+    med, ts = _median_runs(run, runs)
+    pairs = int(((ids[tokens] >= 0) & (ids[tokens] < cfg.E)).sum())
+    flops = 6.0 * pairs * cfg.H * cfg.I
+    return {"value": flops / med / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": med, "runs": [round(t, 3) for t in ts],
+            "sample": f"{tokens.size} of the {cfg.T} tokens of T{cfg.T} H{cfg.H} I{cfg.I} E{cfg.E} top-{cfg.topk} "
+                      f"({pairs} pairs on {len(used)} experts; activation global scale over all T tokens, "
+                      f"quantization, L1 + SwiGLU, L1-output quantization, L2, combine), median of {runs}; "
+                      f"oracle weight quantization excluded"}
+
+
+def cpu_baseline_expert(rows, runs, threads):
+    """The oracle's single-expert stage (M4096 K7168 N 2x2048) on `rows` of
+    its 4096 rows: activation quantization of those rows, L1 + SwiGLU, and
+    quantization of the compact output; median of `runs`."""
+    import oracle
+    import synth
+    orc = oracle.default()
+    xb, w1 = synth.expert_problem(device="cuda:0")
+    wb = synth.torch_bits(w1)
+    gw = orc.global_scale(wb)
+    wq, wsf = orc.quantize(wb, gw)
+    K = xb.shape[1]
+    sel = np.linspace(0, xb.shape[0] - 1, rows).astype(np.int64)
+    xs = np.ascontiguousarray(xb[sel])
+    gx = orc.global_scale(xb)
+    def run():
+        aq, asf = orc.quantize(xs, gx, threads=threads)
+        c, _ = orc.l1_swiglu_rows(aq, asf, gx, wq, wsf, gw, np.arange(rows), threads=threads)
+        orc.quantize(c, np.float32(synth.EXPERT_A2_GS), threads=threads)
+    med, ts = _median_runs(run, runs)
+    flops = 2.0 * rows * K * wq.shape[0]
+    return {"value": flops / med / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": med, "runs": [round(t, 3) for t in ts],
+            "sample": f"{rows} of the 4096 rows (quantize, L1 + SwiGLU, quantize), median of {runs}"}
+
+
+def cpu_baseline_quantize(rows, runs, threads):
+    import oracle
+    import synth
+    orc = oracle.default()
     bits = synth.quant_tensor(rows, synth.QUANT_SHAPE[1], seed=1)
     g = orc.global_scale(bits)
-    t0 = time.time()
-    reps = 0
-    while time.time() - t0 < target_s:
-        orc.quantize(bits, g, threads=threads)
-        reps += 1
-    dt = time.time() - t0
-    n = rows * synth.QUANT_SHAPE[1] * reps
-    return {"value": (2 * n + n // 2 + n // 16) / dt / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": f"{rows} x {synth.QUANT_SHAPE[1]} rows, {reps} repetitions"}
+    med, ts = _median_runs(lambda: orc.quantize(bits, g, threads=threads), runs)
+    n = rows * synth.QUANT_SHAPE[1]
+    return {"value": (2 * n + n // 2 + n // 16) / med / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": med, "runs": [round(t, 3) for t in ts],
+            "sample": f"{rows} x {synth.QUANT_SHAPE[1]} (of the 8192 x 7168 workload; supplied g), median of {runs}"}
 
 
 def main():
@@ -617,7 +736,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="quant,expert,dense,mx,dec,pre")
+    ap.add_argument("--legs", default="quant,expert,dense,mx,dec,pre,tiny")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the unfused and dynamic-scale runs of the prefill layer")
@@ -666,7 +785,7 @@ def main():
         print("# mxfp4 done", flush=True, file=sys.stderr)
         torch.cuda.empty_cache()
     if "dec" in legs:
-        res["decode"], _ = bench_moe(nv, synth.DEC, args.steps, args.warmup)
+        res["decode"], _ = bench_moe(nv, synth.DEC, args.steps, args.warmup, median_iters=50)
         print("# decode done", flush=True, file=sys.stderr)
         torch.cuda.empty_cache()
     pre = None
@@ -679,7 +798,7 @@ def main():
             y_static = pre[4]
             for mode in ("unfused", "interleaved", "dynamic", "aux"):
                 r, extra = bench_moe(nv, synth.PRE, max(3, args.steps // 3), args.warmup, w=pre[0], mode=mode)
-                r = {k: r[k] for k in ("ms_per_step", "TFLOPs", "stage_ms", "a2_gs")}
+                r = {k: r[k] for k in ("ms_per_step", "ms_median", "median_of", "TFLOPs", "stage_ms", "a2_gs")}
                 yd = extra[4]
                 r["y_rel_fro_vs_fused"] = float(torch.linalg.norm(yd - y_static) / torch.linalg.norm(y_static))
                 res["prefill_" + mode] = r
@@ -687,18 +806,34 @@ def main():
                 res["prefill_" + mode]["fusion_saving_ms"] = (res["prefill_" + mode]["ms_per_step"]
                                                              - res["prefill"]["ms_per_step"])
             print("# prefill modes done", flush=True, file=sys.stderr)
+    if "tiny" in legs:
+        # the small workload end to end (launch-latency bound)
+        res["tiny"], _ = bench_moe(nv, synth.TINY, args.steps, args.warmup, median_iters=50)
+        print("# tiny done", flush=True, file=sys.stderr)
     cpu = None
-    if not args.no_cpu and pre is not None:
-        _, xdev, ids, wts, _ = pre
-        xb = synth.activations(synth.PRE)
-        cpu = cpu_baseline_moe(synth.PRE, xb, ids, wts, ntok=48)
+    if not args.no_cpu:
+        # the oracle on this host's cores, same run, bounded samples of each leg
+        info = cpu_info()
+        th = info["threads"]
+        del pre
+        torch.cuda.empty_cache()
+        if "prefill" in res:
+            cpu = dict(cpu_baseline_moe(synth.PRE, ntok=16, runs=1, threads=th), **info)
+        if "decode" in res:
+            res["decode"]["cpu_baseline"] = cpu_baseline_moe(synth.DEC, ntok=8, runs=3, threads=th, pool=128)
         if "quantize" in res:
-            res["quantize"]["cpu_baseline"] = cpu_baseline_quantize()
+            res["quantize"]["cpu_baseline"] = cpu_baseline_quantize(rows=synth.QUANT_SHAPE[0], runs=3, threads=th)
+        if "expert_l1" in res:
+            res["expert_l1"]["cpu_baseline"] = cpu_baseline_expert(rows=32, runs=3, threads=th)
+        if "tiny" in res:
+            res["tiny"]["cpu_baseline"] = cpu_baseline_moe(synth.TINY, ntok=synth.TINY.T, runs=3, threads=th)
+        print("# cpu baseline done", flush=True, file=sys.stderr)
     p = res.get("prefill")
     traffic = mfma = None
     if p:
         traffic = load_traffic("l1_gemm_swiglu_quant_kernel", "pre")
         mfma = load_mfma("l1_gemm_swiglu_quant_kernel", "pre")
+    src = {"file": "profiles/hbm_traffic.md", "kernel_source_hash": source_hash("l1_gemm_swiglu_quant_kernel")}
     line = {
         "metric": "MoE expert-FFN TFLOP/s + quantize GB/s, % of MI355X roofline (1 GPU)",
         "value": p["TFLOPs"] if p else None,
@@ -717,7 +852,14 @@ def main():
                       "algorithmic_flops_per_launch": p["l1_main_flops"],
                       # rocprofv3 counters of the same kernel: MFMA-busy fraction of the SIMD
                       # cycles and the clock it ran at (the 2.5 PFLOP/s peak assumes 2.4 GHz)
-                      "counters": mfma} if p else None),
+                      "counters": mfma,
+                      # traffic and counters are read from the committed rocprofv3 summaries (a
+                      # profiler run of their own), and only while the kernel's sources hash to
+                      # the value recorded with them; achieved comes from this run's HIP events
+                      "traffic_source": dict(src, file="profiles/hbm_traffic.md") if traffic else None,
+                      "counters_source": dict(src, file="profiles/mfma_util.md") if mfma else None,
+                      "achieved_median": p["l1_main_flops"] / p["stage_ms_median"]["l1_main"] / 1e9}
+                     if p else None),
         "cpu_baseline": cpu,
     }
     line.update(res)
