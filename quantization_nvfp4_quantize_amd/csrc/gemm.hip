@@ -156,7 +156,7 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
 // step kb + 2 (read at the start of step kb + 1) and A of step kb + 1, each
 // about two steps after it was issued.  Loads past the end re-read the last
 // step; what they write lands where it is not read again.
-template <int KA, int KB, bool FULL>
+template <int KA, int KB, bool FULL, bool SWAP>
 __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
                                           BScale (&S)[2], f16x8 (&bf)[2], int kb, int bs, int last,
                                           const Operands& op, int wave, int lane, int nmt,
@@ -211,7 +211,8 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
         if (on(mt)) {
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[mt], F.b[nt], acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_f16(F.b[nt], F.a[mt], acc[mt][nt], 0, 0, 0)
+                               : __builtin_amdgcn_mfma_f32_32x32x16_f16(F.a[mt], F.b[nt], acc[mt][nt], 0, 0, 0);
         }
       }
       const int slot = 2 * s + h;
@@ -236,7 +237,7 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
 // All nk steps, A stage period 4 and register-set period 2: whole groups of
 // 4, then the remaining 0..3 steps; bs runs through the B stages 0, 1, 2.
 // Both instantiations pass the same barriers.
-template <bool FULL>
+template <bool FULL, bool SWAP>
 __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
                                            BScale (&S)[2], f16x8 (&bf)[2], int nk,
                                            const Operands& op, int wave, int lane, int nmt,
@@ -245,19 +246,19 @@ __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRa
   int kb = 0, bs = 0;
   auto next = [](int b) { return b == 2 ? 0 : b + 1; };
   for (; kb + 4 <= nk; kb += 4) {
-    gemm_step<0, 0, FULL>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<0, 0, FULL, SWAP>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
-    gemm_step<1, 1, FULL>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<1, 1, FULL, SWAP>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
-    gemm_step<2, 0, FULL>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<2, 0, FULL, SWAP>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
-    gemm_step<3, 1, FULL>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<3, 1, FULL, SWAP>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
   }
   const int rem = nk - kb;
-  if (rem > 0) gemm_step<0, 0, FULL>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
-  if (rem > 1) gemm_step<1, 1, FULL>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
-  if (rem > 2) gemm_step<2, 0, FULL>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
+  if (rem > 0) gemm_step<0, 0, FULL, SWAP>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+  if (rem > 1) gemm_step<1, 1, FULL, SWAP>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
+  if (rem > 2) gemm_step<2, 0, FULL, SWAP>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
 }
 
 // The prologue of a tile's K loop: the direct loads of A steps 0..2 and B
@@ -287,6 +288,7 @@ __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, 
 // scales of step 0 and dequantizes its sub-step 0 fragments, then runs the
 // steps.  Ends with every load landed and all waves past the last LDS read,
 // so the caller may reuse the LDS.
+template <bool SWAP>
 __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int nk, int nrows,
                                           f32x16 (&acc)[4][2], int tid) {
   const int lane = tid & 63;
@@ -314,9 +316,9 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
   }
   lds_barrier();  // B and scale stage 0 are refilled during step 0
   if (nmt == 4)
-    gemm_steps<true>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
+    gemm_steps<true, SWAP>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   else
-    gemm_steps<false>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
+    gemm_steps<false, SWAP>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   wait_vmcnt<0>();
   lds_barrier();
 }
@@ -325,7 +327,7 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
 __device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, int nk, int nrows,
                                               f32x16 (&acc)[4][2]) {
   gemm_prologue(L, op, nk, threadIdx.x);
-  gemm_body(L, op, nk, nrows, acc, threadIdx.x);
+  gemm_body<false>(L, op, nk, nrows, acc, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ persistent grid
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     int claimed = 0;
     if (counter && tid_i == 0) claimed = atomicAdd(counter, 1);
     f32x16 acc[4][2];
-    gemm_body(L, op, nk, t.nrows, acc, tid_i);
+    gemm_body<true>(L, op, nk, t.nrows, acc, tid_i);
     if (counter && tid_i == 0) s_claim[0] = xr.start + claimed;  // published by the epilogue's barrier
     // output row (pair id) and scale alpha * routing weight of every tile row
     if (tid_i < t.nrows) {
@@ -571,15 +573,16 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     __syncthreads();
     const int after = counter ? s_claim[0] : next + (int)(gridDim.x >> 3);
     const int wm = wave_m(tid_i >> 6), wn = wave_n(tid_i >> 6);
-    // A stage 3 is free here (the next item's prologue fills stages 0..2):
-    // 4 KiB of it per wave for the epilogue's transposition
-    float* const scratch = reinterpret_cast<float*>(lds_a + 3 * kLdsOperand) + (tid_i >> 6) * 1024;
     const int64_t col0 = (int64_t)nt * kTileN + wn * 64;
+    // A stage 3 is free here (the next item's prologue fills stages 0..2 and
+    // its first step refills stage 3 only after the barrier that ends every
+    // wave's epilogue): 4 KiB of it per wave for the epilogue's transposition
+    uint4* const scratch = reinterpret_cast<uint4*>(lds_a + 3 * kLdsOperand) + (tid_i >> 6) * 256;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (wm * 128 + mt * 32 >= t.nrows) break;  // wave-uniform
-      l2_store_block(p, acc[mt][0], acc[mt][1], scratch, wm * 128 + mt * 32, t.nrows, col0, lane_i,
-                     [&](int r) { return out_row[r]; }, [&](int r) { return out_scale[r]; });
+      l2_store_rows_t(p, acc[mt], scratch, wm * 128 + mt * 32, t.nrows, col0, lane_i,
+                      [&](int r) { return out_row[r]; }, [&](int r) { return out_scale[r]; });
     }
     if (!more) break;
     item = next;

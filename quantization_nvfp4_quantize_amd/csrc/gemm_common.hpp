@@ -347,5 +347,93 @@ __device__ __forceinline__ void l2_store_block(const L2Params& p, const f32x16& 
   l2_store_rows(p, scratch, r0, nrows, col0, lane, fill, row_of, scale_of);
 }
 
+// Epilogue writer of the L2 / linear GEMMs for the transposed accumulators of
+// one wave's 32-row x 64-column output block, computed as W_tile * A_tile^T
+// (the MFMA operands swapped: the A and B fragments of the 32x32x16 MFMA
+// have the same lane layout): lane l holds tile row r0 + (l & 31) and, in
+// a[nt][i], its column col0 + 32 nt + 8 (i >> 2) + 4 (l >> 5) + (i & 3).  A
+// row's 32-column block nt thus sits in lanes l and l + 32, 16 values each:
+// its maximum takes one exchange between the lane halves, and the values
+// written are those of l2_store_rows -- fp32 (o), bf16 (o_bf16), or f16 with
+// one exponent per (row, 32 columns) (o_f16, o_exp).  fp32 rows go out as
+// four 16 B runs per lane.  The 16-bit forms are packed in registers; four
+// exchanges of packed pairs leave each lane with 16 consecutive columns
+// (16 (l >> 5) .. of each block), which pass through the wave's 4 KiB of LDS
+// (32 rows of 128 B, 16 B chunk c of row r at c ^ (r & 7)) so that every
+// store instruction then writes 8 whole rows of 128 B (lane l: row l / 8 +
+// 8 k, chunk l % 8); the two exponents of a row go out as one 16-bit store.
+// Every lane of the wave must take part.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+template <class RowOf, class ScaleOf>
+__device__ __forceinline__ void l2_store_rows_t(const L2Params& p, const f32x16 (&a)[2], uint4* scratch, int r0,
+                                                int nrows, int64_t col0, int lane, RowOf row_of, ScaleOf scale_of) {
+  const int g = lane >> 5, rl = lane & 31;
+  const int r = r0 + rl;
+  const bool valid = r < nrows;
+  const float sc = valid ? scale_of(r) : 0.0f;
+  if (!p.o_f16 && !p.o_bf16) {
+    if (valid) {
+      const int64_t orow = row_of(r);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& v = a[nt];
+          *reinterpret_cast<float4*>(p.o + orow * p.N + col0 + 32 * nt + 8 * q + 4 * g) =
+              make_float4(v[4 * q] * sc, v[4 * q + 1] * sc, v[4 * q + 2] * sc, v[4 * q + 3] * sc);
+        }
+    }
+    return;
+  }
+  uint32_t ebits = 0;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const f32x16& v = a[nt];
+    uint32_t w[8];
+    if (p.o_f16) {
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+      const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      m = fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1])) * fabsf(sc);
+      const int e = f16_block_exp(m);
+      const float s2 = m > 0.0f ? ldexpf(sc, -e) : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = pack_f16(v[2 * q] * s2, v[2 * q + 1] * s2);
+      ebits |= (uint32_t)(uint8_t)e << (8 * nt);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = pack_bf16(v[2 * q] * sc, v[2 * q + 1] * sc);
+    }
+    // w[q] holds columns 8 (q >> 1) + 4 g + 2 (q & 1) +0, +1; after the
+    // swaps lane half g holds columns 16 g .. 16 g + 15 as w0 w1 w4 w5 w2 w3 w6 w7
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto s = __builtin_amdgcn_permlane32_swap(w[j], w[4 + j], false, false);
+      w[j] = s[0];
+      w[4 + j] = s[1];
+    }
+    const int c0 = 4 * nt + 2 * g;  // 16 B chunk of the row's 128 B
+    scratch[8 * rl + (c0 ^ (rl & 7))] = make_uint4(w[0], w[1], w[4], w[5]);
+    scratch[8 * rl + ((c0 + 1) ^ (rl & 7))] = make_uint4(w[2], w[3], w[6], w[7]);
+  }
+  if (p.o_f16 && valid && g == 0)
+    *reinterpret_cast<uint16_t*>(p.o_exp + (int64_t)row_of(r) * (p.N / 32) + col0 / 32) = (uint16_t)ebits;
+  // the wave's own scratch: its LDS writes above complete before these reads
+  uint16_t* base = p.o_f16 ? p.o_f16 : p.o_bf16;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = (lane >> 3) + 8 * k, c = lane & 7;
+    const uint4 v = scratch[8 * rr + (c ^ (rr & 7))];
+    if (r0 + rr < nrows) *reinterpret_cast<uint4*>(base + (int64_t)row_of(r0 + rr) * p.N + col0 + 8 * c) = v;
+  }
+}
 
 }  // namespace nvfp4
