@@ -327,7 +327,7 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
 __device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, int nk, int nrows,
                                               f32x16 (&acc)[4][2]) {
   gemm_prologue(L, op, nk, threadIdx.x);
-  gemm_body<false>(L, op, nk, nrows, acc, threadIdx.x);
+  gemm_body<true>(L, op, nk, nrows, acc, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ persistent grid
@@ -400,25 +400,44 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   // ---- epilogue: alpha, SwiGLU, bf16 tile in LDS
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
   const int wm = wave_m(wave), wn = wave_n(wave);
-  const int col = 32 * wn + (lane & 31);
   // only the row groups holding valid rows (rows past nrows are never stored)
   const int nmt = __builtin_amdgcn_readfirstlane(active_groups(t.nrows, wm));
   const int64_t I = p.N2 / 2;
   const int hb = tid & 15;
   const int npass = (t.nrows + kGemmThreads / 16 - 1) / (kGemmThreads / 16);
-  // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS
+  // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS.  The
+  // accumulators are transposed (the MFMA computed W_tile * A_tile^T): lane l
+  // holds tile row 128 wm + 32 mt + (l & 31) and, in register i of n tile 0
+  // (gate) and 1 (up), compact column 32 wn + 8 (i >> 2) + 4 (l >> 5) +
+  // (i & 3).  The 16 values are packed in pairs, four exchanges between the
+  // lane halves make them columns 32 wn + 16 (l >> 5) .. + 15 in order, and
+  // two 16 B writes store them.
   auto fill_ctile = [&](bool gate_only) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt < nmt) {
+        uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float gate = acc[mt][0][i] * alpha;
-          const float sg = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
-          const float c = gate_only ? sg : sg * (acc[mt][1][i] * alpha);
-          ctile[(wm * 128 + mt * 32 + acc_row(i, lane)) * kCStride + col] =
-              __builtin_bit_cast(uint16_t, (__bf16)c);
+        for (int q = 0; q < 8; ++q) {
+          float c2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float gate = acc[mt][0][2 * q + h] * alpha;
+            const float sg = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate));
+            c2[h] = gate_only ? sg : sg * (acc[mt][1][2 * q + h] * alpha);
+          }
+          w[q] = pack_bf16(c2[0], c2[1]);
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(w[j], w[4 + j], false, false);
+          w[j] = sw[0];
+          w[4 + j] = sw[1];
+        }
+        uint4* dst = reinterpret_cast<uint4*>(ctile + (wm * 128 + mt * 32 + (lane & 31)) * kCStride +
+                                              32 * wn + 16 * (lane >> 5));
+        dst[0] = make_uint4(w[0], w[1], w[4], w[5]);
+        dst[1] = make_uint4(w[2], w[3], w[6], w[7]);
       }
     }
   };
