@@ -528,6 +528,13 @@ def bench_expert(nv, steps, warmup):
     res = dict(workload=f"M{M} K{K} N2x{I}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS, ms_median=st["ms_median"], median_of=st["median_of"],
                frac_median=flops / st["ms_median"] / 1e9 / F16_PEAK_TFLOPS)
+    # The same stage without a workspace: the GEMM reads the NVFP4
+    # activations and dequantizes each K step into LDS itself (no separate
+    # f16 expansion pass; the expansion then runs inside the MFMA loop).
+    st2 = {}
+    ms_lds = graph_time(lambda i: nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, out=outs, expand_a=False),
+                        steps, warmup, stats=st2)
+    res["nvfp4_activations_in_gemm"] = dict(ms=ms_lds, ms_median=st2["ms_median"], TFLOPs=flops / ms_lds / 1e9)
     # Context, not the product path: the vendor library's plain f16 GEMM
     # (torch -> hipBLASLt) on the same operand values, A [M][K] @ B^T with B
     # [2I][K] already dequantized (e2m1 * block scale, global scales left

@@ -157,9 +157,11 @@ def dequantize(q, sf, gs, out_dtype=torch.bfloat16, out=None):
     return out
 
 
-def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, out=None):
+def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, out=None, expand_a=True):
     """One expert's L1 stage: returns (c bf16 [M][I] or None, c_q [M][I/2],
-    c_sf [M][I/16]).  Weight rows are gate/up interleaved by 8."""
+    c_sf [M][I/16]).  Weight rows are gate/up interleaved by 8.
+    expand_a: pass a workspace (the activations are expanded to f16 once),
+    else none (the GEMM dequantizes the NVFP4 activations into LDS)."""
     for t, n, d in ((a_q, "a_q", torch.uint8), (a_sf, "a_sf", torch.uint8), (a_gs, "a_gs", torch.float32),
                     (w_q, "w_q", torch.uint8), (w_sf, "w_sf", torch.uint8), (w_gs, "w_gs", torch.float32),
                     (out_gs, "out_gs", torch.float32)):
@@ -174,11 +176,10 @@ def gemm_swiglu_quant(a_q, a_sf, a_gs, w_q, w_sf, w_gs, out_gs, want_bf16=True, 
         csf = torch.empty((M, I // 16), dtype=torch.uint8, device=dev)
     else:
         c, cq, csf = out
-    wsz = _lib.nvfp4_gemm_swiglu_quant_workspace_size(M, K, N2)
-    ws = _workspace(wsz, dev)
+    ws = _workspace(_lib.nvfp4_gemm_swiglu_quant_workspace_size(M, K, N2), dev) if expand_a else None
     _check(_lib.nvfp4_gemm_swiglu_quant(_p(a_q), _p(a_sf), _p(a_gs), M, K, _p(w_q), _p(w_sf), _p(w_gs),
-                                        N2, _p(out_gs), _p(c), _p(cq), _p(csf), _p(ws), ws.numel(),
-                                        _stream(dev)), "nvfp4_gemm_swiglu_quant")
+                                        N2, _p(out_gs), _p(c), _p(cq), _p(csf), _p(ws),
+                                        0 if ws is None else ws.numel(), _stream(dev)), "nvfp4_gemm_swiglu_quant")
     return c, cq, csf
 
 

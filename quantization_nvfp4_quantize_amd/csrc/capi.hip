@@ -127,7 +127,7 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
                 (long long)K, (long long)N2);
   if (M > (int64_t)1 << 30) return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: M too large");
   // the GEMM addresses its operands with 32-bit byte offsets
-  if ((__int128)M * K * 2 > kMaxOperandBytes || (__int128)N2 * (K / 2) > kMaxOperandBytes)
+  if ((__int128)M * (K / 2) > kMaxOperandBytes || (__int128)N2 * (K / 2) > kMaxOperandBytes)
     return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: an operand exceeds 4 GiB");
   if (M == 0) return NVFP4_OK;
   if (!a_q || !a_sf || !a_gs || !w_q || !w_sf || !w_gs || !out_gs || !c_q || !c_sf)
@@ -135,16 +135,26 @@ int nvfp4_gemm_swiglu_quant(const uint8_t* a_q, const uint8_t* a_sf, const float
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(a_sf, 4) || !aligned(w_sf, 4) ||
       !aligned(c_q, 4) || !aligned(c_bf16, 16))
     return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: misaligned pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int tiles = (int)((M + nvfp4::gemm_tile_rows() - 1) / nvfp4::gemm_tile_rows());
+  if (!ws) {  // no workspace: the GEMM dequantizes the NVFP4 activations into LDS itself
+    return hip_status(nvfp4::launch_l1(nullptr, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf,
+                                       nullptr, nullptr, nullptr, tiles, M, nullptr, 1, s, nullptr, a_q, a_sf),
+                      "nvfp4_gemm_swiglu_quant");
+  }
+  // with a workspace: expand the activations to exact f16 once, then the GEMM
+  // (measured faster: the expansion inside the MFMA loop costs it more time
+  // than this pass takes)
+  if ((__int128)M * K * 2 > kMaxOperandBytes)
+    return fail(NVFP4_ERR_UNSUPPORTED, "nvfp4_gemm_swiglu_quant: the f16 activations exceed 4 GiB (pass ws = NULL)");
   const size_t need = nvfp4_gemm_swiglu_quant_workspace_size(M, K, N2);
-  if (!ws || ws_bytes < need)
+  if (ws_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "nvfp4_gemm_swiglu_quant: workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned(ws, 256)) return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_gemm_swiglu_quant: ws must be 256-byte aligned");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* a_f16 = static_cast<uint16_t*>(ws);
   int st = hip_status(nvfp4::launch_dequantize_f16(a_q, a_sf, M * K, a_f16, s),
                       "nvfp4_gemm_swiglu_quant (operand)");
   if (st) return st;
-  const int tiles = (int)((M + nvfp4::gemm_tile_rows() - 1) / nvfp4::gemm_tile_rows());
   return hip_status(nvfp4::launch_l1(a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf,
                                      nullptr, nullptr, nullptr, tiles, M, nullptr, 1, s),
                     "nvfp4_gemm_swiglu_quant");
@@ -539,7 +549,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     if (e == hipSuccess)
       e = (skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1)(
           x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf, cf16, tiles, ntiles,
-          L.max_tiles, 0, perm, (int)k, s, c_il);
+          L.max_tiles, 0, perm, (int)k, s, c_il, nullptr, nullptr);
     mark(4);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,

@@ -99,11 +99,30 @@ __device__ __forceinline__ int active_groups(int nrows, int wm) {
 // the 16-lane groups of the fragment reads on distinct banks) | S0 .. S2
 // (1 KiB each: the 4 block-scale bytes of 256 rows).  155 KiB in all.
 
+// With NVFP4 activations (ARAW) the A operand arrives as nibbles and block
+// scales instead of f16: A0, A1 are then the f16 stages, and the space of A2,
+// A3 holds four raw A stages of 9 KiB (512 chunks of nibbles, row r's K half
+// h at chunk 2 r + h, then the 4 scale bytes of each of the 256 rows).  Each
+// lane loads one chunk per step and, during the step before the one that
+// reads it, dequantizes that chunk (32 values) into the step's f16 stage.
+constexpr int kRawChunks = kTileM * 2 + kTileM / 4;  // 576 chunks of 16 B = 9 KiB
+
+__device__ __forceinline__ f16x8* raw_nib(const f16x8* a, int st) {
+  return const_cast<f16x8*>(a) + 2 * kLdsOperand + st * kRawChunks;
+}
+__device__ __forceinline__ uint32_t* raw_sf(const f16x8* a, int st) {
+  return reinterpret_cast<uint32_t*>(raw_nib(a, st) + 2 * kTileM);
+}
+
 // Per-workgroup operand sources of the main loop.  Byte offsets are 32-bit:
 // the A matrix and one expert's weights stay below 4 GiB.
 struct Operands {
   const uint8_t* a;     // A matrix (f16 rows of K), wave-uniform
   uint32_t a_off[4];    // this lane's A sources: tile rows 32 wave + 8 u + lane / 8
+  const uint8_t* aq;    // ARAW: A nibbles (rows of K / 2 bytes), wave-uniform
+  uint32_t aq_off;      // its source: tile row 32 wave + lane / 2, K half lane & 1
+  const uint8_t* asf;   // ARAW: A block scales (rows of K / 16 bytes), wave-uniform
+  uint32_t asf_off;     // its scale source: tile row 64 (wave % 4) + lane
   const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
   uint32_t bq_off;      // this lane's B source: tile row 32 wave + lane / 2, half (lane ^ lane >> 4) & 1
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
@@ -156,7 +175,25 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
 // step kb + 2 (read at the start of step kb + 1) and A of step kb + 1, each
 // about two steps after it was issued.  Loads past the end re-read the last
 // step; what they write lands where it is not read again.
-template <int KA, int KB, bool FULL, bool SWAP>
+// ARAW: dequantize word j (0..3: 8 values) of this lane's raw A chunk in raw
+// stage st (row tid / 2, K half tid & 1; block scale 2 (tid & 1) + j / 2)
+// into its 16 B chunk of f16 stage fst.  The word and the scale byte are
+// read here, so nothing stays live between the calls.
+// Byte offsets (from L.a) are formed from the lane index each time: the
+// caller passes a copy the compiler cannot treat as loop-invariant, so no
+// per-lane addresses stay live across the K loop.
+__device__ __forceinline__ void expand_a_word(const Lds& L, int st, int fst, int wave, int lane, int j) {
+  const uint32_t tid = (uint32_t)(wave * 64 + lane);
+  const uint32_t r = tid >> 1, h = tid & 1;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(L.a) + 2 * kLdsOperand * 16 + st * kRawChunks * 16;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(base + 16 * tid + 4 * j);
+  const uint32_t code = base[2 * kTileM * 16 + 2 * tid + (j >> 1)];  // row r's scale 2 h + j / 2
+  const uint32_t dst = (r * 128 + 16 * ((4 * h) ^ (uint32_t)swz_key((int)r))) ^ (16u * j);
+  *reinterpret_cast<f16x8*>(reinterpret_cast<uint8_t*>(L.a) + fst * kLdsOperand * 16 + dst) =
+      dequant8(w, scale_pair(code));
+}
+
+template <int KA, int KB, bool FULL, bool SWAP, bool ARAW>
 __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
                                           BScale (&S)[2], f16x8 (&bf)[2], int kb, int bs, int last,
                                           const Operands& op, int wave, int lane, int nmt,
@@ -172,7 +209,7 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
   const uint8_t* const a_src = op.a + (size_t)min(kb + 3, last) * (kStepK * 2);
   const uint8_t* const b_src = op.bq + (size_t)min(kb + 3, last) * (kStepK / 2);
   const uint8_t* const s_src = op.bsf + (size_t)min(kb + 3, last) * (kStepK / 16);
-  constexpr int aoff = KA * kLdsOperand;
+  constexpr int aoff = (ARAW ? (KA & 1) : KA) * kLdsOperand;
   // A partial wave (FULL false) reads and multiplies only its row groups
   // mt < nmt; the reads of a full wave stay unconditional, which keeps the
   // compiler's LDS wait counts exact.
@@ -224,20 +261,43 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
           S[KB ^ 1].w[1] = s_next[32];
         }
         dma16s(b_dst, b_src, op.bq_off);
-        if (scales) dma4s(s_dst, s_src, op.bsf_off);
+        if (scales) {
+          dma4s(s_dst, s_src, op.bsf_off);
+        } else if (ARAW) {  // the other half of the waves loads the A scales
+          const int j = min(kb + 3, last);
+          dma4s(raw_sf(L.a, (KA + 3) % 4) + (wave & 3) * 64, op.asf + (size_t)j * (kStepK / 16), op.asf_off);
+        }
       }
-      if (slot >= 1 && slot < 5) dma16s(a_dst + (slot - 1) * 64, a_src, op.a_off[slot - 1]);
+      if (ARAW) {
+        if (slot == 1) {
+          const int j = min(kb + 3, last);
+          dma16s(raw_nib(L.a, (KA + 3) % 4) + wave * 64, op.aq + (size_t)j * (kStepK / 2), op.aq_off);
+        }
+        if (slot >= 2 && slot < 6) {
+          int lane_o = lane;
+          asm volatile("" : "+v"(lane_o));
+          expand_a_word(L, (KA + 1) % 4, (KA + 1) & 1, wave, lane_o, slot - 2);
+        }
+      } else if (slot >= 1 && slot < 5) {
+        dma16s(a_dst + (slot - 1) * 64, a_src, op.a_off[slot - 1]);
+      }
       SCHED_FENCE();
     }
   }
-  wait_vmcnt<10>();
+  // ARAW: 3 loads per step (B, a quarter of the B or A scales, A), so <= 3
+  // outstanding means everything issued during step kb - 1 (all operands
+  // of step kb + 2, needed during step kb + 1) has landed
+  if (ARAW)
+    wait_vmcnt<3>();
+  else
+    wait_vmcnt<10>();
   lds_barrier();
 }
 
 // All nk steps, A stage period 4 and register-set period 2: whole groups of
 // 4, then the remaining 0..3 steps; bs runs through the B stages 0, 1, 2.
 // Both instantiations pass the same barriers.
-template <bool FULL, bool SWAP>
+template <bool FULL, bool SWAP, bool ARAW>
 __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
                                            BScale (&S)[2], f16x8 (&bf)[2], int nk,
                                            const Operands& op, int wave, int lane, int nmt,
@@ -246,39 +306,46 @@ __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRa
   int kb = 0, bs = 0;
   auto next = [](int b) { return b == 2 ? 0 : b + 1; };
   for (; kb + 4 <= nk; kb += 4) {
-    gemm_step<0, 0, FULL, SWAP>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
-    gemm_step<1, 1, FULL, SWAP>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
-    gemm_step<2, 0, FULL, SWAP>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
-    gemm_step<3, 1, FULL, SWAP>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
+    gemm_step<3, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
     bs = next(bs);
   }
   const int rem = nk - kb;
-  if (rem > 0) gemm_step<0, 0, FULL, SWAP>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
-  if (rem > 1) gemm_step<1, 1, FULL, SWAP>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
-  if (rem > 2) gemm_step<2, 0, FULL, SWAP>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
+  if (rem > 0) gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+  if (rem > 1) gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
+  if (rem > 2) gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
 }
 
 // The prologue of a tile's K loop: the direct loads of A steps 0..2 and B
 // steps 0..2 with their scales into LDS stages 0..2.  The LDS stages must be
 // free (every wave past its last read of them).
+template <bool ARAW = false>
 __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, int nk, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int last = nk - 1;
+  if (!ARAW) {
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const uint8_t* a_src = op.a + (size_t)min(j, last) * (kStepK * 2);
+    for (int j = 0; j < 3; ++j) {
+      const uint8_t* a_src = op.a + (size_t)min(j, last) * (kStepK * 2);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      dma16s(L.a + j * kLdsOperand + (4 * wave + u) * 64, a_src, op.a_off[u]);
+      for (int u = 0; u < 4; ++u)
+        dma16s(L.a + j * kLdsOperand + (4 * wave + u) * 64, a_src, op.a_off[u]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    dma16s(L.b + j * kBRaw + wave * 64, op.bq + (size_t)min(j, last) * (kStepK / 2), op.bq_off);
+    const int jj = min(j, last);
+    dma16s(L.b + j * kBRaw + wave * 64, op.bq + (size_t)jj * (kStepK / 2), op.bq_off);
     if ((wave >> 2) == (j & 1))
-      dma4s(L.s + j * kBScale * 4 + (wave & 3) * 64, op.bsf + (size_t)min(j, last) * (kStepK / 16), op.bsf_off);
+      dma4s(L.s + j * kBScale * 4 + (wave & 3) * 64, op.bsf + (size_t)jj * (kStepK / 16), op.bsf_off);
+    else if (ARAW)
+      dma4s(raw_sf(L.a, j) + (wave & 3) * 64, op.asf + (size_t)jj * (kStepK / 16), op.asf_off);
+    if (ARAW) dma16s(raw_nib(L.a, j) + wave * 64, op.aq + (size_t)jj * (kStepK / 2), op.aq_off);
   }
 }
 
@@ -288,7 +355,7 @@ __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, 
 // scales of step 0 and dequantizes its sub-step 0 fragments, then runs the
 // steps.  Ends with every load landed and all waves past the last LDS read,
 // so the caller may reuse the LDS.
-template <bool SWAP>
+template <bool SWAP, bool ARAW = false>
 __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int nk, int nrows,
                                           f32x16 (&acc)[4][2], int tid) {
   const int lane = tid & 63;
@@ -302,6 +369,10 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
   wait_vmcnt<0>();
   lds_barrier();
+  if (ARAW) {  // step 0's A into f16 stage 0 (published by the barrier below)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) expand_a_word(L, 0, 0, wave, lane, j);
+  }
   BRaw R[2];
   BScale S[2];
   R[0].q[0] = __builtin_bit_cast(uint4, rp.b[0]);
@@ -316,18 +387,19 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
   }
   lds_barrier();  // B and scale stage 0 are refilled during step 0
   if (nmt == 4)
-    gemm_steps<true, SWAP>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
+    gemm_steps<true, SWAP, ARAW>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   else
-    gemm_steps<false, SWAP>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
+    gemm_steps<false, SWAP, ARAW>(L, rp, R, S, bf, nk, op, wave, lane, nmt, acc);
   wait_vmcnt<0>();
   lds_barrier();
 }
 
 // The whole K loop of one tile.
+template <bool ARAW>
 __device__ __forceinline__ void gemm_mainloop(const Lds& L, const Operands& op, int nk, int nrows,
                                               f32x16 (&acc)[4][2]) {
-  gemm_prologue(L, op, nk, threadIdx.x);
-  gemm_body<true>(L, op, nk, nrows, acc, threadIdx.x);
+  gemm_prologue<ARAW>(L, op, nk, threadIdx.x);
+  gemm_body<true, ARAW>(L, op, nk, nrows, acc, threadIdx.x);
 }
 
 // ------------------------------------------------------------------ persistent grid
@@ -352,6 +424,7 @@ __device__ __forceinline__ XcdRange xcd_range(int W) {
 }
 
 // ------------------------------------------------------------------ L1
+template <bool ARAW>
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
   __shared__ f16x8 lds_a[kAStages * kLdsOperand];
   __shared__ f16x8 lds_b[kBStages * kBRaw];
@@ -370,14 +443,23 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
     const int rr = r < t.nrows ? r : 0;
     return p.perm ? p.perm[t.row0 + rr] : t.row0 + rr;
   };
+  auto act_row = [&](int r) -> uint32_t {
+    const int o = out_row_of(r);
+    return p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
+  };
   Operands op;
-  op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
+  if (ARAW) {
+    op.aq = p.a_q;
+    op.aq_off = act_row(32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) + 16u * (lane & 1);
+    op.asf = p.a_sf;
+    op.asf_off = act_row(64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
+  } else {
+    op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int R = 32 * wave + 8 * u + (lane >> 3);
-    const int o = out_row_of(R);
-    const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
-    op.a_off[u] = arow * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
+    for (int u = 0; u < 4; ++u) {
+      const int R = 32 * wave + 8 * u + (lane >> 3);
+      op.a_off[u] = act_row(R) * (uint32_t)(p.K * 2) + 16u * ((lane & 7) ^ swz_key(R));
+    }
   }
   op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);
@@ -386,7 +468,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   op.bsf_off = (uint32_t)l1_weight_row(nt, 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
 
   f32x16 acc[4][2];
-  gemm_mainloop(L, op, (int)(p.K / kStepK), t.nrows, acc);
+  gemm_mainloop<ARAW>(L, op, (int)(p.K / kStepK), t.nrows, acc);
 
   // The LDS now holds the epilogue's arrays: the bf16 SwiGLU tile, the
   // reciprocal table and the output row of every tile row.
@@ -636,12 +718,18 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                      uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                     const int* perm, int topk, hipStream_t s, uint16_t* c_il) {
+                     const int* perm, int topk, hipStream_t s, uint16_t* c_il, const uint8_t* a_q,
+                     const uint8_t* a_sf) {
   L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16, c_il,
-             tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
+             tiles, ntiles, M, perm, topk, (int)(N2 / kTileN), a_q, a_sf};
   int64_t grid = (int64_t)max_tiles * p.n_ntiles;
   if (grid == 0) return hipSuccess;
-  l1_gemm_swiglu_quant_kernel<<<(unsigned)grid, kGemmThreads, 0, s>>>(p);
+  if (a_f16)
+    l1_gemm_swiglu_quant_kernel<false><<<(unsigned)grid, kGemmThreads, 0, s>>>(p);
+  else if (a_q && a_sf)
+    l1_gemm_swiglu_quant_kernel<true><<<(unsigned)grid, kGemmThreads, 0, s>>>(p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -207,6 +207,8 @@ struct L1Params {
   const int* perm;      // nullable: sorted position -> pair id
   int topk;             // pair id / topk = activation row
   int n_ntiles;
+  const uint8_t* a_q;   // with a_f16 null (256-row tiles): NVFP4 activations [rows][K/2],
+  const uint8_t* a_sf;  // [rows][K/16], dequantized into LDS inside the GEMM
 };
 
 // Global weight row of the L1 B tile row rb (0..255) for n tile nt: the tile

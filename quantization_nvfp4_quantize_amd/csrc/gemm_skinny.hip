@@ -434,7 +434,11 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                            const int* perm, int topk, hipStream_t s, uint16_t* c_il) {
+                            const int* perm, int topk, hipStream_t s, uint16_t* c_il, const uint8_t* a_q,
+                            const uint8_t* a_sf) {
+  (void)a_q;
+  (void)a_sf;
+  if (!a_f16) return hipErrorInvalidValue;  // the 32-row tiles take f16 activations only
   L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16, c_il,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
   const int64_t grid = (int64_t)max_tiles * p.n_ntiles;

@@ -57,7 +57,8 @@ hipError_t launch_l1(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
                      const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                      uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                      const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                     const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr);
+                     const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr,
+                     const uint8_t* a_q = nullptr, const uint8_t* a_sf = nullptr);
 // L2: o[pair] = alpha * w[pair] * (A @ W_e^T) for the routed rows (fp32), or
 // without routing (tiles, perm, row_w null) over M rows of expert 0, into o
 // (fp32), o_bf16 (bf16) when that is non-null, or o_f16 with o_exp (f16
@@ -78,7 +79,8 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
-                            const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr);
+                            const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr,
+                            const uint8_t* a_q = nullptr, const uint8_t* a_sf = nullptr);
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,

@@ -81,10 +81,19 @@ def test_gemm_stage_rejects(lib):
                                        FAKE, FAKE, None, 0, None) == -1
     assert lib.nvfp4_gemm_swiglu_quant(None, FAKE, FAKE, 4, 64, FAKE, FAKE, FAKE, 256, FAKE, None,
                                        FAKE, FAKE, None, 0, None) == -1
-    # the f16 operand (M * K * 2 bytes) above 4 GiB
-    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, (1 << 25) + 1, 64, FAKE, FAKE, FAKE, 256,
+    # the NVFP4 activation operand (M * K / 2 bytes) above 4 GiB
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, (1 << 27) + 1, 64, FAKE, FAKE, FAKE, 256,
                                        FAKE, None, FAKE, FAKE, None, 0, None) == -2
+    # with a workspace, the f16 copy of the activations (M * K * 2 bytes) above 4 GiB
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, (1 << 25) + 1, 64, FAKE, FAKE, FAKE, 256,
+                                       FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == -2
     assert b"4 GiB" in lib.nvfp4_last_error()
+    # a workspace smaller than the f16 copy
+    need = lib.nvfp4_gemm_swiglu_quant_workspace_size(4, 64, 256)
+    assert need >= 4 * 64 * 2
+    assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, 4, 64, FAKE, FAKE, FAKE, 256,
+                                       FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == -3
+    assert b"workspace" in lib.nvfp4_last_error()
     # M == 0 is a valid no-op
     assert lib.nvfp4_gemm_swiglu_quant(None, None, None, 0, 64, None, None, None, 256, None, None,
                                        None, None, None, 0, None) == 0

@@ -30,12 +30,12 @@ def _problem(M, K, I, seed):
     return x, synth.interleave_gate_up(wn)
 
 
-def _run(nv, orc, x, w, out_gs, rows=None):
+def _run(nv, orc, x, w, out_gs, rows=None, expand_a=True):
     M, K = x.shape
     N2 = w.shape[0]
     xq, xsf, xg = nv.quantize(dev_bf16(x))
     wq, wsf, wg = nv.quantize(dev_bf16(w))
-    c, cq, csf = nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, dev_f32(out_gs))
+    c, cq, csf = nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, dev_f32(out_gs), expand_a=expand_a)
     torch.cuda.synchronize()
     gx, gw = orc.global_scale(x), orc.global_scale(w)
     oq, osf = orc.quantize(x, gx)
@@ -67,11 +67,14 @@ def _gate(r, orc, out_gs, tol=1e-3):
     return err, cos, float((r["csf"] != osf).mean())
 
 
-@pytest.mark.parametrize("M,K,I", [(1, 64, 128), (300, 512, 256), (517, 256, 384)])
-def test_l1_stage_small(nv, orc, M, K, I):
+# expand_a: the activations expanded to f16 in a workspace first, or (False)
+# read as NVFP4 and dequantized into LDS inside the GEMM
+@pytest.mark.parametrize("expand_a", [True, False])
+@pytest.mark.parametrize("M,K,I", [(1, 64, 128), (300, 512, 256), (517, 256, 384), (40, 1216, 128)])
+def test_l1_stage_small(nv, orc, M, K, I, expand_a):
     x, w = _problem(M, K, I, seed=M + K + I)
     out_gs = np.float32(4.0 / 2688.0) * np.float32(np.sqrt(K / 256.0))
-    r = _run(nv, orc, x, w, out_gs)
+    r = _run(nv, orc, x, w, out_gs, expand_a=expand_a)
     err, cos, flip = _gate(r, orc, out_gs)
     print(f"M{M} K{K} I{I}: rel_fro {err:.3e} cos {cos:.7f} scale-byte flips {flip:.2e}")
 
@@ -91,7 +94,8 @@ def test_l1_stage_all_ones(nv, orc):
     assert np.all(r["c"] == want)
 
 
-def test_l1_stage_expert_config_sampled(nv, orc):
+@pytest.mark.parametrize("expand_a", [True, False])
+def test_l1_stage_expert_config_sampled(nv, orc, expand_a):
     """The single-expert workload M4096 K7168 N 2x2048, run in full on the
     GPU, compared on 128 sampled rows (every tile edge included)."""
     x, w1 = synth.expert_problem()
@@ -102,9 +106,23 @@ def test_l1_stage_expert_config_sampled(nv, orc):
     rng = np.random.Generator(np.random.PCG64(41))
     inner = rng.choice(np.setdiff1d(np.arange(4096), edges), size=128 - edges.size, replace=False)
     rows = np.sort(np.concatenate([edges, inner]))
-    r = _run(nv, orc, x, w, np.float32(synth.EXPERT_A2_GS), rows=rows)
+    r = _run(nv, orc, x, w, np.float32(synth.EXPERT_A2_GS), rows=rows, expand_a=expand_a)
     err, cos, flip = _gate(r, orc, np.float32(synth.EXPERT_A2_GS))
     print(f"expert config: rel_fro {err:.3e} cos {cos:.7f} scale-byte flips {flip:.2e}")
+
+
+def test_l1_stage_paths_identical(nv):
+    """Both activation paths feed the same exact f16 values to the same MFMA
+    sequence: every output byte is identical."""
+    x, w = _problem(700, 1024, 256, seed=9)
+    xq, xsf, xg = nv.quantize(dev_bf16(x))
+    wq, wsf, wg = nv.quantize(dev_bf16(w))
+    og = dev_f32(0.01)
+    a = nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, expand_a=True)
+    b = nv.gemm_swiglu_quant(xq, xsf, xg, wq, wsf, wg, og, expand_a=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(a[0]), host_bits(b[0]))
+    assert all(np.array_equal(host(u), host(v)) for u, v in zip(a[1:], b[1:]))
 
 
 def test_l1_stage_deterministic(nv):
