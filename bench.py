@@ -69,10 +69,14 @@ def _ev():
     return e
 
 
-def graph_time(fn, steps, warmup, replays=50, stats=None):
+def graph_time(fn, steps, warmup, replays=50, stats=None, warm_replays=3):
     """ms per call of fn(i): one replay of a graph of `steps` calls between
     two events (the mean), then `replays` more replays each between its own
-    two events, whose median per-call time goes to stats["ms_median"]."""
+    two events, whose median per-call time goes to stats["ms_median"].
+    Before the timed replay, `warm_replays` untimed replays run back to back:
+    a kernel trace showed the per-call time of an MFMA-bound stage still
+    falling through the first two replays after the warm-up calls (211, then
+    205 -> 189, then 181 us per call) while the clock settles."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -81,7 +85,8 @@ def graph_time(fn, steps, warmup, replays=50, stats=None):
         for i in range(steps):
             fn(i)
     torch.cuda.synchronize()
-    g.replay()
+    for _ in range(warm_replays):
+        g.replay()
     torch.cuda.synchronize()
     a, b = _ev(), _ev()
     a.record()
@@ -170,6 +175,8 @@ KERNEL_SOURCES = {
     "mx_quantize_kernel": ["mxfp4.hip", "gemm_common.hpp", "nvfp4_device.hpp", "launch.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+# the dominant kernel of the headline workload: the prefill L1 GEMM (f16 activations)
+ROOFLINE_KERNEL = "l1_gemm_swiglu_quant_kernel<false>"
 
 
 def _code_only(text):
@@ -184,7 +191,7 @@ def _code_only(text):
 def source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in KERNEL_SOURCES[_base(kernel)]:
         with open(os.path.join(ROOT, "quantization_nvfp4_quantize_amd", "csrc", f)) as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -208,7 +215,8 @@ def load_traffic(kernel, workload):
 
 
 def _demangle_last(name):
-    """Innermost identifier of an Itanium-mangled function name (_Z...)."""
+    """Innermost identifier of an Itanium-mangled function name (_Z...), with
+    its template arguments when they are bools or integers ("<true, 8>")."""
     i = 3 if name.startswith("_ZN") else 2
     last = name
     while i < len(name) and name[i].isdigit():
@@ -218,15 +226,32 @@ def _demangle_last(name):
         n = int(name[i:j])
         last = name[j:j + n]
         i = j + n
+    if i < len(name) and name[i] == "I":
+        import re
+        m = re.match(r"I((?:L[bi]\d+E)+)E", name[i:])
+        if m:
+            args = re.findall(r"L([bi])(\d+)E", m.group(1))
+            last += "<" + ", ".join(("true" if v == "1" else "false") if t == "b" else v for t, v in args) + ">"
     return last
 
 
 def _short_name(name):
+    """Kernel name without namespace and parameters, keeping template
+    arguments: l1_gemm_swiglu_quant_kernel<false>."""
     if name.startswith("_Z"):
         return _demangle_last(name)
     base = name.replace("(anonymous namespace)::", "").replace("void ", "")
-    base = base.split("(")[0].split("<")[0]
-    return base.split("::")[-1].strip()
+    base = base.split("(")[0]
+    targs = ""
+    if "<" in base:
+        base, targs = base.split("<", 1)
+        targs = "<" + targs
+    return base.split("::")[-1].strip() + targs
+
+
+def _base(kernel):
+    """A kernel's name without its template arguments."""
+    return kernel.split("<")[0]
 
 
 def _read_counters(path, counter):
@@ -255,15 +280,15 @@ def traffic_summary(copy_fetch, copy_write, legs, cmds):
     copy of known size; one traffic-json line per (leg, kernel, grid)."""
     import collections
     n_copy = 512 << 20
-    cf = [v for k, g, v in _read_counters(copy_fetch, "FETCH_SIZE") if k == "__amd_rocclr_copyBuffer"]
-    cw = [v for k, g, v in _read_counters(copy_write, "WRITE_SIZE") if k == "__amd_rocclr_copyBuffer"]
+    cf = [v for k, g, v in _read_counters(copy_fetch, "FETCH_SIZE") if _base(k) == "__amd_rocclr_copyBuffer"]
+    cw = [v for k, g, v in _read_counters(copy_write, "WRITE_SIZE") if _base(k) == "__amd_rocclr_copyBuffer"]
     f_fac = n_copy / (np.median(cf) * 1024.0)
     w_fac = n_copy / (np.median(cw) * 1024.0)
     agg = collections.defaultdict(lambda: [[], []])
     for leg, fetch, write in legs:
         for i, (path, ctr) in enumerate(((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE"))):
             for k, g, v in _read_counters(path, ctr):
-                if k in KERNEL_SOURCES:
+                if _base(k) in KERNEL_SOURCES:
                     agg[(leg, k, g)][i].append(v)
     out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
            "Commands (from the repository root, on one MI355X; R = repository root; LEG is each of the",
@@ -315,7 +340,7 @@ def trace_summary(legs, cmd):
                                   "route_scan_kernel", "route_place_kernel", "l1_skinny_kernel",
                                   "l2_skinny_kernel", "__amd_rocclr_copyBuffer"}
     for (leg, k, g), v in sorted(agg.items(), key=lambda kv: (kv[0][0], -sum(kv[1]))):
-        if k in mine:
+        if _base(k) in mine:
             out.append(f"| {leg} | {k} | {g} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
     return "\n".join(out) + "\n"
 
@@ -371,7 +396,7 @@ def mfma_summary(legs, cmd):
         util, clk = busy / (gui * SIMDS), gui / dur / 1e9
         out.append(f"| {leg} | {k} | {g} | {n} | {dur * 1e6:.1f} | {clk:.2f} | {100 * util:.1f} % | "
                    f"{flops / dur / 1e12:.0f} |")
-        if k in KERNEL_SOURCES:
+        if _base(k) in KERNEL_SOURCES:
             js.append(json.dumps({"kernel": k, "workload": leg, "grid": g, "src": source_hash(k),
                                   "mfma_busy": util, "clock_ghz": clk, "mfma_flops": flops}))
     out += ["", "Machine-readable lines (bench.py reads these; src = hash of the kernel's sources):", ""]
@@ -442,7 +467,10 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
         aux = (torch.cuda.Stream(), (torch.cuda.Event(), torch.cuda.Event()))
         for e in aux[1]:
             e.record()
-    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out, l1_unfused=flow, aux=aux)
+    # the scale used is read back only in the dynamic flow (elsewhere it is the
+    # supplied one, and asking for it would add a copy launch to every layer)
+    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out if mode == "dynamic" else None, l1_unfused=flow,
+                       aux=aux)
     ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         nv.moe_expert_ffn_raw(args, dev, ws)
@@ -506,7 +534,8 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
         l2_TFLOPs=l2_flops / stage_ms["l2_gemm"] / 1e9,
         l1_main_rows=main_rows, l1_main_flops=l1_main_flops,
         l1_main_TFLOPs=l1_main_flops / stage_ms["l1_main"] / 1e9,
-        l1_flops=l1_flops, l2_flops=l2_flops, mode=mode, a2_gs=float(a2_out.item()),
+        l1_flops=l1_flops, l2_flops=l2_flops, mode=mode,
+        a2_gs=float(a2_out.item()) if mode == "dynamic" else float(a2.item()),
     ), (w, x, ids, wts, out.float())
 
 
@@ -838,9 +867,9 @@ def main():
     p = res.get("prefill")
     traffic = mfma = None
     if p:
-        traffic = load_traffic("l1_gemm_swiglu_quant_kernel", "pre")
-        mfma = load_mfma("l1_gemm_swiglu_quant_kernel", "pre")
-    src = {"file": "profiles/hbm_traffic.md", "kernel_source_hash": source_hash("l1_gemm_swiglu_quant_kernel")}
+        traffic = load_traffic(ROOFLINE_KERNEL, "pre")
+        mfma = load_mfma(ROOFLINE_KERNEL, "pre")
+    src = {"file": "profiles/hbm_traffic.md", "kernel_source_hash": source_hash(ROOFLINE_KERNEL)}
     line = {
         "metric": "MoE expert-FFN TFLOP/s + quantize GB/s, % of MI355X roofline (1 GPU)",
         "value": p["TFLOPs"] if p else None,
@@ -852,7 +881,7 @@ def main():
         "config": {"workload": "prefill-shaped NVFP4 MoE layer T16384 H7168 I2048 E256 top-8 "
                                "(uniform routing), bf16 in/out; plus standalone quantize 8192x7168",
                    "parallelism": "none (1 GPU)"},
-        "roofline": ({"bound": "mfma", "kernel": "l1_gemm_swiglu_quant_kernel (256-row tiles)",
+        "roofline": ({"bound": "mfma", "kernel": ROOFLINE_KERNEL + " (256-row tiles)",
                       "achieved": p["l1_main_TFLOPs"], "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": p["l1_main_TFLOPs"] / F16_PEAK_TFLOPS, "traffic": traffic,
                       "traffic_unit": "bytes per launch (HBM, rocprofv3)",
