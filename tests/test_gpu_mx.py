@@ -116,6 +116,29 @@ def test_mx_linear_vs_oracle(nv, orc, M, K, N):
     assert errb <= 5e-3
 
 
+def test_mx_linear_both_gemm_kernels_agree(nv, orc):
+    """K % 512 == 0 with 16-byte aligned scale codes takes the GEMM that loads
+    the scale codes 4 steps at a time; weight scale codes 4 bytes past a
+    16-byte boundary (the alignment the entry point asks for) take the
+    general GEMM.  Both sum the same MFMA products in the same order,
+    so their outputs agree bit for bit (ragged rows, two column tiles)."""
+    M, K, N = 300, 1024, 512
+    x, (wq, wsc), _ = _mx_problem(nv, orc, M, K, N, seed=11)
+    buf = torch.empty(wsc.numel() + 16, dtype=torch.uint8, device="cuda:0")
+    wsc_odd = buf[4:4 + wsc.numel()].view(wsc.shape)
+    wsc_odd.copy_(wsc)
+    assert wsc.data_ptr() % 16 == 0 and wsc_odd.data_ptr() % 16 == 4
+    xd = dev_bf16(x)
+    y0 = nv.mx_linear(xd, wq, wsc, out_dtype=torch.float32)
+    y1 = nv.mx_linear(xd, wq, wsc_odd, out_dtype=torch.float32)
+    b0 = nv.mx_linear(xd, wq, wsc, out_dtype=torch.bfloat16)
+    b1 = nv.mx_linear(xd, wq, wsc_odd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int32), y1.view(torch.int32))
+    assert torch.equal(b0.view(torch.int16), b1.view(torch.int16))
+    print(f"mx linear M{M} K{K} N{N}: both GEMM kernels bit-identical (fp32 and bf16 out)")
+
+
 def test_mx_linear_full_size_sampled(nv, orc):
     """The benchmark's shape and launch (M4096 K4096 N16384, bf16 out): sampled
     rows and columns against the oracle (MXFP4 quantization is per row, so the
