@@ -27,11 +27,16 @@
 //     that each XCD takes one contiguous range of (M tile, N tile) items,
 //     M-tile-major, and the N tiles of an M tile share one XCD's L2.
 //   * K steps of 64.  A (f16), the raw B nibbles and their block scales go
-//     from global memory straight into LDS (global_load_lds: 8 lanes fetch
-//     one 128 B row, so every request uses whole cache lines and no VGPRs or
-//     LDS write instructions are spent on them), issued three steps ahead
-//     into four A stages and three B / scale stages, each load addressed as
-//     a wave-uniform base plus a 32-bit lane offset.  Their completion is
+//     from global memory straight into LDS (global_load_lds: no VGPRs or LDS
+//     write instructions are spent on them), each load addressed as a
+//     wave-uniform base plus a 32-bit lane offset: A (8 lanes per 128 B row:
+//     whole cache lines) two steps ahead into three A stages, B two steps at
+//     a time (4 lanes per 64 B row: half a line, where one step's 32 B
+//     would use a quarter) about three steps ahead into three two-step B
+//     stages, and the scales three steps ahead into three scale stages.  The
+//     loads are bound by L2-to-L1 line requests more than by bytes: with B
+//     in single steps they were a third of all requests for a tenth of the
+//     bytes.  Their completion is
 //     waited for with explicit load counts before the one LDS-only barrier
 //     per step.  Each wave reads the raw nibbles and scales of its columns
 //     from LDS and dequantizes them in registers with the gfx950 FP4 -> f16
@@ -40,9 +45,9 @@
 //     the 8 MFMA groups of a step (scheduling fences keep the order), and
 //     operand fragments are read one sub-step ahead.
 //   * LDS rows of A are 64 f16 = 8 chunks of 16 B, chunk c stored at
-//     c ^ ((row ^ row >> 3) & 7); raw B half-rows alternate with
-//     (row >> 3) & 1.  Both keep the 16-lane groups of the fragment reads on
-//     distinct banks.
+//     c ^ ((row ^ row >> 3) & 7); the 4 chunks of a two-step raw B row are
+//     permuted with (row >> 2) & 3.  Both keep the 16-lane groups of the
+//     fragment reads on distinct banks.
 //   * The K order inside a 64-chunk is permuted identically for A and B (lane
 //     half g reads physical chunk 4g + s at MFMA step s).
 //   * L1: the 256 B rows of a tile are the gate/up rows of 128 compact SwiGLU
@@ -67,10 +72,13 @@ namespace nvfp4 {
 constexpr int kTileM = 256;
 constexpr int kGemmThreads = 512;
 constexpr int kLdsOperand = kTileM * (kStepK / 8);  // 16 B chunks of one operand stage (32 KiB)
-constexpr int kAStages = 4;
-constexpr int kBStages = 3;
+constexpr int kAStages = 3;     // f16 A stages
+constexpr int kAStagesRaw = 4;  // A room of the NVFP4-A path (2 f16 stages + 4 raw stages)
+constexpr int kBStages = 3;     // single-step B stages of the NVFP4-A path, and scale stages
 constexpr int kBRaw = kTileN * (kStepK / 2) / 16;              // 16 B chunks of raw B per stage (8 KiB)
 constexpr int kBScale = kTileN * (kStepK / 16) / 16;           // 16 B chunks of B scales per stage (1 KiB)
+constexpr int kBPair = 2 * kBRaw;  // 16 B chunks of a two-step B stage of the f16-A path (16 KiB)
+constexpr int kBPairStages = 3;
 
 // The main loop's LDS: three arrays (A stages, raw B stages, scale stages),
 // so that the compiler can tell the A fragment reads and the raw B reads
@@ -93,18 +101,22 @@ __device__ __forceinline__ int active_groups(int nrows, int wm) {
 }
 
 // ------------------------------------------------------------------ operands
-// LDS during the main loop: A0 .. A3 (32 KiB each: 256 rows of 64 f16 =
-// 8 chunks of 16 B) | B0 .. B2 (8 KiB each: 256 rows of 64 raw nibbles =
-// 2 chunks; half h of row r at chunk 2 r + (h ^ ((r >> 3) & 1)), which keeps
-// the 16-lane groups of the fragment reads on distinct banks) | S0 .. S2
-// (1 KiB each: the 4 block-scale bytes of 256 rows).  155 KiB in all.
+// LDS during the main loop (f16 A): A0 .. A2 (32 KiB each: 256 rows of 64
+// f16 = 8 chunks of 16 B) | B0 .. B2 (16 KiB each, two K steps: 256 rows of
+// 2 x 64 raw nibbles = 4 chunks, logical chunk 2 s + h (step s of the two,
+// K half h) of row r at physical chunk (2 s + h) ^ ((r >> 2) & 3), which
+// keeps the 16-lane groups of the fragment reads on distinct banks) |
+// S0 .. S2 (1 KiB each: the 4 block-scale bytes of 256 rows).  147 KiB.
 
 // With NVFP4 activations (ARAW) the A operand arrives as nibbles and block
-// scales instead of f16: A0, A1 are then the f16 stages, and the space of A2,
-// A3 holds four raw A stages of 9 KiB (512 chunks of nibbles, row r's K half
-// h at chunk 2 r + h, then the 4 scale bytes of each of the 256 rows).  Each
-// lane loads one chunk per step and, during the step before the one that
-// reads it, dequantizes that chunk (32 values) into the step's f16 stage.
+// scales instead of f16: A0, A1 are the f16 stages, and after them four raw
+// A stages of 9 KiB (512 chunks of nibbles, row r's K half h at chunk
+// 2 r + h, then the 4 scale bytes of each of the 256 rows) in the room of
+// two more A stages; B then keeps single-step stages (8 KiB each: 256 rows
+// of 2 chunks, half h of row r at chunk 2 r + (h ^ ((r >> 3) & 1))).  Each
+// lane loads one raw A chunk per step and, during the step before the one
+// that reads it, dequantizes that chunk (32 values) into the step's f16
+// stage.
 constexpr int kRawChunks = kTileM * 2 + kTileM / 4;  // 576 chunks of 16 B = 9 KiB
 
 __device__ __forceinline__ f16x8* raw_nib(const f16x8* a, int st) {
@@ -127,6 +139,9 @@ struct Operands {
   uint32_t bq_off;      // this lane's B source: tile row 32 wave + lane / 2, half (lane ^ lane >> 4) & 1
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
   uint32_t bsf_off;     // this lane's scale source: tile row 64 (wave % 4) + lane
+  uint32_t bq_row[2];   // f16-A path: byte offsets of the B rows 32 wave + 16 u + lane / 4
+  uint32_t bq_lc;       // 16 x the logical chunk this lane loads: (lane & 3) ^ ((lane >> 4) & 3)
+  uint32_t bq_lim;      // K / 2 - 16: last 16 B of a row
 };
 
 struct Frags {
@@ -142,6 +157,7 @@ struct ReadPtrs {
   const f16x8* b;     // this lane's raw B chunk of column tile 0 in B stage 0 (tile 1: + 64,
                       // rows 32 apart keep the same swizzle bit)
   const uint32_t* s;  // its scale word of column tile 0 in scale stage 0 (tile 1: + 32)
+  const f16x8* bp[2];  // f16-A path: the raw B chunk of step parity s' in two-step stage 0 (tile 1: + 128)
 };
 
 __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int lane) {
@@ -156,6 +172,9 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
     }
   rp.b = L.b + 2 * (wn * 64 + r) + (g ^ ((r >> 3) & 1));
   rp.s = L.s + wn * 64 + r;
+  const int key4 = (r >> 2) & 3;
+  rp.bp[0] = L.b + 4 * (wn * 64 + r) + (g ^ key4);
+  rp.bp[1] = L.b + 4 * (wn * 64 + r) + ((2 + g) ^ key4);
   return rp;
 }
 
@@ -166,15 +185,21 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
 // dequantizes the next B fragments in registers, the last group preparing the
 // B fragments of sub-step 0 of step kb + 1 (bf).  Between the groups it reads
 // the raw B and the scales of step kb + 1 into R[KB ^ 1], S[KB ^ 1], then
-// issues, in this order, the direct loads of B step kb + 3 into B stage bs,
-// of its scales (waves 4 KB .. 4 KB + 3, a quarter of the rows each) into
-// scale stage bs, and of A step kb + 3 into A stage (KA + 3) % 4.  Over any
-// two consecutive steps a wave issues 11 loads (5 + 6), so waiting at the end
-// of step kb until at most 10 are outstanding means: everything up to and
-// including the first load of step kb - 1 has landed -- B and scales of
-// step kb + 2 (read at the start of step kb + 1) and A of step kb + 1, each
-// about two steps after it was issued.  Loads past the end re-read the last
-// step; what they write lands where it is not read again.
+// issues, in this order, the direct loads of B, of the scales of step kb + 3
+// (waves 4 KB .. 4 KB + 3, a quarter of the rows each) into scale stage bs
+// and of A step kb + 2 into A stage (KA + 2) % 3.  f16 A: B goes two steps
+// at a time, each step one half of the rows of a two-step stage (16 rows per
+// load): in step kb the rows 16 (KB ^ 1) .. of each wave's 32 for the steps
+// 2P, 2P + 1, P = (kb + 5) / 2, into two-step stage P % 3 (the one of steps
+// kb - 1, kb or kb, kb - 1, read by step kb - 1 at the latest).  A wave
+// issues 5 or 6 loads per step, and everything that step kb + 1 reads (A of
+// step kb + 1, B and scales of step kb + 2) was issued before step kb, so
+// waiting at the end of step kb until at most 5 are outstanding (the loads
+// retire in order) is enough.  Loads past the end re-read the last step (the
+// last pair), and a lane's 16 B past the end of a row (an odd step count)
+// re-read the row's last 16 B; what they write is never read.  ARAW: B one
+// step at a time into B stage bs (B step kb + 3), A step kb + 3 as raw
+// nibbles and scales, 3 loads per step (see the end of the step).
 // ARAW: dequantize word j (0..3: 8 values) of this lane's raw A chunk in raw
 // stage st (row tid / 2, K half tid & 1; block scale 2 (tid & 1) + j / 2)
 // into its 16 B chunk of f16 stage fst.  The word and the scale byte are
@@ -200,13 +225,16 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
                                           f32x16 (&acc)[4][2]) {
   const int g = lane >> 5;
   const bool scales = (wave >> 2) == KB;  // this wave loads a quarter of the scales
-  f16x8* const a_dst = L.a + ((KA + 3) % 4) * kLdsOperand + (4 * wave) * 64;
+  f16x8* const a_dst = L.a + (ARAW ? 0 : ((KA + 2) % 3)) * kLdsOperand + (4 * wave) * 64;
   f16x8* const b_dst = L.b + bs * kBRaw + wave * 64;
   uint32_t* const s_dst = L.s + bs * kBScale * 4 + (wave & 3) * 64;
   const int bn = (bs == 2) ? 0 : bs + 1;  // B / scale stage of step kb + 1
-  const f16x8* const b_next = rp.b + bn * kBRaw;
+  // f16 A: kb % 6 from the stage periods; step kb + 1 sits in two-step
+  // stage ((kb + 1) % 6) / 2 at parity (kb + 1) & 1
+  constexpr int kb6 = (3 * KB + 4 * KA) % 6, n6 = (kb6 + 1) % 6;
+  const f16x8* const b_next = ARAW ? rp.b + bn * kBRaw : rp.bp[n6 & 1] + (n6 >> 1) * kBPair;
   const uint32_t* const s_next = rp.s + bn * kBScale * 4;
-  const uint8_t* const a_src = op.a + (size_t)min(kb + 3, last) * (kStepK * 2);
+  const uint8_t* const a_src = op.a + (size_t)min(kb + 2, last) * (kStepK * 2);
   const uint8_t* const b_src = op.bq + (size_t)min(kb + 3, last) * (kStepK / 2);
   const uint8_t* const s_src = op.bsf + (size_t)min(kb + 3, last) * (kStepK / 16);
   constexpr int aoff = (ARAW ? (KA & 1) : KA) * kLdsOperand;
@@ -256,11 +284,20 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
       if (slot == 0) {
         if (on(0)) {  // a wave without valid rows needs no B
           R[KB ^ 1].q[0] = __builtin_bit_cast(uint4, b_next[0]);
-          R[KB ^ 1].q[1] = __builtin_bit_cast(uint4, b_next[64]);
+          R[KB ^ 1].q[1] = __builtin_bit_cast(uint4, b_next[ARAW ? 64 : 128]);
           S[KB ^ 1].w[0] = s_next[0];
           S[KB ^ 1].w[1] = s_next[32];
         }
-        dma16s(b_dst, b_src, op.bq_off);
+        if (ARAW) {
+          dma16s(b_dst, b_src, op.bq_off);
+        } else {
+          // half lu of the rows of the two-step stage of steps 2P, 2P + 1,
+          // P = (kb + 5) / 2 (64 B of each row: half of a line)
+          constexpr int lst = ((kb6 + 5) % 6) >> 1, lu = KB ^ 1;
+          const int P = min((kb + 5) >> 1, last >> 1);
+          const uint32_t off = op.bq_row[lu] + min((uint32_t)(64 * P) + op.bq_lc, op.bq_lim);
+          dma16s(L.b + lst * kBPair + (32 * wave + 16 * lu) * 4, op.bq, off);
+        }
         if (scales) {
           dma4s(s_dst, s_src, op.bsf_off);
         } else if (ARAW) {  // the other half of the waves loads the A scales
@@ -290,13 +327,14 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
   if (ARAW)
     wait_vmcnt<3>();
   else
-    wait_vmcnt<10>();
+    wait_vmcnt<5>();
   lds_barrier();
 }
 
-// All nk steps, A stage period 4 and register-set period 2: whole groups of
-// 4, then the remaining 0..3 steps; bs runs through the B stages 0, 1, 2.
-// Both instantiations pass the same barriers.
+// All nk steps.  f16 A: A stage period 3 and register-set period 2, whole
+// groups of 6, then the remaining 0..5 steps; bs = kb % 3 (the scale stage).
+// ARAW: A stage period 4, groups of 4; bs runs through the B stages 0, 1, 2.
+// Both instantiations (FULL) pass the same barriers.
 template <bool FULL, bool SWAP, bool ARAW>
 __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
                                            BScale (&S)[2], f16x8 (&bf)[2], int nk,
@@ -305,24 +343,44 @@ __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRa
   const int last = nk - 1;
   int kb = 0, bs = 0;
   auto next = [](int b) { return b == 2 ? 0 : b + 1; };
-  for (; kb + 4 <= nk; kb += 4) {
-    gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
-    bs = next(bs);
-    gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
-    bs = next(bs);
-    gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
-    bs = next(bs);
-    gemm_step<3, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
-    bs = next(bs);
+  if (ARAW) {
+    for (; kb + 4 <= nk; kb += 4) {
+      gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+      bs = next(bs);
+      gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, bs, last, op, wave, lane, nmt, acc);
+      bs = next(bs);
+      gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, bs, last, op, wave, lane, nmt, acc);
+      bs = next(bs);
+      gemm_step<3, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 3, bs, last, op, wave, lane, nmt, acc);
+      bs = next(bs);
+    }
+    const int rem = nk - kb;
+    if (rem > 0) gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
+    if (rem > 1) gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
+    if (rem > 2) gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
+    return;
+  }
+  // f16 A: stage period 3 (KA = kb % 3 = bs), register sets period 2
+  for (; kb + 6 <= nk; kb += 6) {
+    gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, 0, last, op, wave, lane, nmt, acc);
+    gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, 1, last, op, wave, lane, nmt, acc);
+    gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, 2, last, op, wave, lane, nmt, acc);
+    gemm_step<0, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 3, 0, last, op, wave, lane, nmt, acc);
+    gemm_step<1, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 4, 1, last, op, wave, lane, nmt, acc);
+    gemm_step<2, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 5, 2, last, op, wave, lane, nmt, acc);
   }
   const int rem = nk - kb;
-  if (rem > 0) gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, bs, last, op, wave, lane, nmt, acc);
-  if (rem > 1) gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, next(bs), last, op, wave, lane, nmt, acc);
-  if (rem > 2) gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, next(next(bs)), last, op, wave, lane, nmt, acc);
+  if (rem > 0) gemm_step<0, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb, 0, last, op, wave, lane, nmt, acc);
+  if (rem > 1) gemm_step<1, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 1, 1, last, op, wave, lane, nmt, acc);
+  if (rem > 2) gemm_step<2, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 2, 2, last, op, wave, lane, nmt, acc);
+  if (rem > 3) gemm_step<0, 1, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 3, 0, last, op, wave, lane, nmt, acc);
+  if (rem > 4) gemm_step<1, 0, FULL, SWAP, ARAW>(L, rp, R, S, bf, kb + 4, 1, last, op, wave, lane, nmt, acc);
 }
 
-// The prologue of a tile's K loop: the direct loads of A steps 0..2 and B
-// steps 0..2 with their scales into LDS stages 0..2.  The LDS stages must be
+// The prologue of a tile's K loop.  f16 A: the direct loads of A steps 0, 1,
+// of B steps 0..3 and the first half of the rows of steps 4, 5 (two-step
+// stages 0, 1 and half of 2), and of the scales of steps 0..2.  ARAW: B, A
+// and the scales of steps 0..2.  The LDS stages must be
 // free (every wave past its last read of them).
 template <bool ARAW = false>
 __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, int nk, int tid) {
@@ -330,17 +388,28 @@ __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, 
   const int last = nk - 1;
   if (!ARAW) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const uint8_t* a_src = op.a + (size_t)min(j, last) * (kStepK * 2);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         dma16s(L.a + j * kLdsOperand + (4 * wave + u) * 64, a_src, op.a_off[u]);
     }
   }
+  if (!ARAW) {  // two-step B stages 0, 1 and the first half of stage 2
+#pragma unroll
+    for (int P = 0; P < 3; ++P)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (P == 2 && u == 1) break;
+        const uint32_t off =
+            op.bq_row[u] + min((uint32_t)(64 * min(P, last >> 1)) + op.bq_lc, op.bq_lim);
+        dma16s(L.b + P * kBPair + (32 * wave + 16 * u) * 4, op.bq, off);
+      }
+  }
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int jj = min(j, last);
-    dma16s(L.b + j * kBRaw + wave * 64, op.bq + (size_t)jj * (kStepK / 2), op.bq_off);
+    if (ARAW) dma16s(L.b + j * kBRaw + wave * 64, op.bq + (size_t)jj * (kStepK / 2), op.bq_off);
     if ((wave >> 2) == (j & 1))
       dma4s(L.s + j * kBScale * 4 + (wave & 3) * 64, op.bsf + (size_t)jj * (kStepK / 16), op.bsf_off);
     else if (ARAW)
@@ -375,8 +444,9 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
   }
   BRaw R[2];
   BScale S[2];
-  R[0].q[0] = __builtin_bit_cast(uint4, rp.b[0]);
-  R[0].q[1] = __builtin_bit_cast(uint4, rp.b[64]);
+  const f16x8* const b0 = ARAW ? rp.b : rp.bp[0];  // step 0: stage 0 (parity 0 of two-step stage 0)
+  R[0].q[0] = __builtin_bit_cast(uint4, b0[0]);
+  R[0].q[1] = __builtin_bit_cast(uint4, b0[ARAW ? 64 : 128]);
   S[0].w[0] = rp.s[0];
   S[0].w[1] = rp.s[32];
   f16x8 bf[2];
@@ -426,8 +496,8 @@ __device__ __forceinline__ XcdRange xcd_range(int W) {
 // ------------------------------------------------------------------ L1
 template <bool ARAW>
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
-  __shared__ f16x8 lds_a[kAStages * kLdsOperand];
-  __shared__ f16x8 lds_b[kBStages * kBRaw];
+  __shared__ f16x8 lds_a[(ARAW ? kAStagesRaw : kAStages) * kLdsOperand];
+  __shared__ f16x8 lds_b[ARAW ? kBStages * kBRaw : kBPairStages * kBPair];
   __shared__ uint32_t lds_s[kBStages * kBScale * 4];
   const Lds L{lds_a, lds_b, lds_s};
 
@@ -466,6 +536,11 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
   op.bq_off = (uint32_t)l1_weight_row(nt, 32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) +
               16u * ((lane ^ (lane >> 4)) & 1);
   op.bsf_off = (uint32_t)l1_weight_row(nt, 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    op.bq_row[u] = (uint32_t)l1_weight_row(nt, 32 * wave + 16 * u + (lane >> 2)) * (uint32_t)(p.K / 2);
+  op.bq_lc = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  op.bq_lim = (uint32_t)(p.K / 2) - 16u;
 
   f32x16 acc[4][2];
   gemm_mainloop<ARAW>(L, op, (int)(p.K / kStepK), t.nrows, acc);
@@ -572,7 +647,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
 // larger epilogue state pushed the K loop into register spills.
 __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   __shared__ f16x8 lds_a[kAStages * kLdsOperand];
-  __shared__ f16x8 lds_b[kBStages * kBRaw];
+  __shared__ f16x8 lds_b[kBPairStages * kBPair];
   __shared__ uint32_t lds_s[kBStages * kBScale * 4];
   __shared__ int out_row[kTileM];
   __shared__ float out_scale[kTileM];
@@ -636,6 +711,11 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     op.bq_off = (uint32_t)(nt * kTileN + 32 * wave + (lane >> 1)) * (uint32_t)(p.K / 2) +
                 16u * ((lane ^ (lane >> 4)) & 1);
     op.bsf_off = (uint32_t)(nt * kTileN + 64 * (wave & 3) + lane) * (uint32_t)(p.K / 16);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      op.bq_row[u] = (uint32_t)(nt * kTileN + 32 * wave + 16 * u + (lane >> 2)) * (uint32_t)(p.K / 2);
+    op.bq_lc = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    op.bq_lim = (uint32_t)(p.K / 2) - 16u;
   };
 
   GemmTile t;
@@ -678,7 +758,7 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
     // A stage 3 is free here (the next item's prologue fills stages 0..2 and
     // its first step refills stage 3 only after the barrier that ends every
     // wave's epilogue): 4 KiB of it per wave for the epilogue's transposition
-    uint4* const scratch = reinterpret_cast<uint4*>(lds_a + 3 * kLdsOperand) + (tid_i >> 6) * 256;
+    uint4* const scratch = reinterpret_cast<uint4*>(lds_a + 2 * kLdsOperand) + (tid_i >> 6) * 256;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (wm * 128 + mt * 32 >= t.nrows) break;  // wave-uniform
