@@ -33,10 +33,11 @@
 //     whole cache lines) two steps ahead into three A stages, B two steps at
 //     a time (4 lanes per 64 B row: half a line, where one step's 32 B
 //     would use a quarter) about three steps ahead into three two-step B
-//     stages, and the scales three steps ahead into three scale stages.  The
-//     loads are bound by L2-to-L1 line requests more than by bytes: with B
-//     in single steps they were a third of all requests for a tenth of the
-//     bytes.  Their completion is
+//     stages, and the scales four steps at a time (4 lanes per row's 16 B,
+//     where one step's 4 B took a line request of its own) into two
+//     four-step scale stages.  The loads are bound by L2-to-L1 line requests
+//     more than by bytes: with B and scales in single steps these two took
+//     two thirds of all requests for a fifth of the bytes.  Their completion is
 //     waited for with explicit load counts before the one LDS-only barrier
 //     per step.  Each wave reads the raw nibbles and scales of its columns
 //     from LDS and dequantizes them in registers with the gfx950 FP4 -> f16
@@ -74,11 +75,12 @@ constexpr int kGemmThreads = 512;
 constexpr int kLdsOperand = kTileM * (kStepK / 8);  // 16 B chunks of one operand stage (32 KiB)
 constexpr int kAStages = 3;     // f16 A stages
 constexpr int kAStagesRaw = 4;  // A room of the NVFP4-A path (2 f16 stages + 4 raw stages)
-constexpr int kBStages = 3;     // single-step B stages of the NVFP4-A path, and scale stages
+constexpr int kBStages = 3;     // single-step B and scale stages of the NVFP4-A path
 constexpr int kBRaw = kTileN * (kStepK / 2) / 16;              // 16 B chunks of raw B per stage (8 KiB)
 constexpr int kBScale = kTileN * (kStepK / 16) / 16;           // 16 B chunks of B scales per stage (1 KiB)
 constexpr int kBPair = 2 * kBRaw;  // 16 B chunks of a two-step B stage of the f16-A path (16 KiB)
 constexpr int kBPairStages = 3;
+constexpr int kSQuad = kTileN * 4;  // dwords of a four-step scale stage of the f16-A path (4 KiB)
 
 // The main loop's LDS: three arrays (A stages, raw B stages, scale stages),
 // so that the compiler can tell the A fragment reads and the raw B reads
@@ -106,14 +108,16 @@ __device__ __forceinline__ int active_groups(int nrows, int wm) {
 // 2 x 64 raw nibbles = 4 chunks, logical chunk 2 s + h (step s of the two,
 // K half h) of row r at physical chunk (2 s + h) ^ ((r >> 2) & 3), which
 // keeps the 16-lane groups of the fragment reads on distinct banks) |
-// S0 .. S2 (1 KiB each: the 4 block-scale bytes of 256 rows).  147 KiB.
+// S0, S1 (4 KiB each, four K steps: row r's 4 block-scale bytes of step s
+// at dword 4 r + s).  152 KiB.
 
 // With NVFP4 activations (ARAW) the A operand arrives as nibbles and block
 // scales instead of f16: A0, A1 are the f16 stages, and after them four raw
 // A stages of 9 KiB (512 chunks of nibbles, row r's K half h at chunk
 // 2 r + h, then the 4 scale bytes of each of the 256 rows) in the room of
-// two more A stages; B then keeps single-step stages (8 KiB each: 256 rows
-// of 2 chunks, half h of row r at chunk 2 r + (h ^ ((r >> 3) & 1))).  Each
+// two more A stages; B and the scales then keep single-step stages (8 KiB
+// each: 256 rows of 2 chunks, half h of row r at chunk 2 r + (h ^ ((r >> 3)
+// & 1)); 1 KiB each: the 4 scale bytes of 256 rows).  Each
 // lane loads one raw A chunk per step and, during the step before the one
 // that reads it, dequantizes that chunk (32 values) into the step's f16
 // stage.
@@ -142,6 +146,7 @@ struct Operands {
   uint32_t bq_row[2];   // f16-A path: byte offsets of the B rows 32 wave + 16 u + lane / 4
   uint32_t bq_lc;       // 16 x the logical chunk this lane loads: (lane & 3) ^ ((lane >> 4) & 3)
   uint32_t bq_lim;      // K / 2 - 16: last 16 B of a row
+  uint32_t sf_lim;      // K / 16 - 4: last 4 B of a scale row
 };
 
 struct Frags {
@@ -158,6 +163,7 @@ struct ReadPtrs {
                       // rows 32 apart keep the same swizzle bit)
   const uint32_t* s;  // its scale word of column tile 0 in scale stage 0 (tile 1: + 32)
   const f16x8* bp[2];  // f16-A path: the raw B chunk of step parity s' in two-step stage 0 (tile 1: + 128)
+  const uint32_t* sq;  // f16-A path: its scale words of four-step scale stage 0 (step j: + j % 4; tile 1: + 128)
 };
 
 __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int lane) {
@@ -175,6 +181,7 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
   const int key4 = (r >> 2) & 3;
   rp.bp[0] = L.b + 4 * (wn * 64 + r) + (g ^ key4);
   rp.bp[1] = L.b + 4 * (wn * 64 + r) + ((2 + g) ^ key4);
+  rp.sq = L.s + 4 * (wn * 64 + r);
   return rp;
 }
 
@@ -185,21 +192,23 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
 // dequantizes the next B fragments in registers, the last group preparing the
 // B fragments of sub-step 0 of step kb + 1 (bf).  Between the groups it reads
 // the raw B and the scales of step kb + 1 into R[KB ^ 1], S[KB ^ 1], then
-// issues, in this order, the direct loads of B, of the scales of step kb + 3
-// (waves 4 KB .. 4 KB + 3, a quarter of the rows each) into scale stage bs
-// and of A step kb + 2 into A stage (KA + 2) % 3.  f16 A: B goes two steps
-// at a time, each step one half of the rows of a two-step stage (16 rows per
-// load): in step kb the rows 16 (KB ^ 1) .. of each wave's 32 for the steps
-// 2P, 2P + 1, P = (kb + 5) / 2, into two-step stage P % 3 (the one of steps
-// kb - 1, kb or kb, kb - 1, read by step kb - 1 at the latest).  A wave
-// issues 5 or 6 loads per step, and everything that step kb + 1 reads (A of
-// step kb + 1, B and scales of step kb + 2) was issued before step kb, so
-// waiting at the end of step kb until at most 5 are outstanding (the loads
-// retire in order) is enough.  Loads past the end re-read the last step (the
-// last pair), and a lane's 16 B past the end of a row (an odd step count)
-// re-read the row's last 16 B; what they write is never read.  ARAW: B one
-// step at a time into B stage bs (B step kb + 3), A step kb + 3 as raw
-// nibbles and scales, 3 loads per step (see the end of the step).
+// issues, in this order, the direct loads of B, of scales and of A step
+// kb + 2 into A stage (KA + 2) % 3.  f16 A: B goes two steps at a time,
+// each step one half of the rows of a two-step stage (16 rows per load): in
+// step kb the rows 16 (KB ^ 1) .. of each wave's 32 for the steps 2P,
+// 2P + 1, P = (kb + 5) / 2, into two-step stage P % 3 (the one of steps
+// kb - 1, kb or kb, kb - 1, read by step kb - 1 at the latest).  The scales
+// go four steps at a time, half of the rows per load, in the steps
+// kb % 4 == 3 and 0 (see there).  A wave issues 5 or 6 loads per step, and
+// everything that step kb + 1 reads (A of step kb + 1, B and scales of step
+// kb + 2) was issued before step kb, so waiting at the end of step kb until
+// at most 5 are outstanding (the loads retire in order) is enough.  Loads
+// past the end re-read the last step (the last pair or group), and a lane's
+// bytes past the end of a row (a step count that is not a multiple of 2 or
+// 4) re-read the row's last ones; what they write is never read.  ARAW: B
+// and the scales of step kb + 3 (waves 4 KB .. 4 KB + 3, a quarter of the
+// rows each) one step at a time into stage bs, A step kb + 3 as raw nibbles
+// and scales, 3 loads per step (see the end of the step).
 // ARAW: dequantize word j (0..3: 8 values) of this lane's raw A chunk in raw
 // stage st (row tid / 2, K half tid & 1; block scale 2 (tid & 1) + j / 2)
 // into its 16 B chunk of f16 stage fst.  The word and the scale byte are
@@ -233,7 +242,8 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
   // stage ((kb + 1) % 6) / 2 at parity (kb + 1) & 1
   constexpr int kb6 = (3 * KB + 4 * KA) % 6, n6 = (kb6 + 1) % 6;
   const f16x8* const b_next = ARAW ? rp.b + bn * kBRaw : rp.bp[n6 & 1] + (n6 >> 1) * kBPair;
-  const uint32_t* const s_next = rp.s + bn * kBScale * 4;
+  const uint32_t* const s_next =
+      ARAW ? rp.s + bn * kBScale * 4 : rp.sq + (((kb + 1) >> 2) & 1) * kSQuad + ((kb + 1) & 3);
   const uint8_t* const a_src = op.a + (size_t)min(kb + 2, last) * (kStepK * 2);
   const uint8_t* const b_src = op.bq + (size_t)min(kb + 3, last) * (kStepK / 2);
   const uint8_t* const s_src = op.bsf + (size_t)min(kb + 3, last) * (kStepK / 16);
@@ -286,7 +296,7 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
           R[KB ^ 1].q[0] = __builtin_bit_cast(uint4, b_next[0]);
           R[KB ^ 1].q[1] = __builtin_bit_cast(uint4, b_next[ARAW ? 64 : 128]);
           S[KB ^ 1].w[0] = s_next[0];
-          S[KB ^ 1].w[1] = s_next[32];
+          S[KB ^ 1].w[1] = s_next[ARAW ? 32 : 128];
         }
         if (ARAW) {
           dma16s(b_dst, b_src, op.bq_off);
@@ -298,9 +308,23 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
           const uint32_t off = op.bq_row[lu] + min((uint32_t)(64 * P) + op.bq_lc, op.bq_lim);
           dma16s(L.b + lst * kBPair + (32 * wave + 16 * lu) * 4, op.bq, off);
         }
-        if (scales) {
+        if (!ARAW) {
+          // scales four steps at a time: group Q (steps 4Q .. 4Q + 3) into
+          // four-step stage Q & 1, rows 16 u .. of each wave's 32 in step
+          // 4Q - 5 + u, 16 B per row in 4 lanes (the stage of steps
+          // 4Q - 8 .. 4Q - 5, read by step 4Q - 6 at the latest)
+          const int k4 = kb & 3;
+          if (k4 == 3 || k4 == 0) {
+            const int u = k4 == 0 ? 1 : 0, Q = (kb + 5) >> 2;
+            // the scale row of B row bq_row / (K / 2) starts at bq_row / 8
+            const uint32_t row = u ? op.bq_row[1] : op.bq_row[0];  // a select: no indexed private array
+            const uint32_t off = (row >> 3) +
+                                 min((uint32_t)(16 * min(Q, last >> 2)) + 4u * (uint32_t)(lane & 3), op.sf_lim);
+            dma4s(L.s + (Q & 1) * kSQuad + 4 * (32 * wave + 16 * u), op.bsf, off);
+          }
+        } else if (scales) {
           dma4s(s_dst, s_src, op.bsf_off);
-        } else if (ARAW) {  // the other half of the waves loads the A scales
+        } else {  // the other half of the waves loads the A scales
           const int j = min(kb + 3, last);
           dma4s(raw_sf(L.a, (KA + 3) % 4) + (wave & 3) * 64, op.asf + (size_t)j * (kStepK / 16), op.asf_off);
         }
@@ -379,8 +403,8 @@ __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRa
 
 // The prologue of a tile's K loop.  f16 A: the direct loads of A steps 0, 1,
 // of B steps 0..3 and the first half of the rows of steps 4, 5 (two-step
-// stages 0, 1 and half of 2), and of the scales of steps 0..2.  ARAW: B, A
-// and the scales of steps 0..2.  The LDS stages must be
+// stages 0, 1 and half of 2), and of the scales of steps 0..3 and the first
+// half of the rows of steps 4..7.  ARAW: B, A and the scales of steps 0..2.  The LDS stages must be
 // free (every wave past its last read of them).
 template <bool ARAW = false>
 __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, int nk, int tid) {
@@ -405,6 +429,18 @@ __device__ __forceinline__ void gemm_prologue(const Lds& L, const Operands& op, 
             op.bq_row[u] + min((uint32_t)(64 * min(P, last >> 1)) + op.bq_lc, op.bq_lim);
         dma16s(L.b + P * kBPair + (32 * wave + 16 * u) * 4, op.bq, off);
       }
+  }
+  if (!ARAW) {  // scales: four-step group 0 and the first half of group 1
+#pragma unroll
+    for (int Q = 0; Q < 2; ++Q)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (Q == 1 && u == 1) break;
+        const uint32_t off = (op.bq_row[u] >> 3) +
+                             min((uint32_t)(16 * min(Q, last >> 2)) + 4u * (uint32_t)(tid & 3), op.sf_lim);
+        dma4s(L.s + Q * kSQuad + 4 * (32 * wave + 16 * u), op.bsf, off);
+      }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
@@ -447,8 +483,9 @@ __device__ __forceinline__ void gemm_body(const Lds& L, const Operands& op, int 
   const f16x8* const b0 = ARAW ? rp.b : rp.bp[0];  // step 0: stage 0 (parity 0 of two-step stage 0)
   R[0].q[0] = __builtin_bit_cast(uint4, b0[0]);
   R[0].q[1] = __builtin_bit_cast(uint4, b0[ARAW ? 64 : 128]);
-  S[0].w[0] = rp.s[0];
-  S[0].w[1] = rp.s[32];
+  const uint32_t* const s0 = ARAW ? rp.s : rp.sq;  // step 0: scale stage 0
+  S[0].w[0] = s0[0];
+  S[0].w[1] = s0[ARAW ? 32 : 128];
   f16x8 bf[2];
   {
     const ScalePairs p0 = scale_pairs(S[0], g);
@@ -498,7 +535,7 @@ template <bool ARAW>
 __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Params p) {
   __shared__ f16x8 lds_a[(ARAW ? kAStagesRaw : kAStages) * kLdsOperand];
   __shared__ f16x8 lds_b[ARAW ? kBStages * kBRaw : kBPairStages * kBPair];
-  __shared__ uint32_t lds_s[kBStages * kBScale * 4];
+  __shared__ uint32_t lds_s[ARAW ? kBStages * kBScale * 4 : 2 * kSQuad];
   const Lds L{lds_a, lds_b, lds_s};
 
   GemmTile t;
@@ -541,6 +578,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
     op.bq_row[u] = (uint32_t)l1_weight_row(nt, 32 * wave + 16 * u + (lane >> 2)) * (uint32_t)(p.K / 2);
   op.bq_lc = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
   op.bq_lim = (uint32_t)(p.K / 2) - 16u;
+  op.sf_lim = (uint32_t)(p.K / 16) - 4u;
 
   f32x16 acc[4][2];
   gemm_mainloop<ARAW>(L, op, (int)(p.K / kStepK), t.nrows, acc);
@@ -648,7 +686,7 @@ __global__ __launch_bounds__(kGemmThreads) void l1_gemm_swiglu_quant_kernel(L1Pa
 __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
   __shared__ f16x8 lds_a[kAStages * kLdsOperand];
   __shared__ f16x8 lds_b[kBPairStages * kBPair];
-  __shared__ uint32_t lds_s[kBStages * kBScale * 4];
+  __shared__ uint32_t lds_s[2 * kSQuad];
   __shared__ int out_row[kTileM];
   __shared__ float out_scale[kTileM];
   const Lds L{lds_a, lds_b, lds_s};
@@ -716,6 +754,7 @@ __global__ __launch_bounds__(kGemmThreads) void l2_gemm_kernel(L2Params p) {
       op.bq_row[u] = (uint32_t)(nt * kTileN + 32 * wave + 16 * u + (lane >> 2)) * (uint32_t)(p.K / 2);
     op.bq_lc = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     op.bq_lim = (uint32_t)(p.K / 2) - 16u;
+    op.sf_lim = (uint32_t)(p.K / 16) - 4u;
   };
 
   GemmTile t;
