@@ -28,12 +28,13 @@ TFLOP/s (6 * P * H * I per step).  Other legs, reported alongside:
   tiny      the small MoE layer T64 H256 I128 E8 top-2 (launch-latency bound)
 Timing: W untimed warmups, then K timed steps.  quantize, expert, dense and mx
 replay a HIP graph of K launches between two events (no host gaps), then 50
-more replays each between its own events for a median; the MoE legs run K
-layers eagerly between two events, then at least 10 (prefill) or 50 (decode,
-tiny) layers with an event between consecutive layers for a median, then K
-layers with the library's stage events (HIP events between its stages on the
-same stream), which give every stage's duration (the L1 GEMM's feeds
-`roofline.achieved`).
+more replays each between its own events for a median.  The MoE legs warm up
+for W layers, and a short layer for more, up to ~100 ms of work while the
+clock settles; then they run K layers eagerly between two events, then at
+least 10 (prefill) or 50 (decode, tiny) layers with an event between
+consecutive layers for a median, then K layers with the library's stage
+events (HIP events between its stages on the same stream), which give every
+stage's duration (the L1 GEMM's feeds `roofline.achieved`).
 cpu_baseline: the CPU oracle, timed in the same run on this host's cores
 (the CPUs this process may use, at most 16), on bounded samples: the prefill
 layer (top level, the unit of `value`), and per leg the decode layer, the
@@ -474,6 +475,19 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
     ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
     for _ in range(warmup):
         nv.moe_expert_ffn_raw(args, dev, ws)
+    # The clock settles over about 0.1 s of sustained work: a short layer
+    # (decode) gets more untimed layers, up to ~100 ms in all.  (With 3
+    # warm-up layers the decode layer's mean came out 8 % above its median;
+    # after 100 the two agreed within 1 %.)
+    w0, w1 = _ev(), _ev()
+    torch.cuda.synchronize()
+    w0.record()
+    nv.moe_expert_ffn_raw(args, dev, ws)
+    w1.record()
+    torch.cuda.synchronize()
+    est = max(w0.elapsed_time(w1), 1e-3)
+    for _ in range(int(min(2000, max(0.0, (100.0 - (warmup + 1) * est) / est)))):
+        nv.moe_expert_ffn_raw(args, dev, ws)
     torch.cuda.synchronize()
     # the layer time: `steps` back-to-back layers between two events, with no
     # stage events inside (each event record costs the stream a few us)
@@ -517,11 +531,11 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
     l2_flops = 2.0 * cfg.P * cfg.I * cfg.H
     # rows on the main (256-row) tiles: with more than 16 pairs per expert
     # (and H, I multiples of 256) the library picks the mixed tiling, whose
-    # main list holds all but each expert's last block of at most 32 rows
+    # main list holds all but each expert's last block of at most 64 rows
     n = np.bincount(ids[(ids >= 0) & (ids < cfg.E)].reshape(-1), minlength=cfg.E)
     r = n % 256
     mixed = cfg.P > 16 * cfg.E
-    main_rows = int(n.sum() - (r[(r > 0) & (r <= 32)].sum() if mixed else 0))
+    main_rows = int(n.sum() - (r[(r > 0) & (r <= 64)].sum() if mixed else 0))
     l1_main_flops = 2.0 * main_rows * cfg.H * 2 * cfg.I
     return dict(
         workload=f"T{cfg.T} H{cfg.H} I{cfg.I} E{cfg.E} top{cfg.topk} ({cfg.routing} routing)",

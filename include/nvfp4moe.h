@@ -186,7 +186,7 @@ typedef struct {
   void *const *stage_events;
   /* GEMM tiling.  32: 32-row tiles that stream the weights.  256: 256-row
      MFMA tiles.  288 (mixed): 256-row tiles, except that each expert's last
-     block of at most 32 rows goes on a 32-row tile.  0 chooses from the
+     block of at most 64 rows goes on one or two 32-row tiles.  0 chooses from the
      routing shape: 32 when there are at most 16 pairs per expert on average,
      else 288; 256 when H or I is not a multiple of 256 (or equal to 128),
      which 32 and 288 need (NVFP4_ERR_UNSUPPORTED).  Other values:

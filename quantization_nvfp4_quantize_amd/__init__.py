@@ -271,7 +271,7 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
     memory reused while a launch still reads it).
     tile_rows: 0 lets the library choose the GEMM tiles; 32 or 256 forces
     one tile height, 288 the mixed tiling (256-row tiles, each expert's last
-    block of at most 32 rows on a 32-row tile).
+    block of at most 64 rows on one or two 32-row tiles).
     a2_gs None: dynamic L1-output global scale (unfused flow); l1_unfused:
     True / 1 the unfused flow with the supplied a2_gs, "interleaved" / 2 the
     interleaved-output flow; a2_gs_out receives the scale.  aux: None, or

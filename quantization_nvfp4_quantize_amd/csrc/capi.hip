@@ -356,10 +356,12 @@ bool moe_f16_rows(const nvfp4_moe_args* a) { return a->out_dtype == 0; }
 
 // GEMM tiling: 32-row tiles (weights streamed through registers) when the
 // experts get few rows each; else 256-row tiles (MFMA-bound), each expert's
-// last block of at most 32 rows on a 32-row tile of its own when the 32-row
-// kernels take H and I (mixed, tile_rows 256 + 32: such a short block would
-// cost a 256-row tile most of a full tile's time).
+// last block of at most 64 rows on one or two 32-row tiles of its own when
+// the 32-row kernels take H and I (mixed, tile_rows 256 + 32: such a short
+// block would cost a 256-row tile most of a full tile's time, two 32-row
+// tiles about 60 % of it).
 int kMixedTileRows() { return nvfp4::gemm_tile_rows() + nvfp4::skinny_tile_rows(); }
+constexpr int kMaxShortTiles = 2;  // 32-row tiles per expert's short last block
 
 bool moe_skinny_fits(const nvfp4_moe_args* a) {
   return nvfp4::skinny_supports_k(a->H) && nvfp4::skinny_supports_k(a->I);
@@ -393,7 +395,7 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.perm = take(sizeof(int) * (size_t)(P > 0 ? P : 1));
   L.tiles = take(sizeof(nvfp4::GemmTile) * (size_t)L.max_tiles);
   L.ntiles = take(sizeof(int));
-  L.small = take(sizeof(nvfp4::GemmTile) * (size_t)E);
+  L.small = take(sizeof(nvfp4::GemmTile) * (size_t)kMaxShortTiles * (size_t)E);
   L.nsmall = take(sizeof(int));
   L.err = take(sizeof(int));
   L.route = take(nvfp4::route_workspace_bytes(P, (int)E));
@@ -529,7 +531,8 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   };
   if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E,
                                            skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows(),
-                                           mixed ? nvfp4::skinny_tile_rows() : 0, offsets, perm, tiles, ntiles,
+                                           mixed ? kMaxShortTiles * nvfp4::skinny_tile_rows() : 0,
+                                           nvfp4::skinny_tile_rows(), offsets, perm, tiles, ntiles,
                                            small, nsmall, err, reinterpret_cast<int*>(w + L.route),
                                            reinterpret_cast<int*>(w + L.sched), s),
                        "route")))
@@ -553,7 +556,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     mark(4);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
-                                  cf16, small, nsmall, (int)E, 0, perm, (int)k, aux, c_il);
+                                  cf16, small, nsmall, kMaxShortTiles * (int)E, 0, perm, (int)k, aux, c_il);
     if (e == hipSuccess) e = join();
     return hip_status(e, "L1 GEMM");
   };
@@ -602,7 +605,7 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     mark(6);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, small, nsmall,
-                                  (int)E, perm, aux, 0, nullptr, nullptr, o16, oexp);
+                                  kMaxShortTiles * (int)E, perm, aux, 0, nullptr, nullptr, o16, oexp);
     if (e == hipSuccess) e = join();
     if ((st = hip_status(e, "L2 GEMM"))) return st;
   }

@@ -92,7 +92,7 @@ size_t route_workspace_bytes(int64_t P, int E);
 // > 0 each expert's last block of at most small_rows rows is listed in
 // small / *nsmall (at most E entries) instead of tiles.  Also zeroes
 // sched[0 .. 16) (nullable): the GEMMs' work counters.
-hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int* offsets,
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int small_tile, int* offsets,
                         int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
                         int* ws, int* sched, hipStream_t s);
 // y[t] = sum over the k rows of token t of o (fp32), or of the f16 form

@@ -70,15 +70,16 @@ __device__ __forceinline__ int block_exclusive_scan(int* scan, int v, int* total
 }
 
 // Tiles of an expert with np rows: blocks of tile_rows rows; with
-// small_rows > 0, a last block of at most small_rows rows goes on a small
-// tile of its own instead (big: 0.., small: 0 or 1).
+// small_rows > 0, a last block of at most small_rows rows goes on small
+// tiles of small_tile rows instead (big: 0.., small: 0..).
 struct TileCounts {
   int big, small;
 };
-__device__ __forceinline__ TileCounts tile_counts(int np, int tile_rows, int small_rows) {
+__device__ __forceinline__ TileCounts tile_counts(int np, int tile_rows, int small_rows, int small_tile) {
   if (small_rows > 0) {
     const int r = np % tile_rows;
-    return {np / tile_rows + (r > small_rows ? 1 : 0), (r > 0 && r <= small_rows) ? 1 : 0};
+    return {np / tile_rows + (r > small_rows ? 1 : 0),
+            (r > 0 && r <= small_rows) ? (r + small_tile - 1) / small_tile : 0};
   }
   return {(np + tile_rows - 1) / tile_rows, 0};
 }
@@ -87,7 +88,7 @@ __device__ __forceinline__ TileCounts tile_counts(int np, int tile_rows, int sma
 // chunk: count_of(e) gives expert e's pairs, on_start(e, start) hears its
 // first sorted position.  Every thread must call it.
 template <class CountOf, class OnStart>
-__device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows, int* scan,
+__device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows, int small_tile, int* scan,
                                             int* offsets, GemmTile* tiles, int* ntiles,
                                             GemmTile* small, int* nsmall, CountOf count_of,
                                             OnStart on_start) {
@@ -96,7 +97,7 @@ __device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows
   for (int e0 = 0; e0 < E; e0 += kRouteThreads) {
     const int e = e0 + tid;
     const int np = (e < E) ? count_of(e) : 0;
-    const TileCounts c = tile_counts(np, tile_rows, small_rows);
+    const TileCounts c = tile_counts(np, tile_rows, small_rows, small_tile);
     int chunk_p, chunk_t, chunk_s;
     const int xp = block_exclusive_scan(scan, np, &chunk_p);
     const int xt = block_exclusive_scan(scan, c.big, &chunk_t);
@@ -107,7 +108,10 @@ __device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows
       on_start(e, start);
       for (int k = 0; k < c.big; ++k)
         tiles[base_t + xt + k] = GemmTile{e, start + k * tile_rows, min(tile_rows, np - k * tile_rows), 0};
-      if (c.small) small[base_s + xs] = GemmTile{e, start + c.big * tile_rows, np - c.big * tile_rows, 0};
+      for (int k = 0; k < c.small; ++k) {
+        const int r0 = c.big * tile_rows + k * small_tile;
+        small[base_s + xs + k] = GemmTile{e, start + r0, min(small_tile, np - r0), 0};
+      }
     }
     base_p += chunk_p;
     base_t += chunk_t;
@@ -122,7 +126,7 @@ __device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int64_t P, int E, int tile_rows,
-                                                              int small_rows,
+                                                              int small_rows, int small_tile,
                                                               int* __restrict__ offsets,
                                                               int* __restrict__ perm,
                                                               GemmTile* __restrict__ tiles,
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
   __syncthreads();
 
-  group_tiles(E, tile_rows, small_rows, scan, offsets, tiles, ntiles, small, nsmall,
+  group_tiles(E, tile_rows, small_rows, small_tile, scan, offsets, tiles, ntiles, small, nsmall,
               [&](int e) { return total[e]; },
               [&](int e, int start) {
                 for (int w = 0; w < kRouteWaves; ++w) cnt[w * E + e] += start;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(const int32_
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int G, int E, int tile_rows,
-                                                                   int small_rows,
+                                                                   int small_rows, int small_tile,
                                                                    int* __restrict__ gcount,
                                                                    const int* __restrict__ gerr,
                                                                    int* __restrict__ offsets,
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int G, int E,
   const int tid = threadIdx.x;
   // each expert's pairs per workgroup -> exclusive starts within the expert,
   // then (with the expert's start) the workgroup's first position per expert
-  group_tiles(E, tile_rows, small_rows, scan, offsets, tiles, ntiles, small, nsmall,
+  group_tiles(E, tile_rows, small_rows, small_tile, scan, offsets, tiles, ntiles, small, nsmall,
               [&](int e) {
                 int np = 0;
                 for (int g = 0; g < G; ++g) {
@@ -428,19 +432,22 @@ size_t route_workspace_bytes(int64_t P, int E) {
   return sizeof(int) * ((size_t)G * E + G);
 }
 
-hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int* offsets,
+hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int small_tile,
+                        int* offsets,
                         int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
                         int* ws, int* sched, hipStream_t s) {
   const int G = route_groups(P);
   if (G == 1 || !ws) {
-    route_kernel<<<1, kRouteThreads, route_lds_bytes(E), s>>>(ids, P, E, tile_rows, small_rows, offsets, perm,
+    route_kernel<<<1, kRouteThreads, route_lds_bytes(E), s>>>(ids, P, E, tile_rows, small_rows, small_tile,
+                                                              offsets, perm,
                                                               tiles, ntiles, small, nsmall, err_count, sched);
     return hipGetLastError();
   }
   int* gcount = ws;
   int* gerr = ws + (size_t)G * E;
   route_count_kernel<<<G, kRouteThreads, sizeof(int) * E, s>>>(ids, P, E, gcount, gerr);
-  route_scan_kernel<<<1, kRouteThreads, 0, s>>>(G, E, tile_rows, small_rows, gcount, gerr, offsets, tiles, ntiles,
+  route_scan_kernel<<<1, kRouteThreads, 0, s>>>(G, E, tile_rows, small_rows, small_tile, gcount, gerr, offsets,
+                                                 tiles, ntiles,
                                                  small, nsmall, err_count, sched);
   route_place_kernel<<<G, kRouteThreads, sizeof(int) * kRouteWaves * E, s>>>(ids, P, E, gcount, perm);
   return hipGetLastError();

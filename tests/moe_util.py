@@ -71,11 +71,12 @@ def expert_rows(ids, E):
     return {e: order[np.searchsorted(fs, e, "left"):np.searchsorted(fs, e, "right")] for e in range(E)}
 
 
-def boundary_tokens(ids, E, k, tile=256, short=32, n_edge_experts=8, seed=0, extra=()):
+def boundary_tokens(ids, E, k, tile=256, short=64, short_tile=32, n_edge_experts=8, seed=0, extra=()):
     """Tokens chosen so that the oracle comparison reaches every kind of row
     of the mixed tiling at full size: for each expert whose last block of at
-    most `short` rows goes on a short tile, the token of a seeded row of that
-    block (of its last row for every eighth such expert); for `n_edge_experts` experts with more than
+    most `short` rows goes on `short_tile`-row tiles, the token of a seeded
+    row of each of those tiles (of its last row for every eighth such
+    expert); for `n_edge_experts` experts with more than
     `tile` + 1 rows, the tokens of rows tile - 1, tile and tile + 1; the
     tokens of each expert's first row for experts with at most `short` rows
     in all; plus `extra`.  Returns (sorted token ids, dict of what each
@@ -90,9 +91,12 @@ def boundary_tokens(ids, E, k, tile=256, short=32, n_edge_experts=8, seed=0, ext
         n = rows[e].size
         rem = n % tile
         if n > tile and 0 < rem <= short:
-            # a seeded row of the short block; its last row for every 8th expert
-            r = n - 1 if len(short_e) % 8 == 0 else n - rem + int(rng.integers(rem))
-            short_tok.append(rows[e][r] // k)
+            # a seeded row of each short tile; its last row for every 8th expert
+            last = len(short_e) % 8 == 0
+            for t0 in range(0, rem, short_tile):
+                t1 = min(rem, t0 + short_tile)
+                r = n - rem + (t1 - 1 if last else t0 + int(rng.integers(t1 - t0)))
+                short_tok.append(rows[e][r] // k)
             short_e.append(e)
         if 0 < n <= short:
             small_tok.append(rows[e][0] // k)

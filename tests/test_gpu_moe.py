@@ -28,7 +28,7 @@ def nv():
 
 
 # GEMM tilings: 32 (weights streamed), 256 (MFMA-bound), 288 (256-row tiles,
-# each expert's last <= 32 rows on a 32-row tile)
+# each expert's last <= 64 rows on one or two 32-row tiles)
 TILES = [32, 256, 288]
 
 
@@ -417,11 +417,12 @@ def test_moe_mixed_aux_stream(nv, flow):
 def test_moe_mixed_tiles_remainders(nv, orc):
     """The mixed tiling on expert row counts chosen around its boundaries:
     256 + 10 (one 256-row tile and a 10-row short tile), 512 + 32 (two and a
-    32-row short tile), 256 + 33 (a 33-row block stays on a 256-row tile),
-    255 and 32 (one tile each), 0 (no tile): every token against the oracle,
-    and bit-identical to the 256-row tiling."""
+    32-row short tile), 256 + 33 and 256 + 64 (a 256-row tile and two short
+    tiles), 256 + 65 (a 65-row block stays on a 256-row tile), 255 and 32
+    (one tile each), 0 (no tile): every token against the oracle, and
+    bit-identical to the 256-row tiling."""
     import dataclasses
-    counts = [266, 544, 289, 255, 32, 0]
+    counts = [266, 544, 289, 320, 321, 255, 32, 0]
     cfg = dataclasses.replace(synth.TINY, T=sum(counts), E=len(counts), topk=1, name="mixed")
     w = gpu_weights(nv, cfg)
     x = synth.activations(cfg)
@@ -471,9 +472,9 @@ def test_moe_decode_config_sampled(nv, orc, tile_rows):
 def test_moe_prefill_config_sampled(nv, orc):
     """Prefill-shaped layer (T16384, uniform top-8) in the mixed tiling, full
     GPU run; against the oracle on tokens chosen from the stable grouping:
-    a row on the 32-row short tile of every expert that has one (108
-    experts), rows 255, 256 and 257 of eight experts' 256-row tiles, and the
-    first, middle and last token."""
+    a row on each 32-row short tile of every expert that has them (125
+    experts, 142 tiles), rows 255, 256 and 257 of eight experts' 256-row
+    tiles, and the first, middle and last token."""
     from moe_util import boundary_tokens
     cfg = synth.PRE
     w = gpu_weights(nv, cfg)
@@ -481,8 +482,8 @@ def test_moe_prefill_config_sampled(nv, orc):
     ids, wts = synth.routing(cfg)
     y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=288)
     tokens, info = boundary_tokens(ids, cfg.E, cfg.topk, extra=(0, cfg.T // 2, cfg.T - 1))
-    # every expert with a short tile (108 of them) has a sampled row on it
-    assert len(info["short_experts"]) == 108 and info["edge"].size >= 20, {k: len(v) for k, v in info.items()}
+    # every short tile (142, of 125 experts) has a sampled row on it
+    assert len(info["short_experts"]) == 125 and info["edge"].size >= 20, {k: len(v) for k, v in info.items()}
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, y, dbg, device="cuda:0")
     print(f"prefill ({tokens.size} tokens: {info['short'].size} on short tiles, {info['edge'].size} at "
           "256-row edges): y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
