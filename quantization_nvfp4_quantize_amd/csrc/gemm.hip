@@ -86,9 +86,9 @@ constexpr int kSQuad = kTileN * 4;  // dwords of a four-step scale stage of the 
 // so that the compiler can tell the A fragment reads and the raw B reads
 // apart from the direct loads still in flight into the other arrays.
 struct Lds {
-  f16x8* a;     // kAStages x kLdsOperand chunks (also the epilogue's arrays)
-  f16x8* b;     // kBStages x kBRaw chunks
-  uint32_t* s;  // kBStages x kBScale x 4 words
+  f16x8* a;     // kAStages (ARAW: kAStagesRaw) x kLdsOperand chunks (also the epilogue's arrays)
+  f16x8* b;     // kBPairStages x kBPair chunks (ARAW: kBStages x kBRaw)
+  uint32_t* s;  // 2 x kSQuad words (ARAW: kBStages x kBScale x 4)
 };
 
 // Tile rows and columns of wave w: rows 128 wave_m .. +128, columns
@@ -140,9 +140,9 @@ struct Operands {
   const uint8_t* asf;   // ARAW: A block scales (rows of K / 16 bytes), wave-uniform
   uint32_t asf_off;     // its scale source: tile row 64 (wave % 4) + lane
   const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
-  uint32_t bq_off;      // this lane's B source: tile row 32 wave + lane / 2, half (lane ^ lane >> 4) & 1
+  uint32_t bq_off;      // ARAW: this lane's B source: tile row 32 wave + lane / 2, half (lane ^ lane >> 4) & 1
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
-  uint32_t bsf_off;     // this lane's scale source: tile row 64 (wave % 4) + lane
+  uint32_t bsf_off;     // ARAW: this lane's scale source: tile row 64 (wave % 4) + lane
   uint32_t bq_row[2];   // f16-A path: byte offsets of the B rows 32 wave + 16 u + lane / 4
   uint32_t bq_lc;       // 16 x the logical chunk this lane loads: (lane & 3) ^ ((lane >> 4) & 3)
   uint32_t bq_lim;      // K / 2 - 16: last 16 B of a row
@@ -159,9 +159,9 @@ struct Frags {
 // (B uses the same K permutation).
 struct ReadPtrs {
   const f16x8* a[4][2];
-  const f16x8* b;     // this lane's raw B chunk of column tile 0 in B stage 0 (tile 1: + 64,
+  const f16x8* b;     // ARAW: this lane's raw B chunk of column tile 0 in B stage 0 (tile 1: + 64,
                       // rows 32 apart keep the same swizzle bit)
-  const uint32_t* s;  // its scale word of column tile 0 in scale stage 0 (tile 1: + 32)
+  const uint32_t* s;  // ARAW: its scale word of column tile 0 in scale stage 0 (tile 1: + 32)
   const f16x8* bp[2];  // f16-A path: the raw B chunk of step parity s' in two-step stage 0 (tile 1: + 128)
   const uint32_t* sq;  // f16-A path: its scale words of four-step scale stage 0 (step j: + j % 4; tile 1: + 128)
 };
@@ -185,8 +185,9 @@ __device__ __forceinline__ ReadPtrs read_ptrs(const Lds& L, int wm, int wn, int 
   return rp;
 }
 
-// One K step kb on A stage KA = kb % 4; bs = kb % 3 is the B / scale stage
-// holding step kb, and the register sets R, S alternate with KB = kb % 2.
+// One K step kb on A stage KA (f16 A: kb % 3; ARAW: kb % 4); bs = kb % 3 is
+// the single-step B / scale stage holding step kb (ARAW only), and the
+// register sets R, S alternate with KB = kb % 2.
 // The wave's 32 MFMAs run in 8 groups of 4 (those of row groups mt >= nmt
 // skipped); ahead of each group it reads the next A fragments from LDS and
 // dequantizes the next B fragments in registers, the last group preparing the
@@ -356,8 +357,9 @@ __device__ __forceinline__ void gemm_step(const Lds& L, const ReadPtrs& rp, BRaw
 }
 
 // All nk steps.  f16 A: A stage period 3 and register-set period 2, whole
-// groups of 6, then the remaining 0..5 steps; bs = kb % 3 (the scale stage).
-// ARAW: A stage period 4, groups of 4; bs runs through the B stages 0, 1, 2.
+// groups of 6, then the remaining 0..5 steps (the two-step B and four-step
+// scale stages follow from kb itself).  ARAW: A stage period 4, groups of 4;
+// bs runs through the single-step B / scale stages 0, 1, 2.
 // Both instantiations (FULL) pass the same barriers.
 template <bool FULL, bool SWAP, bool ARAW>
 __device__ __forceinline__ void gemm_steps(const Lds& L, const ReadPtrs& rp, BRaw (&R)[2],
