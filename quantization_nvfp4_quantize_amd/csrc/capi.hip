@@ -242,11 +242,12 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t K, const float* x_gs_in, 
   const bool skinny = M <= kLinearSkinnyRows && nvfp4::skinny_supports_k(K);
   const int64_t tm = skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
   const int tiles = (int)((M + tm - 1) / tm);
-  auto gemm = skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2;
   float* o32 = out_dtype == 1 ? static_cast<float*>(out) : nullptr;
   uint16_t* o16 = out_dtype == 0 ? static_cast<uint16_t*>(out) : nullptr;
-  return hip_status(gemm(x_f16, gs, K, w_q, w_sf, w_gs, N, nullptr, o32, nullptr, nullptr, tiles, nullptr,
-                         s, M, o16, nullptr, nullptr, nullptr),
+  return hip_status(skinny ? nvfp4::launch_l2_skinny(x_f16, gs, K, w_q, w_sf, w_gs, N, nullptr, o32, nullptr,
+                                                     nullptr, tiles, nullptr, s, M, o16)
+                           : nvfp4::launch_l2(x_f16, gs, K, w_q, w_sf, w_gs, N, nullptr, o32, nullptr, nullptr,
+                                              tiles, nullptr, s, M, o16),
                     "nvfp4_linear");
 }
 
@@ -337,8 +338,8 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* w_q, co
 namespace {
 
 struct MoeLayout {
-  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, small, nsmall, err, route, sched, a2_gs,
-      c, a2q, a2sf, a2_f16, o, oexp, total;
+  size_t partial, x_gs, xq, xsf, x_f16, offsets, perm, tiles, ntiles, small, nsmall, err, route, sched, split,
+      a2_gs, c, a2q, a2sf, a2_f16, o, oexp, total;
   int max_tiles;
 };
 
@@ -399,7 +400,9 @@ MoeLayout moe_layout(const nvfp4_moe_args* a) {
   L.nsmall = take(sizeof(int));
   L.err = take(sizeof(int));
   L.route = take(nvfp4::route_workspace_bytes(P, (int)E));
-  L.sched = take(16 * sizeof(int));
+  L.sched = take(nvfp4::kSchedCounters * sizeof(int));
+  // the 32-row GEMMs' partial sums of the items they split along K
+  L.split = take(moe_tile_rows(a) == nvfp4::skinny_tile_rows() ? nvfp4::skinny_split_bytes() : 0);
   L.a2_gs = take(sizeof(float));
   L.c = take(moe_interleaved(a) ? sizeof(uint16_t) * (size_t)(2 * P * I)
              : moe_unfused(a) && !a->l1_c_bf16 ? sizeof(uint16_t) * (size_t)(P * I) : 0);
@@ -546,13 +549,19 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   uint8_t* a2sf = a->l1_sf ? a->l1_sf : reinterpret_cast<uint8_t*>(w + L.a2sf);
   uint16_t* a2_f16 = reinterpret_cast<uint16_t*>(w + L.a2_f16);
   // the L1 GEMM over the tile list (and the short tiles of the mixed tiling)
+  // 32-row tiles only: the buffers of the tail split (its counters follow
+  // the 256-row GEMMs' in the zeroed sched area)
+  float* split_ws = skinny ? reinterpret_cast<float*>(w + L.split) : nullptr;
+  int* split_cnt = skinny ? reinterpret_cast<int*>(w + L.sched) + 16 : nullptr;
   auto l1 = [&](const float* out_gs, uint16_t* c_bf16, uint8_t* cq, uint8_t* csf, uint16_t* cf16,
                 uint16_t* c_il) {
     hipError_t e = fork();
     if (e == hipSuccess)
-      e = (skinny ? nvfp4::launch_l1_skinny : nvfp4::launch_l1)(
-          x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf, cf16, tiles, ntiles,
-          L.max_tiles, 0, perm, (int)k, s, c_il, nullptr, nullptr);
+      e = skinny ? nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq,
+                                           csf, cf16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, c_il,
+                                           nullptr, nullptr, split_ws, split_cnt)
+                 : nvfp4::launch_l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
+                                    cf16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, c_il);
     mark(4);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
@@ -599,9 +608,12 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   {
     hipError_t e = fork();
     if (e == hipSuccess)
-      e = (skinny ? nvfp4::launch_l2_skinny : nvfp4::launch_l2)(
-          a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles, L.max_tiles, perm, s,
-          0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16, oexp);
+      e = skinny ? nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles,
+                                           ntiles, L.max_tiles, perm, s, 0, nullptr, nullptr, o16, oexp, split_ws,
+                                           split_cnt)
+                 : nvfp4::launch_l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
+                                    L.max_tiles, perm, s, 0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16,
+                                    oexp);
     mark(6);
     if (e == hipSuccess && mixed)
       e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, small, nsmall,

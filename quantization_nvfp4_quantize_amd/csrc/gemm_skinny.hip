@@ -30,7 +30,18 @@
 //     super-step.
 //   * 32 KiB of LDS for the activations plus 18 KiB of scales, and at most
 //     168 VGPRs, so three workgroups (12 waves) share a CU.
+//   * Tail split.  Each XCD runs its contiguous range of items `slots` at a
+//     time (resident workgroups per XCD).  When that range is a few items
+//     past a whole number of rounds, those last items would run nearly
+//     alone at the end of the launch; instead each of them is split along K
+//     into a few pieces run by as many workgroups.  A piece writes its fp32
+//     accumulators to a partial slot; the last piece of an item to arrive
+//     (an atomic count) adds the item's partials in piece order and runs
+//     the epilogue.  No workgroup waits for another.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "gemm_common.hpp"
 
@@ -280,6 +291,127 @@ __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64
   op.a_rows = __builtin_amdgcn_readfirstlane(8 * wave < nrows ? 1 : 0) != 0;
 }
 
+// ------------------------------------------------------------------ work items
+constexpr int kSplitItems = skinny_split_counters() / 8;  // at most this many items per XCD are split
+constexpr int kSplitPieces = 32;  // pieces (partial slots) per XCD
+constexpr int kSplitMax = 4;      // pieces per item
+constexpr int kSplitMinSteps = 6; // super-steps per piece, at least (shorter pieces cost more than they save)
+
+// The split's buffers (partial null: no split).
+struct SkSplit {
+  f32x4* partial;  // 8 x kSplitPieces slots of 8 x kSkThreads f32x4 (32 KiB each)
+  int* count;      // 8 x kSplitItems arrival counters, zero at launch
+  int slots;       // workgroups resident per XCD
+};
+
+// A workgroup's work: super-steps [ss0, ss0 + nss) of item (t, nt), piece
+// `piece` of `npieces` (1: the whole item, nk steps of 64 from step 0).
+struct SkWork {
+  GemmTile t;
+  int nt;
+  int nk;       // K steps of 64 of this piece
+  int ss0;      // its first super-step
+  int piece, npieces;
+  int slot;     // partial slot of piece 0 of the item (piece p: slot + p)
+  int counter;  // the item's arrival counter
+};
+
+// Items are numbered M-tile-major (item = tile * n_ntiles + nt) and dealt to
+// the XCDs in contiguous ranges as in work_item: block b runs on XCD b % 8
+// as its (b / 8)-th workgroup.  XCD x's n items, with R = n % slots: the
+// first n - R are whole; with a split, each of the last R (R <= kSplitItems)
+// becomes s = min(kSplitMax, kSplitPieces / R, nss / kSplitMinSteps) >= 2
+// pieces, numbered item-major after the whole items.  False for workgroups
+// without work.
+__device__ __forceinline__ bool sk_work_of(const GemmTile* tiles, const int* ntiles, int64_t M, int n_ntiles,
+                                           int nk, const SkSplit& sp, SkWork* w) {
+  const int mtiles = tiles ? *ntiles : (int)((M + kSkTileM - 1) / kSkTileM);
+  const int W = mtiles * n_ntiles;
+  const int b = blockIdx.x, x = b & 7, j = b >> 3;
+  const int q = W >> 3, r = W & 7;
+  const int n = q + (x < r ? 1 : 0), base = x * q + min(x, r);
+  const int nss = nk / kSkSteps;
+  int R = 0, s = 1;
+  if (sp.partial && sp.slots > 0 && nk % kSkSteps == 0) {
+    R = __builtin_amdgcn_readfirstlane(n % sp.slots);
+    s = (R > 0 && R <= kSplitItems) ? __builtin_amdgcn_readfirstlane(min(min(kSplitMax, kSplitPieces / R), nss / kSplitMinSteps)) : 1;
+    if (s < 2) {
+      R = 0;
+      s = 1;
+    }
+  }
+  const int whole = n - R;
+  int item;
+  w->nk = nk;
+  w->ss0 = 0;
+  w->piece = 0;
+  w->npieces = 1;
+  w->slot = 0;
+  w->counter = 0;
+  if (j < whole) {
+    item = base + j;
+  } else {
+    const int k = j - whole;  // piece k % s of split item k / s
+    if (k >= R * s) return false;
+    // (the divisions run on the vector ALU: readfirstlane keeps these
+    // workgroup-uniform values in scalar registers across the K loop)
+    const int ks = __builtin_amdgcn_readfirstlane(k / s);
+    item = base + whole + ks;
+    w->piece = k - ks * s;
+    w->npieces = s;
+    w->ss0 = __builtin_amdgcn_readfirstlane(w->piece * nss / s);
+    w->nk = (__builtin_amdgcn_readfirstlane((w->piece + 1) * nss / s) - w->ss0) * kSkSteps;
+    w->slot = x * kSplitPieces + ks * s;
+    w->counter = x * kSplitItems + ks;
+  }
+  const int ti = item / n_ntiles;
+  w->nt = item % n_ntiles;
+  if (tiles) {
+    w->t = tiles[ti];
+  } else {
+    const int64_t r0 = (int64_t)ti * kSkTileM;
+    w->t = GemmTile{0, (int)r0, (int)((M - r0) < kSkTileM ? (M - r0) : kSkTileM), 0};
+  }
+  return true;
+}
+
+// A piece of a split item: store its accumulators to its partial slot and
+// count its arrival.  The last piece of the item to arrive (true) gets the
+// sum of all pieces' partials, added in piece order (the same result
+// whichever arrives last), and resets the item's counter for the next
+// launch; the others (false) are done.
+__device__ __forceinline__ bool sk_split_sum(const SkSplit& sp, const SkWork& w, f32x4 (&acc)[2][4], int tid,
+                                             int* flag) {
+  f32x4* const part = sp.partial + (size_t)w.slot * (8 * kSkThreads);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[(w.piece * 8 + i) * kSkThreads + tid] = acc[i >> 2][i & 3];
+  // Release: every thread's partial before the count.  The workgroup's
+  // stores are ordered before thread 0's agent-scope release RMW by the
+  // workgroup-scope fence and barrier (one agent-scope fence per workgroup,
+  // not per thread: each costs an L2 write-back).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (tid == 0) {
+    int* const c = sp.count + w.counter;
+    const int old = __hip_atomic_fetch_add(c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == w.npieces - 1;
+    if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!*flag) return false;
+  // acquire: thread 0's RMW, then the barrier, orders every piece's partial
+  // before these loads
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f32x4 v = part[i * kSkThreads + tid];
+    for (int pc = 1; pc < w.npieces; ++pc) v += part[(pc * 8 + i) * kSkThreads + tid];
+    acc[i >> 2][i & 3] = v;
+  }
+  return true;
+}
+
 #define SK_LDS_DECL                                              \
   __shared__ f16x8 lds_a[2 * kSkABuf];                           \
   __shared__ __attribute__((aligned(16))) uint8_t lds_sf[kSkSfMacro]; \
@@ -287,11 +419,13 @@ __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64
   const SkLds L{lds_a, lds_sf, lds_sft}
 
 // ------------------------------------------------------------------ L1
-__global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
+__global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, SkSplit sp) {
   SK_LDS_DECL;
-  GemmTile t;
-  int nt;
-  if (!tile_of<kSkTileM>(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
+  __shared__ int last_piece;
+  SkWork wk;
+  if (!sk_work_of(p.tiles, p.ntiles, p.M, p.n_ntiles, (int)(p.K / kStepK), sp, &wk)) return;
+  const GemmTile t = wk.t;
+  const int nt = wk.nt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto out_row_of = [&](int r) -> int {
@@ -301,9 +435,10 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
   auto wrow = [&](int tr) { return l1_weight_row(nt, tr); };
   auto sf_row = [&](int tr) { return (uint32_t)l1_weight_row(nt, tr) * (uint32_t)(p.K / 16); };
   SkOperands op;
-  op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
-  op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2);
-  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);
+  // a piece starts at super-step ss0: the row offsets stay, the bases move
+  op.a = reinterpret_cast<const uint8_t*>(p.a_f16) + (size_t)wk.ss0 * (kSkSteps * kStepK * 2);
+  op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2) + (size_t)wk.ss0 * (kSkSteps * kStepK / 2);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
   {
     const int R = 8 * wave + (lane >> 3);
     const int o = out_row_of(R);
@@ -311,7 +446,10 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     sk_operands(op, arow, p.K, wave, lane, R, t.nrows, wrow);
   }
   f32x4 acc[2][4];
-  sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
+  sk_mainloop(L, op, wk.nk, acc, sf_row);
+  // a piece that is not its item's last runs the epilogue with no rows (an
+  // early return here made the compiler spill in the K loop)
+  const int nrows = (wk.npieces > 1 && !sk_split_sum(sp, wk, acc, tid, &last_piece)) ? 0 : t.nrows;
 
   // epilogue: SwiGLU -> bf16 tile (32 x 128) in LDS, then NVFP4 of its rows
   constexpr int kCStride = 136;
@@ -324,7 +462,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
   const float alpha = p.a_gs[0] * p.w_gs[t.expert];
   const int64_t I = p.N2 / 2;
   const int hb = tid & 15;
-  const int npass = (t.nrows + kSkThreads / 16 - 1) / (kSkThreads / 16);
+  const int npass = (nrows + kSkThreads / 16 - 1) / (kSkThreads / 16);
   // bf16 tile of SiLU(gate) (gate_only) or SiLU(gate) * up in LDS: column
   // tiles ct and ct + 2 (ct < 2) hold the gate and up values of SwiGLU
   // columns 32 wave + 16 ct + lane % 16, at rows 16 mt + 4 (lane / 16) + i
@@ -348,7 +486,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     __syncthreads();
     for (int pass = 0; pass < npass; ++pass) {
       const int qrow = pass * (kSkThreads / 16) + (tid >> 4);
-      if (qrow < t.nrows) {
+      if (qrow < nrows) {
         const uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
         const int64_t g8 = 16 * (int64_t)nt + hb;
         *reinterpret_cast<uint4*>(p.c_il + (int64_t)out_row[qrow] * p.N2 + 16 * g8) = w;
@@ -365,7 +503,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
     const uint4 w = *reinterpret_cast<const uint4*>(ctile + qrow * kCStride + 8 * hb);
     uint32_t code = 0, q = 0;
     if (p.c_q) q = quantize_half_block(w, E2, rtab, &code);  // tile-uniform branch
-    if (qrow < t.nrows) {
+    if (qrow < nrows) {
       const int64_t o = out_row[qrow];
       const int64_t col0 = 128 * (int64_t)nt + 8 * hb;  // compact column of this lane's 8
       if (p.c_q) {
@@ -380,11 +518,13 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p) {
 }
 
 // ------------------------------------------------------------------ L2
-__global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
+__global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p, SkSplit sp) {
   SK_LDS_DECL;
-  GemmTile t;
-  int nt;
-  if (!tile_of<kSkTileM>(p.tiles, p.ntiles, p.M, p.n_ntiles, &t, &nt)) return;
+  __shared__ int last_piece;
+  SkWork wk;
+  if (!sk_work_of(p.tiles, p.ntiles, p.M, p.n_ntiles, (int)(p.K / kStepK), sp, &wk)) return;
+  const GemmTile t = wk.t;
+  const int nt = wk.nt;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto pair_of = [&](int r) -> int {
@@ -394,13 +534,16 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
   auto wrow = [&](int tr) { return nt * kTileN + tr; };
   auto sf_row = [&](int tr) { return (uint32_t)(nt * kTileN + tr) * (uint32_t)(p.K / 16); };
   SkOperands op;
-  op.a = reinterpret_cast<const uint8_t*>(p.a_f16);
-  op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2);
-  op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);
+  op.a = reinterpret_cast<const uint8_t*>(p.a_f16) + (size_t)wk.ss0 * (kSkSteps * kStepK * 2);
+  op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2) + (size_t)wk.ss0 * (kSkSteps * kStepK / 2);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
   sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), t.nrows,
               wrow);
   f32x4 acc[2][4];
-  sk_mainloop(L, op, (int)(p.K / kStepK), acc, sf_row);
+  sk_mainloop(L, op, wk.nk, acc, sf_row);
+  // a piece that is not its item's last runs the epilogue with no rows (an
+  // early return here made the compiler spill in the K loop)
+  const int nrows = (wk.npieces > 1 && !sk_split_sum(sp, wk, acc, tid, &last_piece)) ? 0 : t.nrows;
   // the scales' LDS holds the output rows, the A buffers each wave's
   // 4 KiB transposition scratch
   int* out_row = reinterpret_cast<int*>(lds_sf);
@@ -418,13 +561,42 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p) {
         for (int i = 0; i < 4; ++i)
           sc[l2_scratch_index(16 * mt + 4 * (lane >> 4) + i, 16 * c2 + (lane & 15))] = acc[mt][2 * half + c2][i];
   };
-  l2_store_rows(p, scratch, 0, t.nrows, (int64_t)nt * kTileN + wave * 64, lane, fill,
+  l2_store_rows(p, scratch, 0, nrows, (int64_t)nt * kTileN + wave * 64, lane, fill,
                 [&](int r) { return out_row[r]; },
                 [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
 }
 
 // ------------------------------------------------------------------ launchers
 int skinny_tile_rows() { return kSkTileM; }
+
+size_t skinny_split_bytes() { return (size_t)8 * kSplitPieces * 8 * kSkThreads * sizeof(f32x4); }
+
+namespace {
+
+// Workgroups of `kernel` resident per XCD on the current device (CUs / 8 x
+// workgroups per CU), looked up once per device and kernel; 0 if unknown.
+template <class Kernel>
+int resident_per_xcd(Kernel kernel, std::atomic<int> (&cache)[64]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kSkThreads, 0) != hipSuccess)
+    return 0;
+  v = std::max(0, cus / 8 * per_cu);
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+std::atomic<int> g_l1_slots[64], g_l2_slots[64];
+
+// Blocks for W items at most: each XCD's range, plus its pieces beyond the
+// items they split.
+int64_t skinny_grid(int64_t W, bool split) { return 8 * ((W + 7) / 8 + (split ? kSplitPieces : 0)); }
+
+}  // namespace
 
 // K of whole super-steps (the scale rows then stay 16-byte aligned for the
 // direct loads), or a single tail super-step of 128.
@@ -435,16 +607,18 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
                             const int* perm, int topk, hipStream_t s, uint16_t* c_il, const uint8_t* a_q,
-                            const uint8_t* a_sf) {
+                            const uint8_t* a_sf, float* split_ws, int* split_cnt) {
   (void)a_q;
   (void)a_sf;
   if (!a_f16) return hipErrorInvalidValue;  // the 32-row tiles take f16 activations only
   L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16, c_il,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
-  const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
-  if (grid == 0) return hipSuccess;
+  const int64_t W = (int64_t)max_tiles * p.n_ntiles;
+  if (W == 0) return hipSuccess;
   if (!skinny_supports_k(K)) return hipErrorInvalidValue;
-  l1_skinny_kernel<<<(unsigned)grid, kSkThreads, 0, s>>>(p);
+  SkSplit sp{nullptr, nullptr, 0};
+  if (split_ws && split_cnt) sp = SkSplit{reinterpret_cast<f32x4*>(split_ws), split_cnt, resident_per_xcd(l1_skinny_kernel, g_l1_slots)};
+  l1_skinny_kernel<<<(unsigned)skinny_grid(W, sp.slots > 0), kSkThreads, 0, s>>>(p, sp);
   return hipGetLastError();
 }
 
@@ -452,14 +626,16 @@ hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
                             const int* perm, hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched,
-                            uint16_t* o_f16, int8_t* o_exp) {
-  (void)sched;  // one workgroup per item here
+                            uint16_t* o_f16, int8_t* o_exp, float* split_ws, int* split_cnt) {
+  (void)sched;  // one workgroup per item (or piece) here
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN),
              nullptr, o_f16, o_exp};
-  const int64_t grid = (int64_t)max_tiles * p.n_ntiles;
-  if (grid == 0) return hipSuccess;
+  const int64_t W = (int64_t)max_tiles * p.n_ntiles;
+  if (W == 0) return hipSuccess;
   if (!skinny_supports_k(K)) return hipErrorInvalidValue;
-  l2_skinny_kernel<<<(unsigned)grid, kSkThreads, 0, s>>>(p);
+  SkSplit sp{nullptr, nullptr, 0};
+  if (split_ws && split_cnt) sp = SkSplit{reinterpret_cast<f32x4*>(split_ws), split_cnt, resident_per_xcd(l2_skinny_kernel, g_l2_slots)};
+  l2_skinny_kernel<<<(unsigned)skinny_grid(W, sp.slots > 0), kSkThreads, 0, s>>>(p, sp);
   return hipGetLastError();
 }
 

@@ -74,24 +74,35 @@ hipError_t launch_l2(const uint16_t* a_f16, const float* a_gs, int64_t K, const 
 // ---- moe.hip
 size_t route_lds_bytes(int E);
 // Same operations as launch_l1 / launch_l2 on tiles of at most
-// skinny_tile_rows() rows (weights streamed through registers).
+// skinny_tile_rows() rows (weights streamed through registers).  With
+// split_ws (skinny_split_bytes(), 16-byte aligned) and split_cnt
+// (skinny_split_counters() ints, zero at launch and zero again after it) the
+// few items that would run alone at the end of the launch are split along K.
+// Two launches that share these buffers must not overlap.
 hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
                             const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr,
-                            const uint8_t* a_q = nullptr, const uint8_t* a_sf = nullptr);
+                            const uint8_t* a_q = nullptr, const uint8_t* a_sf = nullptr,
+                            float* split_ws = nullptr, int* split_cnt = nullptr);
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
                             const int* perm, hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr, int* sched = nullptr,
-                            uint16_t* o_f16 = nullptr, int8_t* o_exp = nullptr);
+                            uint16_t* o_f16 = nullptr, int8_t* o_exp = nullptr, float* split_ws = nullptr,
+                            int* split_cnt = nullptr);
+size_t skinny_split_bytes();
+constexpr int skinny_split_counters() { return 8 * 16; }
+// Work counters that launch_route zeroes: [0, 16) those of the 256-row
+// GEMMs, then the 32-row GEMMs' split counters.
+constexpr int kSchedCounters = 16 + skinny_split_counters();
 // Scratch (ints) of the many-workgroup grouping for P pairs and E experts.
 size_t route_workspace_bytes(int64_t P, int E);
 // Groups the pairs by expert into tiles of tile_rows rows; with small_rows
 // > 0 each expert's last block of at most small_rows rows is listed in
 // small / *nsmall (at most E entries) instead of tiles.  Also zeroes
-// sched[0 .. 16) (nullable): the GEMMs' work counters.
+// sched[0 .. kSchedCounters) (nullable): the GEMMs' work counters.
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int small_tile, int* offsets,
                         int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
                         int* ws, int* sched, hipStream_t s);

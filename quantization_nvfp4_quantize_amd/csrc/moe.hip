@@ -35,7 +35,6 @@ namespace nvfp4 {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRouteThreads = 1024;
-constexpr int kSchedCounters = 16;  // the GEMMs' work counters, zeroed with the grouping
 constexpr int kRouteWaves = kRouteThreads / 64;
 
 // Exclusive prefix of v over the threads of the workgroup (one value per

@@ -261,6 +261,27 @@ def test_moe_skinny_k_schedules(nv, orc, H, I):
     _gate(*res[:4])
 
 
+@pytest.mark.parametrize("H,I", [(6400, 256), (256, 3072), (3328, 3328)])
+def test_moe_skinny_tail_split(nv, orc, H, I):
+    """32-row tiles where the launch's last items are split along K into
+    pieces whose partial sums the last piece adds: with a handful of items per
+    XCD every item is such a tail item.  H 6400 splits each L1 item into four
+    pieces of 6, 6, 6 and 7 super-steps; I 3072 splits each L2 item in two;
+    3328 splits both GEMMs' items into 6 + 7.  Against the oracle, and the
+    same bytes on a second call (the arrival counters start from zero again)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=40, H=H, I=I, E=4, name=f"split{H}x{I}", a2_gs=4.0 / 2688.0)
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=32)
+    y2, _ = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=32)
+    assert np.array_equal(host(y).view(np.uint32), host(y2).view(np.uint32))
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), y, dbg)
+    print(f"H{H} I{I}: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
+
+
 @pytest.mark.parametrize("tile_rows", TILES)
 @pytest.mark.parametrize("flow", [1, "interleaved"])
 def test_moe_unfused_static_matches_fused(nv, orc, tile_rows, flow):
