@@ -182,7 +182,9 @@ typedef struct {
      (256-row tiles, or the 32-row tiles of tiling 32), the whole L1 stage
      (with the short tiles of the mixed tiling and any separate quantization
      pass), the L2 GEMM's main tile list, the whole L2 stage and the
-     combine. */
+     combine.  When the global scale is computed and the grouping fits one
+     workgroup (at most 4096 pairs), the grouping runs in the global scale's
+     launch: the first interval then holds both and the third is empty. */
   void *const *stage_events;
   /* GEMM tiling.  32: 32-row tiles that stream the weights.  256: 256-row
      MFMA tiles.  288 (mixed): 256-row tiles, except that each expert's last

@@ -480,17 +480,39 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   };
   mark(0);
 
-  // a1: activation global scale
+  // a1: activation global scale.  With a computed scale and a grouping that
+  // runs in one workgroup, the grouping (a3) shares the launch of the first
+  // pass of the scale, and the second pass runs inside the quantization.
+  const int64_t mode = moe_tile_rows(a);
+  const bool skinny = mode == nvfp4::skinny_tile_rows(), mixed = mode == kMixedTileRows();
+  const int route_tile = skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows();
+  const int route_small = mixed ? kMaxShortTiles * nvfp4::skinny_tile_rows() : 0;
+  int* offsets = reinterpret_cast<int*>(w + L.offsets);
+  int* perm = reinterpret_cast<int*>(w + L.perm);
+  nvfp4::GemmTile* tiles = reinterpret_cast<nvfp4::GemmTile*>(w + L.tiles);
+  int* ntiles = reinterpret_cast<int*>(w + L.ntiles);
+  int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
+  nvfp4::GemmTile* small = reinterpret_cast<nvfp4::GemmTile*>(w + L.small);
+  int* nsmall = reinterpret_cast<int*>(w + L.nsmall);
+  int* sched = reinterpret_cast<int*>(w + L.sched);
+  const int namax = nvfp4::amax_route_blocks(T * H / 8);
+  const bool fold = !a->x_gs_in && T > 0 && nvfp4::route_single(P) && namax < 256;
+  float* partial = reinterpret_cast<float*>(w + L.partial);
   const float* x_gs;
-  if (a->x_gs_in) {
+  if (fold) {
+    if ((st = hip_status(nvfp4::launch_amax_route(a->x, T * H, partial, namax, a->topk_ids, P, (int)E, route_tile,
+                                                  route_small, nvfp4::skinny_tile_rows(), offsets, perm, tiles,
+                                                  ntiles, small, nsmall, err, sched, s),
+                         "global scale + route")))
+      return st;
+    x_gs = a->x_gs_out ? a->x_gs_out : reinterpret_cast<float*>(w + L.x_gs);
+  } else if (a->x_gs_in) {
     x_gs = a->x_gs_in;
     if (a->x_gs_out && (st = hip_status(nvfp4::launch_copy_scalar(a->x_gs_in, a->x_gs_out, s), "copy x_gs")))
       return st;
   } else {
     float* g = a->x_gs_out ? a->x_gs_out : reinterpret_cast<float*>(w + L.x_gs);
-    if ((st = hip_status(nvfp4::launch_global_scale(a->x, T * H, reinterpret_cast<float*>(w + L.partial), g, s),
-                         "global scale")))
-      return st;
+    if ((st = hip_status(nvfp4::launch_global_scale(a->x, T * H, partial, g, s), "global scale"))) return st;
     x_gs = g;
   }
   mark(1);
@@ -502,19 +524,13 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   uint8_t* xq = a->xq ? a->xq : reinterpret_cast<uint8_t*>(w + L.xq);
   uint8_t* xsf = a->xsf ? a->xsf : reinterpret_cast<uint8_t*>(w + L.xsf);
   uint16_t* x_f16 = reinterpret_cast<uint16_t*>(w + L.x_f16);
-  if ((st = hip_status(nvfp4::launch_quantize(a->x, T * H, x_gs, xq, xsf, x_f16, s), "quantize x")))
+  if ((st = hip_status(fold ? nvfp4::launch_quantize_folded(a->x, T * H, partial, namax,
+                                                            const_cast<float*>(x_gs), xq, xsf, x_f16, s)
+                            : nvfp4::launch_quantize(a->x, T * H, x_gs, xq, xsf, x_f16, s),
+                       "quantize x")))
     return st;
   mark(2);
-  // a3: group pairs by expert
-  int* offsets = reinterpret_cast<int*>(w + L.offsets);
-  int* perm = reinterpret_cast<int*>(w + L.perm);
-  nvfp4::GemmTile* tiles = reinterpret_cast<nvfp4::GemmTile*>(w + L.tiles);
-  int* ntiles = reinterpret_cast<int*>(w + L.ntiles);
-  int* err = a->err_count ? a->err_count : reinterpret_cast<int*>(w + L.err);
-  const int64_t mode = moe_tile_rows(a);
-  const bool skinny = mode == nvfp4::skinny_tile_rows(), mixed = mode == kMixedTileRows();
-  nvfp4::GemmTile* small = reinterpret_cast<nvfp4::GemmTile*>(w + L.small);
-  int* nsmall = reinterpret_cast<int*>(w + L.nsmall);
+  // a3: group pairs by expert (done above when folded)
   // the short tiles of the mixed tiling run on the caller's second stream
   // when it gave one: fork after the work they depend on, join before the
   // work that depends on them
@@ -532,13 +548,11 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
     hipError_t e = hipEventRecord(ev, aux);
     return e == hipSuccess ? hipStreamWaitEvent(s, ev, 0) : e;
   };
-  if ((st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E,
-                                           skinny ? nvfp4::skinny_tile_rows() : nvfp4::gemm_tile_rows(),
-                                           mixed ? kMaxShortTiles * nvfp4::skinny_tile_rows() : 0,
-                                           nvfp4::skinny_tile_rows(), offsets, perm, tiles, ntiles,
-                                           small, nsmall, err, reinterpret_cast<int*>(w + L.route),
-                                           reinterpret_cast<int*>(w + L.sched), s),
-                       "route")))
+  if (!fold && (st = hip_status(nvfp4::launch_route(a->topk_ids, P, (int)E, route_tile, route_small,
+                                                    nvfp4::skinny_tile_rows(), offsets, perm, tiles, ntiles,
+                                                    small, nsmall, err, reinterpret_cast<int*>(w + L.route),
+                                                    sched, s),
+                                "route")))
     return st;
   mark(3);
   // a4-a6: L1 GEMM + SwiGLU + compact bf16 + NVFP4 (fused: in the GEMM's

@@ -30,6 +30,11 @@ hipError_t launch_copy_scalar(const float* src, float* dst, hipStream_t s);
 // f16out (nullable) [n]: exact f16 of e2m1 * block scale (the GEMM operand)
 hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_t* q, uint8_t* sf,
                            uint16_t* f16out, hipStream_t s);
+// The same with the global scale formed from namax partial maxima of |x|
+// (amax_part, as the second pass of launch_global_scale would) and stored to
+// gs_out; f16out is required.
+hipError_t launch_quantize_folded(const uint16_t* x, int64_t n, const float* amax_part, int namax, float* gs_out,
+                                  uint8_t* q, uint8_t* sf, uint16_t* f16out, hipStream_t s);
 // The same for the SwiGLU columns of an interleaved [rows][2I] bf16 matrix
 // (groups of 8 columns alternating SiLU(gate), SiLU(gate) * up): the compact
 // [rows][I] values are quantized (rows * I / 8 < 2^32).
@@ -106,6 +111,18 @@ size_t route_workspace_bytes(int64_t P, int E);
 hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int small_rows, int small_tile, int* offsets,
                         int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall, int* err_count,
                         int* ws, int* sched, hipStream_t s);
+// launch_route runs in one workgroup for these P (else in many).
+bool route_single(int64_t P);
+// Workgroups of the global-scale maxima that launch_amax_route uses for n8
+// 8-element chunks (at most 256).
+int amax_route_blocks(int64_t n8);
+// launch_route (P with route_single) and, in the same launch, the first pass
+// of the global scale of the n bf16 values x: namax = amax_route_blocks(n /
+// 8) maxima of |x| into partial[0 .. namax), for launch_quantize_folded.
+hipError_t launch_amax_route(const uint16_t* x, int64_t n, float* partial, int namax, const int32_t* ids,
+                             int64_t P, int E, int tile_rows, int small_rows, int small_tile, int* offsets,
+                             int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall,
+                             int* err_count, int* sched, hipStream_t s);
 // y[t] = sum over the k rows of token t of o (fp32), or of the f16 form
 // o_f16 * 2^o_exp when o_f16 is non-null (one exponent per 32 columns).
 hipError_t launch_combine(const float* o, const int32_t* ids, int E, int64_t T, int k, int64_t H,

@@ -29,6 +29,7 @@
 #include <algorithm>
 
 #include "launch.hpp"
+#include "nvfp4_device.hpp"
 
 namespace nvfp4 {
 
@@ -123,22 +124,17 @@ __device__ __forceinline__ void group_tiles(int E, int tile_rows, int small_rows
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
-                                                              int64_t P, int E, int tile_rows,
-                                                              int small_rows, int small_tile,
-                                                              int* __restrict__ offsets,
-                                                              int* __restrict__ perm,
-                                                              GemmTile* __restrict__ tiles,
-                                                              int* __restrict__ ntiles,
-                                                              GemmTile* __restrict__ small,
-                                                              int* __restrict__ nsmall,
-                                                              int* __restrict__ err_count,
-                                                              int* __restrict__ sched) {
-  extern __shared__ int sm[];
+// The grouping in one workgroup of kRouteThreads threads; sm is its LDS
+// (route_lds_bytes(E)).
+__device__ __forceinline__ void route_block(int* sm, int& s_err, const int32_t* __restrict__ ids, int64_t P,
+                                            int E, int tile_rows, int small_rows, int small_tile,
+                                            int* __restrict__ offsets, int* __restrict__ perm,
+                                            GemmTile* __restrict__ tiles, int* __restrict__ ntiles,
+                                            GemmTile* __restrict__ small, int* __restrict__ nsmall,
+                                            int* __restrict__ err_count, int* __restrict__ sched) {
   int* cnt = sm;                            // [waves][E]: pass-1 counts, then running positions
   int* total = cnt + kRouteWaves * E;       // [E]
   int* scan = total + E;                    // [1024] block scan scratch
-  __shared__ int s_err;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
@@ -196,6 +192,65 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
       perm[pos] = (int)p;
       if ((match & lt_mask) == 0) mycnt[e] = pos - rank + __popcll(match);
     }
+  }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
+                                                              int64_t P, int E, int tile_rows,
+                                                              int small_rows, int small_tile,
+                                                              int* __restrict__ offsets,
+                                                              int* __restrict__ perm,
+                                                              GemmTile* __restrict__ tiles,
+                                                              int* __restrict__ ntiles,
+                                                              GemmTile* __restrict__ small,
+                                                              int* __restrict__ nsmall,
+                                                              int* __restrict__ err_count,
+                                                              int* __restrict__ sched) {
+  extern __shared__ int sm[];
+  __shared__ int s_err;
+  route_block(sm, s_err, ids, P, E, tile_rows, small_rows, small_tile, offsets, perm, tiles, ntiles, small,
+              nsmall, err_count, sched);
+}
+
+// The grouping (workgroup 0, as route_kernel) and, independent of it, the
+// first pass of the activations' global scale (workgroups 1 .. namax: the
+// maximum of |x| over a grid-stride range of 8-element chunks each, into
+// partial[0 .. namax)): one launch instead of two, the grouping running
+// beside the maxima.
+__global__ __launch_bounds__(kRouteThreads) void amax_route_kernel(const uint4* __restrict__ x, int64_t n8,
+                                                                   float* __restrict__ partial, int namax,
+                                                                   const int32_t* __restrict__ ids,
+                                                                   int64_t P, int E, int tile_rows,
+                                                                   int small_rows, int small_tile,
+                                                                   int* __restrict__ offsets,
+                                                                   int* __restrict__ perm,
+                                                                   GemmTile* __restrict__ tiles,
+                                                                   int* __restrict__ ntiles,
+                                                                   GemmTile* __restrict__ small,
+                                                                   int* __restrict__ nsmall,
+                                                                   int* __restrict__ err_count,
+                                                                   int* __restrict__ sched) {
+  extern __shared__ int sm[];
+  __shared__ int s_err;
+  if (blockIdx.x == 0) {
+    route_block(sm, s_err, ids, P, E, tile_rows, small_rows, small_tile, offsets, perm, tiles, ntiles, small,
+                nsmall, err_count, sched);
+    return;
+  }
+  const int b = (int)blockIdx.x - 1, tid = threadIdx.x;
+  float m = 0.0f;
+  for (int64_t i = (int64_t)b * kRouteThreads + tid; i < n8; i += (int64_t)namax * kRouteThreads) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + i));  // read once
+    m = fmaxf(m, abs_max8(make_uint4(v.x, v.y, v.z, v.w)));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float* red = reinterpret_cast<float*>(sm);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float r = red[0];
+    for (int w = 1; w < kRouteWaves; ++w) r = fmaxf(r, red[w]);
+    partial[b] = r;
   }
 }
 
@@ -419,6 +474,7 @@ size_t route_lds_bytes(int E) { return sizeof(int) * ((size_t)kRouteWaves * E + 
 
 // Pairs per workgroup of the many-workgroup grouping, and the most workgroups.
 constexpr int64_t kRouteChunk = 4096;
+constexpr int kAmaxRouteMax = 256;  // maxima of the fused global-scale pass, at most
 constexpr int kRouteMaxGroups = 256;
 
 int route_groups(int64_t P) {
@@ -449,6 +505,24 @@ hipError_t launch_route(const int32_t* ids, int64_t P, int E, int tile_rows, int
                                                  tiles, ntiles,
                                                  small, nsmall, err_count, sched);
   route_place_kernel<<<G, kRouteThreads, sizeof(int) * kRouteWaves * E, s>>>(ids, P, E, gcount, perm);
+  return hipGetLastError();
+}
+
+bool route_single(int64_t P) { return route_groups(P) == 1; }
+
+int amax_route_blocks(int64_t n8) {
+  const int64_t b = (n8 + 4 * kRouteThreads - 1) / (4 * kRouteThreads);
+  return (int)(b < 1 ? 1 : b > kAmaxRouteMax ? kAmaxRouteMax : b);
+}
+
+hipError_t launch_amax_route(const uint16_t* x, int64_t n, float* partial, int namax, const int32_t* ids,
+                             int64_t P, int E, int tile_rows, int small_rows, int small_tile, int* offsets,
+                             int* perm, GemmTile* tiles, int* ntiles, GemmTile* small, int* nsmall,
+                             int* err_count, int* sched, hipStream_t s) {
+  if (!route_single(P) || namax < 1 || namax > kAmaxRouteMax) return hipErrorInvalidValue;
+  amax_route_kernel<<<namax + 1, kRouteThreads, route_lds_bytes(E), s>>>(
+      reinterpret_cast<const uint4*>(x), n / 8, partial, namax, ids, P, E, tile_rows, small_rows, small_tile,
+      offsets, perm, tiles, ntiles, small, nsmall, err_count, sched);
   return hipGetLastError();
 }
 

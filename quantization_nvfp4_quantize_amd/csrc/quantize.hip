@@ -99,16 +99,21 @@ __global__ void copy_scalar_kernel(const float* __restrict__ src, float* __restr
 // IL: the input is an interleaved [rows][2 * 8 il8] matrix whose 8-column
 // groups alternate SiLU(gate) and SwiGLU values; chunk i of the compact
 // [rows][8 il8] tensor is its row's group 2 (i % il8) + 1.
+// With amax_part (namax per-workgroup maxima of |x|) instead of gs, every
+// workgroup reduces the maxima itself and forms g = amax / (6 * 448) (1 for
+// an all-zero tensor) exactly as amax_finalize_kernel does, and workgroup 0
+// stores it to gs_out: the reduction pass without a launch of its own.
 template <bool F16OUT, bool IL = false>
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t n8,
                                                              const float* __restrict__ gs,
                                                              uint32_t* __restrict__ q,
                                                              uint8_t* __restrict__ sf,
                                                              f16x8* __restrict__ f16out,
-                                                             uint32_t il8 = 0) {
+                                                             uint32_t il8 = 0,
+                                                             const float* __restrict__ amax_part = nullptr,
+                                                             int namax = 0, float* __restrict__ gs_out = nullptr) {
   __shared__ float rtab[128];
-  const float E = 1.0f / gs[0];
-  fill_rtab(rtab, E, threadIdx.x);
+  __shared__ float red[kQThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kQChunksPerWG + threadIdx.x;
   uint4 w[kQUnroll];
 #pragma unroll
@@ -121,6 +126,22 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     }
     w[u] = (i < n8) ? load_nt(x + src) : make_uint4(0, 0, 0, 0);
   }
+  float g;
+  if (amax_part) {  // kernel-uniform
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < namax; i += kQThreads) m = fmaxf(m, amax_part[i]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float r = red[0];
+    for (int k = 1; k < kQThreads / 64; ++k) r = fmaxf(r, red[k]);
+    g = (r > 0.0f) ? r / 2688.0f : 1.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) gs_out[0] = g;
+  } else {
+    g = gs[0];
+  }
+  const float E = 1.0f / g;
+  fill_rtab(rtab, E, threadIdx.x);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < kQUnroll; ++u) {
@@ -248,6 +269,18 @@ hipError_t launch_quantize(const uint16_t* x, int64_t n, const float* gs, uint8_
   else
     quantize_kernel<false><<<(unsigned)wg, kQThreads, 0, s>>>(
         reinterpret_cast<const uint4*>(x), n8, gs, reinterpret_cast<uint32_t*>(q), sf, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_folded(const uint16_t* x, int64_t n, const float* amax_part, int namax, float* gs_out,
+                                  uint8_t* q, uint8_t* sf, uint16_t* f16out, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  if (!amax_part || namax < 1 || !gs_out || !f16out) return hipErrorInvalidValue;
+  const int64_t wg = (n8 + kQChunksPerWG - 1) / kQChunksPerWG;
+  quantize_kernel<true><<<(unsigned)wg, kQThreads, 0, s>>>(
+      reinterpret_cast<const uint4*>(x), n8, nullptr, reinterpret_cast<uint32_t*>(q), sf,
+      reinterpret_cast<f16x8*>(f16out), 0u, amax_part, namax, gs_out);
   return hipGetLastError();
 }
 
