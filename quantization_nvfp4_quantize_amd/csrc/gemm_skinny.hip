@@ -62,10 +62,10 @@ struct SkOperands {
   uint32_t a_base;      // this lane's A row (tile row 8 wave + lane / 8) + 16 c, c = (lane & 7) ^ key(row)
   const uint8_t* bq;    // B nibbles of the tile's expert, wave-uniform
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
-  uint32_t bq_row[4];   // byte offsets of this lane's column rows (tile rows 64 wave + 16 ct + lane % 16)
+  uint32_t bq_row;      // byte offset of this lane's nibbles in column tile 0: tile row 64 wave + lane % 16, + 16 (lane / 16)
+  uint32_t bq_step[4];  // wave-uniform: from it to column tile ct (tile rows 64 wave + 16 ct + lane % 16)
   uint32_t sf_dma;      // scale-row offset of the tile row 64 wave + lane / 4
   uint32_t sf_step[4];  // wave-uniform: from it to the scale rows of the tile rows 64 wave + 16 i + lane / 4
-  int g;                // lane group (lane / 16)
   bool a_rows;          // wave-uniform: this wave's 8 A rows include a valid one
 };
 
@@ -113,9 +113,12 @@ __device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int ss, int m) {
   SkB b;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    const uint8_t* q = op.bq + (size_t)ss * (kSkSteps * kStepK / 2) + op.bq_row[ct] + 16 * op.g;
+    // a wave-uniform base plus a 32-bit lane offset: the scalar-base form of
+    // the load, no 64-bit address per lane
+    const uint8_t* base = op.bq + (size_t)ss * (kSkSteps * kStepK / 2);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) b.q[ct][h] = *reinterpret_cast<const uint4*>(q + 64 * (h & (m >> 2)));
+    for (int h = 0; h < 2; ++h)
+      b.q[ct][h] = *reinterpret_cast<const uint4*>(base + (op.bq_row + op.bq_step[ct] + 64u * (uint32_t)(h & (m >> 2))));
   }
   return b;
 }
@@ -153,19 +156,27 @@ __device__ __forceinline__ void sk_load_sf_tail(uint8_t* sftail, const SkOperand
 
 // This lane's block-scale pairs of super-step ss for its four column tiles:
 // s[ct][h] holds, in its low 16 bits, the scales of the 16-K blocks 8 h + 2 g
-// and 8 h + 2 g + 1 (those of MFMA steps (h, 0..1) and (h, 2..3)).
+// and 8 h + 2 g + 1 (those of MFMA steps (h, 0..1) and (h, 2..3)).  The
+// rows tr = 64 wave + 16 ct + lane % 16 of the four column tiles share
+// sk_sf_swz(tr) = (lane % 16) / 4 & 3, so one lane address and immediate
+// offsets (1024 B, resp. 128 B of the tail area, per column tile) reach all
+// four.
 __device__ __forceinline__ void sk_read_sf(const uint8_t* sfbuf, const uint8_t* sftail, int ss, int nfull,
                                            int wave, int lane, uint32_t (&s)[4][2]) {
-  const int g = lane >> 4, sh = 16 * (g & 1);
+  const int g = lane >> 4, sh = 16 * (g & 1), r = lane & 15;
+  if (ss < nfull) {
+    const uint8_t* const p = sfbuf + 64 * (64 * wave + r) + 16 * ((ss & 3) ^ ((r >> 2) & 3));
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int tr = 64 * wave + 16 * ct + (lane & 15);
-    if (ss < nfull) {
-      const uint4 v = *reinterpret_cast<const uint4*>(sfbuf + 64 * tr + 16 * ((ss & 3) ^ sk_sf_swz(tr)));
+    for (int ct = 0; ct < 4; ++ct) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + 1024 * ct);
       s[ct][0] = word_of(v, g >> 1) >> sh;
       s[ct][1] = word_of(v, 2 + (g >> 1)) >> sh;
-    } else {
-      s[ct][0] = *reinterpret_cast<const uint32_t*>(sftail + 8 * tr + 4 * (g >> 1)) >> sh;
+    }
+  } else {
+    const uint8_t* const p = sftail + 8 * (64 * wave + r) + 4 * (g >> 1);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      s[ct][0] = *reinterpret_cast<const uint32_t*>(p + 128 * ct) >> sh;
       s[ct][1] = 0;
     }
   }
@@ -277,8 +288,12 @@ __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64
                                             int nrows, WRow wrow) {
   const int c = (lane & 7) ^ swz_key(R);
   op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)c;
+  const int b0 = wrow(64 * wave + (lane & 15));
+  op.bq_row = (uint32_t)b0 * (uint32_t)(K / 2) + 16u * (uint32_t)(lane >> 4);
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) op.bq_row[ct] = (uint32_t)wrow(64 * wave + 16 * ct + (lane & 15)) * (uint32_t)(K / 2);
+  for (int ct = 0; ct < 4; ++ct)
+    op.bq_step[ct] =
+        (uint32_t)__builtin_amdgcn_readfirstlane((wrow(64 * wave + 16 * ct + (lane & 15)) - b0) * (int)(K / 2));
   // the weight rows of tile rows 64 wave + 16 i + r (r < 16) lie the same
   // number of rows after that of 64 wave + r for every r (plain order: 16 i;
   // the L1 gate/up order: 32 (i & 1) + 8 (i >> 1)), so the steps are scalars
@@ -287,7 +302,6 @@ __device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     op.sf_step[i] = (uint32_t)__builtin_amdgcn_readfirstlane((wrow(64 * wave + 16 * i + (lane >> 2)) - w0) * (int)(K / 16));
-  op.g = lane >> 4;
   op.a_rows = __builtin_amdgcn_readfirstlane(8 * wave < nrows ? 1 : 0) != 0;
 }
 
