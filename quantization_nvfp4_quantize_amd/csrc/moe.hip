@@ -37,6 +37,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteIdRegs = 4;  // steps of 64 pairs per wave whose ids one workgroup's grouping keeps in registers
 
 // Exclusive prefix of v over the threads of the workgroup (one value per
 // thread, kRouteThreads threads, scratch of at least 2 kRouteWaves ints);
@@ -137,19 +138,31 @@ __device__ __forceinline__ void route_block(int* sm, int& s_err, const int32_t* 
   int* scan = total + E;                    // [1024] block scan scratch
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave w owns pairs [p0, p1), 64 per step; the ids of its first
+  // kRouteIdRegs steps are loaded once, before anything else (both passes
+  // use them), the rest of a larger range is read in each pass
+  const int64_t p0 = P * wave / kRouteWaves, p1 = P * (wave + 1) / kRouteWaves;
+  int idr[kRouteIdRegs];
+#pragma unroll
+  for (int c = 0; c < kRouteIdRegs; ++c) {
+    const int64_t p = p0 + 64 * c + lane;
+    idr[c] = p < p1 ? ids[p] : -1;
+  }
   for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) cnt[i] = 0;
   if (tid == 0) s_err = 0;
   __syncthreads();
 
-  const int64_t p0 = P * wave / kRouteWaves, p1 = P * (wave + 1) / kRouteWaves;
   int* mycnt = cnt + wave * E;
-  for (int64_t p = p0 + lane; p < p1; p += 64) {
-    int e = ids[p];
+  auto count = [&](int64_t p, int e) {
+    if (p >= p1) return;
     if (e >= 0 && e < E)
       atomicAdd(&mycnt[e], 1);
     else
       atomicAdd(&s_err, 1);
-  }
+  };
+#pragma unroll
+  for (int c = 0; c < kRouteIdRegs; ++c) count(p0 + 64 * c + lane, idr[c]);
+  for (int64_t p = p0 + 64 * kRouteIdRegs + lane; p < p1; p += 64) count(p, ids[p]);
   __syncthreads();
 
   // per expert: total, and each wave's start relative to the expert start
@@ -177,9 +190,8 @@ __device__ __forceinline__ void route_block(int* sm, int& s_err, const int32_t* 
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t b = p0; b < p1; b += 64) {
-    const int64_t p = b + lane;
-    int e = (p < p1) ? ids[p] : -1;
+  // one step of 64 pairs (e = -1 past the range; every lane takes part)
+  auto place = [&](int64_t p, int e) {
     const bool valid = e >= 0 && e < E;
     uint64_t match = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -192,6 +204,13 @@ __device__ __forceinline__ void route_block(int* sm, int& s_err, const int32_t* 
       perm[pos] = (int)p;
       if ((match & lt_mask) == 0) mycnt[e] = pos - rank + __popcll(match);
     }
+  };
+#pragma unroll
+  for (int c = 0; c < kRouteIdRegs; ++c)
+    if (p0 + 64 * c < p1) place(p0 + 64 * c + lane, idr[c]);
+  for (int64_t b = p0 + 64 * kRouteIdRegs; b < p1; b += 64) {
+    const int64_t p = b + lane;
+    place(p, (p < p1) ? ids[p] : -1);
   }
 }
 
@@ -432,10 +451,13 @@ __global__ __launch_bounds__(256) void combine_f16_kernel(const uint16_t* __rest
       }
       uint4 v[KMAX > 0 ? KMAX : 1];
       int s[KMAX > 0 ? KMAX : 1];
+      // every row of the token is loaded together with the ids (rows of
+      // skipped pairs hold stale bytes and are not added): one round trip
+      // to memory instead of two
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         const int64_t r = t * k + j;
-        if (ok[j]) {
+        if (j < k) {  // kernel-uniform
           const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o16 + r * H + c));
           v[j] = make_uint4(x.x, x.y, x.z, x.w);
           s[j] = oexp[r * nb + c / 32];
