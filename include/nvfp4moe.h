@@ -252,8 +252,8 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args *args, void *ws, size_t ws_bytes, 
  * until the process ends.  The caller still passes every input and output.
  * Calls whose workspace (moe_expert_ffn_nvfp4_workspace_size) exceeds that
  * size are rejected with NVFP4_ERR_WORKSPACE before anything is enqueued;
- * 64 MiB holds, e.g., the T128 H7168 I2048 k8 decode layer (21.6 MiB with a
- * bf16 output, 35.4 MiB with fp32) and T256 with a bf16 output.  The first
+ * 64 MiB holds, e.g., the T128 H7168 I2048 k8 decode layer (29.6 MiB with a
+ * bf16 output, 43.4 MiB with fp32) and T256 with a bf16 output (51.2 MiB).  The first
  * call on a device looks the buffer's device address up (no allocation);
  * make that first call outside graph capture.  Every call on one GPU uses
  * that GPU's one buffer: calls that overlap on the same GPU (two streams,
