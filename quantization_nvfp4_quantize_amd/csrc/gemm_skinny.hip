@@ -248,10 +248,11 @@ __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB
 
 // The K loop over nk steps of 64 (nk even); ends with all loads landed and
 // every wave past its last LDS read.  row_of(tr) is the byte offset of the
-// scale row of tile row tr within the expert's scales.
-template <class RowOf>
+// scale row of tile row tr within the expert's scales.  after_first() runs
+// once the first loads are issued (loads it issues then land with them).
+template <class RowOf, class AfterFirst>
 __device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op, int nk, f32x4 (&acc)[2][4],
-                                            RowOf row_of) {
+                                            RowOf row_of, AfterFirst after_first) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
@@ -264,6 +265,7 @@ __device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op
   else
     sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
   W[0] = sk_load_b(op, 0, sk_steps(0, nfull));
+  after_first();
   // A fragment of step (0, s) for row r (group 0): K [32 g + 8 s, +8) is
   // chunk 4 (g & 1) + s of region g >> 1
   int ra[4];
@@ -453,6 +455,14 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16) + (size_t)wk.ss0 * (kSkSteps * kStepK * 2);
   op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2) + (size_t)wk.ss0 * (kSkSteps * kStepK / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
+  // what the epilogue reads from memory, loaded as raw values beside the A
+  // rows (used only there, so nothing waits for them before): the pair of
+  // tile row tid, alpha's factors, the output scale -- each would otherwise
+  // cost the epilogue a round trip
+  int my_perm = 0;
+  if (tid < kSkTileM && p.perm) my_perm = p.perm[t.row0 + (tid < t.nrows ? tid : 0)];
+  const float a_gs = p.a_gs[0], w_gs = p.w_gs[t.expert];
+  const float out_gs = p.c_q ? p.out_gs[0] : 1.0f;
   {
     const int R = 8 * wave + (lane >> 3);
     const int o = out_row_of(R);
@@ -460,7 +470,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
     sk_operands(op, arow, p.K, wave, lane, R, t.nrows, wrow);
   }
   f32x4 acc[2][4];
-  sk_mainloop(L, op, wk.nk, acc, sf_row);
+  sk_mainloop(L, op, wk.nk, acc, sf_row, [] {});
   // a piece that is not its item's last runs the epilogue with no rows (an
   // early return here made the compiler spill in the K loop)
   const int nrows = (wk.npieces > 1 && !sk_split_sum(sp, wk, acc, tid, &last_piece)) ? 0 : t.nrows;
@@ -472,8 +482,8 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
   uint16_t* ctile = reinterpret_cast<uint16_t*>(lds_a);
   float* rtab = reinterpret_cast<float*>(lds_a + kCTileChunks);
   int* out_row = reinterpret_cast<int*>(lds_a + kCTileChunks + 32);
-  if (tid < kSkTileM) out_row[tid] = out_row_of(tid);
-  const float alpha = p.a_gs[0] * p.w_gs[t.expert];
+  if (tid < kSkTileM) out_row[tid] = p.perm ? my_perm : t.row0 + (tid < t.nrows ? tid : 0);
+  const float alpha = a_gs * w_gs;
   const int64_t I = p.N2 / 2;
   const int hb = tid & 15;
   const int npass = (nrows + kSkThreads / 16 - 1) / (kSkThreads / 16);
@@ -509,7 +519,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
     __syncthreads();
   }
   fill_ctile(false);
-  const float E2 = p.c_q ? 1.0f / p.out_gs[0] : 1.0f;  // no quantization without c_q
+  const float E2 = p.c_q ? 1.0f / out_gs : 1.0f;  // no quantization without c_q
   fill_rtab(rtab, E2, tid);
   __syncthreads();
   for (int pass = 0; pass < npass; ++pass) {
@@ -553,17 +563,31 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p, Sk
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
   sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), t.nrows,
               wrow);
+  // what the epilogue reads from memory, loaded as raw values with the first
+  // operands (used only there): the pair of tile row tid (read beside the A
+  // rows), alpha's factors, and, once the first operands are on their way,
+  // the pair's routing weight -- each would otherwise cost the epilogue a
+  // round trip
+  const int my_pair = tid < kSkTileM ? pair_of(tid) : 0;
+  const float a_gs = p.a_gs[0], w_gs = p.w_gs[t.expert];
+  float my_w = 1.0f;
   f32x4 acc[2][4];
-  sk_mainloop(L, op, wk.nk, acc, sf_row);
+  sk_mainloop(L, op, wk.nk, acc, sf_row, [&] {
+    if (tid < kSkTileM && p.row_w) my_w = p.row_w[my_pair];
+  });
   // a piece that is not its item's last runs the epilogue with no rows (an
   // early return here made the compiler spill in the K loop)
   const int nrows = (wk.npieces > 1 && !sk_split_sum(sp, wk, acc, tid, &last_piece)) ? 0 : t.nrows;
-  // the scales' LDS holds the output rows, the A buffers each wave's
-  // 4 KiB transposition scratch
+  // the scales' LDS holds the output rows and their scales, the A buffers
+  // each wave's 4 KiB transposition scratch
   int* out_row = reinterpret_cast<int*>(lds_sf);
-  if (tid < kSkTileM) out_row[tid] = pair_of(tid);
+  float* row_scale = reinterpret_cast<float*>(lds_sf) + kSkTileM;
+  if (tid < kSkTileM) {
+    const float alpha = a_gs * w_gs;
+    out_row[tid] = my_pair;
+    row_scale[tid] = p.row_w ? alpha * my_w : alpha;
+  }
   __syncthreads();
-  const float alpha = p.a_gs[0] * p.w_gs[t.expert];
   float* const scratch = reinterpret_cast<float*>(lds_a) + wave * 1024;
   // half h of the wave's 64 columns is column tiles 2 h, 2 h + 1
   auto fill = [&](int half, float* sc) {
@@ -577,7 +601,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p, Sk
   };
   l2_store_rows(p, scratch, 0, nrows, (int64_t)nt * kTileN + wave * 64, lane, fill,
                 [&](int r) { return out_row[r]; },
-                [&](int r) { return p.row_w ? alpha * p.row_w[out_row[r]] : alpha; });
+                [&](int r) { return row_scale[r]; });
 }
 
 // ------------------------------------------------------------------ launchers
