@@ -29,10 +29,11 @@ def _problem(nv, orc, M, K, N, seed):
     return x, (wq, wsf, wg), (oq, osf, gw)
 
 
-# 32-row tiles (M <= 64, K a multiple of 256 or 128), 256-row tiles with
-# ragged rows, and K values with and without whole 256-K super-steps
+# 32-row tiles (M <= 64, K a multiple of 256 or 128; N 768: an odd number of
+# column tiles), 256-row tiles with ragged rows, and K values with and
+# without whole 256-K super-steps
 SHAPES = [(1, 256, 256), (3, 128, 256), (64, 1280, 512), (65, 256, 256), (300, 512, 768),
-          (257, 7168, 256), (40, 64, 256)]
+          (257, 7168, 256), (40, 64, 256), (17, 1024, 768)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)

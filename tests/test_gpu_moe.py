@@ -245,11 +245,12 @@ def test_moe_bf16_combine_skipped_pairs(nv, orc, topk):
     assert rel_fro(yb, yo) <= 5e-3 and cosine(yb, yo) >= 0.9999
 
 
-@pytest.mark.parametrize("H,I", [(1280, 768), (1024, 512), (256, 1280)])
+@pytest.mark.parametrize("H,I", [(1280, 768), (1024, 512), (256, 1280), (1280, 1024)])
 def test_moe_skinny_k_schedules(nv, orc, H, I):
     """32-row tiles with reduction lengths whose 256-K super-steps leave a
     partial group of four (H 1280: five, I 768: three), exactly one group
-    (H 1024) and two groups and a half (I 1280), all against the oracle."""
+    (H 1024) and two groups and a half (I 1280), all against the oracle;
+    H 1280 I 1024 gives the L2 an odd number of column tiles."""
     import dataclasses
     cfg = dataclasses.replace(synth.TINY, T=40, H=H, I=I, E=4, name=f"mid{H}x{I}", a2_gs=4.0 / 2688.0)
     w = gpu_weights(nv, cfg)
