@@ -221,8 +221,10 @@ struct SkLds {
 // also tells every wave that A buffer BUF ^ 1 is no longer read), read its
 // scale words; at the end of a macro-step, once every wave has read them,
 // fetch the next macro-step's scales; issue the loads of super-step ss + 1
-// (A first, then B; past the end they repeat the last super-step and are not
-// used, and the tail's scales with the tail), then run its MFMAs.
+// (A first, then B, and the tail's scales with the tail; the last super-step
+// issues none: a wasted super-step of loads per item, which the epilogue
+// would also wait for, cost the 8-super-step L2 items 3 %), then run its
+// MFMAs.
 template <int BUF, class RowOf>
 __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB (&W)[2], const SkOperands& op,
                                          int ss, int nss, int nfull, int wave, int lane, f32x4 (&acc)[2][4],
@@ -235,11 +237,13 @@ __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB
     lds_barrier();
     sk_load_sf_macro(L.sf, op, (ss + 1) >> 2, nfull, wave, lane);
   }
-  const int nx = min(ss + 1, nss - 1);
-  const int mx = sk_steps(nx, nfull);
-  sk_load_a(L.a + (BUF ^ 1) * kSkABuf, op, nx, mx, wave);
-  W[BUF ^ 1] = sk_load_b(op, nx, mx);
-  if (ss + 1 == nfull && nss > nfull) sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
+  if (ss + 1 < nss) {
+    const int nx = ss + 1;
+    const int mx = sk_steps(nx, nfull);
+    sk_load_a(L.a + (BUF ^ 1) * kSkABuf, op, nx, mx, wave);
+    W[BUF ^ 1] = sk_load_b(op, nx, mx);
+    if (nx == nfull && nss > nfull) sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
+  }
   SCHED_FENCE();
   const f16x8* buf = L.a + BUF * kSkABuf;
   sk_half(buf, ra, W[BUF], sw, 0, acc);
@@ -250,21 +254,25 @@ __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB
 // every wave past its last LDS read.  row_of(tr) is the byte offset of the
 // scale row of tile row tr within the expert's scales.  after_first() runs
 // once the first loads are issued (loads it issues then land with them).
-template <class RowOf, class AfterFirst>
-__device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op, int nk, f32x4 (&acc)[2][4],
-                                            RowOf row_of, AfterFirst after_first) {
+template <class RowOf, class ABase, class AfterFirst>
+__device__ __forceinline__ void sk_mainloop(const SkLds& L, SkOperands& op, int nk, f32x4 (&acc)[2][4],
+                                            RowOf row_of, ABase a_base_of, AfterFirst after_first) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int nfull = nk / kSkSteps;
   const int nss = nfull + (nk % kSkSteps ? 1 : 0);
   SkB W[2];
-  sk_load_a(L.a, op, 0, sk_steps(0, nfull), wave);
+  // the weights first: their addresses need only the tile; the activation
+  // rows' (a_base_of) also the routing permutation, whose load then
+  // overlaps these
+  W[0] = sk_load_b(op, 0, sk_steps(0, nfull));
   if (nfull > 0)
     sk_load_sf_macro(L.sf, op, 0, nfull, wave, lane);
   else
     sk_load_sf_tail(L.sftail, op, nfull, wave, lane, row_of);
-  W[0] = sk_load_b(op, 0, sk_steps(0, nfull));
+  op.a_base = a_base_of();
+  sk_load_a(L.a, op, 0, sk_steps(0, nfull), wave);
   after_first();
   // A fragment of step (0, s) for row r (group 0): K [32 g + 8 s, +8) is
   // chunk 4 (g & 1) + s of region g >> 1
@@ -283,13 +291,16 @@ __device__ __forceinline__ void sk_mainloop(const SkLds& L, const SkOperands& op
   lds_barrier();
 }
 
-// Operand sources of this lane for a tile: A row `arow` (lane's tile row is
-// 8 wave + lane / 8); row_of(tr) gives the global weight row of tile row tr.
+// This lane's A source (a_base) for A row `arow` at tile row R = 8 wave +
+// lane / 8.
+__device__ __forceinline__ uint32_t sk_a_base(uint32_t arow, int64_t K, int lane, int R) {
+  return arow * (uint32_t)(K * 2) + 16u * (uint32_t)((lane & 7) ^ swz_key(R));
+}
+
+// Weight and scale sources of this lane for a tile (a_base is set by the
+// main loop); wrow(tr) gives the global weight row of tile row tr.
 template <class WRow>
-__device__ __forceinline__ void sk_operands(SkOperands& op, uint32_t arow, int64_t K, int wave, int lane, int R,
-                                            int nrows, WRow wrow) {
-  const int c = (lane & 7) ^ swz_key(R);
-  op.a_base = arow * (uint32_t)(K * 2) + 16u * (uint32_t)c;
+__device__ __forceinline__ void sk_operands(SkOperands& op, int64_t K, int wave, int lane, int nrows, WRow wrow) {
   const int b0 = wrow(64 * wave + (lane & 15));
   op.bq_row = (uint32_t)b0 * (uint32_t)(K / 2) + 16u * (uint32_t)(lane >> 4);
 #pragma unroll
@@ -463,14 +474,12 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
   if (tid < kSkTileM && p.perm) my_perm = p.perm[t.row0 + (tid < t.nrows ? tid : 0)];
   const float a_gs = p.a_gs[0], w_gs = p.w_gs[t.expert];
   const float out_gs = p.c_q ? p.out_gs[0] : 1.0f;
-  {
-    const int R = 8 * wave + (lane >> 3);
-    const int o = out_row_of(R);
-    const uint32_t arow = p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o;
-    sk_operands(op, arow, p.K, wave, lane, R, t.nrows, wrow);
-  }
+  const int R = 8 * wave + (lane >> 3);
+  const int o = out_row_of(R);  // the A row's pair, used once the weights' first loads are out
+  sk_operands(op, p.K, wave, lane, t.nrows, wrow);
   f32x4 acc[2][4];
-  sk_mainloop(L, op, wk.nk, acc, sf_row, [] {});
+  sk_mainloop(L, op, wk.nk, acc, sf_row,
+              [&] { return sk_a_base(p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o, p.K, lane, R); }, [] {});
   // a piece that is not its item's last runs the epilogue with no rows (an
   // early return here made the compiler spill in the K loop)
   const int nrows = (wk.npieces > 1 && !sk_split_sum(sp, wk, acc, tid, &last_piece)) ? 0 : t.nrows;
@@ -561,8 +570,9 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p, Sk
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16) + (size_t)wk.ss0 * (kSkSteps * kStepK * 2);
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2) + (size_t)wk.ss0 * (kSkSteps * kStepK / 2);
   op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
-  sk_operands(op, (uint32_t)pair_of(8 * wave + (lane >> 3)), p.K, wave, lane, 8 * wave + (lane >> 3), t.nrows,
-              wrow);
+  const int R = 8 * wave + (lane >> 3);
+  const int a_pair = pair_of(R);  // used once the weights' first loads are out
+  sk_operands(op, p.K, wave, lane, t.nrows, wrow);
   // what the epilogue reads from memory, loaded as raw values with the first
   // operands (used only there): the pair of tile row tid (read beside the A
   // rows), alpha's factors, and, once the first operands are on their way,
@@ -572,9 +582,11 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p, Sk
   const float a_gs = p.a_gs[0], w_gs = p.w_gs[t.expert];
   float my_w = 1.0f;
   f32x4 acc[2][4];
-  sk_mainloop(L, op, wk.nk, acc, sf_row, [&] {
-    if (tid < kSkTileM && p.row_w) my_w = p.row_w[my_pair];
-  });
+  sk_mainloop(
+      L, op, wk.nk, acc, sf_row, [&] { return sk_a_base((uint32_t)a_pair, p.K, lane, R); },
+      [&] {
+        if (tid < kSkTileM && p.row_w) my_w = p.row_w[my_pair];
+      });
   // a piece that is not its item's last runs the epilogue with no rows (an
   // early return here made the compiler spill in the K loop)
   const int nrows = (wk.npieces > 1 && !sk_split_sum(sp, wk, acc, tid, &last_piece)) ? 0 : t.nrows;
