@@ -262,9 +262,9 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel_k128(MxParams p) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x16{};
 
-  // The sub-step s fragments of stage st, and the stage's scale dwords
-  // shifted so that byte 0 is the K block of sub-step 0 and byte 2 that of
-  // sub-step 1 for this lane's half g.
+  // The sub-step s fragments of stage st, and the stage's scale dwords (as
+  // read; shifted right by 8 g where they are used, so that byte 0 is the K
+  // block of sub-step 0 and byte 2 that of sub-step 1 for this lane's half g).
   auto read_frags = [&](int st, int s, uint4 (&fa)[4], uint4 (&fb)[2]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) fa[mt] = a_frag[s][st * kMxOperand + 128 * mt];
@@ -273,9 +273,9 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel_k128(MxParams p) {
   };
   auto read_scales = [&](int st, uint32_t (&sa)[4], uint32_t (&sb)[2]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sa[mt] = a_scale[st * kMxScales + 32 * mt] >> (8 * g);
+    for (int mt = 0; mt < 4; ++mt) sa[mt] = a_scale[st * kMxScales + 32 * mt];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) sb[nt] = b_scale[st * kMxScales + 32 * nt] >> (8 * g);
+    for (int nt = 0; nt < 2; ++nt) sb[nt] = b_scale[st * kMxScales + 32 * nt];
   };
   // the 8 MFMAs of one sub-step (OPSEL 0: sub-step 0, scale byte 0; 2:
   // sub-step 1, scale byte 2)
@@ -297,9 +297,12 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel_k128(MxParams p) {
   };
 
   // Software pipeline, one step kb per iteration: c0 holds the step's
-  // sub-step 0 fragments (and sa, sb its scales), read during the previous
-  // iteration.  Read the sub-step 1 fragments c1 while the sub-step 0 MFMAs
-  // run; then the barrier, which ends every wave's reads of stage kb and
+  // sub-step 0 fragments (and sa, sb its scale dwords), read during the
+  // previous iteration.  Read the sub-step 1 fragments c1, shift the scale
+  // dwords into sa1, sb1 (the shift waits for those reads: done here, a
+  // sub-step after them, rather than right after the barrier, where it held
+  // back the fragment reads and loads that follow, -1.5 %), and run the
+  // sub-step 0 MFMAs; then the barrier, which ends every wave's reads of stage kb and
   // publishes stage kb + 1; then read the sub-step 0 fragments and scales of
   // step kb + 1 (a stale but valid stage in the last iteration), load step
   // kb + 4 into the stage of step kb, and run the sub-step 1 MFMAs while
@@ -317,11 +320,11 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel_k128(MxParams p) {
     const int st = kb & 3;
     read_frags(st, 1, c1a, c1b);
     SCHED_FENCE();
-    mfmas0(c0a, c0b, sa, sb);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sa1[mt] = sa[mt];
+    for (int mt = 0; mt < 4; ++mt) sa1[mt] = sa[mt] >> (8 * g);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) sb1[nt] = sb[nt];
+    for (int nt = 0; nt < 2; ++nt) sb1[nt] = sb[nt] >> (8 * g);
+    mfmas0(c0a, c0b, sa1, sb1);
     SCHED_FENCE();
     wait_vmcnt<10>();
     lds_barrier();
@@ -444,9 +447,9 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(MxParams p) {
   auto read_scales = [&](int j, uint32_t (&sa)[4], uint32_t (&sb)[2]) {
     const int o = ((j >> 2) & 1) * kMxQuad + (j & 3);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sa[mt] = a_scale[o + 4 * 32 * mt] >> (8 * g);
+    for (int mt = 0; mt < 4; ++mt) sa[mt] = a_scale[o + 4 * 32 * mt];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) sb[nt] = b_scale[o + 4 * 32 * nt] >> (8 * g);
+    for (int nt = 0; nt < 2; ++nt) sb[nt] = b_scale[o + 4 * 32 * nt];
   };
   auto mfmas0 = [&](const uint4 (&fa)[4], const uint4 (&fb)[2], const uint32_t (&sa)[4], const uint32_t (&sb)[2]) {
 #pragma unroll
@@ -481,11 +484,11 @@ __global__ __launch_bounds__(kMxThreads) void mx_gemm_kernel(MxParams p) {
     const int st = kb & 3;
     read_frags(st, 1, c1a, c1b);
     SCHED_FENCE();
-    mfmas0(c0a, c0b, sa, sb);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) sa1[mt] = sa[mt];
+    for (int mt = 0; mt < 4; ++mt) sa1[mt] = sa[mt] >> (8 * g);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) sb1[nt] = sb[nt];
+    for (int nt = 0; nt < 2; ++nt) sb1[nt] = sb[nt] >> (8 * g);
+    mfmas0(c0a, c0b, sa1, sb1);
     SCHED_FENCE();
     wait_vmcnt<KM == 3 ? 8 : 9>();
     lds_barrier();
