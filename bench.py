@@ -338,8 +338,9 @@ def trace_summary(legs, cmd):
            "|---|---|---|---|---|---|---|"]
     mine = set(KERNEL_SOURCES) | {"amax_rows_partial_kernel", "amax_finalize_kernel", "copy_scalar_kernel",
                                   "dequantize_f16_kernel", "route_kernel", "route_count_kernel",
-                                  "route_scan_kernel", "route_place_kernel", "l1_skinny_kernel",
-                                  "l2_skinny_kernel", "__amd_rocclr_copyBuffer"}
+                                  "route_scan_kernel", "route_place_kernel", "amax_route_kernel",
+                                  "l1_skinny_kernel", "l2_skinny_kernel", "mx_dequantize_kernel",
+                                  "__amd_rocclr_copyBuffer"}
     for (leg, k, g), v in sorted(agg.items(), key=lambda kv: (kv[0][0], -sum(kv[1]))):
         if _base(k) in mine:
             out.append(f"| {leg} | {k} | {g} | {len(v)} | {np.mean(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} |")
