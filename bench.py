@@ -613,6 +613,38 @@ def bench_dense(nv, steps, warmup):
                 frac=flops / ms / 1e9 / F16_PEAK_TFLOPS, ms_median=st["ms_median"], median_of=st["median_of"])
 
 
+def _vendor_mx_gemm(nv, x, wq, wsc, steps, warmup):
+    """Context, not the product path: the vendor library's MXFP4 GEMM
+    (torch._scaled_mm -> hipBLASLt) on the same operand bytes (E2M1 nibbles,
+    one E8M0 code per 32 elements, the activations quantized once outside the
+    timed calls), bf16 out, timed eagerly over back-to-back calls.  Its
+    output is not checked (the library may expect another scale layout); None
+    when this torch build has no MXFP4 GEMM."""
+    f4, e8 = getattr(torch, "float4_e2m1fn_x2", None), getattr(torch, "float8_e8m0fnu", None)
+    if f4 is None or e8 is None:
+        return None
+    try:
+        xq, xsc = nv.mx_quantize(x)
+        a, sa = xq.view(f4), xsc.view(e8)
+        b, sb = wq.view(f4).t(), wsc.view(e8)
+        fn = lambda: torch._scaled_mm(a, b, scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        for _ in range(max(warmup, 3)):
+            fn()
+        e0, e1 = _ev(), _ev()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        M, N, K = xq.shape[0], wq.shape[0], 2 * xq.shape[1]
+        return dict(ms=ms, TFLOPs=2.0 * M * N * K / ms / 1e9,
+                    library="torch._scaled_mm (hipBLASLt), MXFP4 operands, bf16 out; GEMM only, eager")
+    except Exception as ex:  # not in this torch / hipBLASLt build
+        return dict(unavailable=f"{type(ex).__name__}: {str(ex)[:120]}")
+
+
 def bench_mx(nv, steps, warmup):
     """The separately labelled MXFP4 variant (OCP MX v1.0: E8M0 scale per 32
     elements) on the scaled FP4 MFMA: quantize 8192 x 7168 (inputs rotated
@@ -640,7 +672,8 @@ def bench_mx(nv, steps, warmup):
     st = {}
     l_ms = graph_time(lambda i: nv.mx_linear(x, wq, wsc, out=out, ws=ws), steps, warmup, stats=st)
     flops = 2.0 * Md * Nd * Kd
-    return dict(format="MXFP4 (OCP MX v1.0, E8M0 scale per 32 elements; not NVFP4)",
+    vendor = _vendor_mx_gemm(nv, x, wq, wsc, steps, warmup)
+    return dict(format="MXFP4 (OCP MX v1.0, E8M0 scale per 32 elements; not NVFP4)", vendor_mxfp4_gemm=vendor,
                 quantize_shape=[M, K], quantize_algorithmic_bytes=qbytes, quantize_ms=q_ms,
                 quantize_GBps=qbytes / q_ms / 1e6, quantize_frac=qbytes / q_ms / 1e6 / HBM_PEAK_GBS,
                 linear_workload=f"M{Md} K{Kd} N{Nd}", linear_ms=l_ms, linear_TFLOPs=flops / l_ms / 1e9,
