@@ -609,8 +609,21 @@ def bench_dense(nv, steps, warmup):
     st = {}
     ms = graph_time(lambda i: nv.linear(x, wq, wsf, wg, out=out, ws=ws), steps, warmup, stats=st)
     flops = 2.0 * M * N * K
+    # Context, not the product path: the vendor library's plain f16 GEMM
+    # (torch -> hipBLASLt) on the same operand values, both already
+    # dequantized (e2m1 * block scale, global scales left out: exact in f16),
+    # f16 out; no quantization pass and 4x the weight bytes.
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    xq, xsf, _ = nv.quantize(x)
+    a16 = nv.dequantize(xq, xsf, one).to(torch.float16)
+    b16 = nv.dequantize(wq, wsf, one).to(torch.float16).t().contiguous()  # [K][N]
+    c16 = torch.empty((M, N), dtype=torch.float16, device=dev)
+    del xq, xsf
+    ms_v = graph_time(lambda i: torch.matmul(a16, b16, out=c16), steps, warmup)
     return dict(workload=f"M{M} K{K} N{N}", ms=ms, TFLOPs=flops / ms / 1e9, algorithmic_flops=flops,
-                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS, ms_median=st["ms_median"], median_of=st["median_of"])
+                frac=flops / ms / 1e9 / F16_PEAK_TFLOPS, ms_median=st["ms_median"], median_of=st["median_of"],
+                vendor_f16_gemm=dict(ms=ms_v, TFLOPs=flops / ms_v / 1e9,
+                                     library="torch.matmul (hipBLASLt), f16 in/out, operands pre-dequantized"))
 
 
 def _vendor_mx_gemm(nv, x, wq, wsc, steps, warmup):
