@@ -252,8 +252,10 @@ __device__ __forceinline__ void sk_super(const SkLds& L, const int (&ra)[4], SkB
 
 // The K loop over nk steps of 64 (nk even); ends with all loads landed and
 // every wave past its last LDS read.  row_of(tr) is the byte offset of the
-// scale row of tile row tr within the expert's scales.  after_first() runs
-// once the first loads are issued (loads it issues then land with them).
+// scale row of tile row tr within the expert's scales.  a_base_of() gives
+// this lane's A source (op.a_base), asked for once the first weight and scale
+// loads are out; after_first() runs once the first loads are issued (loads
+// it issues then land with them).
 template <class RowOf, class ABase, class AfterFirst>
 __device__ __forceinline__ void sk_mainloop(const SkLds& L, SkOperands& op, int nk, f32x4 (&acc)[2][4],
                                             RowOf row_of, ABase a_base_of, AfterFirst after_first) {
