@@ -424,7 +424,10 @@ def load_mfma(kernel, workload):
 
 # ------------------------------------------------------------------ MoE
 def moe_weights(nv, cfg):
-    """All experts' NVFP4 weights on the GPU (model preparation, untimed)."""
+    """All experts' NVFP4 weights on the GPU (model preparation, untimed):
+    (w1q, w1sf, w1gs, w2q, w2sf, w2gs, w1sf_paired, w2sf_paired), the last two
+    the row-paired copies of the scales that the 32-row tiles read (None
+    where H, resp. I, is not a multiple of 1024)."""
     import synth
     E, I, H = cfg.E, cfg.I, cfg.H
     dev = torch.device("cuda:0")
@@ -438,8 +441,10 @@ def moe_weights(nv, cfg):
         a, b = synth.expert_weights(cfg, e, device=dev)
         nv.quantize(a, out=(w1q[e], w1sf[e], w1gs[e:e + 1]))
         nv.quantize(b, out=(w2q[e], w2sf[e], w2gs[e:e + 1]))
+    w1p = nv.pair_scales(w1sf) if H % 1024 == 0 else None
+    w2p = nv.pair_scales(w2sf) if I % 1024 == 0 else None
     torch.cuda.synchronize()
-    return w1q, w1sf, w1gs, w2q, w2sf, w2gs
+    return w1q, w1sf, w1gs, w2q, w2sf, w2gs, w1p, w2p
 
 
 def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
@@ -471,7 +476,8 @@ def bench_moe(nv, cfg, steps, warmup, w=None, mode="fused", median_iters=10):
             e.record()
     # the scale used is read back only in the dynamic flow (elsewhere it is the
     # supplied one, and asking for it would add a copy launch to every layer)
-    args = nv.moe_args(x, ti, tw, *w, a2, out, a2_gs_out=a2_out if mode == "dynamic" else None, l1_unfused=flow,
+    args = nv.moe_args(x, ti, tw, *w[:6], a2, out, a2_gs_out=a2_out if mode == "dynamic" else None, l1_unfused=flow,
+                       w1_sf_paired=w[6], w2_sf_paired=w[7],
                        aux=aux)
     ws = torch.empty(nv.moe_workspace_size(args), dtype=torch.uint8, device=dev)
     for _ in range(warmup):

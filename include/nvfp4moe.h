@@ -143,6 +143,20 @@ int nvfp4_linear(const uint16_t *x, int64_t M, int64_t K, const float *x_gs_in, 
                  float *x_gs_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * nvfp4_pair_scales -- a weight block-scale matrix sf [R][C] (C = K/16 bytes
+ * per row) rewritten once, at weight preparation, in the row-paired layout
+ * the 32-row MoE tiles read (nvfp4_moe_args.w1_sf_paired, w2_sf_paired):
+ *   out[(r/2) * 2C + 128 * (c/64) + 64 * (r%2) + c%64] = sf[r][c]
+ * so each 128-byte line holds 64 bytes of rows 2j and 2j + 1.  The MI355X
+ * counterpart of the pages' remap of the scale factors into the layout
+ * their hardware reads, checked there by a byte-for-byte roundtrip
+ * (DEBUG_LOG.md, "Current State": the SF remap and its forward mapping).
+ *   R >= 0 even, C % 64 == 0 (K % 1024 == 0); sf and out 16-byte aligned,
+ *   not overlapping.  Else NVFP4_ERR_INVALID_ARG.  Asynchronous on stream.
+ */
+int nvfp4_pair_scales(const uint8_t *sf, int64_t R, int64_t C, uint8_t *out, void *stream);
+
+/*
  * MoE expert FFN (DEBUG_LOG.md, "NVFP4 MoE Pipeline"), T tokens, hidden H,
  * intermediate I, E experts, top-k routing; P = T * k (token, expert) pairs,
  * pair p = t * k + j.
@@ -219,6 +233,16 @@ typedef struct {
      aux_events: NVFP4_ERR_INVALID_ARG. */
   void *aux_stream;
   void *const *aux_events;
+  /* nullable: w1_sf and w2_sf in the row-paired layout of nvfp4_pair_scales
+     (prepared once with the weights), read by the 32-row tiles that stream
+     the weights.  Their scale loads then use whole 128-byte lines; with the
+     plain layout a line's second half is needed four 256-K steps after its
+     first, when the weight stream has evicted it, and the line is fetched
+     twice.  Used for w1 when H % 1024 == 0 and for w2 when I % 1024 == 0,
+     ignored otherwise; the 256-row tiles read w1_sf and w2_sf.  The
+     results are the same either way. */
+  const uint8_t *w1_sf_paired;
+  const uint8_t *w2_sf_paired;
 } nvfp4_moe_args;
 
 /*

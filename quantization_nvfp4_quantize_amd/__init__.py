@@ -42,6 +42,7 @@ class MoeArgs(ctypes.Structure):
         ("l1_unfused", ctypes.c_int32),
         ("aux_stream", _vp),
         ("aux_events", ctypes.POINTER(_vp)),
+        ("w1_sf_paired", _vp), ("w2_sf_paired", _vp),
     ]
 
 
@@ -52,6 +53,7 @@ _SIG = {
     "nvfp4_quantize_workspace_size": (_sz, [_i64, _i64]),
     "nvfp4_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_dequantize": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
+    "nvfp4_pair_scales": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp]),
     "nvfp4_gemm_swiglu_quant_workspace_size": (_sz, [_i64, _i64, _i64]),
     "nvfp4_gemm_swiglu_quant": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64,
                                                _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -262,9 +264,27 @@ def mx_linear_workspace(M, K, N, device):
                        device=device)
 
 
+def pair_scales(sf, out=None):
+    """A weight block-scale tensor [..., R, C] (uint8, C = K/16 bytes per row)
+    in the row-paired layout of nvfp4_pair_scales (each 128-byte line holds
+    64 bytes of rows 2j and 2j + 1), for the 32-row MoE tiles.  The leading
+    dimensions are taken as more rows (the experts' rows are consecutive);
+    needs an even row count per matrix and C % 64 == 0.  Returns a new
+    tensor of the same shape (or fills out)."""
+    _require(sf, torch.uint8, "sf")
+    C = sf.shape[-1]
+    R = sf.numel() // C if C else 0
+    if out is None:
+        out = torch.empty_like(sf)
+    _require(out, torch.uint8, "out")
+    _check(_lib.nvfp4_pair_scales(_p(sf), R, C, _p(out), _stream(sf.device)), "nvfp4_pair_scales")
+    return out
+
+
 def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
              x_gs=None, xq=None, xsf=None, x_gs_out=None, l1_c=None, l1_q=None, l1_sf=None,
-             err_count=None, tile_rows=0, a2_gs_out=None, l1_unfused=False, aux=None):
+             err_count=None, tile_rows=0, a2_gs_out=None, l1_unfused=False, aux=None,
+             w1_sf_paired=None, w2_sf_paired=None):
     """Build the nvfp4_moe_args struct from tensors.  The struct holds
     references to every tensor it points at, so they stay allocated for as
     long as the struct lives (a temporary passed here cannot be freed and its
@@ -278,7 +298,9 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
     (torch.cuda.Stream, (torch.cuda.Event, torch.cuda.Event)) on which the
     short tiles of the mixed tiling run concurrently (the events must have
     been recorded once, so that they exist); the struct then holds the event
-    handle array, which the caller keeps alive with the struct."""
+    handle array, which the caller keeps alive with the struct.
+    w1_sf_paired, w2_sf_paired: pair_scales(w1_sf), pair_scales(w2_sf), read
+    by the 32-row tiles when H (resp. I) is a multiple of 1024."""
     _require(x, torch.bfloat16, "x")
     _require(topk_ids, torch.int32, "topk_ids")
     _require(topk_w, torch.float32, "topk_w")
@@ -290,8 +312,12 @@ def moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
                 _p(w1_q), _p(w1_sf), _p(w1_gs), _p(w2_q), _p(w2_sf), _p(w2_gs), _p(a2_gs),
                 _p(out), code, _p(xq), _p(xsf), _p(x_gs_out), _p(l1_c), _p(l1_q), _p(l1_sf),
                 _p(err_count))
+    _require(w1_sf_paired, torch.uint8, "w1_sf_paired")
+    _require(w2_sf_paired, torch.uint8, "w2_sf_paired")
     a._refs = (x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out, x_gs, xq, xsf, x_gs_out,
-               l1_c, l1_q, l1_sf, err_count, a2_gs_out)
+               l1_c, l1_q, l1_sf, err_count, a2_gs_out, w1_sf_paired, w2_sf_paired)
+    a.w1_sf_paired = _p(w1_sf_paired)
+    a.w2_sf_paired = _p(w2_sf_paired)
     a.tile_rows = int(tile_rows)
     a.a2_gs_out = _p(a2_gs_out)
     a.l1_unfused = {False: 0, True: 1, 0: 0, 1: 1, 2: 2, "interleaved": 2}[l1_unfused]
@@ -325,11 +351,12 @@ def moe_expert_ffn_noalloc(args, device):
 
 def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs,
                    out_dtype=torch.bfloat16, x_gs=None, debug=False, tile_rows=0, l1_unfused=False,
-                   aux=None):
+                   aux=None, w1_sf_paired=None, w2_sf_paired=None):
     """NVFP4 MoE expert FFN.  Returns y [T][H] (out_dtype), plus with
     debug=True a dict of the intermediate outputs (xq, xsf, x_gs, l1_c,
     l1_q, l1_sf, err_count, a2_gs_out).  a2_gs None: dynamic L1-output
-    global scale.  tile_rows, l1_unfused, aux: see moe_args."""
+    global scale.  tile_rows, l1_unfused, aux, w1_sf_paired, w2_sf_paired:
+    see moe_args."""
     T, H = x.shape
     I = w1_q.shape[1] // 2
     k = topk_ids.shape[1]
@@ -347,7 +374,8 @@ def moe_expert_ffn(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, 
                    err_count=torch.zeros(1, dtype=torch.int32, device=dev),
                    a2_gs_out=torch.empty(1, dtype=torch.float32, device=dev))
     args = moe_args(x, topk_ids, topk_w, w1_q, w1_sf, w1_gs, w2_q, w2_sf, w2_gs, a2_gs, out,
-                    x_gs=x_gs, tile_rows=tile_rows, l1_unfused=l1_unfused, aux=aux, **dbg)
+                    x_gs=x_gs, tile_rows=tile_rows, l1_unfused=l1_unfused, aux=aux,
+                    w1_sf_paired=w1_sf_paired, w2_sf_paired=w2_sf_paired, **dbg)
     moe_expert_ffn_raw(args, dev)
     if debug:
         return out, dbg

@@ -107,6 +107,22 @@ int nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* gs, int64
                     "nvfp4_dequantize");
 }
 
+// ------------------------------------------------------------------ paired scale rows
+int nvfp4_pair_scales(const uint8_t* sf, int64_t R, int64_t C, uint8_t* out, void* stream) {
+  g_last_error[0] = 0;
+  if (R < 0 || C < 0 || (R & 1) || C % 64 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_pair_scales: need R >= 0 even and C %% 64 == 0 (R=%lld C=%lld)",
+                (long long)R, (long long)C);
+  const size_t n = (size_t)(R * C);
+  if (n == 0) return NVFP4_OK;
+  if (!sf || !out) return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_pair_scales: null pointer");
+  if (!aligned(sf, 16) || !aligned(out, 16))
+    return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_pair_scales: sf and out must be 16-byte aligned");
+  if (sf < out + n && out < sf + n) return fail(NVFP4_ERR_INVALID_ARG, "nvfp4_pair_scales: sf and out overlap");
+  return hip_status(nvfp4::launch_pair_scales(sf, R, C, out, reinterpret_cast<hipStream_t>(stream)),
+                    "nvfp4_pair_scales");
+}
+
 // ------------------------------------------------------------------ GEMM stage
 size_t nvfp4_gemm_swiglu_quant_workspace_size(int64_t M, int64_t K, int64_t N2) {
   (void)N2;
@@ -452,7 +468,8 @@ int moe_validate(const nvfp4_moe_args* a) {
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: null required pointer");
   if (!aligned(a->x, 16) || !aligned(a->w1_q, 16) || !aligned(a->w2_q, 16) || !aligned(a->out, 16) ||
       !aligned(a->xq, 16) || !aligned(a->l1_q, 16) || !aligned(a->l1_c_bf16, 16) ||
-      !aligned(a->w1_sf, 4) || !aligned(a->w2_sf, 4) || !aligned(a->xsf, 4) || !aligned(a->l1_sf, 4))
+      !aligned(a->w1_sf, 4) || !aligned(a->w2_sf, 4) || !aligned(a->xsf, 4) || !aligned(a->l1_sf, 4) ||
+      !aligned(a->w1_sf_paired, 16) || !aligned(a->w2_sf_paired, 16))
     return fail(NVFP4_ERR_INVALID_ARG, "moe_expert_ffn_nvfp4: misaligned pointer");
   return NVFP4_OK;
 }
@@ -567,19 +584,25 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   // the 256-row GEMMs' in the zeroed sched area)
   float* split_ws = skinny ? reinterpret_cast<float*>(w + L.split) : nullptr;
   int* split_cnt = skinny ? reinterpret_cast<int*>(w + L.sched) + 16 : nullptr;
+  // the 32-row tiles' weight scales: the row-paired copies when given and
+  // K (H for L1, I for L2) is a multiple of 1024
+  const bool pair1 = a->w1_sf_paired && H % 1024 == 0, pair2 = a->w2_sf_paired && I % 1024 == 0;
+  const uint8_t* w1_sf_sk = pair1 ? a->w1_sf_paired : a->w1_sf;
+  const uint8_t* w2_sf_sk = pair2 ? a->w2_sf_paired : a->w2_sf;
   auto l1 = [&](const float* out_gs, uint16_t* c_bf16, uint8_t* cq, uint8_t* csf, uint16_t* cf16,
                 uint16_t* c_il) {
     hipError_t e = fork();
     if (e == hipSuccess)
-      e = skinny ? nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq,
+      e = skinny ? nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, w1_sf_sk, a->w1_gs, 2 * I, out_gs, c_bf16, cq,
                                            csf, cf16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, c_il,
-                                           nullptr, nullptr, split_ws, split_cnt)
+                                           nullptr, nullptr, split_ws, split_cnt, pair1)
                  : nvfp4::launch_l1(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
                                     cf16, tiles, ntiles, L.max_tiles, 0, perm, (int)k, s, c_il);
     mark(4);
     if (e == hipSuccess && mixed)
-      e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, a->w1_sf, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
-                                  cf16, small, nsmall, kMaxShortTiles * (int)E, 0, perm, (int)k, aux, c_il);
+      e = nvfp4::launch_l1_skinny(x_f16, x_gs, H, a->w1_q, w1_sf_sk, a->w1_gs, 2 * I, out_gs, c_bf16, cq, csf,
+                                  cf16, small, nsmall, kMaxShortTiles * (int)E, 0, perm, (int)k, aux, c_il,
+                                  nullptr, nullptr, nullptr, nullptr, pair1);
     if (e == hipSuccess) e = join();
     return hip_status(e, "L1 GEMM");
   };
@@ -622,16 +645,17 @@ int moe_expert_ffn_nvfp4(const nvfp4_moe_args* a, void* ws, size_t ws_bytes, voi
   {
     hipError_t e = fork();
     if (e == hipSuccess)
-      e = skinny ? nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles,
+      e = skinny ? nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, w2_sf_sk, a->w2_gs, H, a->topk_w, o, tiles,
                                            ntiles, L.max_tiles, perm, s, 0, nullptr, nullptr, o16, oexp, split_ws,
-                                           split_cnt)
+                                           split_cnt, pair2)
                  : nvfp4::launch_l2(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, tiles, ntiles,
                                     L.max_tiles, perm, s, 0, nullptr, reinterpret_cast<int*>(w + L.sched) + 8, o16,
                                     oexp);
     mark(6);
     if (e == hipSuccess && mixed)
-      e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, a->w2_sf, a->w2_gs, H, a->topk_w, o, small, nsmall,
-                                  kMaxShortTiles * (int)E, perm, aux, 0, nullptr, nullptr, o16, oexp);
+      e = nvfp4::launch_l2_skinny(a2_f16, a2_gs, I, a->w2_q, w2_sf_sk, a->w2_gs, H, a->topk_w, o, small, nsmall,
+                                  kMaxShortTiles * (int)E, perm, aux, 0, nullptr, nullptr, o16, oexp, nullptr,
+                                  nullptr, pair2);
     if (e == hipSuccess) e = join();
     if ((st = hip_status(e, "L2 GEMM"))) return st;
   }

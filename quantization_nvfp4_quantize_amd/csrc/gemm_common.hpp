@@ -209,6 +209,7 @@ struct L1Params {
   int n_ntiles;
   const uint8_t* a_q;   // with a_f16 null (256-row tiles): NVFP4 activations [rows][K/2],
   const uint8_t* a_sf;  // [rows][K/16], dequantized into LDS inside the GEMM
+  int sf_paired;        // 32-row tiles: w_sf in the row-paired layout (K % 1024 == 0)
 };
 
 // Global weight row of the L1 B tile row rb (0..255) for n tile nt: the tile
@@ -244,6 +245,7 @@ struct L2Params {
   int* sched;           // nullable: 8 zeroed work counters (one per XCD) for dynamic item claiming
   uint16_t* o_f16;      // nullable [rows][N] f16 output (used with o_exp instead of o):
   int8_t* o_exp;        // value = o_f16 * 2^o_exp, one exponent per (row, 32-column block) [rows][N/32]
+  int sf_paired;        // 32-row tiles: w_sf in the row-paired layout (K % 1024 == 0)
 };
 
 // Exponent for storing the values of one (row, 32-column block) in f16:

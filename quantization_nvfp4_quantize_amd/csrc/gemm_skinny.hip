@@ -64,8 +64,11 @@ struct SkOperands {
   const uint8_t* bsf;   // B scales of the tile's expert, wave-uniform
   uint32_t bq_row;      // byte offset of this lane's nibbles in column tile 0: tile row 64 wave + lane % 16, + 16 (lane / 16)
   uint32_t bq_step[4];  // wave-uniform: from it to column tile ct (tile rows 64 wave + 16 ct + lane % 16)
-  uint32_t sf_dma;      // scale-row offset of the tile row 64 wave + lane / 4
+  uint32_t sf_dma;      // scale-row offset of the tile row 64 wave + lane / 4 (row-paired: of its pair's
+                        // line half)
   uint32_t sf_step[4];  // wave-uniform: from it to the scale rows of the tile rows 64 wave + 16 i + lane / 4
+  uint32_t sf_ss0;      // wave-uniform: the first super-step of the piece (its scales' column offset)
+  bool sf_pair;         // wave-uniform: the scales are in the row-paired layout
   bool a_rows;          // wave-uniform: this wave's 8 A rows include a valid one
 };
 
@@ -124,7 +127,10 @@ __device__ __forceinline__ SkB sk_load_b(const SkOperands& op, int ss, int m) {
 }
 
 // Direct loads of the scales of macro-step mac (super-steps 4 mac .. 4 mac
-// + 3; chunks past the last whole super-step re-read it and are not used).
+// + 3 of the piece; chunks past the last whole super-step re-read it and are
+// not used).  Super-step j's 16 B of a row sit at 16 j in the plain layout,
+// and at 128 (j / 4) + 16 (j % 4) past the row's half of its pair's lines in
+// the row-paired one (then every line a load touches is used whole).
 __device__ __forceinline__ void sk_load_sf_macro(uint8_t* sfbuf, const SkOperands& op, int mac, int nfull,
                                                  int wave, int lane) {
   // the lane writes position lane & 3 of its rows tr = 64 wave + 16 i +
@@ -133,16 +139,16 @@ __device__ __forceinline__ void sk_load_sf_macro(uint8_t* sfbuf, const SkOperand
   int l = lane;
   asm volatile("" : "+v"(l));
   const int sf_c = (l & 3) ^ ((l >> 4) & 3);
+  const uint32_t j = op.sf_ss0 + (uint32_t)min(4 * mac + sf_c, nfull - 1);
+  const uint32_t off = op.sf_dma + (op.sf_pair ? 128u * (j >> 2) + 16u * (j & 3) : 16u * j);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ssrc = min(4 * mac + sf_c, nfull - 1);
-    dma16s(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf + op.sf_step[i], op.sf_dma + 16u * ssrc);
-  }
+  for (int i = 0; i < 4; ++i)
+    dma16s(reinterpret_cast<f16x8*>(sfbuf + 1024 * (4 * wave + i)), op.bsf + op.sf_step[i], off);
 }
 
 // Direct loads of the 8 tail scale bytes of every tile row (dword d of the
 // area holds half d & 1 of row d >> 1); row_of maps a tile row to its scale
-// row offset.
+// row offset (plain layout: a K with a tail is never row-paired).
 template <class RowOf>
 __device__ __forceinline__ void sk_load_sf_tail(uint8_t* sftail, const SkOperands& op, int nfull, int wave,
                                                 int lane, RowOf row_of) {
@@ -150,7 +156,7 @@ __device__ __forceinline__ void sk_load_sf_tail(uint8_t* sftail, const SkOperand
   for (int i = 0; i < 2; ++i) {
     const int d = 256 * i + 64 * wave + lane;
     dma4(reinterpret_cast<uint32_t*>(sftail + 1024 * i + 256 * wave),
-         op.bsf + row_of(d >> 1) + 16 * nfull + 4 * (d & 1));
+         op.bsf + row_of(d >> 1) + 16 * (op.sf_ss0 + nfull) + 4 * (d & 1));
   }
 }
 
@@ -302,7 +308,8 @@ __device__ __forceinline__ uint32_t sk_a_base(uint32_t arow, int64_t K, int lane
 // Weight and scale sources of this lane for a tile (a_base is set by the
 // main loop); wrow(tr) gives the global weight row of tile row tr.
 template <class WRow>
-__device__ __forceinline__ void sk_operands(SkOperands& op, int64_t K, int wave, int lane, int nrows, WRow wrow) {
+__device__ __forceinline__ void sk_operands(SkOperands& op, int64_t K, int wave, int lane, int nrows, bool sf_pair,
+                                            WRow wrow) {
   const int b0 = wrow(64 * wave + (lane & 15));
   op.bq_row = (uint32_t)b0 * (uint32_t)(K / 2) + 16u * (uint32_t)(lane >> 4);
 #pragma unroll
@@ -312,8 +319,13 @@ __device__ __forceinline__ void sk_operands(SkOperands& op, int64_t K, int wave,
   // the weight rows of tile rows 64 wave + 16 i + r (r < 16) lie the same
   // number of rows after that of 64 wave + r for every r (plain order: 16 i;
   // the L1 gate/up order: 32 (i & 1) + 8 (i >> 1)), so the steps are scalars
+  // row-paired scales: pair w0 / 2 starts at (w0 & ~1) K / 16 and row w0's
+  // half of each line at + 64 (w0 & 1); the rows 16 i after w0 have its
+  // parity, so the steps below are the same in both layouts
   const int w0 = wrow(64 * wave + (lane >> 2));
-  op.sf_dma = (uint32_t)w0 * (uint32_t)(K / 16);
+  op.sf_dma = sf_pair ? (uint32_t)(w0 & ~1) * (uint32_t)(K / 16) + 64u * (uint32_t)(w0 & 1)
+                      : (uint32_t)w0 * (uint32_t)(K / 16);
+  op.sf_pair = sf_pair;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     op.sf_step[i] = (uint32_t)__builtin_amdgcn_readfirstlane((wrow(64 * wave + 16 * i + (lane >> 2)) - w0) * (int)(K / 16));
@@ -467,7 +479,8 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
   // a piece starts at super-step ss0: the row offsets stay, the bases move
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16) + (size_t)wk.ss0 * (kSkSteps * kStepK * 2);
   op.bq = p.w_q + (int64_t)t.expert * p.N2 * (p.K / 2) + (size_t)wk.ss0 * (kSkSteps * kStepK / 2);
-  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N2 * (p.K / 16);  // the piece's scales: sf_ss0
+  op.sf_ss0 = (uint32_t)wk.ss0;
   // what the epilogue reads from memory, loaded as raw values beside the A
   // rows (used only there, so nothing waits for them before): the pair of
   // tile row tid, alpha's factors, the output scale -- each would otherwise
@@ -478,7 +491,7 @@ __global__ __launch_bounds__(kSkThreads, 3) void l1_skinny_kernel(L1Params p, Sk
   const float out_gs = p.c_q ? p.out_gs[0] : 1.0f;
   const int R = 8 * wave + (lane >> 3);
   const int o = out_row_of(R);  // the A row's pair, used once the weights' first loads are out
-  sk_operands(op, p.K, wave, lane, t.nrows, wrow);
+  sk_operands(op, p.K, wave, lane, t.nrows, p.sf_paired != 0, wrow);
   f32x4 acc[2][4];
   sk_mainloop(L, op, wk.nk, acc, sf_row,
               [&] { return sk_a_base(p.perm ? (uint32_t)(o / p.topk) : (uint32_t)o, p.K, lane, R); }, [] {});
@@ -571,10 +584,11 @@ __global__ __launch_bounds__(kSkThreads, 3) void l2_skinny_kernel(L2Params p, Sk
   SkOperands op;
   op.a = reinterpret_cast<const uint8_t*>(p.a_f16) + (size_t)wk.ss0 * (kSkSteps * kStepK * 2);
   op.bq = p.w_q + (int64_t)t.expert * p.N * (p.K / 2) + (size_t)wk.ss0 * (kSkSteps * kStepK / 2);
-  op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16) + (size_t)wk.ss0 * (kSkSteps * kStepK / 16);
+  op.bsf = p.w_sf + (int64_t)t.expert * p.N * (p.K / 16);  // the piece's scales: sf_ss0
+  op.sf_ss0 = (uint32_t)wk.ss0;
   const int R = 8 * wave + (lane >> 3);
   const int a_pair = pair_of(R);  // used once the weights' first loads are out
-  sk_operands(op, p.K, wave, lane, t.nrows, wrow);
+  sk_operands(op, p.K, wave, lane, t.nrows, p.sf_paired != 0, wrow);
   // what the epilogue reads from memory, loaded as raw values with the first
   // operands (used only there): the pair of tile row tid (read beside the A
   // rows), alpha's factors, and, once the first operands are on their way,
@@ -659,12 +673,14 @@ hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
                             const int* perm, int topk, hipStream_t s, uint16_t* c_il, const uint8_t* a_q,
-                            const uint8_t* a_sf, float* split_ws, int* split_cnt) {
+                            const uint8_t* a_sf, float* split_ws, int* split_cnt, bool sf_paired) {
   (void)a_q;
   (void)a_sf;
   if (!a_f16) return hipErrorInvalidValue;  // the 32-row tiles take f16 activations only
+  if (sf_paired && K % 1024 != 0) return hipErrorInvalidValue;
   L1Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N2, out_gs, c_bf16, c_q, c_sf, c_f16, c_il,
              tiles, ntiles, M, perm, topk, (int)(N2 / kTileN)};
+  p.sf_paired = sf_paired ? 1 : 0;
   const int64_t W = (int64_t)max_tiles * p.n_ntiles;
   if (W == 0) return hipSuccess;
   if (!skinny_supports_k(K)) return hipErrorInvalidValue;
@@ -678,10 +694,12 @@ hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
                             const int* perm, hipStream_t s, int64_t M, uint16_t* o_bf16, int* sched,
-                            uint16_t* o_f16, int8_t* o_exp, float* split_ws, int* split_cnt) {
+                            uint16_t* o_f16, int8_t* o_exp, float* split_ws, int* split_cnt, bool sf_paired) {
   (void)sched;  // one workgroup per item (or piece) here
+  if (sf_paired && K % 1024 != 0) return hipErrorInvalidValue;
   L2Params p{a_f16, a_gs, K, w_q, w_sf, w_gs, N, row_w, o, o_bf16, tiles, ntiles, M, perm, (int)(N / kTileN),
              nullptr, o_f16, o_exp};
+  p.sf_paired = sf_paired ? 1 : 0;
   const int64_t W = (int64_t)max_tiles * p.n_ntiles;
   if (W == 0) return hipSuccess;
   if (!skinny_supports_k(K)) return hipErrorInvalidValue;

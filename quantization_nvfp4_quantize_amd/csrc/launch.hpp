@@ -43,6 +43,8 @@ hipError_t launch_quantize_interleaved(const uint16_t* x_il, int64_t rows, int64
 // NVFP4 (n values) -> exact f16 of e2m1 * block scale
 hipError_t launch_dequantize_f16(const uint8_t* q, const uint8_t* sf, int64_t n, uint16_t* out,
                                  hipStream_t s);
+// sf [R][C] -> its row-paired layout (nvfp4_pair_scales); R even, C % 64 == 0.
+hipError_t launch_pair_scales(const uint8_t* sf, int64_t R, int64_t C, uint8_t* out, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* q, const uint8_t* sf, const float* gs, int64_t n,
                              bool bf16_out, void* out, hipStream_t s);
 
@@ -83,20 +85,22 @@ size_t route_lds_bytes(int E);
 // split_ws (skinny_split_bytes(), 16-byte aligned) and split_cnt
 // (skinny_split_counters() ints, zero at launch and zero again after it) the
 // few items that would run alone at the end of the launch are split along K.
-// Two launches that share these buffers must not overlap.
+// Two launches that share these buffers must not overlap.  sf_paired: w_sf
+// is in the row-paired layout of nvfp4_pair_scales (K % 1024 == 0, else
+// hipErrorInvalidValue).
 hipError_t launch_l1_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N2, const float* out_gs,
                             uint16_t* c_bf16, uint8_t* c_q, uint8_t* c_sf, uint16_t* c_f16,
                             const GemmTile* tiles, const int* ntiles, int max_tiles, int64_t M,
                             const int* perm, int topk, hipStream_t s, uint16_t* c_il = nullptr,
                             const uint8_t* a_q = nullptr, const uint8_t* a_sf = nullptr,
-                            float* split_ws = nullptr, int* split_cnt = nullptr);
+                            float* split_ws = nullptr, int* split_cnt = nullptr, bool sf_paired = false);
 hipError_t launch_l2_skinny(const uint16_t* a_f16, const float* a_gs, int64_t K, const uint8_t* w_q,
                             const uint8_t* w_sf, const float* w_gs, int64_t N, const float* row_w,
                             float* o, const GemmTile* tiles, const int* ntiles, int max_tiles,
                             const int* perm, hipStream_t s, int64_t M = 0, uint16_t* o_bf16 = nullptr, int* sched = nullptr,
                             uint16_t* o_f16 = nullptr, int8_t* o_exp = nullptr, float* split_ws = nullptr,
-                            int* split_cnt = nullptr);
+                            int* split_cnt = nullptr, bool sf_paired = false);
 size_t skinny_split_bytes();
 constexpr int skinny_split_counters() { return 8 * 16; }
 // Work counters that launch_route zeroes: [0, 16) those of the 256-row

@@ -9,6 +9,8 @@
 // stores 256 consecutive bytes), the even lane of a pair stores the scale.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -304,6 +306,31 @@ hipError_t launch_dequantize_f16(const uint8_t* q, const uint8_t* sf, int64_t n,
   if (wg > 65536) wg = 65536;
   dequantize_f16_kernel<<<(unsigned)wg, kQThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(q), sf,
                                                             n8, reinterpret_cast<f16x8*>(out));
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ paired scale rows
+// The row-paired layout of a block-scale matrix [R][C] (R even, C % 64 == 0):
+// byte c of row r goes to (r / 2) 2C + 128 (c / 64) + 64 (r % 2) + c % 64, so
+// each 128-byte line holds 64 bytes of rows 2j and 2j + 1, the form in which
+// the 32-row GEMMs load a tile's scales in whole lines.  One 16-byte chunk
+// per thread (all offsets below in chunks).
+__global__ __launch_bounds__(256) void pair_scales_kernel(const uint4* __restrict__ sf, int64_t R, int64_t c16,
+                                                          uint4* __restrict__ out) {
+  const int64_t n = R * c16;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / c16, cc = i - r * c16;
+    out[(r >> 1) * (2 * c16) + 8 * (cc >> 2) + 4 * (r & 1) + (cc & 3)] = sf[i];
+  }
+}
+
+hipError_t launch_pair_scales(const uint8_t* sf, int64_t R, int64_t C, uint8_t* out, hipStream_t s) {
+  const int64_t n = R * (C / 16);
+  if (n == 0) return hipSuccess;
+  if ((R & 1) || C % 64 != 0) return hipErrorInvalidValue;
+  const int64_t wg = std::min<int64_t>((n + 255) / 256, 65536);
+  pair_scales_kernel<<<(unsigned)wg, 256, 0, s>>>(reinterpret_cast<const uint4*>(sf), R, C / 16,
+                                                   reinterpret_cast<uint4*>(out));
   return hipGetLastError();
 }
 

@@ -71,6 +71,20 @@ def test_dequantize_rejects(lib):
     assert lib.nvfp4_dequantize(None, FAKE, FAKE, 4, 16, 0, FAKE, None) == -1
 
 
+def test_pair_scales_rejects(lib):
+    # odd row count, a row length that is not a multiple of 64, null,
+    # misaligned, overlapping: all rejected before any launch; nothing to do
+    # for zero rows
+    assert lib.nvfp4_pair_scales(FAKE, 3, 64, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.nvfp4_pair_scales(FAKE, 4, 48, ctypes.c_void_p(0x20000), None) == -1
+    assert b"C % 64" in lib.nvfp4_last_error()
+    assert lib.nvfp4_pair_scales(None, 4, 64, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.nvfp4_pair_scales(ctypes.c_void_p(0x10008), 4, 64, ctypes.c_void_p(0x20000), None) == -1
+    assert lib.nvfp4_pair_scales(FAKE, 4, 64, ctypes.c_void_p(0x10000 + 128), None) == -1
+    assert b"overlap" in lib.nvfp4_last_error()
+    assert lib.nvfp4_pair_scales(None, 0, 64, None, None) == 0
+
+
 def test_gemm_stage_rejects(lib):
     # K not a multiple of 64, N2 not a multiple of 256, negative M
     assert lib.nvfp4_gemm_swiglu_quant(FAKE, FAKE, FAKE, 4, 48, FAKE, FAKE, FAKE, 256, FAKE, None,
@@ -123,6 +137,9 @@ def test_moe_rejects(lib):
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(out_dtype=3)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w2_gs=None)), FAKE, 1 << 30, None) == -1
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(x=0x10008)), FAKE, 1 << 30, None) == -1
+    # row-paired weight scales are read 16 bytes at a time
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w1_sf_paired=0x10004)), FAKE, 1 << 30, None) == -1
+    assert lib.moe_expert_ffn_nvfp4(by(_moe_args(w2_sf_paired=0x10008)), FAKE, 1 << 30, None) == -1
     # GEMM tiling: 0 (automatic), 32, 256 or 288 (mixed) only
     assert lib.moe_expert_ffn_nvfp4(by(_moe_args(tile_rows=64)), FAKE, 1 << 30, None) == -1
     assert b"tile_rows" in lib.nvfp4_last_error()

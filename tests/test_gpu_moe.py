@@ -33,14 +33,20 @@ TILES = [32, 256, 288]
 
 
 def _gpu_moe(nv, cfg, w, x_bits, ids, wts, out_dtype=torch.float32, tile_rows=0, dynamic=False,
-             l1_unfused=False):
+             l1_unfused=False, paired=False):
     x = dev_bf16(x_bits)
     ti = torch.from_numpy(np.ascontiguousarray(ids, np.int32)).cuda()
     tw = torch.from_numpy(np.ascontiguousarray(wts, np.float32)).cuda()
     a2 = None if dynamic else dev_f32(cfg.a2_gs)
+    # paired: the 32-row tiles read row-paired copies of the weight scales
+    ps = {}
+    if paired and cfg.H % 1024 == 0:
+        ps["w1_sf_paired"] = nv.pair_scales(w["w1sf"])
+    if paired and cfg.I % 1024 == 0:
+        ps["w2_sf_paired"] = nv.pair_scales(w["w2sf"])
     y, dbg = nv.moe_expert_ffn(x, ti, tw, w["w1q"], w["w1sf"], w["w1gs"], w["w2q"], w["w2sf"],
                                w["w2gs"], a2, out_dtype=out_dtype, debug=True,
-                               tile_rows=tile_rows, l1_unfused=l1_unfused)
+                               tile_rows=tile_rows, l1_unfused=l1_unfused, **ps)
     torch.cuda.synchronize()
     return y, dbg
 
@@ -488,6 +494,11 @@ def test_moe_decode_config_sampled(nv, orc, tile_rows):
     res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, y, dbg, ref=ref)
     print("decode: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
     _gate(*res[:4])
+    # the same layer with the row-paired weight scales on its 32-row tiles
+    # (H and I multiples of 1024; the L1's split pieces start 7, 14 and 21
+    # super-steps in, inside a scale line): the same bytes
+    yp, dbgp = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=tile_rows, paired=True)
+    _assert_same(y, dbg, yp, dbgp)
 
 
 @pytest.mark.timeout(900)
@@ -510,11 +521,63 @@ def test_moe_prefill_config_sampled(nv, orc):
     print(f"prefill ({tokens.size} tokens: {info['short'].size} on short tiles, {info['edge'].size} at "
           "256-row edges): y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
     _gate(*res[:4])
-    del dbg
+    # row-paired weight scales on the short tiles: the same bytes
+    yp, dbgp = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=288, paired=True)
+    _assert_same(y, dbg, yp, dbgp)
+    del dbg, dbgp
     # the bench's configuration (automatic tiling, bf16 output through f16
     # pair rows) matches this fp32-output run on every token
     yb, _ = _gpu_moe(nv, cfg, w, x, ids, wts, out_dtype=torch.bfloat16)
     print("prefill bf16 output vs the fp32-output run: rel_fro %.3e" % _check_bf16_vs_fp32(yb, y))
+
+
+def _assert_same(y, dbg, yb, dbgb):
+    """Bit-identical outputs and L1 intermediates of two runs."""
+    assert np.array_equal(host(y).view(np.uint32), host(yb).view(np.uint32))
+    assert np.array_equal(host_bits(dbg["l1_c"]), host_bits(dbgb["l1_c"]))
+    for key in ("l1_q", "l1_sf", "xq", "xsf"):
+        assert np.array_equal(host(dbg[key]), host(dbgb[key])), key
+
+
+@pytest.mark.parametrize("H,I", [(1024, 3072), (3072, 1024)])
+def test_moe_paired_scales_split(nv, orc, H, I):
+    """Row-paired weight scales (nvfp4_pair_scales) on the 32-row tiles,
+    where the launch's last items are split along K into two pieces of 6
+    super-steps, the second starting inside a 128-byte scale line (I 3072:
+    the L2's items; H 3072: the L1's): the same bytes as with the plain
+    scales, and against the oracle."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, T=40, H=H, I=I, E=4, name=f"pair{H}x{I}", a2_gs=4.0 / 2688.0)
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=32)
+    yp, dbgp = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=32, paired=True)
+    _assert_same(y, dbg, yp, dbgp)
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, np.arange(cfg.T), yp, dbgp)
+    print(f"paired H{H} I{I}: y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | sf flips %.2e" % res)
+    _gate(*res[:4])
+
+
+def test_moe_paired_scales_mixed(nv, orc):
+    """The mixed tiling with row-paired scales: its short tiles read them,
+    its 256-row tiles the plain ones; the same bytes as with the plain scales
+    alone, and against the oracle on tokens of every short tile."""
+    import dataclasses
+    from moe_util import boundary_tokens
+    cfg = dataclasses.replace(synth.TINY, T=1100, H=1024, I=1024, E=8, name="pairmixed", a2_gs=4.0 / 2688.0)
+    w = gpu_weights(nv, cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, dbg = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=288)
+    yp, dbgp = _gpu_moe(nv, cfg, w, x, ids, wts, tile_rows=288, paired=True)
+    _assert_same(y, dbg, yp, dbgp)
+    tokens, info = boundary_tokens(ids, cfg.E, cfg.topk, n_edge_experts=2, extra=(0, cfg.T - 1))
+    assert info["short"].size > 0
+    res = _check_tokens(nv, orc, cfg, w, x, ids, wts, tokens, yp, dbgp)
+    print(f"paired mixed ({tokens.size} tokens): y rel_fro %.3e cos %.7f | c rel_fro %.3e cos %.7f | "
+          "sf flips %.2e" % res)
+    _gate(*res[:4])
 
 
 def test_moe_empty(nv):

@@ -302,3 +302,24 @@ def test_e4m3_encoder_dense_bf16_maxima(nv, orc, g):
     bits = synth.bf16_bits(blocks)
     bits[:, 0] = v
     _check(nv, orc, bits.reshape(-1, 128), g=g, what=f"dense maxima, g={g}")
+
+
+@pytest.mark.parametrize("E,R,C", [(1, 2, 64), (3, 4, 128), (2, 256, 448), (1, 0, 64)])
+def test_pair_scales_layout(nv, E, R, C):
+    """nvfp4_pair_scales moves byte c of row r to (r / 2) 2C + 128 (c / 64) +
+    64 (r % 2) + c % 64 (the rows of all matrices taken in order): checked
+    byte for byte against that formula applied with numpy, the layout's
+    definition (a forward-mapping roundtrip, like the pages' scale-factor
+    remap verifier in DEBUG_LOG.md, "Current State")."""
+    rng = np.random.default_rng(1000 * E + R + C)
+    sf = rng.integers(0, 256, size=(E, R, C), dtype=np.uint8)
+    out = host(nv.pair_scales(torch.from_numpy(sf).cuda()))
+    torch.cuda.synchronize()
+    flat = sf.reshape(-1, C)
+    r = np.arange(flat.shape[0])[:, None]
+    c = np.arange(C)[None, :]
+    idx = (r // 2) * 2 * C + 128 * (c // 64) + 64 * (r % 2) + c % 64
+    ref = np.zeros(flat.size, np.uint8)
+    ref[idx.ravel()] = flat.ravel()
+    assert np.unique(idx).size == flat.size  # a permutation
+    assert np.array_equal(out.reshape(-1), ref)
